@@ -1,0 +1,132 @@
+"""Seeded synthetic anisotropic operands (inputs only; none of the method's
+arithmetic lives here, so both the HIP path and the CPU oracle may use it).
+
+The Metis notes page (研究背景与动机) reports that under 3% of the singular
+values dominate the spectrum: 0.63% for weights, 3.15% for activations and
+2.91% for gradients.  An r x c operand is built as
+
+    M = U diag(sigma) V^T + 0.01 N(0, 1)
+
+with rho = min(r, c), n_dom = ceil(frac * rho) dominant values
+sigma_i = 10**(1 + u_i), u_i ~ U[0, 1) sorted descending, a tail
+sigma_i = i**-0.5 (global 1-based index i > n_dom), and U (r x rho), V (c x rho)
+Haar-distributed (Q of the QR of a Gaussian, columns signed so diag(R) > 0).
+The sum is formed in float32 or wider and rounded once to the target dtype.
+
+Generator seeds: 1000 * config + 10 * operand + step (operand W=1, X=2, D=3).
+"""
+
+import math
+
+import torch
+
+FRAC_W = 0.0063
+FRAC_X = 0.0315
+FRAC_D = 0.0291
+OPERAND_ID = {"W": 1, "X": 2, "D": 3}
+
+
+def gen_seed(config, operand, step=0):
+    return 1000 * config + 10 * OPERAND_ID[operand] + step
+
+
+def n_dominant(rows, cols, frac):
+    # small epsilon guards against binary rounding of frac * rho
+    return int(math.ceil(frac * min(rows, cols) - 1e-9))
+
+
+def spectrum(rho, n_dom, gen, dtype=torch.float64):
+    """Dominant log-uniform values in [10, 100) then the i**-0.5 tail."""
+    u = torch.rand(n_dom, generator=gen, dtype=torch.float64, device=gen.device)
+    dom = torch.sort(10.0 ** (1.0 + u), descending=True).values
+    i = torch.arange(n_dom + 1, rho + 1, dtype=torch.float64, device=gen.device)
+    return torch.cat([dom, i ** -0.5]).to(dtype)
+
+
+def haar(rows, cols, gen, dtype=torch.float32):
+    """rows x cols matrix with Haar-distributed orthonormal columns."""
+    g = torch.randn(rows, cols, generator=gen, dtype=dtype, device=gen.device)
+    q, r = torch.linalg.qr(g, mode="reduced")
+    d = torch.sign(torch.diagonal(r))
+    d[d == 0] = 1
+    return q * d
+
+
+def _generator(seed, device):
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    return gen
+
+
+def anisotropic(rows, cols, frac, seed, out_dtype=torch.bfloat16, device="cpu",
+                work_dtype=None, noise=0.01, return_parts=False, v=None):
+    """One operand as described in the module docstring.
+
+    ``v`` may supply the right singular basis (cols x rho) to reuse a subspace
+    across steps.  With ``return_parts`` the float work-precision (U, sigma,
+    V) are returned too."""
+    if work_dtype is None:
+        work_dtype = torch.float64 if str(device) == "cpu" else torch.float32
+    gen = _generator(seed, device)
+    rho = min(rows, cols)
+    n_dom = n_dominant(rows, cols, frac)
+    sigma = spectrum(rho, n_dom, gen, work_dtype)
+    u = haar(rows, rho, gen, work_dtype)
+    if v is None:
+        v = haar(cols, rho, gen, work_dtype)
+    m = (u * sigma) @ v.T.to(work_dtype)
+    m += noise * torch.randn(rows, cols, generator=gen, dtype=work_dtype, device=device)
+    out = m.to(out_dtype)
+    if return_parts:
+        return out, (u, sigma, v, n_dom)
+    return out
+
+
+def rotate_dominant(v, n_dom, theta):
+    """Rotate each dominant right vector v_i in the plane (v_i, v_{n_dom+i})
+    by angle theta; the partner turns the other way so V stays orthonormal."""
+    v = v.clone()
+    a = v[:, :n_dom].clone()
+    b = v[:, n_dom:2 * n_dom].clone()
+    c, s = math.cos(theta), math.sin(theta)
+    v[:, :n_dom] = c * a + s * b
+    v[:, n_dom:2 * n_dom] = -s * a + c * b
+    return v
+
+
+def drift_weight(w_master, seed, scale=1e-3):
+    """W_{t+1} = W_t + scale * ||W_t||_F / sqrt(numel) * N(0, 1) (float master)."""
+    gen = _generator(seed, w_master.device)
+    step = scale * torch.linalg.norm(w_master) / math.sqrt(w_master.numel())
+    return w_master + step * torch.randn(w_master.shape, generator=gen,
+                                         dtype=w_master.dtype, device=w_master.device)
+
+
+# ---------------------------------------------------------------- configs ---
+
+C0 = dict(name="c0_fwd_256x512", X=(256, 512), W=(512, 512), k=8, s=8, l_k=64,
+          rounding="rne", dtype=torch.float32)
+C1 = dict(name="c1_gpt2_130m_mlp_up", X=(8192, 768), W=(768, 3072), D=(8192, 3072),
+          k=12, s=8, l_k=82, rounding="sr", dtype=torch.bfloat16)
+C2 = dict(name="c2_llama3_8b_q_proj", X=(16384, 4096), W=(4096, 4096), D=(16384, 4096),
+          k=61, s=8, l_k=164, rounding="sr", dtype=torch.bfloat16)
+C3 = dict(name="c3_llama3_8b_mlp_8step", tokens=16384, hidden=4096, ffn=14336,
+          k=61, s=8, l_k=164, refresh=8, rounding="sr", dtype=torch.bfloat16)
+C4 = dict(name="c4_activation_1m_x_4096", X=(1048576, 4096), k=61, s=8, l_k=10486,
+          rounding="sr", dtype=torch.bfloat16)
+CONFIGS = {0: C0, 1: C1, 2: C2, 3: C3, 4: C4}
+FRACS = {"W": FRAC_W, "X": FRAC_X, "D": FRAC_D}
+
+
+def layer_operands(config, device="cpu", step=0):
+    """(X, W, D) of config 0/1/2 (D is None for config 0)."""
+    cfg = CONFIGS[config]
+    out = {}
+    for op in ("X", "W", "D"):
+        if op not in cfg:
+            out[op] = None
+            continue
+        r, c = cfg[op]
+        out[op] = anisotropic(r, c, FRACS[op], gen_seed(config, op, step),
+                              out_dtype=cfg["dtype"], device=device)
+    return out["X"], out["W"], out["D"]

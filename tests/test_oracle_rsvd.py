@@ -1,0 +1,210 @@
+"""Pins of the oracle's spectral split (oracle.rsvd): brute-force SVD on tiny
+inputs, exact rank-k recovery, the decomposition identity of the Metis notes
+page (关键设计 1), the narrow/flat residual it reports, and the factor cache
+(关键设计 3)."""
+
+import math
+
+import numpy as np
+import torch
+
+from oracle import linalg, nvfp4, philox, rsvd, split_gemm
+from spectral_split_quantized_amd import synth
+
+
+def _haar(rng, n, k):
+    q, r = np.linalg.qr(rng.standard_normal((n, k)))
+    return q * np.sign(np.diag(r))
+
+
+def _sin_max(a, b):
+    """sine of the largest principal angle between span(a) and span(b)."""
+    qa = np.linalg.qr(a)[0]
+    qb = np.linalg.qr(b)[0]
+    return float(np.linalg.norm(qb - qa @ (qa.T @ qb), 2))
+
+
+def test_rsvd_matches_brute_force_svd_with_gap():
+    rng = np.random.default_rng(0)
+    r, c, k = 60, 40, 5
+    sig = np.concatenate([[100, 80, 60, 40, 30], np.linspace(0.2, 0.01, 35)])
+    m = (_haar(rng, r, 40) * sig) @ _haar(rng, c, 40).T
+    _, s_bf, v_bf = linalg.jacobi_svd(m)
+    cfg = rsvd.Config(k=k, s=8, l_k=r)
+    v = rsvd.rsvd_sketch(m, cfg, sample_rows=False, tag=philox.make_tag(0, 1, 0), step=0)
+    gap = s_bf[k] / s_bf[k - 1]
+    assert gap < 1e-2
+    assert _sin_max(v, v_bf[:, :k]) <= 10 * gap
+    u, s, v2, _ = rsvd.project_rediag(m, v)
+    assert np.allclose(s, s_bf[:k], rtol=1e-3)
+
+
+def test_exact_rank_k_recovery():
+    rng = np.random.default_rng(1)
+    r, c, k = 96, 64, 6
+    sig = np.array([50.0, 20, 9, 5, 2, 1])
+    m = (_haar(rng, r, k) * sig) @ _haar(rng, c, k).T
+    cfg = rsvd.Config(k=k, s=8, l_k=r)
+    u, s, v, refreshed = rsvd.decompose(m, cfg, False, philox.make_tag(0, 1, 0), 0)
+    assert refreshed
+    mr = rsvd.residual(m, u, s, v)
+    assert np.linalg.norm(mr) / np.linalg.norm(m) <= 1e-12
+    assert np.allclose(s, sig, rtol=1e-12)
+    assert np.abs(u.T @ u - np.eye(k)).max() <= 1e-12
+    assert np.abs(v.T @ v - np.eye(k)).max() <= 1e-12
+
+
+def test_rank_deficient_input_zeroes_extra_columns():
+    rng = np.random.default_rng(2)
+    m = (_haar(rng, 64, 3) * [10.0, 5, 1]) @ _haar(rng, 48, 3).T
+    cfg = rsvd.Config(k=6, s=8, l_k=64)
+    u, s, v, _ = rsvd.decompose(m, cfg, False, 0, 0)
+    assert np.all(s[3:] == 0) and np.all(u[:, 3:] == 0)
+    assert np.linalg.norm(rsvd.residual(m, u, s, v)) <= 1e-12 * np.linalg.norm(m)
+
+
+def test_reconstruction_orthonormality_and_projection_identity():
+    rng = np.random.default_rng(3)
+    m = rng.standard_normal((128, 64)) @ np.diag(np.logspace(1, -1, 64))
+    cfg = rsvd.Config(k=8, s=8, l_k=32)
+    tag = philox.make_tag(0, 2, 0)
+    v0 = rsvd.rsvd_sketch(m, cfg, True, tag, 0)
+    u, s, v, p = rsvd.project_rediag(m, v0)
+    mr = rsvd.residual(m, u, s, v)
+    assert np.linalg.norm(m - ((u * s) @ v.T + mr)) <= 1e-14 * np.linalg.norm(m)
+    assert np.abs(u.T @ u - np.eye(8)).max() <= 1e-12
+    assert np.abs(v.T @ v - np.eye(8)).max() <= 1e-12
+    # U S V^T = M V_old V_old^T
+    assert np.linalg.norm((u * s) @ v.T - m @ v0 @ v0.T) <= 1e-12 * np.linalg.norm(m)
+    assert np.all(np.diff(s) <= 0)
+
+
+def _c0_weight():
+    w = synth.anisotropic(512, 512, synth.FRAC_W, synth.gen_seed(0, "W"),
+                          out_dtype=torch.float32)
+    return w.double().numpy()
+
+
+def test_generator_spectrum():
+    w, (u, sig, v, n_dom) = synth.anisotropic(256, 512, synth.FRAC_X, 5, out_dtype=torch.float64,
+                                               return_parts=True)
+    assert n_dom == 9
+    s = np.linalg.svd(w.numpy(), compute_uv=False)
+    sig = sig.numpy()
+    assert np.all((sig[:n_dom] >= 10) & (sig[:n_dom] < 100))
+    assert np.allclose(sig[n_dom:], np.arange(n_dom + 1, 257) ** -0.5)
+    # noise 0.01 N(0,1) moves the dominant values by at most ~0.01 (sqrt r + sqrt c)
+    assert np.all(np.abs(s[:n_dom] - sig[:n_dom]) < 0.4)
+    assert np.abs(u.T @ u - torch.eye(256, dtype=u.dtype)).max() < 1e-12
+
+
+def test_generator_rotation_angles():
+    # config 3's drift: principal angles between the step-0 and step-t
+    # dominant subspaces equal 0.01 t
+    _, (_, _, v, n_dom) = synth.anisotropic(64, 200, 0.05, 3, out_dtype=torch.float64,
+                                            return_parts=True)
+    for t in (1, 3, 7):
+        vt = synth.rotate_dominant(v, n_dom, 0.01 * t)
+        a = v[:, :n_dom].numpy()
+        b = vt[:, :n_dom].numpy()
+        cosines = np.linalg.svd(a.T @ b, compute_uv=False)
+        assert np.allclose(np.arccos(np.clip(cosines, -1, 1)), 0.01 * t, atol=1e-7)
+        assert np.abs(vt.T @ vt - torch.eye(vt.shape[1], dtype=vt.dtype)).max() < 1e-12
+
+
+def test_residual_narrow_and_flat_where_k_covers_the_dominant_band():
+    w = _c0_weight()
+    cfg = rsvd.Config(k=8, s=8, l_k=512)
+    u, s, v, _ = rsvd.decompose(w, cfg, False, philox.make_tag(0, 1, 0), 0)
+    mr = rsvd.residual(w, u, s, v)
+    assert np.abs(mr).max() / np.abs(w).max() <= 0.1            # 1-2 orders narrower
+    sm = np.linalg.svd(w, compute_uv=False)
+    sr = np.linalg.svd(mr, compute_uv=False)
+    half = int(math.ceil(len(sm) / 2)) - 1
+    assert sm[0] / sm[half] >= 100
+    assert sr[0] / sr[half] <= 10                                 # flat spectrum
+
+
+def test_metis_spectral_distortion_below_direct_nvfp4():
+    """The notes page (研究背景与动机, 关键设计 1) says direct block quantisation
+    drowns the small singular components (spectral distortion) while each
+    Metis sub-distribution is narrow.  Pinned here on the part of the error
+    that lies outside the dominant subspace and on the tail singular values.
+    The total Frobenius error is only reported: FP4 singular vectors carry
+    ~10% relative error, so on these inputs it is not below direct NVFP4."""
+    w = _c0_weight()
+    cfg = rsvd.Config(k=8, s=8, l_k=512)
+    tag = philox.make_tag(0, 1, 0)
+    u, s, v, _ = rsvd.decompose(w, cfg, False, tag, 0)
+    split = split_gemm.quantize_operand(w, u.astype(np.float32), s.astype(np.float32),
+                                        v.astype(np.float32), "rne", 0, tag, 0, axes=(1,))
+    direct = split_gemm.quantize_operand(w, None, None, None, "rne", 0, tag, 0, axes=(1,))
+    mh = split_gemm.dense(split, 1)
+    dh = split_gemm.dense(direct, 1)
+    uu, ss, vt = np.linalg.svd(w)
+    r = 16
+    pu = np.eye(512) - uu[:, :r] @ uu[:, :r].T
+    pv = np.eye(512) - vt[:r].T @ vt[:r]
+    base = np.linalg.norm(pu @ w @ pv)
+    tail_metis = np.linalg.norm(pu @ (mh - w) @ pv) / base
+    tail_direct = np.linalg.norm(pu @ (dh - w) @ pv) / base
+    assert tail_metis < 0.25 * tail_direct
+    sm = np.linalg.svd(mh, compute_uv=False)
+    sd = np.linalg.svd(dh, compute_uv=False)
+    t = slice(r, 512)
+    sv_metis = np.linalg.norm(sm[t] - ss[t]) / np.linalg.norm(ss[t])
+    sv_direct = np.linalg.norm(sd[t] - ss[t]) / np.linalg.norm(ss[t])
+    assert sv_metis < 0.1 * sv_direct
+    e_metis = split_gemm.rel_fro(mh, w)
+    e_direct = split_gemm.rel_fro(dh, w)
+    codes = nvfp4.unpack_codes(direct.r_ax1)
+    zero = (codes & 7) == 0
+    small = np.abs(w) <= np.quantile(np.abs(w), 0.1)
+    print("tail-subspace error metis %.3f direct %.3f; tail sv error metis %.4f direct %.4f; "
+          "total fro metis %.4f direct %.4f; zero codes (direct) all %.3f smallest-decile %.3f"
+          % (tail_metis, tail_direct, sv_metis, sv_direct, e_metis, e_direct,
+             zero.mean(), zero[small].mean()))
+
+
+def test_k0_split_equals_direct_codes():
+    rng = np.random.default_rng(6)
+    m = rng.standard_normal((32, 48)).astype(np.float32)
+    a = split_gemm.quantize_operand(m, None, None, None, "sr", 3, philox.make_tag(1, 2, 0), 2)
+    z = np.zeros((32, 0), np.float32)
+    b = split_gemm.quantize_operand(m, z, np.zeros(0, np.float32), np.zeros((48, 0), np.float32),
+                                    "sr", 3, philox.make_tag(1, 2, 0), 2)
+    assert np.array_equal(a.r_ax0.codes, b.r_ax0.codes) and np.array_equal(a.r_ax1.codes, b.r_ax1.codes)
+    q = nvfp4.quantize(m, 1, "sr", 3, philox.make_tag(1, 2, philox.ROLE_RESID_AX1), 2)
+    assert np.array_equal(a.r_ax1.codes, q.codes) and np.array_equal(a.r_ax1.scales, q.scales)
+
+
+def test_factor_cache_refresh_schedule_and_reuse():
+    rng = np.random.default_rng(7)
+    base = rng.standard_normal((64, 4)) @ rng.standard_normal((4, 32)) * 10
+    cfg = rsvd.Config(k=4, s=4, l_k=16, refresh=8)
+    cache = rsvd.FactorCache()
+    tag = philox.make_tag(0, 2, 0)
+    flags = []
+    for step in range(10):
+        m = base + 0.01 * rng.standard_normal(base.shape)
+        v_before = None if cache.v is None else cache.v.copy()
+        u, s, v, refreshed = rsvd.decompose(m, cfg, True, tag, step, cache)
+        flags.append(refreshed)
+        if not refreshed:
+            # reuse: the product is M V_old V_old^T with the cached basis
+            assert np.linalg.norm((u * s) @ v.T - m @ v_before @ v_before.T) <= 1e-12 * np.linalg.norm(m)
+    assert flags == [True] + [False] * 7 + [True, False]
+
+
+def test_one_percent_sampling_alignment_report():
+    # report only (the pages quote about 0.9 alignment at 1% sampling)
+    x = synth.anisotropic(2048, 256, synth.FRAC_X, 77, out_dtype=torch.float64).numpy()
+    k = 4
+    cfg_full = rsvd.Config(k=k, s=8, l_k=2048)
+    cfg_s = rsvd.Config(k=k, s=8, l_k=21)
+    tag = philox.make_tag(0, 2, 0)
+    v_full = rsvd.rsvd_sketch(x, cfg_full, False, tag, 0)
+    v_s = rsvd.rsvd_sketch(x, cfg_s, True, tag, 0)
+    cos2 = np.linalg.svd(v_full.T @ v_s, compute_uv=False) ** 2
+    print("mean cos^2 of principal angles, 1%% sample vs all rows: %.3f" % cos2.mean())
+    assert 0 <= cos2.mean() <= 1 + 1e-12
