@@ -14,7 +14,7 @@ The pages leave the scale rules open; the readings taken are:
   Q7  y = RN32(|x| * inv); an input of +-0 always gives magnitude 0
   Q8  RNE: nearest grid value, ties to even mantissa, saturate at 6.
       SR: y >= 6 -> 6; otherwise hi iff u < (y - lo) / (hi - lo), with u the
-      element's Philox uniform
+      element's 16-bit Philox uniform (oracle.philox, 16-bit draws)
   Q9  code = sign(x) << 3 | m  (the sign bit of x is kept, also for zeros)
 
 RN32 is one binary32 round-to-nearest-even operation.  Every binary32 operand
@@ -105,7 +105,7 @@ def quantize(x, axis, rounding="rne", seed=0, tag=0, step=0):
         jj = np.arange(cols, dtype=np.uint64)[None, :]
         e = ii * np.uint64(cols) + jj                     # logical index of x
         et = e if axis == 1 else e.T
-        u = philox.uniform_from_words(philox.words(et, seed, tag, step))
+        u = philox.uniform_from_halves(philox.halves(et, seed, tag, step))
         m = formats.e2m1_sr(y, u.reshape(n_outer, K // BLOCK, BLOCK))
     else:
         raise ValueError("rounding must be 'rne' or 'sr'")

@@ -9,9 +9,13 @@ GPU and this oracle consume identical randomness.
 
 Layout (a reading; the pages fix none):
   key     = (seed & 0xffffffff, seed >> 32)
-  counter = (q & 0xffffffff, q >> 32, tag, step), q = e >> 2
-  word    = output word (e & 3) of that block belongs to logical element e
-  uniform = (word >> 8) * 2**-24, exact in binary32
+  counter = (q & 0xffffffff, q >> 32, tag, step)
+  32-bit draws (row sampling): q = e >> 2, element e takes word (e & 3)
+  16-bit draws (stochastic rounding, Omega): q = e >> 3, element e takes
+      16-bit half (e & 1) (low half first) of word ((e >> 1) & 3); the
+      rounding uniform is u = h * 2**-16, exact in binary32.  Sixteen random
+      bits per element keep the probability error of the rounding below
+      2**-16 of a grid step while one block serves eight elements.
 
 Round function (paper, section 3 "Philox"): with multipliers M0, M1 the block
 (c0, c1, c2, c3) becomes (hi(M1*c2) ^ c1 ^ k0, lo(M1*c2), hi(M0*c0) ^ c3 ^ k1,
@@ -109,6 +113,26 @@ def word_scalar(e, seed, tag, step):
     return out[e & 3]
 
 
-def uniform_from_words(w):
-    """u = (w >> 8) * 2**-24 in [0, 1), exact in binary32 (returned as float64)."""
-    return (np.asarray(w, np.uint64) >> np.uint64(8)).astype(np.float64) * 2.0 ** -24
+def halves(elem, seed, tag, step):
+    """16-bit draw of each logical element index (uint64 array -> int64)."""
+    e = np.asarray(elem, np.uint64)
+    q = e >> np.uint64(3)
+    word = ((e >> np.uint64(1)) & np.uint64(3)).astype(np.int64)
+    half = (e & np.uint64(1)).astype(np.uint64)
+    m = np.uint64(MASK32)
+    out = block_vec(q & m, q >> np.uint64(32), np.uint64(tag & MASK32),
+                    np.uint64(step & MASK32), seed & MASK32, (seed >> 32) & MASK32)
+    w = np.take_along_axis(np.stack(out, axis=0), word[None, ...], axis=0)[0]
+    return ((w >> (half * np.uint64(16))) & np.uint64(0xFFFF)).astype(np.int64)
+
+
+def half_scalar(e, seed, tag, step):
+    """Scalar form of :func:`halves` on Python ints."""
+    q = e >> 3
+    out = block((q & MASK32, q >> 32, tag, step), (seed & MASK32, seed >> 32))
+    return (out[(e >> 1) & 3] >> (16 * (e & 1))) & 0xFFFF
+
+
+def uniform_from_halves(h):
+    """u = h * 2**-16 in [0, 1), exact in binary32 (returned as float64)."""
+    return np.asarray(h, np.float64) * 2.0 ** -16

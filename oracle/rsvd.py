@@ -11,7 +11,7 @@ Sources (Metis notes page):
   损失函数/训练策略  rank k = 1.5%, refresh period 8.
 
 Readings where the pages are silent:
-  * Omega_ij = T[w & 0xffff] with w the Philox word of element i*(k+s)+j and
+  * Omega_ij = T[h] with h the 16-bit Philox draw of element i*(k+s)+j and
     T[t] = bf16-RNE(Phi^{-1}((t + 0.5) / 65536)): a quantile-exact discretised
     Gaussian whose values are exact in bf16.
   * Rows are sampled uniformly without replacement: row i gets the Philox
@@ -76,9 +76,8 @@ def omega_table():
 def omega(cols, n, seed, tag, step):
     """Gaussian test matrix Omega (cols x n) for a sketch of width n = k + s."""
     e = np.arange(cols * n, dtype=np.uint64)
-    w = philox.words(e, seed, philox.with_role(tag, philox.ROLE_OMEGA), step)
-    idx = (w & np.uint64(0xFFFF)).astype(np.int64)
-    return omega_table()[idx].reshape(cols, n)
+    h = philox.halves(e, seed, philox.with_role(tag, philox.ROLE_OMEGA), step)
+    return omega_table()[h].reshape(cols, n)
 
 
 def sample_indices(rows, l_k, seed, tag, step):

@@ -35,7 +35,7 @@ def test_bit_balance_and_serial_independence():
     bits = ((w[:, None] >> np.arange(32, dtype=np.uint64)[None, :]) & np.uint64(1)).astype(np.float64)
     frac = bits.mean(axis=0)
     assert np.all(np.abs(frac - 0.5) < 6 * 0.5 / math.sqrt(1 << 16))
-    u = philox.uniform_from_words(w)
+    u = (w >> np.uint64(8)).astype(np.float64) * 2.0 ** -24
     r = np.corrcoef(u[:-1], u[1:])[0, 1]
     assert abs(r) < 6 / math.sqrt(1 << 16)
 
@@ -56,10 +56,22 @@ def test_counter_avalanche():
 
 
 def test_uniform_is_exact_binary32():
-    w = philox.words(np.arange(4096, dtype=np.uint64), 9, 0, 0)
-    u = philox.uniform_from_words(w)
+    h = philox.halves(np.arange(4096, dtype=np.uint64), 9, 0, 0)
+    u = philox.uniform_from_halves(h)
     assert np.all(u.astype(np.float32).astype(np.float64) == u)
     assert u.min() >= 0 and u.max() < 1
+
+
+def test_halves_scalar_vector_and_uniformity():
+    e = np.array([0, 1, 2, 7, 8, 9, 15, 2 ** 35 + 11], dtype=np.uint64)
+    vec = philox.halves(e, 77, 0x21400, 3)
+    assert [int(v) for v in vec] == [philox.half_scalar(int(x), 77, 0x21400, 3) for x in e]
+    h = philox.halves(np.arange(1 << 18, dtype=np.uint64), 2, 0x100, 0)
+    hist = np.bincount(h >> 8, minlength=256)
+    exp = (1 << 18) / 256
+    assert float(np.sum((hist - exp) ** 2 / exp)) < 255 + 6 * 22.6
+    # the two halves of one word are not the same draw
+    assert np.mean(h[0::2] == h[1::2]) < 0.01
 
 
 # ------------------------------------------------------------- Omega table --
