@@ -1,0 +1,191 @@
+/*
+ * metis.h -- C ABI of the MI355X (gfx950) Metis spectral-split NVFP4 GEMM.
+ *
+ * The method is described on the web page "Metis: Training LLMs with FP4
+ * Quantization" (ICLR 2026 reading notes):
+ *   - section 关键设计 1: every GEMM operand M (weight W, activation X, output
+ *     gradient D) is split as M = U_k S_k V_k^T + M_R; the factors and the
+ *     residual are quantised, the singular values stay in high precision, and
+ *     the forward GEMM is
+ *       Y = (Q(A_k) L_k Q(B_k^T) + Q(X_R)) (Q(U_k) S_k Q(V_k^T) + Q(W_R));
+ *   - section 关键设计 2: the dominant subspace is estimated from a sparse
+ *     random row sample and a Gaussian random projection (randomized SVD);
+ *   - section 关键设计 3: the factors are reused across steps (refresh every 8);
+ *   - section 研究背景与动机: NVFP4 = E2M1 values in blocks of 16 with one FP8
+ *     (here E4M3) scale per block; section 损失函数/训练策略: W4A4G4 with
+ *     stochastic rounding, rank 1.5%.
+ *
+ * Conventions shared by every entry point
+ *   Memory.  Every pointer argument except the metis_* descriptor structs and
+ *     the host-only self-test helpers is DEVICE memory owned by the caller.
+ *     The library allocates no device memory in these calls; scratch space is
+ *     the caller's workspace (size from the *_workspace functions, 256-byte
+ *     aligned).  Buffers must stay valid until the enqueued work completes.
+ *   Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
+ *     stream).  Calls only enqueue work and return; they are safe to call from
+ *     several threads on distinct streams with distinct workspaces.
+ *   Layouts.  Matrices are row-major with a leading dimension `ld` (elements).
+ *     A quantised orientation (metis_q4) stores codes[n_outer][k_len/2] with the
+ *     even K index in the low nibble, scales[n_outer][k_len/16] as E4M3 bytes,
+ *     and one binary32 tensor scale.  "K axis" is the reduction axis of the GEMM
+ *     the orientation feeds.
+ *   Errors.  Argument errors are reported synchronously with METIS_E_INVALID
+ *     (nothing is enqueued) and a message from metis_last_error().  Numeric
+ *     failure inside a kernel (non-finite input, a Cholesky breakdown that the
+ *     shift cannot repair) sets a per-device flag that metis_status_sync()
+ *     returns as METIS_E_NUMERIC; outputs are then unspecified.
+ *   Determinism.  Identical inputs, seed, tag and step give bit-identical
+ *     outputs: reductions that feed quantisation use max, never sums in
+ *     varying order.
+ */
+#ifndef METIS_H
+#define METIS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define METIS_ABI_VERSION 1
+
+typedef enum {
+  METIS_OK = 0,
+  METIS_E_INVALID = -1,     /* bad argument or shape; nothing was enqueued */
+  METIS_E_UNSUPPORTED = -2, /* valid but not implemented (e.g. k + s > 96) */
+  METIS_E_HIP = -3,         /* a HIP runtime call failed */
+  METIS_E_NUMERIC = -4,     /* device-side numeric failure (status_sync only) */
+  METIS_E_WORKSPACE = -5    /* workspace too small */
+} metis_status;
+
+typedef enum { METIS_BF16 = 0, METIS_F32 = 1 } metis_dtype;
+typedef enum { METIS_RNE = 0, METIS_SR = 1 } metis_rounding;
+
+/* Operand roles used in the Philox tag: tag = layer << 16 | operand << 12.
+ * The library fills bits 8..11 (the draw's role) itself. */
+enum { METIS_OPERAND_W = 1, METIS_OPERAND_X = 2, METIS_OPERAND_D = 3 };
+
+/* Hyper-parameters (Metis notes page, 关键设计 2/3 and 损失函数/训练策略). */
+typedef struct {
+  int32_t k;        /* rank kept in high precision (1..96) */
+  int32_t s;        /* sketch oversampling; the sketch has k + s columns */
+  int64_t l_k;      /* sampled rows for operands with sample_rows != 0 */
+  int32_t refresh;  /* factor-cache period in steps (>= 1) */
+  int32_t rounding; /* metis_rounding */
+  uint64_t seed;    /* Philox4x32-10 key */
+} metis_config;
+
+/* Factors of one operand (rows x cols).  U: rows x k, S: k (descending),
+ * V: cols x k, all binary32 row-major device buffers owned by the caller.
+ * V doubles as the factor cache: it holds the basis between calls.
+ * refreshed_at is host state: -1 means "no basis yet". */
+typedef struct {
+  float *U;
+  float *S;
+  float *V;
+  int64_t rows, cols;
+  int32_t k;
+  int64_t refreshed_at;
+} metis_factors;
+
+/* One quantised orientation (device buffers owned by the caller). */
+typedef struct {
+  uint8_t *codes;       /* n_outer * k_len / 2 bytes */
+  uint8_t *scales;      /* n_outer * k_len / 16 bytes */
+  float *tensor_scale;  /* 1 binary32 */
+  int64_t n_outer;
+  int64_t k_len;        /* multiple of 16 */
+} metis_q4;
+
+/* A quantised operand M (rows x cols): Q(U) (blocked along rows of U, so
+ * n_outer = k, k_len = rows), S (binary32, not quantised), Q(V) (n_outer = k,
+ * k_len = cols), and the residual along K = rows (R_ax0: n_outer = cols,
+ * k_len = rows) and/or K = cols (R_ax1: n_outer = rows, k_len = cols).
+ * k == 0 is direct NVFP4 (U, V, S unused). */
+typedef struct {
+  int64_t rows, cols;
+  int32_t k;
+  const float *S;
+  metis_q4 U, V, R_ax0, R_ax1;
+} metis_qoperand;
+
+enum { METIS_AXIS0 = 1, METIS_AXIS1 = 2 }; /* bitmask for metis_quantize */
+
+int32_t metis_abi_version(void);
+const char *metis_last_error(void);
+
+/* Workspace sizes in bytes (0 never means "no workspace needed"; always
+ * pass at least the returned size). */
+size_t metis_decompose_workspace(int64_t rows, int64_t cols, const metis_config *cfg,
+                                 int32_t sample_rows);
+size_t metis_quantize_workspace(int64_t rows, int64_t cols, int32_t k);
+size_t metis_gemm_fwd_workspace(const metis_qoperand *X, const metis_qoperand *W);
+size_t metis_gemm_bwd_workspace(const metis_qoperand *D, const metis_qoperand *W,
+                                const metis_qoperand *X);
+
+/* metis_decompose -- spectral split of one operand (关键设计 1-3).
+ * M: rows x cols (dtype metis_dtype, leading dimension ld >= cols).
+ * If f->refreshed_at < 0 or step - f->refreshed_at >= cfg->refresh, a new
+ * basis is sketched: sample l_k rows (sample_rows != 0; weights use all rows),
+ * Y = M_s Omega (Omega: cols x (k+s) quantile-exact bf16 Gaussian), shifted
+ * CholeskyQR3 of Y, B = Q^T M_s, Jacobi on B B^T, V = B^T Z Theta^-1/2.
+ * f->refreshed_at is then set to step (host side, before the call returns).
+ * Every call then projects P = M V, rediagonalises P^T P by Jacobi and writes
+ * U = P R Lambda^-1/2, S = Lambda^1/2, V <- V R, so U S V^T = M V_old V_old^T.
+ * Requires 1 <= k, k + s <= 96 and k + s <= min(l_k (or rows), cols).
+ * tag: layer << 16 | operand << 12 (Omega and the row sample take roles 4, 5). */
+metis_status metis_decompose(const void *M, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                             const metis_config *cfg, int32_t sample_rows, uint32_t tag,
+                             int64_t step, metis_factors *f, void *ws, size_t ws_bytes,
+                             void *stream);
+
+/* metis_quantize -- NVFP4 fake quantisation of an operand (关键设计 1).
+ * With f == NULL the tensor M itself is quantised (direct NVFP4); otherwise
+ * the factors are quantised (U and V blocked along their rows) and the
+ * residual M_R = M - U diag(S) V^T is formed on the fly (never stored) and
+ * quantised along each requested axis (axes: METIS_AXIS0 | METIS_AXIS1).
+ * Quantiser: tensor amax A_T, s_g = A_T/2688, block scale = E4M3(RNE, satfinite)
+ * of a_b/(6 s_g), y = |x| * (1/(s_b s_g)), E2M1 by RNE or Philox stochastic
+ * rounding (16-bit uniform per element).  out->S is set to f->S.
+ * residual_out: optional rows x cols binary32 (ld = cols) copy of the exact
+ * binary32 residual the quantiser consumed (for verification; NULL normally).
+ * Requires K (rows for AXIS0, cols for AXIS1) to be a multiple of 16. */
+metis_status metis_quantize(const void *M, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                            const metis_factors *f, const metis_config *cfg, uint32_t tag,
+                            int64_t step, int32_t axes, metis_qoperand *out, float *residual_out,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/* metis_gemm_fwd -- Y = X-hat W-hat (关键设计 1, the split forward GEMM).
+ * X: l x m with R_ax1 (K = m); W: m x n with R_ax0 (K = m).  Y: l x n
+ * binary32, leading dimension ldy.  Evaluated as
+ *   Y = Q(X_R) Q(W_R) + P' Q(V_W)^T + Q(U_X) G,
+ *   P' = Q(X_R) Q(U_W) S_W,  G = S_X (Q(V_X)^T Q(W_R) + (Q(V_X)^T Q(U_W)) S_W Q(V_W)^T),
+ * which equals the product of the dense dequantised operands. */
+metis_status metis_gemm_fwd(const metis_qoperand *X, const metis_qoperand *W, float *Y, int64_t ldy,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/* metis_gemm_bwd -- dX = D-hat W-hat^T (K = n: D needs R_ax1, W needs R_ax1)
+ * and dW = X-hat^T D-hat (K = l: X needs R_ax0, D needs R_ax0), the same
+ * split embedded in the backward GEMMs (W4A4G4).  dX: l x m, dW: m x n,
+ * binary32.  Either output pointer may be NULL to skip that product. */
+metis_status metis_gemm_bwd(const metis_qoperand *D, const metis_qoperand *W, const metis_qoperand *X,
+                            float *dX, int64_t lddx, float *dW, int64_t lddw, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/* Waits for `stream`, then returns and clears the current device's numeric
+ * failure flag (METIS_OK or METIS_E_NUMERIC). */
+metis_status metis_status_sync(void *stream);
+
+/* Host-only helpers (no GPU needed) exposing the library's own definitions
+ * of its random draws, for verification against an independent model.
+ * metis_omega_table: the 65536 bf16 bit patterns of the Gaussian quantile
+ * table, T[t] = bf16(Phi^-1((t + 0.5) / 65536)).
+ * metis_philox4x32_10: one Philox4x32-10 block (Salmon et al., SC'11). */
+void metis_omega_table(uint16_t *out65536);
+void metis_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* METIS_H */

@@ -90,8 +90,9 @@ def sample_indices(rows, l_k, seed, tag, step):
     return np.sort(order[:l_k]).astype(np.int64)
 
 
-def rsvd_sketch(m, cfg, sample_rows, tag, step):
-    """Right basis V (cols x k) of the dominant subspace from a sketch."""
+def rsvd_sketch(m, cfg, sample_rows, tag, step, return_theta=False):
+    """Right basis V (cols x k) of the dominant subspace from a sketch
+    (and the sketch eigenvalues Theta when ``return_theta``)."""
     m = np.asarray(m, dtype=np.float64)
     r, c = m.shape
     k, n = cfg.k, cfg.k + cfg.s
@@ -113,7 +114,7 @@ def rsvd_sketch(m, cfg, sample_rows, tag, step):
     for j in range(k):
         if top > 0 and theta[j] > EIG_ZERO * top:
             v[:, j] = (b.T @ z[:, j]) / math.sqrt(theta[j])
-    return v
+    return (v, theta) if return_theta else v
 
 
 def project_rediag(m, v):

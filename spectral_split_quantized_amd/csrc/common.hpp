@@ -1,0 +1,193 @@
+// common.hpp -- shared device/host helpers of libmetis (gfx950).
+//
+// Philox4x32-10: Salmon, Moraes, Dror & Shaw, "Parallel Random Numbers: As
+// Easy as 1, 2, 3" (SC'11), section 3.  Draw layout (the Metis pages fix
+// none): key = (seed lo, seed hi), counter = (q lo, q hi, tag, step).
+//   32-bit draws: q = e >> 2, element e takes word e & 3.
+//   16-bit draws: q = e >> 3, element e takes half (e & 1) (low half first) of
+//   word (e >> 1) & 3.  Used for stochastic rounding (u = h * 2^-16) and for
+//   the Gaussian test matrix (Omega = T[h]).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace metis {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr uint32_t kPhiloxM0 = 0xD2511F53u;
+constexpr uint32_t kPhiloxM1 = 0xCD9E8D57u;
+constexpr uint32_t kPhiloxW0 = 0x9E3779B9u;
+constexpr uint32_t kPhiloxW1 = 0xBB67AE85u;
+
+// Draw roles, bits 8..11 of the tag.
+enum : uint32_t {
+  kRoleResidAx0 = 0,
+  kRoleResidAx1 = 1,
+  kRoleU = 2,
+  kRoleV = 3,
+  kRoleOmega = 4,
+  kRoleSample = 5
+};
+
+__host__ __device__ inline uint32_t tag_with_role(uint32_t tag, uint32_t role) {
+  return (tag & ~0xF00u) | ((role & 0xFu) << 8);
+}
+
+struct Philox4 {
+  uint32_t v[4];
+};
+
+__host__ __device__ inline Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                 uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)kPhiloxM0 * c0;
+    const uint64_t p1 = (uint64_t)kPhiloxM1 * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += kPhiloxW0;
+    k1 += kPhiloxW1;
+  }
+  Philox4 out;
+  out.v[0] = c0;
+  out.v[1] = c1;
+  out.v[2] = c2;
+  out.v[3] = c3;
+  return out;
+}
+
+__host__ __device__ inline Philox4 philox_block(uint64_t q, uint32_t tag, uint32_t step,
+                                                uint64_t seed) {
+  return philox4x32_10((uint32_t)q, (uint32_t)(q >> 32), tag, step, (uint32_t)seed,
+                       (uint32_t)(seed >> 32));
+}
+
+// 32-bit draw of element e.
+__host__ __device__ inline uint32_t philox_word(uint64_t e, uint32_t tag, uint32_t step,
+                                                uint64_t seed) {
+  const Philox4 b = philox_block(e >> 2, tag, step, seed);
+  return b.v[e & 3];
+}
+
+// 16-bit half of a block for element offset o = e & 7.
+__host__ __device__ inline uint32_t philox_half_of(const Philox4& b, uint32_t o) {
+  return (b.v[(o >> 1) & 3] >> ((o & 1) * 16)) & 0xFFFFu;
+}
+
+// ----------------------------------------------------------------- formats --
+
+// E4M3 ("FN": bias 7, max 448) value of a non-negative byte, exact in fp32.
+__host__ __device__ inline float e4m3_decode(uint32_t b) {
+  const int e = (int)((b >> 3) & 0xF);
+  const int m = (int)(b & 7);
+  if (e == 0) return ldexpf((float)m, -9);
+  return ldexpf((float)(8 + m), e - 10);
+}
+
+// Round-to-nearest-even E4M3 byte of t >= 0, saturating at 448 (0x7E).
+// Every step is exact in binary32: scalings by powers of two, 2f - 1 with
+// f in [0.5, 1), and rintf (round half to even).
+__host__ __device__ inline uint32_t e4m3_encode_rne_sat(float t) {
+  if (!(t < 448.0f)) return 0x7Eu;          // also +inf (NaN never reaches here)
+  if (t < 0.015625f) {                      // below 2^-6: subnormal grid 2^-9
+    const float q = rintf(t * 512.0f);      // 0..8; 8 encodes 2^-6 = 0x08
+    return (uint32_t)q;
+  }
+  int ex;
+  const float f = frexpf(t, &ex);           // t = f 2^ex, f in [0.5, 1)
+  int e = ex - 1;                           // t = (2f) 2^e
+  int mq = (int)rintf((2.0f * f - 1.0f) * 8.0f);
+  if (mq == 8) {
+    mq = 0;
+    e += 1;
+  }
+  if (e > 8 || (e == 8 && mq == 7)) return 0x7Eu;
+  return (uint32_t)(((e + 7) << 3) | mq);
+}
+
+// E2M1 magnitude index of y >= 0, nearest with ties to the even mantissa,
+// saturating at 6 (index 7).
+__host__ __device__ inline uint32_t e2m1_rne(float y) {
+  if (y <= 0.25f) return 0;
+  if (y < 0.75f) return 1;
+  if (y <= 1.25f) return 2;
+  if (y < 1.75f) return 3;
+  if (y <= 2.5f) return 4;
+  if (y < 3.5f) return 5;
+  if (y <= 5.0f) return 6;
+  return 7;
+}
+
+// Stochastic E2M1 rounding of y >= 0 with a 16-bit draw h (u = h 2^-16):
+// hi iff u < (y - lo) / (hi - lo); the quotient is exact (power-of-two step).
+__host__ __device__ inline uint32_t e2m1_sr(float y, uint32_t h) {
+  if (!(y < 6.0f)) return 7;
+  uint32_t lo;
+  float glo, inv_step;
+  if (y < 0.5f) { lo = 0; glo = 0.0f; inv_step = 2.0f; }
+  else if (y < 1.0f) { lo = 1; glo = 0.5f; inv_step = 2.0f; }
+  else if (y < 1.5f) { lo = 2; glo = 1.0f; inv_step = 2.0f; }
+  else if (y < 2.0f) { lo = 3; glo = 1.5f; inv_step = 2.0f; }
+  else if (y < 3.0f) { lo = 4; glo = 2.0f; inv_step = 1.0f; }
+  else if (y < 4.0f) { lo = 5; glo = 3.0f; inv_step = 1.0f; }
+  else { lo = 6; glo = 4.0f; inv_step = 0.5f; }
+  const float p = (y - glo) * inv_step;
+  const float u = (float)h * (1.0f / 65536.0f);
+  return (u < p) ? lo + 1 : lo;
+}
+
+// ----------------------------------------------------------- status flag --
+
+// Per-device numeric failure flag (bit 0: non-finite input, bit 1: Cholesky
+// breakdown, bit 2: row-sample selection overflow).
+__device__ int g_metis_status;
+
+__device__ inline void raise_status(int bits) { atomicOr(&g_metis_status, bits); }
+
+constexpr int kStatusNonFinite = 1;
+constexpr int kStatusCholesky = 2;
+constexpr int kStatusSample = 4;
+
+// ------------------------------------------------------------------- misc --
+
+template <typename T>
+__host__ __device__ inline T ceil_div(T a, T b) {
+  return (a + b - 1) / b;
+}
+
+__device__ inline float load_as_float(const void* p, int dtype, int64_t idx) {
+  if (dtype == 0) {
+    const uint16_t b = ((const uint16_t*)p)[idx];
+    return __uint_as_float((uint32_t)b << 16);
+  }
+  return ((const float*)p)[idx];
+}
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ inline double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+}  // namespace metis

@@ -1,0 +1,711 @@
+// metis.hip -- host side of libmetis: the C ABI declared in include/metis.h.
+//
+// Argument validation is synchronous; all work is enqueued on the caller's
+// stream; scratch memory is carved from the caller's workspace.  The only
+// device state the library owns is a per-device numeric status word and the
+// Gaussian quantile table, both static __device__ arrays.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+
+#include "../../include/metis.h"
+#include "common.hpp"
+#include "gemm.hpp"
+#include "quant.hpp"
+#include "rsvd.hpp"
+
+using namespace metis;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+metis_status fail(metis_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+#define HIP_TRY(expr)                                                                     \
+  do {                                                                                    \
+    hipError_t e__ = (expr);                                                              \
+    if (e__ != hipSuccess) return fail(METIS_E_HIP, "%s: %s", #expr, hipGetErrorString(e__)); \
+  } while (0)
+
+#define LAUNCH_CHECK()                                                                    \
+  do {                                                                                    \
+    hipError_t e__ = hipGetLastError();                                                   \
+    if (e__ != hipSuccess) return fail(METIS_E_HIP, "kernel launch: %s", hipGetErrorString(e__)); \
+  } while (0)
+
+// ------------------------------------------------------- Omega quantile table
+
+// Phi^{-1}(p) for 0 < p < 0.5 by Newton's method on Phi(x) = erfc(-x/sqrt2)/2,
+// started from the rational approximation of Abramowitz & Stegun 26.2.23.
+double norm_quantile_lower(double p) {
+  const double t = sqrt(-2.0 * log(p));
+  double x = -(t - (2.515517 + 0.802853 * t + 0.010328 * t * t) /
+                       (1.0 + 1.432788 * t + 0.189269 * t * t + 0.001308 * t * t * t));
+  for (int it = 0; it < 8; ++it) {
+    const double f = 0.5 * erfc(-x / sqrt(2.0)) - p;
+    const double d = exp(-0.5 * x * x) / sqrt(2.0 * M_PI);
+    const double step = f / d;
+    x -= step;
+    if (fabs(step) <= 1e-17 * fabs(x)) break;
+  }
+  return x;
+}
+
+uint16_t bf16_bits_rne(double x) {
+  if (x == 0.0) return 0;
+  int e;
+  const double m = frexp(x, &e);          // x = m 2^e, 0.5 <= |m| < 1
+  const double q = nearbyint(m * 256.0);  // 8 significant bits, ties to even
+  const float f = (float)ldexp(q, e - 8); // exact
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return (uint16_t)(u >> 16);
+}
+
+const uint16_t* host_omega_table() {
+  static uint16_t table[65536];
+  static std::once_flag once;
+  std::call_once(once, [] {
+    for (int t = 0; t < 32768; ++t) {
+      const double x = norm_quantile_lower((t + 0.5) / 65536.0);
+      const uint16_t b = bf16_bits_rne(x);
+      table[t] = b;
+      table[65535 - t] = b ^ 0x8000u;  // Phi^-1(1 - p) = -Phi^-1(p)
+    }
+  });
+  return table;
+}
+
+metis_status ensure_device_tables() {
+  static std::mutex mu;
+  static bool done[64] = {false};
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return fail(METIS_E_UNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lk(mu);
+  if (!done[dev]) {
+    HIP_TRY(hipMemcpyToSymbol(HIP_SYMBOL(g_omega_table), host_omega_table(), 65536 * 2));
+    const int zero = 0;
+    HIP_TRY(hipMemcpyToSymbol(HIP_SYMBOL(g_metis_status), &zero, sizeof(int)));
+    done[dev] = true;
+  }
+  return METIS_OK;
+}
+
+// ------------------------------------------------------------- workspace --
+
+struct Carver {
+  char* base;
+  size_t off = 0;
+  size_t cap;
+  explicit Carver(void* b, size_t c) : base((char*)b), cap(c) {}
+  template <typename T>
+  T* take(size_t count) {
+    off = (off + 255) & ~(size_t)255;
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+  size_t used() const { return (off + 255) & ~(size_t)255; }
+};
+
+inline int round_up(int a, int b) { return (a + b - 1) / b * b; }
+
+inline unsigned grid1(int64_t n, int block) { return (unsigned)((n + block - 1) / block); }
+
+bool dtype_ok(int32_t dt) { return dt == METIS_BF16 || dt == METIS_F32; }
+
+// --------------------------------------------------------- decomposition --
+
+struct DecompWs {
+  uint32_t *keys, *hist, *meta;
+  uint2* cand;
+  uint8_t* flags;
+  int32_t* idx;
+  float *om, *y, *q, *bpart, *b, *p, *vn, *sign;
+  double *gpart, *g, *rinv, *z, *theta, *ptp, *rot, *lam;
+  int gblocks, slices;
+  int64_t rows_per_gblock, rows_per_slice;
+};
+
+DecompWs carve_decompose(Carver& cv, int64_t rows, int64_t cols, int k, int n, int64_t lr,
+                         bool sample) {
+  DecompWs w{};
+  if (sample) {
+    w.keys = cv.take<uint32_t>(rows);
+    w.hist = cv.take<uint32_t>(65536);
+    w.meta = cv.take<uint32_t>(16);
+    w.cand = cv.take<uint2>(kCandMax);
+    w.flags = cv.take<uint8_t>(rows);
+  }
+  w.idx = cv.take<int32_t>(lr);
+  w.om = cv.take<float>(cols * n);
+  w.y = cv.take<float>(lr * n);
+  w.q = cv.take<float>(lr * n);
+  const int64_t gmax = rows > lr ? rows : lr;
+  const int64_t gsrc = gmax > cols ? gmax : cols;
+  w.gblocks = (int)((gsrc + 255) / 256 < 512 ? (gsrc + 255) / 256 : 512);
+  if (w.gblocks < 1) w.gblocks = 1;
+  w.gpart = cv.take<double>((size_t)w.gblocks * kMaxN * kMaxN);
+  w.g = cv.take<double>(kMaxN * kMaxN);
+  w.rinv = cv.take<double>(kMaxN * kMaxN);
+  w.slices = (int)(lr >= 4096 ? 16 : (lr >= 512 ? 4 : 1));
+  w.rows_per_slice = (lr + w.slices - 1) / w.slices;
+  w.bpart = cv.take<float>((size_t)w.slices * n * cols);
+  w.b = cv.take<float>((size_t)n * cols);
+  w.z = cv.take<double>(kMaxN * kMaxN);
+  w.theta = cv.take<double>(kMaxN);
+  w.p = cv.take<float>(rows * k);
+  w.ptp = cv.take<double>(kMaxN * kMaxN);
+  w.rot = cv.take<double>(kMaxN * kMaxN);
+  w.lam = cv.take<double>(kMaxN);
+  w.vn = cv.take<float>(cols * k);
+  w.sign = cv.take<float>(kMaxN);
+  return w;
+}
+
+metis_status launch_gram(const float* X, int64_t nr, int n, int64_t rs, int64_t cs, int maxblocks,
+                         double* part, double* G, hipStream_t st) {
+  int64_t per = (nr + maxblocks - 1) / maxblocks;
+  per = (per + 31) / 32 * 32;
+  if (per < 32) per = 32;
+  const int blocks = (int)((nr + per - 1) / per);
+  hipLaunchKernelGGL(gram_partial_kernel, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, st, X, nr, n,
+                     rs, cs, per, part);
+  LAUNCH_CHECK();
+  hipLaunchKernelGGL(reduce_gram_kernel, dim3(grid1(n * n, 256)), dim3(256), 0, st, part,
+                     blocks > 0 ? blocks : 1, n * n, G);
+  LAUNCH_CHECK();
+  return METIS_OK;
+}
+
+metis_status validate_config(const metis_config* cfg) {
+  if (!cfg) return fail(METIS_E_INVALID, "cfg is NULL");
+  if (cfg->k < 1 || cfg->k > kMaxN) return fail(METIS_E_INVALID, "k=%d outside [1, %d]", cfg->k, kMaxN);
+  if (cfg->s < 0) return fail(METIS_E_INVALID, "s=%d negative", cfg->s);
+  if (cfg->k + cfg->s > kMaxN)
+    return fail(METIS_E_UNSUPPORTED, "k + s = %d exceeds %d", cfg->k + cfg->s, kMaxN);
+  if (cfg->refresh < 1) return fail(METIS_E_INVALID, "refresh=%d < 1", cfg->refresh);
+  if (cfg->rounding != METIS_RNE && cfg->rounding != METIS_SR)
+    return fail(METIS_E_INVALID, "rounding=%d", cfg->rounding);
+  return METIS_OK;
+}
+
+// ------------------------------------------------------------ quantiser --
+
+struct QuantWs {
+  uint32_t* amax;  // 3 words: residual, U, V
+  float* pre;
+  float* pscale;
+  _Float16* acat;
+  _Float16* bcat;
+};
+
+QuantWs carve_quantize(Carver& cv, int64_t rows, int64_t cols, int k) {
+  QuantWs w{};
+  w.amax = cv.take<uint32_t>(4);
+  w.pre = cv.take<float>(1);
+  w.pscale = cv.take<float>(1);
+  if (k > 0) {
+    const int kc = 3 * round_up(k, 16);
+    w.acat = cv.take<_Float16>((size_t)rows * kc);
+    w.bcat = cv.take<_Float16>((size_t)cols * kc);
+  }
+  return w;
+}
+
+metis_status run_quant(const QuantParams& qp, bool has_f, int64_t rows, int64_t cols,
+                       hipStream_t st) {
+  const dim3 grid((unsigned)ceil_div<int64_t>(cols, kQT_C), (unsigned)ceil_div<int64_t>(rows, kQT_R));
+  if (grid.y > 65535u) return fail(METIS_E_UNSUPPORTED, "too many rows (%lld)", (long long)rows);
+  if (has_f) {
+    hipLaunchKernelGGL((quant_kernel<true, false>), grid, dim3(kQThreads), 0, st, qp);
+    LAUNCH_CHECK();
+    hipLaunchKernelGGL((quant_kernel<true, true>), grid, dim3(kQThreads), 0, st, qp);
+  } else {
+    hipLaunchKernelGGL((quant_kernel<false, false>), grid, dim3(kQThreads), 0, st, qp);
+    LAUNCH_CHECK();
+    hipLaunchKernelGGL((quant_kernel<false, true>), grid, dim3(kQThreads), 0, st, qp);
+  }
+  LAUNCH_CHECK();
+  return METIS_OK;
+}
+
+bool q4_ok(const metis_q4& q, int64_t n_outer, int64_t k_len) {
+  return q.codes && q.scales && q.tensor_scale && q.n_outer == n_outer && q.k_len == k_len &&
+         (k_len % 16) == 0;
+}
+
+// ----------------------------------------------------------------- GEMMs --
+
+template <int BM, int BN>
+metis_status launch_gemm_cfg(const GemmParams& gp, hipStream_t st) {
+  const int64_t tiles = ceil_div<int64_t>(gp.M, BM) * ceil_div<int64_t>(gp.N, BN);
+  if (tiles <= 0) return METIS_OK;
+  const size_t lds = gemm_lds_bytes<BM, BN>();
+  static std::once_flag once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(once, [&] {
+    attr_err = hipFuncSetAttribute((const void*)gemm_fp4_kernel<BM, BN>,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  });
+  if (attr_err != hipSuccess) return fail(METIS_E_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(attr_err));
+  hipLaunchKernelGGL((gemm_fp4_kernel<BM, BN>), dim3((unsigned)tiles), dim3(256), lds, st, gp);
+  LAUNCH_CHECK();
+  return METIS_OK;
+}
+
+metis_status launch_gemm(const GemmParams& gp, hipStream_t st) {
+  if (gp.M <= 0 || gp.N <= 0) return METIS_OK;
+  const int64_t t256 = ceil_div<int64_t>(gp.M, 256) * ceil_div<int64_t>(gp.N, 256);
+  const int64_t t128 = ceil_div<int64_t>(gp.M, 128) * ceil_div<int64_t>(gp.N, 128);
+  (void)t256;
+  if (gp.M >= 128 && gp.N >= 128 && t128 >= 256) return launch_gemm_cfg<128, 128>(gp, st);
+  return launch_gemm_cfg<64, 64>(gp, st);
+}
+
+struct SideQ {
+  const metis_q4* res;  // residual in the product's K orientation
+  const metis_q4* out;  // factor along the output rows (left) / cols (right)
+  const metis_q4* kf;   // factor along K
+  const float* S;
+  int k;
+};
+
+struct SplitWs {
+  float *praw, *t1, *t2, *ones;
+  uint16_t *a_ext, *b_ext;
+  int64_t kext;
+  int ksR, ksL;
+};
+
+SplitWs carve_split(Carver& cv, int64_t M, int64_t N, int kL, int kR) {
+  SplitWs w{};
+  w.ksR = round_up(kR, 16);
+  w.ksL = round_up(kL, 16);
+  w.kext = round_up(2 * w.ksR + 2 * w.ksL, 64);
+  w.ones = cv.take<float>(4);
+  if (kR > 0) w.praw = cv.take<float>((size_t)M * kR);
+  if (kL > 0) w.t1 = cv.take<float>((size_t)kL * N);
+  if (kL > 0 && kR > 0) w.t2 = cv.take<float>((size_t)kL * kR);
+  if (w.kext > 0) {
+    w.a_ext = cv.take<uint16_t>((size_t)M * w.kext);
+    w.b_ext = cv.take<uint16_t>((size_t)N * w.kext);
+  }
+  return w;
+}
+
+// out (M x N) = L-hat R-hat with L = H S_L F^T + L_R, R^T = E S_R J^T + R_R^T
+// along K.
+metis_status split_product(const SideQ& L, const SideQ& R, int64_t M, int64_t N, int64_t K,
+                           float* C, int64_t ldc, void* ws, size_t ws_bytes, hipStream_t st) {
+  Carver cv(ws, ws_bytes);
+  SplitWs w = carve_split(cv, M, N, L.k, R.k);
+  if (cv.used() > ws_bytes) return fail(METIS_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, cv.used());
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, st, (uint32_t*)w.ones, 0x3F800000u,
+                     (int64_t)4);
+  LAUNCH_CHECK();
+  metis_status s;
+  GemmParams g{};
+  if (R.k > 0) {  // P_raw = L_R . E   (M x kR)
+    g = GemmParams{M, R.k, K, L.res->codes, L.res->scales, R.kf->codes, R.kf->scales,
+                   nullptr, nullptr, 0, nullptr, nullptr, w.praw, R.k};
+    if ((s = launch_gemm(g, st)) != METIS_OK) return s;
+  }
+  if (L.k > 0) {  // T1 = F . R_R   (kL x N)
+    g = GemmParams{L.k, N, K, L.kf->codes, L.kf->scales, R.res->codes, R.res->scales,
+                   nullptr, nullptr, 0, nullptr, nullptr, w.t1, N};
+    if ((s = launch_gemm(g, st)) != METIS_OK) return s;
+  }
+  if (L.k > 0 && R.k > 0) {  // T2 = F . E   (kL x kR)
+    g = GemmParams{L.k, R.k, K, L.kf->codes, L.kf->scales, R.kf->codes, R.kf->scales,
+                   nullptr, nullptr, 0, nullptr, nullptr, w.t2, R.k};
+    if ((s = launch_gemm(g, st)) != METIS_OK) return s;
+  }
+  int64_t kext = 0;
+  if (L.k > 0 || R.k > 0) {
+    kext = w.kext;
+    ExtParams e{};
+    e.rows = M;
+    e.cols = N;
+    e.kR = R.k;
+    e.kL = L.k;
+    e.ksR = w.ksR;
+    e.ksL = w.ksL;
+    e.kext = kext;
+    e.praw = w.praw;
+    e.t1 = w.t1;
+    e.t2 = w.t2;
+    e.S_R = R.k > 0 ? R.S : w.ones;
+    e.S_L = L.k > 0 ? L.S : w.ones;
+    e.s_LR = L.res->tensor_scale;
+    e.s_RR = R.res->tensor_scale;
+    e.s_E = R.k > 0 ? R.kf->tensor_scale : w.ones;
+    e.s_F = L.k > 0 ? L.kf->tensor_scale : w.ones;
+    e.H = SplitSide{L.k > 0 ? L.out->codes : nullptr, L.k > 0 ? L.out->scales : nullptr,
+                    L.k > 0 ? L.out->tensor_scale : w.ones, L.k, M};
+    e.J = SplitSide{R.k > 0 ? R.out->codes : nullptr, R.k > 0 ? R.out->scales : nullptr,
+                    R.k > 0 ? R.out->tensor_scale : w.ones, R.k, N};
+    e.a_ext = w.a_ext;
+    e.b_ext = w.b_ext;
+    hipLaunchKernelGGL(ext_prep_a_kernel, dim3(grid1(M * kext, 256)), dim3(256), 0, st, e);
+    LAUNCH_CHECK();
+    hipLaunchKernelGGL(ext_prep_b_kernel, dim3(grid1(N, 64)), dim3(256), 0, st, e);
+    LAUNCH_CHECK();
+  }
+  g = GemmParams{M, N, K, L.res->codes, L.res->scales, R.res->codes, R.res->scales,
+                 L.res->tensor_scale, R.res->tensor_scale, kext, w.a_ext, w.b_ext, C, ldc};
+  return launch_gemm(g, st);
+}
+
+size_t split_ws_size(int64_t M, int64_t N, int kL, int kR) {
+  Carver cv(nullptr, 0);
+  carve_split(cv, M, N, kL, kR);
+  return cv.used();
+}
+
+bool qop_has(const metis_qoperand* q, int axis) {
+  const metis_q4& r = axis == 0 ? q->R_ax0 : q->R_ax1;
+  const int64_t n_outer = axis == 0 ? q->cols : q->rows;
+  const int64_t k_len = axis == 0 ? q->rows : q->cols;
+  return q4_ok(r, n_outer, k_len);
+}
+
+bool qop_factors_ok(const metis_qoperand* q) {
+  if (q->k == 0) return true;
+  if (q->k < 0 || q->k > kMaxN || !q->S) return false;
+  return q4_ok(q->U, q->k, q->rows) && q4_ok(q->V, q->k, q->cols);
+}
+
+}  // namespace
+
+// =================================================================== ABI ===
+
+extern "C" {
+
+int32_t metis_abi_version(void) { return METIS_ABI_VERSION; }
+
+const char* metis_last_error(void) { return g_last_error.c_str(); }
+
+void metis_omega_table(uint16_t* out65536) {
+  if (out65536) memcpy(out65536, host_omega_table(), 65536 * sizeof(uint16_t));
+}
+
+void metis_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  const Philox4 b = philox4x32_10(ctr[0], ctr[1], ctr[2], ctr[3], key[0], key[1]);
+  for (int i = 0; i < 4; ++i) out[i] = b.v[i];
+}
+
+size_t metis_decompose_workspace(int64_t rows, int64_t cols, const metis_config* cfg,
+                                 int32_t sample_rows) {
+  if (!cfg || rows <= 0 || cols <= 0 || cfg->k < 1) return 0;
+  const int n = cfg->k + cfg->s;
+  const int64_t lr = sample_rows ? cfg->l_k : rows;
+  Carver cv(nullptr, 0);
+  carve_decompose(cv, rows, cols, cfg->k, n, lr, sample_rows != 0);
+  return cv.used();
+}
+
+size_t metis_quantize_workspace(int64_t rows, int64_t cols, int32_t k) {
+  Carver cv(nullptr, 0);
+  carve_quantize(cv, rows, cols, k);
+  return cv.used();
+}
+
+size_t metis_gemm_fwd_workspace(const metis_qoperand* X, const metis_qoperand* W) {
+  if (!X || !W) return 0;
+  return split_ws_size(X->rows, W->cols, X->k, W->k);
+}
+
+size_t metis_gemm_bwd_workspace(const metis_qoperand* D, const metis_qoperand* W,
+                                const metis_qoperand* X) {
+  if (!D || !W || !X) return 0;
+  const size_t a = split_ws_size(D->rows, W->rows, D->k, W->k);
+  const size_t b = split_ws_size(X->cols, D->cols, X->k, D->k);
+  return a > b ? a : b;
+}
+
+metis_status metis_decompose(const void* M, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                             const metis_config* cfg, int32_t sample_rows, uint32_t tag,
+                             int64_t step, metis_factors* f, void* ws, size_t ws_bytes,
+                             void* stream) {
+  metis_status s = validate_config(cfg);
+  if (s != METIS_OK) return s;
+  if (!M || !f || !f->U || !f->S || !f->V) return fail(METIS_E_INVALID, "NULL pointer argument");
+  if (!dtype_ok(dtype)) return fail(METIS_E_INVALID, "dtype=%d", dtype);
+  if (rows <= 0 || cols <= 0 || ld < cols) return fail(METIS_E_INVALID, "bad shape %lldx%lld ld=%lld",
+                                                      (long long)rows, (long long)cols, (long long)ld);
+  if (rows > INT32_MAX) return fail(METIS_E_UNSUPPORTED, "rows > 2^31");
+  if (f->rows != rows || f->cols != cols || f->k != cfg->k)
+    return fail(METIS_E_INVALID, "factors describe %lldx%lld k=%d, operand %lldx%lld k=%d",
+                (long long)f->rows, (long long)f->cols, f->k, (long long)rows, (long long)cols, cfg->k);
+  const int k = cfg->k, n = cfg->k + cfg->s;
+  const bool sample = sample_rows != 0;
+  const int64_t lr = sample ? cfg->l_k : rows;
+  if (sample && (cfg->l_k <= 0 || cfg->l_k > rows))
+    return fail(METIS_E_INVALID, "l_k=%lld outside (0, rows=%lld]", (long long)cfg->l_k, (long long)rows);
+  if (n > lr || n > cols)
+    return fail(METIS_E_INVALID, "k + s = %d exceeds min(l_k or rows, cols)", n);
+  if (step < 0 || step > UINT32_MAX) return fail(METIS_E_INVALID, "step=%lld", (long long)step);
+  Carver cv(ws, ws_bytes);
+  DecompWs w = carve_decompose(cv, rows, cols, k, n, lr, sample);
+  if (!ws || cv.used() > ws_bytes)
+    return fail(METIS_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, cv.used());
+  if ((s = ensure_device_tables()) != METIS_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  const uint32_t ustep = (uint32_t)step;
+  const bool refresh = f->refreshed_at < 0 || step - f->refreshed_at >= cfg->refresh;
+
+  if (refresh) {
+    const float scale = sample ? (float)sqrt((double)rows / (double)lr) : 1.0f;
+    if (sample) {
+      const uint32_t tag_s = tag_with_role(tag, kRoleSample);
+      hipLaunchKernelGGL(fill_u32_kernel, dim3(grid1(65536, 256)), dim3(256), 0, st, w.hist, 0u,
+                         (int64_t)65536);
+      LAUNCH_CHECK();
+      hipLaunchKernelGGL(sample_keys_kernel, dim3(grid1(rows, 256)), dim3(256), 0, st, w.keys, w.hist,
+                         rows, tag_s, ustep, cfg->seed);
+      LAUNCH_CHECK();
+      hipLaunchKernelGGL(sample_threshold_kernel, dim3(1), dim3(1024), 0, st, w.hist, w.meta, lr);
+      LAUNCH_CHECK();
+      hipLaunchKernelGGL(sample_mark_kernel, dim3(grid1(rows, 256)), dim3(256), 0, st, w.keys, w.meta,
+                         w.flags, w.cand, rows);
+      LAUNCH_CHECK();
+      hipLaunchKernelGGL(sample_resolve_kernel, dim3(1), dim3(1024), 0, st, w.meta, w.cand, w.flags);
+      LAUNCH_CHECK();
+      hipLaunchKernelGGL(sample_compact_kernel, dim3(1), dim3(1024), 0, st, w.flags, rows, lr, w.idx);
+      LAUNCH_CHECK();
+    } else {
+      hipLaunchKernelGGL(iota_kernel, dim3(grid1(rows, 256)), dim3(256), 0, st, w.idx, rows);
+      LAUNCH_CHECK();
+    }
+    hipLaunchKernelGGL(omega_kernel, dim3(grid1(ceil_div<int64_t>(cols * n, 8), 256)), dim3(256), 0,
+                       st, w.om, cols, n, tag_with_role(tag, kRoleOmega), ustep, cfg->seed);
+    LAUNCH_CHECK();
+    hipLaunchKernelGGL(sketch_y_kernel, dim3(grid1(lr, 32)), dim3(256), 0, st, M, dtype, ld, w.idx,
+                       lr, cols, w.om, n, scale, w.y);
+    LAUNCH_CHECK();
+    float* src = w.y;
+    float* dst = w.q;
+    for (int pass = 0; pass < 3; ++pass) {
+      if ((s = launch_gram(src, lr, n, n, 1, w.gblocks, w.gpart, w.g, st)) != METIS_OK) return s;
+      hipLaunchKernelGGL(cholinv_kernel, dim3(1), dim3(256), 0, st, w.g, n, lr, pass, w.rinv);
+      LAUNCH_CHECK();
+      hipLaunchKernelGGL(apply_rinv_kernel, dim3(grid1(lr, 64)), dim3(256), 0, st, src, lr, n, w.rinv,
+                         dst);
+      LAUNCH_CHECK();
+      float* t = src;  // next pass reads what was just written
+      src = dst;
+      dst = t;
+    }
+    const float* Q = src;
+    hipLaunchKernelGGL(sketch_b_kernel, dim3(grid1(cols, 64), w.slices), dim3(256), 0, st, M, dtype, ld,
+                       w.idx, lr, cols, Q, n, w.rows_per_slice, w.bpart);
+    LAUNCH_CHECK();
+    hipLaunchKernelGGL(reduce_slices_kernel, dim3(grid1((int64_t)n * cols, 256)), dim3(256), 0, st,
+                       w.bpart, w.slices, (int64_t)n * cols, scale, w.b);
+    LAUNCH_CHECK();
+    if ((s = launch_gram(w.b, cols, n, 1, cols, w.gblocks, w.gpart, w.g, st)) != METIS_OK) return s;
+    hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(1024), 0, st, w.g, n, w.theta, w.z);
+    LAUNCH_CHECK();
+    hipLaunchKernelGGL(sketch_v_kernel, dim3(grid1(cols * k, 256)), dim3(256), 0, st, w.b, cols, n, k,
+                       w.z, w.theta, f->V);
+    LAUNCH_CHECK();
+  }
+
+  // projection and rediagonalisation (every step)
+  hipLaunchKernelGGL(project_kernel, dim3(grid1(rows, 64)), dim3(256), 0, st, M, dtype, ld, rows, cols,
+                     f->V, k, w.p);
+  LAUNCH_CHECK();
+  if ((s = launch_gram(w.p, rows, k, k, 1, w.gblocks, w.gpart, w.ptp, st)) != METIS_OK) return s;
+  hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(1024), 0, st, w.ptp, k, w.lam, w.rot);
+  LAUNCH_CHECK();
+  hipLaunchKernelGGL(rotate_kernel, dim3(grid1(cols * k, 256)), dim3(256), 0, st, f->V, cols, k, w.rot,
+                     w.vn);
+  LAUNCH_CHECK();
+  hipLaunchKernelGGL(column_sign_kernel, dim3(k), dim3(256), 0, st, w.vn, cols, k, w.sign);
+  LAUNCH_CHECK();
+  hipLaunchKernelGGL(finalize_v_kernel, dim3(grid1(cols * k, 256)), dim3(256), 0, st, w.vn, cols, k,
+                     w.sign, f->V);
+  LAUNCH_CHECK();
+  hipLaunchKernelGGL(finalize_s_kernel, dim3(1), dim3(128), 0, st, w.lam, k, f->S);
+  LAUNCH_CHECK();
+  hipLaunchKernelGGL(finalize_u_kernel, dim3(grid1(rows, 64)), dim3(256), 0, st, w.p, rows, k, w.rot,
+                     w.lam, w.sign, f->U);
+  LAUNCH_CHECK();
+  if (refresh) f->refreshed_at = step;
+  return METIS_OK;
+}
+
+metis_status metis_quantize(const void* M, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                            const metis_factors* f, const metis_config* cfg, uint32_t tag,
+                            int64_t step, int32_t axes, metis_qoperand* out, float* residual_out,
+                            void* ws, size_t ws_bytes, void* stream) {
+  if (!M || !out || !cfg) return fail(METIS_E_INVALID, "NULL pointer argument");
+  if (!dtype_ok(dtype)) return fail(METIS_E_INVALID, "dtype=%d", dtype);
+  if (rows <= 0 || cols <= 0 || ld < cols) return fail(METIS_E_INVALID, "bad shape");
+  if (cfg->rounding != METIS_RNE && cfg->rounding != METIS_SR)
+    return fail(METIS_E_INVALID, "rounding=%d", cfg->rounding);
+  if (axes <= 0 || axes > 3) return fail(METIS_E_INVALID, "axes=%d", axes);
+  if (step < 0 || step > UINT32_MAX) return fail(METIS_E_INVALID, "step=%lld", (long long)step);
+  if ((axes & METIS_AXIS0) && rows % 16) return fail(METIS_E_INVALID, "rows %% 16 != 0 for axis 0");
+  if ((axes & METIS_AXIS1) && cols % 16) return fail(METIS_E_INVALID, "cols %% 16 != 0 for axis 1");
+  if (out->rows != rows || out->cols != cols) return fail(METIS_E_INVALID, "out describes another shape");
+  if ((axes & METIS_AXIS0) && !q4_ok(out->R_ax0, cols, rows))
+    return fail(METIS_E_INVALID, "R_ax0 must be cols x rows/2 codes");
+  if ((axes & METIS_AXIS1) && !q4_ok(out->R_ax1, rows, cols))
+    return fail(METIS_E_INVALID, "R_ax1 must be rows x cols/2 codes");
+  const int k = f ? f->k : 0;
+  if (f) {
+    if (!f->U || !f->S || !f->V || f->rows != rows || f->cols != cols || k < 1 || k > kMaxN)
+      return fail(METIS_E_INVALID, "factors do not match the operand");
+    if (rows % 16 || cols % 16) return fail(METIS_E_INVALID, "factor blocks need rows, cols %% 16 == 0");
+    if (out->k != k || !q4_ok(out->U, k, rows) || !q4_ok(out->V, k, cols))
+      return fail(METIS_E_INVALID, "out->U / out->V must be k x rows/2 and k x cols/2");
+  } else if (out->k != 0) {
+    return fail(METIS_E_INVALID, "out->k must be 0 for direct quantisation");
+  }
+  Carver cv(ws, ws_bytes);
+  QuantWs w = carve_quantize(cv, rows, cols, k);
+  if (!ws || cv.used() > ws_bytes) return fail(METIS_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, cv.used());
+  metis_status s;
+  if ((s = ensure_device_tables()) != METIS_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, st, w.amax, 0u, (int64_t)4);
+  LAUNCH_CHECK();
+
+  QuantParams qp{};
+  qp.M = M;
+  qp.dtype = dtype;
+  qp.rows = rows;
+  qp.cols = cols;
+  qp.ld = ld;
+  qp.amax = w.amax;
+  qp.axes = axes;
+  qp.sr = cfg->rounding == METIS_SR;
+  qp.seed = cfg->seed;
+  qp.tag0 = tag_with_role(tag, kRoleResidAx0);
+  qp.tag1 = tag_with_role(tag, kRoleResidAx1);
+  qp.step = (uint32_t)step;
+  qp.resid = residual_out;
+  if (axes & METIS_AXIS0) {
+    qp.codes0 = out->R_ax0.codes;
+    qp.scales0 = out->R_ax0.scales;
+    qp.sg0 = out->R_ax0.tensor_scale;
+  }
+  if (axes & METIS_AXIS1) {
+    qp.codes1 = out->R_ax1.codes;
+    qp.scales1 = out->R_ax1.scales;
+    qp.sg1 = out->R_ax1.tensor_scale;
+  }
+  if (f) {
+    const int kp = round_up(k, 16);
+    hipLaunchKernelGGL(resid_scale_kernel, dim3(1), dim3(64), 0, st, f->S, k, w.pre, w.pscale);
+    LAUNCH_CHECK();
+    hipLaunchKernelGGL(resid_prep_kernel, dim3(grid1((rows + cols) * kp, 256)), dim3(256), 0, st, f->U,
+                       f->S, f->V, rows, cols, k, kp, w.pre, w.acat, w.bcat);
+    LAUNCH_CHECK();
+    qp.acat = w.acat;
+    qp.bcat = w.bcat;
+    qp.kc = 3 * kp;
+    qp.pscale = w.pscale;
+  }
+  if ((s = run_quant(qp, f != nullptr, rows, cols, st)) != METIS_OK) return s;
+
+  if (f) {
+    // factors: U (rows x k) and V (cols x k), blocked along their rows
+    for (int which = 0; which < 2; ++which) {
+      QuantParams fq{};
+      const int64_t fr = which == 0 ? rows : cols;
+      const metis_q4& o = which == 0 ? out->U : out->V;
+      fq.M = which == 0 ? (const void*)f->U : (const void*)f->V;
+      fq.dtype = METIS_F32;
+      fq.rows = fr;
+      fq.cols = k;
+      fq.ld = k;
+      fq.amax = w.amax + 1 + which;
+      fq.axes = METIS_AXIS0;
+      fq.sr = qp.sr;
+      fq.seed = cfg->seed;
+      fq.tag0 = tag_with_role(tag, which == 0 ? kRoleU : kRoleV);
+      fq.step = (uint32_t)step;
+      fq.codes0 = o.codes;
+      fq.scales0 = o.scales;
+      fq.sg0 = o.tensor_scale;
+      if ((s = run_quant(fq, false, fr, k, st)) != METIS_OK) return s;
+    }
+    out->S = f->S;
+  }
+  return METIS_OK;
+}
+
+metis_status metis_gemm_fwd(const metis_qoperand* X, const metis_qoperand* W, float* Y, int64_t ldy,
+                            void* ws, size_t ws_bytes, void* stream) {
+  if (!X || !W || !Y) return fail(METIS_E_INVALID, "NULL pointer argument");
+  if (X->cols != W->rows) return fail(METIS_E_INVALID, "inner dimensions differ (%lld vs %lld)",
+                                      (long long)X->cols, (long long)W->rows);
+  if (ldy < W->cols) return fail(METIS_E_INVALID, "ldy < n");
+  if (!qop_has(X, 1)) return fail(METIS_E_INVALID, "X lacks its residual along m (R_ax1)");
+  if (!qop_has(W, 0)) return fail(METIS_E_INVALID, "W lacks its residual along m (R_ax0)");
+  if (!qop_factors_ok(X) || !qop_factors_ok(W)) return fail(METIS_E_INVALID, "bad factor descriptors");
+  const SideQ L{&X->R_ax1, &X->U, &X->V, X->S, X->k};
+  const SideQ R{&W->R_ax0, &W->V, &W->U, W->S, W->k};
+  return split_product(L, R, X->rows, W->cols, X->cols, Y, ldy, ws, ws_bytes, (hipStream_t)stream);
+}
+
+metis_status metis_gemm_bwd(const metis_qoperand* D, const metis_qoperand* W, const metis_qoperand* X,
+                            float* dX, int64_t lddx, float* dW, int64_t lddw, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (!D || !W || !X) return fail(METIS_E_INVALID, "NULL pointer argument");
+  if (D->cols != W->cols || D->rows != X->rows || X->cols != W->rows)
+    return fail(METIS_E_INVALID, "shapes of D, W, X do not form a linear layer");
+  if (!qop_factors_ok(D) || !qop_factors_ok(W) || !qop_factors_ok(X))
+    return fail(METIS_E_INVALID, "bad factor descriptors");
+  hipStream_t st = (hipStream_t)stream;
+  metis_status s;
+  if (dX) {
+    if (lddx < W->rows) return fail(METIS_E_INVALID, "lddx < m");
+    if (!qop_has(D, 1) || !qop_has(W, 1)) return fail(METIS_E_INVALID, "dX needs D and W along n (R_ax1)");
+    const SideQ L{&D->R_ax1, &D->U, &D->V, D->S, D->k};
+    const SideQ R{&W->R_ax1, &W->U, &W->V, W->S, W->k};
+    if ((s = split_product(L, R, D->rows, W->rows, D->cols, dX, lddx, ws, ws_bytes, st)) != METIS_OK)
+      return s;
+  }
+  if (dW) {
+    if (lddw < D->cols) return fail(METIS_E_INVALID, "lddw < n");
+    if (!qop_has(X, 0) || !qop_has(D, 0)) return fail(METIS_E_INVALID, "dW needs X and D along l (R_ax0)");
+    const SideQ L{&X->R_ax0, &X->V, &X->U, X->S, X->k};
+    const SideQ R{&D->R_ax0, &D->V, &D->U, D->S, D->k};
+    if ((s = split_product(L, R, X->cols, D->cols, X->rows, dW, lddw, ws, ws_bytes, st)) != METIS_OK)
+      return s;
+  }
+  return METIS_OK;
+}
+
+metis_status metis_status_sync(void* stream) {
+  HIP_TRY(hipStreamSynchronize((hipStream_t)stream));
+  int v = 0;
+  HIP_TRY(hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_metis_status), sizeof(int)));
+  if (v != 0) {
+    const int zero = 0;
+    HIP_TRY(hipMemcpyToSymbol(HIP_SYMBOL(g_metis_status), &zero, sizeof(int)));
+    return fail(METIS_E_NUMERIC, "device numeric status 0x%x (1: non-finite input, 2: Cholesky, 4: sampler)", v);
+  }
+  return METIS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,685 @@
+// rsvd.hpp -- randomized truncated SVD of one operand with the cross-step
+// basis cache ("Metis: Training LLMs with FP4 Quantization", 关键设计 2:
+// sparse random row sampling + Gaussian random projection; 关键设计 3: reuse
+// of the factors; 关键设计 1: M = U_k S_k V_k^T + M_R).
+//
+// Refresh (every `refresh` steps):
+//   idx   = the l_k rows with the smallest (Philox key, row) pairs, ascending
+//   Y     = sqrt(r / l_k) M[idx] Omega           (l_k x n, n = k + s)
+//   Q     = shifted CholeskyQR3(Y)                (fp64 Gram / Cholesky)
+//   B     = Q^T sqrt(r / l_k) M[idx]              (n x cols)
+//   Z, T  = Jacobi(B B^T)  (fp64, one workgroup)
+//   V     = B^T Z[:, :k] T^-1/2                    (cols x k, the cached basis)
+// Every step:
+//   P = M V, Jacobi(P^T P) = (R, lambda), V <- V R (sign rule),
+//   U = P R lambda^-1/2, S = lambda^1/2.
+// Small dense algebra (n <= 96) runs in fp64 inside one workgroup so no
+// device-to-host synchronisation is needed anywhere on the path.
+#pragma once
+
+#include "common.hpp"
+
+namespace metis {
+
+constexpr int kMaxN = 96;       // largest sketch width / rank handled in LDS
+constexpr int kCandMax = 4096;  // candidate slots of the sampler's boundary bin
+constexpr double kEigZero = 1e-12;
+
+// The 65536-entry bf16 Gaussian quantile table (filled from the host once
+// per device).
+__device__ uint16_t g_omega_table[65536];
+
+// ----------------------------------------------------------------- sampler --
+
+__global__ void sample_keys_kernel(uint32_t* __restrict__ keys, uint32_t* __restrict__ hist,
+                                   int64_t rows, uint32_t tag, uint32_t step, uint64_t seed) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows) return;
+  const uint32_t k = philox_word((uint64_t)i, tag, step, seed);
+  keys[i] = k;
+  atomicAdd(&hist[k >> 16], 1u);
+}
+
+// meta[0] = boundary bin b*, meta[1] = rows still needed from b*, meta[2] =
+// candidate count (zeroed here).
+__global__ __launch_bounds__(1024) void sample_threshold_kernel(const uint32_t* __restrict__ hist,
+                                                                uint32_t* __restrict__ meta,
+                                                                int64_t l_k) {
+  __shared__ uint32_t part[1024];
+  const int tid = threadIdx.x;
+  uint32_t s = 0;
+  for (int b = 0; b < 64; ++b) s += hist[tid * 64 + b];
+  part[tid] = s;
+  __syncthreads();
+  // inclusive scan (Hillis-Steele)
+  for (int o = 1; o < 1024; o <<= 1) {
+    const uint32_t v = tid >= o ? part[tid - o] : 0u;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  const uint32_t incl = part[tid];
+  const uint32_t excl = incl - s;
+  if (excl < (uint32_t)l_k && (uint32_t)l_k <= incl) {
+    uint32_t c = excl;
+    for (int b = 0; b < 64; ++b) {
+      const uint32_t h = hist[tid * 64 + b];
+      if (c + h >= (uint32_t)l_k) {
+        meta[0] = (uint32_t)(tid * 64 + b);
+        meta[1] = (uint32_t)l_k - c;
+        meta[2] = 0;
+        break;
+      }
+      c += h;
+    }
+  }
+}
+
+__global__ void sample_mark_kernel(const uint32_t* __restrict__ keys, uint32_t* __restrict__ meta,
+                                   uint8_t* __restrict__ flags, uint2* __restrict__ cand,
+                                   int64_t rows) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows) return;
+  const uint32_t k = keys[i];
+  const uint32_t b = k >> 16, bs = meta[0];
+  flags[i] = b < bs ? 1 : 0;
+  if (b == bs) {
+    const uint32_t slot = atomicAdd(&meta[2], 1u);
+    if (slot < (uint32_t)kCandMax)
+      cand[slot] = make_uint2(k, (uint32_t)i);
+    else
+      raise_status(kStatusSample);
+  }
+}
+
+__global__ __launch_bounds__(1024) void sample_resolve_kernel(const uint32_t* __restrict__ meta,
+                                                              const uint2* __restrict__ cand,
+                                                              uint8_t* __restrict__ flags) {
+  const uint32_t n = min(meta[2], (uint32_t)kCandMax);
+  const uint32_t need = meta[1];
+  for (uint32_t a = threadIdx.x; a < n; a += blockDim.x) {
+    const uint2 ca = cand[a];
+    uint32_t rank = 0;
+    for (uint32_t b = 0; b < n; ++b) {
+      const uint2 cb = cand[b];
+      rank += (cb.x < ca.x || (cb.x == ca.x && cb.y < ca.y)) ? 1u : 0u;
+    }
+    if (rank < need) flags[ca.y] = 1;
+  }
+}
+
+// idx = ascending list of flagged rows (one workgroup scan over all rows).
+__global__ __launch_bounds__(1024) void sample_compact_kernel(const uint8_t* __restrict__ flags,
+                                                              int64_t rows, int64_t l_k,
+                                                              int32_t* __restrict__ idx) {
+  __shared__ uint32_t part[1024];
+  const int tid = threadIdx.x;
+  const int64_t chunk = ceil_div<int64_t>(rows, 1024);
+  const int64_t b = tid * chunk, e = min(rows, b + chunk);
+  uint32_t c = 0;
+  for (int64_t i = b; i < e; ++i) c += flags[i];
+  part[tid] = c;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const uint32_t v = tid >= o ? part[tid - o] : 0u;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  uint32_t pos = part[tid] - c;
+  for (int64_t i = b; i < e; ++i)
+    if (flags[i]) {
+      if ((int64_t)pos < l_k) idx[pos] = (int32_t)i;
+      ++pos;
+    }
+  if (tid == 1023 && (int64_t)part[1023] != l_k) raise_status(kStatusSample);
+}
+
+__global__ void iota_kernel(int32_t* idx, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) idx[i] = (int32_t)i;
+}
+
+// ------------------------------------------------------------------ Omega --
+
+__global__ void omega_kernel(float* __restrict__ om, int64_t cols, int n, uint32_t tag,
+                             uint32_t step, uint64_t seed) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // block of 8
+  const int64_t total = cols * n;
+  const int64_t e0 = q * 8;
+  if (e0 >= total) return;
+  const Philox4 b = philox_block((uint64_t)q, tag, step, seed);
+#pragma unroll
+  for (int o = 0; o < 8; ++o) {
+    const int64_t e = e0 + o;
+    if (e < total) {
+      const uint32_t h = philox_half_of(b, (uint32_t)o);
+      om[e] = __uint_as_float((uint32_t)g_omega_table[h] << 16);
+    }
+  }
+}
+
+// ------------------------------------------------------------ sketch GEMMs --
+
+// Y[s][j] = scale * sum_c M[idx[s]][c] Om[c][j]; 32 sample rows per block.
+__global__ __launch_bounds__(256) void sketch_y_kernel(const void* __restrict__ M, int dtype,
+                                                       int64_t ld, const int32_t* __restrict__ idx,
+                                                       int64_t ns, int64_t cols,
+                                                       const float* __restrict__ om, int n,
+                                                       float scale, float* __restrict__ Y) {
+  __shared__ float ms[32][65];
+  __shared__ float os[64][kMaxN + 1];
+  const int tid = threadIdx.x;
+  const int64_t s0 = (int64_t)blockIdx.x * 32;
+  const int sl = tid >> 3, jg = tid & 7;
+  float acc[kMaxN / 8];
+#pragma unroll
+  for (int t = 0; t < kMaxN / 8; ++t) acc[t] = 0.0f;
+  for (int64_t c0 = 0; c0 < cols; c0 += 64) {
+    for (int e = tid; e < 32 * 64; e += 256) {
+      const int r = e >> 6, c = e & 63;
+      const int64_t s = s0 + r;
+      float v = 0.0f;
+      if (s < ns && c0 + c < cols) v = load_as_float(M, dtype, (int64_t)idx[s] * ld + c0 + c);
+      ms[r][c] = v;
+    }
+    for (int e = tid; e < 64 * n; e += 256) {
+      const int c = e / n, j = e % n;
+      os[c][j] = (c0 + c < cols) ? om[(c0 + c) * n + j] : 0.0f;
+    }
+    __syncthreads();
+    for (int c = 0; c < 64; ++c) {
+      const float mv = ms[sl][c];
+#pragma unroll
+      for (int t = 0; t < kMaxN / 8; ++t) {
+        const int j = jg + 8 * t;
+        if (j < n) acc[t] = fmaf(mv, os[c][j], acc[t]);
+      }
+    }
+    __syncthreads();
+  }
+  const int64_t s = s0 + sl;
+  if (s < ns)
+#pragma unroll
+    for (int t = 0; t < kMaxN / 8; ++t) {
+      const int j = jg + 8 * t;
+      if (j < n) Y[s * n + j] = acc[t] * scale;
+    }
+}
+
+// Partial B[j][c] over a slice of sample rows: part[slice][j][c].
+// 64 columns per block; threads: column = tid % 64, j group = tid / 64.
+__global__ __launch_bounds__(256) void sketch_b_kernel(const void* __restrict__ M, int dtype,
+                                                       int64_t ld, const int32_t* __restrict__ idx,
+                                                       int64_t ns, int64_t cols,
+                                                       const float* __restrict__ Q, int n,
+                                                       int64_t rows_per_slice,
+                                                       float* __restrict__ part) {
+  __shared__ float qs[64][kMaxN + 1];
+  const int tid = threadIdx.x;
+  const int64_t c = (int64_t)blockIdx.x * 64 + (tid & 63);
+  const int jg = tid >> 6;
+  const int64_t sb = (int64_t)blockIdx.y * rows_per_slice;
+  const int64_t se = min(ns, sb + rows_per_slice);
+  float acc[kMaxN / 4];
+#pragma unroll
+  for (int t = 0; t < kMaxN / 4; ++t) acc[t] = 0.0f;
+  for (int64_t s0 = sb; s0 < se; s0 += 64) {
+    __syncthreads();
+    for (int e = tid; e < 64 * n; e += 256) {
+      const int r = e / n, j = e % n;
+      qs[r][j] = (s0 + r < se) ? Q[(s0 + r) * n + j] : 0.0f;
+    }
+    __syncthreads();
+    const int lim = (int)min((int64_t)64, se - s0);
+    for (int r = 0; r < lim; ++r) {
+      const float mv = (c < cols) ? load_as_float(M, dtype, (int64_t)idx[s0 + r] * ld + c) : 0.0f;
+#pragma unroll
+      for (int t = 0; t < kMaxN / 4; ++t) {
+        const int j = jg + 4 * t;
+        if (j < n) acc[t] = fmaf(qs[r][j], mv, acc[t]);
+      }
+    }
+  }
+  if (c < cols)
+#pragma unroll
+    for (int t = 0; t < kMaxN / 4; ++t) {
+      const int j = jg + 4 * t;
+      if (j < n) part[((int64_t)blockIdx.y * n + j) * cols + c] = acc[t];
+    }
+}
+
+// B[j][c] = scale * sum over slices (fixed order -> deterministic).
+__global__ void reduce_slices_kernel(const float* __restrict__ part, int slices, int64_t count,
+                                     float scale, float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= count) return;
+  float s = 0.0f;
+  for (int k = 0; k < slices; ++k) s += part[(int64_t)k * count + i];
+  out[i] = s * scale;
+}
+
+// --------------------------------------------------------------- fp64 Grams --
+
+// Partial Gram of an nr x n matrix X (element (r, j) at X[r*rs + j*cs]):
+// part[block][a][b] = sum over this block's rows of X[r][a] X[r][b].
+__global__ __launch_bounds__(256) void gram_partial_kernel(const float* __restrict__ X, int64_t nr,
+                                                           int n, int64_t rs, int64_t cs,
+                                                           int64_t rows_per_block,
+                                                           double* __restrict__ part) {
+  __shared__ float xs[32][kMaxN + 1];
+  const int tid = threadIdx.x;
+  const int64_t rb = (int64_t)blockIdx.x * rows_per_block;
+  const int64_t re = min(nr, rb + rows_per_block);
+  const int nn = n * n;
+  double acc[(kMaxN * kMaxN + 255) / 256];
+  const int per = (nn + 255) / 256;
+  for (int t = 0; t < per; ++t) acc[t] = 0.0;
+  for (int64_t r0 = rb; r0 < re; r0 += 32) {
+    __syncthreads();
+    for (int e = tid; e < 32 * n; e += 256) {
+      const int r = e / n, j = e % n;
+      xs[r][j] = (r0 + r < re) ? X[(r0 + r) * rs + (int64_t)j * cs] : 0.0f;
+    }
+    __syncthreads();
+    for (int t = 0; t < per; ++t) {
+      const int e = tid + 256 * t;
+      if (e < nn) {
+        const int a = e / n, b = e % n;
+        double s = 0.0;
+        for (int r = 0; r < 32; ++r) s += (double)xs[r][a] * (double)xs[r][b];
+        acc[t] += s;
+      }
+    }
+  }
+  for (int t = 0; t < per; ++t) {
+    const int e = tid + 256 * t;
+    if (e < nn) part[(int64_t)blockIdx.x * nn + e] = acc[t];
+  }
+}
+
+__global__ void reduce_gram_kernel(const double* __restrict__ part, int blocks, int nn,
+                                   double* __restrict__ G) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= nn) return;
+  double s = 0.0;
+  for (int b = 0; b < blocks; ++b) s += part[(int64_t)b * nn + e];
+  G[e] = s;
+}
+
+// ------------------------------------------------------ Cholesky (one WG) --
+
+// Rinv = R^-1 with R^T R = G + shift I.  pass 0: shift = c u32 tr(G);
+// passes 1, 2: no shift unless the factorisation breaks down, then the
+// guard shift c u64 tr(G).  c = 11 (p n + n (n + 1)).
+__global__ __launch_bounds__(256) void cholinv_kernel(const double* __restrict__ G, int n,
+                                                      int64_t p, int pass,
+                                                      double* __restrict__ Rinv) {
+  __shared__ double L[kMaxN][kMaxN + 1];
+  __shared__ double Li[kMaxN][kMaxN + 1];
+  __shared__ int fail;
+  const int tid = threadIdx.x;
+  double tr = 0.0;
+  for (int i = 0; i < n; ++i) tr += G[i * n + i];
+  const double c = 11.0 * ((double)p * n + (double)n * (n + 1));
+  const int attempts = pass == 0 ? 1 : 2;
+  for (int att = 0; att < attempts; ++att) {
+    double shift = 0.0;
+    if (pass == 0) shift = c * ldexp(1.0, -24) * tr;
+    else if (att == 1) shift = c * ldexp(1.0, -53) * tr;
+    __syncthreads();
+    for (int e = tid; e < n * n; e += blockDim.x) {
+      const int a = e / n, b = e % n;
+      L[a][b] = G[e] + (a == b ? shift : 0.0);
+    }
+    if (tid == 0) fail = 0;
+    __syncthreads();
+    for (int j = 0; j < n; ++j) {
+      if (tid == 0) {
+        double d = L[j][j];
+        for (int k = 0; k < j; ++k) d -= L[j][k] * L[j][k];
+        if (!(d > 0.0)) {
+          fail = 1;
+          d = 1.0;
+        }
+        L[j][j] = sqrt(d);
+      }
+      __syncthreads();
+      for (int i = j + 1 + tid; i < n; i += blockDim.x) {
+        double s = L[i][j];
+        for (int k = 0; k < j; ++k) s -= L[i][k] * L[j][k];
+        L[i][j] = s / L[j][j];
+      }
+      __syncthreads();
+    }
+    if (!fail) break;
+  }
+  if (fail && tid == 0) raise_status(kStatusCholesky);
+  // Li = L^-1 (lower): column j by forward substitution
+  for (int j = tid; j < n; j += blockDim.x) {
+    for (int i = 0; i < n; ++i) Li[i][j] = 0.0;
+    Li[j][j] = 1.0 / L[j][j];
+    for (int i = j + 1; i < n; ++i) {
+      double s = 0.0;
+      for (int k = j; k < i; ++k) s += L[i][k] * Li[k][j];
+      Li[i][j] = -s / L[i][i];
+    }
+  }
+  __syncthreads();
+  // R^-1 = (L^-1)^T
+  for (int e = tid; e < n * n; e += blockDim.x) {
+    const int a = e / n, b = e % n;
+    Rinv[e] = Li[b][a];
+  }
+}
+
+// Qout[s] = Y[s] Rinv (fp64 accumulation), 64 rows per block.
+__global__ __launch_bounds__(256) void apply_rinv_kernel(const float* __restrict__ Y, int64_t ns,
+                                                         int n, const double* __restrict__ Rinv,
+                                                         float* __restrict__ Qout) {
+  __shared__ double ri[kMaxN][kMaxN + 1];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < n * n; e += blockDim.x) ri[e / n][e % n] = Rinv[e];
+  __syncthreads();
+  const int64_t s0 = (int64_t)blockIdx.x * 64;
+  for (int e = tid; e < 64 * n; e += blockDim.x) {
+    const int r = e / n, j = e % n;
+    const int64_t s = s0 + r;
+    if (s >= ns) continue;
+    double acc = 0.0;
+    for (int a = 0; a <= j; ++a) acc += (double)Y[s * n + a] * ri[a][j];
+    Qout[s * n + j] = (float)acc;
+  }
+}
+
+// --------------------------------------------------------- Jacobi (one WG) --
+
+// Cyclic Jacobi with the Golub & Van Loan symmetric 2x2 Schur rotation, in a
+// parallel round-robin pair order; stops when off(A) <= 1e-15 ||A||_F (or 30
+// sweeps).  Output: eigenvalues descending (ties by index) and eigenvectors
+// (column-major in Z: Z[a * n + i] = component a of vector i) signed so the
+// largest-magnitude component is positive (lowest index on ties).
+__global__ __launch_bounds__(1024) void jacobi_kernel(const double* __restrict__ Ain, int n,
+                                                      double* __restrict__ w_out,
+                                                      double* __restrict__ Z) {
+  __shared__ double A[kMaxN][kMaxN + 1];
+  __shared__ double V[kMaxN][kMaxN + 1];
+  __shared__ double cs[kMaxN / 2], sn[kMaxN / 2];
+  __shared__ int pp[kMaxN / 2], qq[kMaxN / 2];
+  __shared__ double red[32];
+  __shared__ int go;
+  const int tid = threadIdx.x;
+  const int np = (n + 1) & ~1;  // even, padded with a zero row/column
+  const int half = np / 2;
+  for (int e = tid; e < np * np; e += blockDim.x) {
+    const int a = e / np, b = e % np;
+    A[a][b] = (a < n && b < n) ? 0.5 * (Ain[a * n + b] + Ain[b * n + a]) : 0.0;
+    V[a][b] = (a == b) ? 1.0 : 0.0;
+  }
+  __syncthreads();
+  // ||A||_F^2
+  double loc = 0.0;
+  for (int e = tid; e < np * np; e += blockDim.x) {
+    const double v = A[e / np][e % np];
+    loc += v * v;
+  }
+  loc = wave_sum_d(loc);
+  if ((tid & 63) == 0) red[tid >> 6] = loc;
+  __syncthreads();
+  double norm2 = 0.0;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) norm2 += red[i];
+  const double tol2 = 1e-30 * norm2;
+  for (int sweep = 0; sweep < 30; ++sweep) {
+    // off(A)^2
+    __syncthreads();
+    double o = 0.0;
+    for (int e = tid; e < np * np; e += blockDim.x) {
+      const int a = e / np, b = e % np;
+      if (a != b) o += A[a][b] * A[a][b];
+    }
+    o = wave_sum_d(o);
+    __syncthreads();
+    if ((tid & 63) == 0) red[tid >> 6] = o;
+    __syncthreads();
+    if (tid == 0) {
+      double off2 = 0.0;
+      for (int i = 0; i < (int)(blockDim.x >> 6); ++i) off2 += red[i];
+      go = off2 > tol2;
+    }
+    __syncthreads();
+    if (!go) break;
+    for (int round = 0; round < np - 1; ++round) {
+      if (tid < half) {
+        // circle method: player np-1 fixed, others rotate
+        int a, b;
+        if (tid == 0) {
+          a = np - 1;
+          b = round;
+        } else {
+          a = (round + tid) % (np - 1);
+          b = (round - tid + (np - 1)) % (np - 1);
+        }
+        const int p = min(a, b), q = max(a, b);
+        pp[tid] = p;
+        qq[tid] = q;
+        const double apq = A[p][q];
+        double c = 1.0, s = 0.0;
+        if (apq != 0.0) {
+          const double diff = A[q][q] - A[p][p];
+          double t;
+          if (fabs(diff) > 1e300 * fabs(apq)) {
+            t = apq / diff;
+          } else {
+            const double tau = diff / (2.0 * apq);
+            const double h = hypot(1.0, tau);
+            t = tau >= 0.0 ? 1.0 / (tau + h) : -1.0 / (-tau + h);
+          }
+          c = 1.0 / sqrt(1.0 + t * t);
+          s = t * c;
+        }
+        cs[tid] = c;
+        sn[tid] = s;
+      }
+      __syncthreads();
+      // rows: A <- J^T A
+      for (int e = tid; e < half * np; e += blockDim.x) {
+        const int k = e / np, j = e % np;
+        const int p = pp[k], q = qq[k];
+        const double c = cs[k], s = sn[k];
+        const double ap = A[p][j], aq = A[q][j];
+        A[p][j] = c * ap - s * aq;
+        A[q][j] = s * ap + c * aq;
+      }
+      __syncthreads();
+      // columns: A <- A J, V <- V J
+      for (int e = tid; e < half * np; e += blockDim.x) {
+        const int k = e / np, i = e % np;
+        const int p = pp[k], q = qq[k];
+        const double c = cs[k], s = sn[k];
+        const double ap = A[i][p], aq = A[i][q];
+        A[i][p] = c * ap - s * aq;
+        A[i][q] = s * ap + c * aq;
+        const double vp = V[i][p], vq = V[i][q];
+        V[i][p] = c * vp - s * vq;
+        V[i][q] = s * vp + c * vq;
+      }
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+  // sort (descending, ties by index) and sign
+  for (int i = tid; i < n; i += blockDim.x) {
+    const double wi = A[i][i];
+    int rank = 0;
+    for (int j = 0; j < n; ++j) {
+      const double wj = A[j][j];
+      rank += (wj > wi || (wj == wi && j < i)) ? 1 : 0;
+    }
+    int am = 0;
+    double best = -1.0;
+    for (int a = 0; a < n; ++a) {
+      const double v = fabs(V[a][i]);
+      if (v > best) {
+        best = v;
+        am = a;
+      }
+    }
+    const double sg = V[am][i] < 0.0 ? -1.0 : 1.0;
+    w_out[rank] = wi;
+    for (int a = 0; a < n; ++a) Z[a * n + rank] = sg * V[a][i];
+  }
+}
+
+// V[c][i] = sum_p B[p][c] Z[p][i] / sqrt(theta_i) for i < k; zero columns
+// with theta_i <= 1e-12 theta_0.
+__global__ void sketch_v_kernel(const float* __restrict__ B, int64_t cols, int n, int k,
+                                const double* __restrict__ Z, const double* __restrict__ theta,
+                                float* __restrict__ V) {
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= cols * k) return;
+  const int64_t c = id / k;
+  const int i = (int)(id % k);
+  const double t0 = theta[0], ti = theta[i];
+  float out = 0.0f;
+  if (t0 > 0.0 && ti > kEigZero * t0) {
+    double s = 0.0;
+    for (int p = 0; p < n; ++p) s += (double)B[(int64_t)p * cols + c] * Z[p * n + i];
+    out = (float)(s / sqrt(ti));
+  }
+  V[c * k + i] = out;
+}
+
+// ------------------------------------------------- projection and rediag --
+
+// P[i][j] = sum_c M[i][c] V[c][j]; 64 rows per block, fp32 accumulation.
+__global__ __launch_bounds__(256) void project_kernel(const void* __restrict__ M, int dtype,
+                                                      int64_t ld, int64_t rows, int64_t cols,
+                                                      const float* __restrict__ V, int k,
+                                                      float* __restrict__ P) {
+  __shared__ float ms[64][65];
+  __shared__ float vs[64][kMaxN + 1];
+  const int tid = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  const int rl = tid >> 2, jg = tid & 3;
+  float acc[kMaxN / 4];
+#pragma unroll
+  for (int t = 0; t < kMaxN / 4; ++t) acc[t] = 0.0f;
+  for (int64_t c0 = 0; c0 < cols; c0 += 64) {
+    __syncthreads();
+    for (int e = tid; e < 64 * 64; e += 256) {
+      const int r = e >> 6, c = e & 63;
+      float v = 0.0f;
+      if (r0 + r < rows && c0 + c < cols) v = load_as_float(M, dtype, (r0 + r) * ld + c0 + c);
+      ms[r][c] = v;
+    }
+    for (int e = tid; e < 64 * k; e += 256) {
+      const int c = e / k, j = e % k;
+      vs[c][j] = (c0 + c < cols) ? V[(c0 + c) * k + j] : 0.0f;
+    }
+    __syncthreads();
+    for (int c = 0; c < 64; ++c) {
+      const float mv = ms[rl][c];
+#pragma unroll
+      for (int t = 0; t < kMaxN / 4; ++t) {
+        const int j = jg + 4 * t;
+        if (j < k) acc[t] = fmaf(mv, vs[c][j], acc[t]);
+      }
+    }
+  }
+  const int64_t r = r0 + rl;
+  if (r < rows)
+#pragma unroll
+    for (int t = 0; t < kMaxN / 4; ++t) {
+      const int j = jg + 4 * t;
+      if (j < k) P[r * k + j] = acc[t];
+    }
+}
+
+// Vn = V R (cols x k), fp64 accumulation.
+__global__ void rotate_kernel(const float* __restrict__ V, int64_t cols, int k,
+                              const double* __restrict__ R, float* __restrict__ Vn) {
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= cols * k) return;
+  const int64_t c = id / k;
+  const int j = (int)(id % k);
+  double s = 0.0;
+  for (int p = 0; p < k; ++p) s += (double)V[c * k + p] * R[p * k + j];
+  Vn[id] = (float)s;
+}
+
+// sign[j] = -1 if the largest-magnitude entry of column j of Vn (lowest row
+// on ties) is negative, else +1.  One block per column.
+__global__ __launch_bounds__(256) void column_sign_kernel(const float* __restrict__ Vn,
+                                                          int64_t cols, int k,
+                                                          float* __restrict__ sign) {
+  __shared__ float bv[256];
+  __shared__ int64_t bi[256];
+  const int j = blockIdx.x, tid = threadIdx.x;
+  float best = -1.0f;
+  int64_t bidx = 0;
+  for (int64_t c = tid; c < cols; c += 256) {
+    const float v = fabsf(Vn[c * k + j]);
+    if (v > best) {
+      best = v;
+      bidx = c;
+    }
+  }
+  bv[tid] = best;
+  bi[tid] = bidx;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) {
+      const float v2 = bv[tid + o];
+      const int64_t i2 = bi[tid + o];
+      if (v2 > bv[tid] || (v2 == bv[tid] && i2 < bi[tid])) {
+        bv[tid] = v2;
+        bi[tid] = i2;
+      }
+    }
+    __syncthreads();
+  }
+  if (tid == 0) sign[j] = Vn[bi[0] * k + j] < 0.0f ? -1.0f : 1.0f;
+}
+
+// V = sign * Vn; S = sqrt(lambda) (0 below the threshold); U = P (R sign) lambda^-1/2.
+__global__ void finalize_v_kernel(const float* __restrict__ Vn, int64_t cols, int k,
+                                  const float* __restrict__ sign, float* __restrict__ V) {
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= cols * k) return;
+  V[id] = Vn[id] * sign[id % k];
+}
+
+__global__ void finalize_s_kernel(const double* __restrict__ lam, int k, float* __restrict__ S) {
+  const int j = threadIdx.x;
+  if (j >= k) return;
+  const double l0 = lam[0], lj = lam[j];
+  S[j] = (l0 > 0.0 && lj > kEigZero * l0) ? (float)sqrt(lj) : 0.0f;
+}
+
+__global__ __launch_bounds__(256) void finalize_u_kernel(const float* __restrict__ P, int64_t rows,
+                                                         int k, const double* __restrict__ R,
+                                                         const double* __restrict__ lam,
+                                                         const float* __restrict__ sign,
+                                                         float* __restrict__ U) {
+  __shared__ double rs[kMaxN][kMaxN + 1];
+  const int tid = threadIdx.x;
+  const double l0 = lam[0];
+  for (int e = tid; e < k * k; e += blockDim.x) {
+    const int p = e / k, j = e % k;
+    const double lj = lam[j];
+    const bool keep = l0 > 0.0 && lj > kEigZero * l0;
+    rs[p][j] = keep ? R[e] * (double)sign[j] / sqrt(lj) : 0.0;
+  }
+  __syncthreads();
+  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  for (int e = tid; e < 64 * k; e += blockDim.x) {
+    const int rl = e / k, j = e % k;
+    const int64_t r = r0 + rl;
+    if (r >= rows) continue;
+    double s = 0.0;
+    for (int p = 0; p < k; ++p) s += (double)P[r * k + p] * rs[p][j];
+    U[r * k + j] = (float)s;
+  }
+}
+
+}  // namespace metis

@@ -1,0 +1,264 @@
+"""ctypes binding of libmetis (include/metis.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  torch supplies device memory and the current HIP stream.  If the
+library is missing the first call raises; there is no fallback.
+"""
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmetis.so")
+
+OK, E_INVALID, E_UNSUPPORTED, E_HIP, E_NUMERIC, E_WORKSPACE = 0, -1, -2, -3, -4, -5
+BF16, F32 = 0, 1
+RNE, SR = 0, 1
+OPERAND_W, OPERAND_X, OPERAND_D = 1, 2, 3
+AXIS0, AXIS1 = 1, 2
+
+
+class MetisError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("metis status %d: %s" % (status, msg))
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_int32), ("s", ctypes.c_int32), ("l_k", ctypes.c_int64),
+                ("refresh", ctypes.c_int32), ("rounding", ctypes.c_int32),
+                ("seed", ctypes.c_uint64)]
+
+
+class _Factors(ctypes.Structure):
+    _fields_ = [("U", ctypes.c_void_p), ("S", ctypes.c_void_p), ("V", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("k", ctypes.c_int32),
+                ("refreshed_at", ctypes.c_int64)]
+
+
+class _Q4(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("tensor_scale", ctypes.c_void_p), ("n_outer", ctypes.c_int64),
+                ("k_len", ctypes.c_int64)]
+
+
+class _QOperand(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("k", ctypes.c_int32),
+                ("S", ctypes.c_void_p), ("U", _Q4), ("V", _Q4), ("R_ax0", _Q4), ("R_ax1", _Q4)]
+
+
+_lib = None
+
+
+def load():
+    """Load libmetis.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libmetis.so not found at %s; run python -m "
+                          "spectral_split_quantized_amd.build" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    i32, i64, u32, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_size_t
+    lib.metis_abi_version.restype = i32
+    lib.metis_last_error.restype = ctypes.c_char_p
+    lib.metis_decompose_workspace.argtypes = [i64, i64, ctypes.POINTER(Config), i32]
+    lib.metis_decompose_workspace.restype = sz
+    lib.metis_quantize_workspace.argtypes = [i64, i64, i32]
+    lib.metis_quantize_workspace.restype = sz
+    lib.metis_gemm_fwd_workspace.argtypes = [ctypes.POINTER(_QOperand)] * 2
+    lib.metis_gemm_fwd_workspace.restype = sz
+    lib.metis_gemm_bwd_workspace.argtypes = [ctypes.POINTER(_QOperand)] * 3
+    lib.metis_gemm_bwd_workspace.restype = sz
+    lib.metis_decompose.argtypes = [P, i32, i64, i64, i64, ctypes.POINTER(Config), i32, u32, i64,
+                                    ctypes.POINTER(_Factors), P, sz, P]
+    lib.metis_decompose.restype = i32
+    lib.metis_quantize.argtypes = [P, i32, i64, i64, i64, ctypes.POINTER(_Factors),
+                                   ctypes.POINTER(Config), u32, i64, i32,
+                                   ctypes.POINTER(_QOperand), P, P, sz, P]
+    lib.metis_quantize.restype = i32
+    lib.metis_gemm_fwd.argtypes = [ctypes.POINTER(_QOperand), ctypes.POINTER(_QOperand), P, i64, P,
+                                   sz, P]
+    lib.metis_gemm_fwd.restype = i32
+    lib.metis_gemm_bwd.argtypes = [ctypes.POINTER(_QOperand)] * 3 + [P, i64, P, i64, P, sz, P]
+    lib.metis_gemm_bwd.restype = i32
+    lib.metis_status_sync.argtypes = [P]
+    lib.metis_status_sync.restype = i32
+    lib.metis_omega_table.argtypes = [P]
+    lib.metis_omega_table.restype = None
+    lib.metis_philox4x32_10.argtypes = [ctypes.POINTER(ctypes.c_uint32)] * 3
+    lib.metis_philox4x32_10.restype = None
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != OK:
+        raise MetisError(status, load().metis_last_error().decode(errors="replace"))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError("operands must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def make_config(k, s=8, l_k=0, refresh=8, rounding=RNE, seed=0):
+    return Config(k, s, l_k, refresh, rounding, seed)
+
+
+def make_tag(layer, operand):
+    return ((layer & 0xFFFF) << 16) | ((operand & 0xF) << 12)
+
+
+class Factors:
+    """Device factors U (rows x k), S (k), V (cols x k) and the cache state."""
+
+    def __init__(self, rows, cols, k, device="cuda"):
+        self.U = torch.empty(rows, k, dtype=torch.float32, device=device)
+        self.S = torch.empty(k, dtype=torch.float32, device=device)
+        self.V = torch.zeros(cols, k, dtype=torch.float32, device=device)
+        self.rows, self.cols, self.k = rows, cols, k
+        self.refreshed_at = -1
+
+    def _c(self):
+        return _Factors(self.U.data_ptr(), self.S.data_ptr(), self.V.data_ptr(), self.rows,
+                        self.cols, self.k, self.refreshed_at)
+
+
+class Q4:
+    """One quantised orientation: codes [n_outer, k_len/2], scales
+    [n_outer, k_len/16] (E4M3 bytes), tensor scale (1 float)."""
+
+    def __init__(self, n_outer, k_len, device="cuda"):
+        self.codes = torch.empty(n_outer, k_len // 2, dtype=torch.uint8, device=device)
+        self.scales = torch.empty(n_outer, k_len // 16, dtype=torch.uint8, device=device)
+        self.tensor_scale = torch.empty(1, dtype=torch.float32, device=device)
+        self.n_outer, self.k_len = n_outer, k_len
+
+    def _c(self):
+        return _Q4(self.codes.data_ptr(), self.scales.data_ptr(), self.tensor_scale.data_ptr(),
+                   self.n_outer, self.k_len)
+
+
+class QOperand:
+    """Quantised operand (rows x cols): Q(U), S, Q(V) and the residual in the
+    requested K orientations."""
+
+    def __init__(self, rows, cols, k, axes, device="cuda"):
+        self.rows, self.cols, self.k = rows, cols, k
+        self.U = Q4(k, rows, device) if k else None
+        self.V = Q4(k, cols, device) if k else None
+        self.R_ax0 = Q4(cols, rows, device) if axes & AXIS0 else None
+        self.R_ax1 = Q4(rows, cols, device) if axes & AXIS1 else None
+        self.S = None
+
+    def _c(self):
+        z = _Q4(None, None, None, 0, 0)
+        return _QOperand(self.rows, self.cols, self.k,
+                         self.S.data_ptr() if self.S is not None else None,
+                         self.U._c() if self.U else z, self.V._c() if self.V else z,
+                         self.R_ax0._c() if self.R_ax0 else z,
+                         self.R_ax1._c() if self.R_ax1 else z)
+
+
+def _workspace(nbytes, device):
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def decompose(M, cfg, sample_rows, tag, step, factors, workspace=None):
+    """Spectral split of M (metis_decompose); updates ``factors`` in place."""
+    lib = load()
+    rows, cols = M.shape
+    need = lib.metis_decompose_workspace(rows, cols, ctypes.byref(cfg), int(sample_rows))
+    ws = workspace if workspace is not None and workspace.numel() >= need else _workspace(need, M.device)
+    fc = factors._c()
+    _check(lib.metis_decompose(_ptr(M), _dtype_code(M), rows, cols, M.stride(0), ctypes.byref(cfg),
+                               int(sample_rows), tag, step, ctypes.byref(fc), _ptr(ws), ws.numel(),
+                               _stream()))
+    factors.refreshed_at = fc.refreshed_at
+    return factors
+
+
+def quantize(M, cfg, tag, step, axes, factors=None, out=None, residual_out=None, workspace=None):
+    """NVFP4 quantisation of M or of its residual (metis_quantize)."""
+    lib = load()
+    rows, cols = M.shape
+    k = factors.k if factors is not None else 0
+    if out is None:
+        out = QOperand(rows, cols, k, axes, M.device)
+    need = lib.metis_quantize_workspace(rows, cols, k)
+    ws = workspace if workspace is not None and workspace.numel() >= need else _workspace(need, M.device)
+    oc = out._c()
+    fcp = ctypes.byref(factors._c()) if factors is not None else None
+    _check(lib.metis_quantize(_ptr(M), _dtype_code(M), rows, cols, M.stride(0), fcp, ctypes.byref(cfg),
+                              tag, step, axes, ctypes.byref(oc), _ptr(residual_out), _ptr(ws),
+                              ws.numel(), _stream()))
+    out.S = factors.S if factors is not None else None
+    return out
+
+
+def gemm_fwd(xq, wq, Y=None, workspace=None):
+    """Y = X-hat W-hat (metis_gemm_fwd), binary32."""
+    lib = load()
+    if Y is None:
+        Y = torch.empty(xq.rows, wq.cols, dtype=torch.float32, device=xq.R_ax1.codes.device)
+    xc, wc = xq._c(), wq._c()
+    need = lib.metis_gemm_fwd_workspace(ctypes.byref(xc), ctypes.byref(wc))
+    ws = workspace if workspace is not None and workspace.numel() >= need else _workspace(need, Y.device)
+    _check(lib.metis_gemm_fwd(ctypes.byref(xc), ctypes.byref(wc), _ptr(Y), Y.stride(0), _ptr(ws),
+                              ws.numel(), _stream()))
+    return Y
+
+
+def gemm_bwd(dq, wq, xq, dX=None, dW=None, want_dx=True, want_dw=True, workspace=None):
+    """(dX, dW) = (D-hat W-hat^T, X-hat^T D-hat) (metis_gemm_bwd), binary32."""
+    lib = load()
+    dev = (dq.R_ax1 or dq.R_ax0).codes.device
+    if want_dx and dX is None:
+        dX = torch.empty(dq.rows, wq.rows, dtype=torch.float32, device=dev)
+    if want_dw and dW is None:
+        dW = torch.empty(xq.cols, dq.cols, dtype=torch.float32, device=dev)
+    dc, wc, xc = dq._c(), wq._c(), xq._c()
+    need = lib.metis_gemm_bwd_workspace(ctypes.byref(dc), ctypes.byref(wc), ctypes.byref(xc))
+    ws = workspace if workspace is not None and workspace.numel() >= need else _workspace(need, dev)
+    _check(lib.metis_gemm_bwd(ctypes.byref(dc), ctypes.byref(wc), ctypes.byref(xc),
+                              _ptr(dX) if want_dx else None, dX.stride(0) if want_dx else 0,
+                              _ptr(dW) if want_dw else None, dW.stride(0) if want_dw else 0,
+                              _ptr(ws), ws.numel(), _stream()))
+    return dX, dW
+
+
+def status_sync():
+    """Synchronise the current stream and raise on a device numeric failure."""
+    _check(load().metis_status_sync(_stream()))
+
+
+def omega_table_bits():
+    """The library's 65536 bf16 bit patterns of the Gaussian quantile table (host only)."""
+    import numpy as np
+    out = np.zeros(65536, dtype=np.uint16)
+    load().metis_omega_table(out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def philox_block(ctr, key):
+    """The library's Philox4x32-10 block function (host only)."""
+    c = (ctypes.c_uint32 * 4)(*ctr)
+    k = (ctypes.c_uint32 * 2)(*key)
+    o = (ctypes.c_uint32 * 4)()
+    load().metis_philox4x32_10(c, k, o)
+    return tuple(o)

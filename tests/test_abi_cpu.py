@@ -1,0 +1,95 @@
+"""CPU-side checks of the C-ABI library (no GPU calls): it loads, exports every
+symbol include/metis.h declares, its host-side definitions of the random draws
+agree with the oracle's independent ones, and argument errors are reported
+synchronously."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import philox, rsvd
+from spectral_split_quantized_amd import metis
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "metis.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(metis_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = metis.load()
+    names = _declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.metis_abi_version() == 1
+
+
+def test_omega_table_matches_oracle():
+    ours = metis.omega_table_bits().astype(np.uint32)
+    lib_vals = (ours << 16).view(np.float32).astype(np.float64)
+    assert np.array_equal(lib_vals, rsvd.omega_table())
+
+
+def test_philox_matches_oracle():
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        ctr = [int(v) for v in rng.integers(0, 2 ** 32, 4, dtype=np.uint64)]
+        key = [int(v) for v in rng.integers(0, 2 ** 32, 2, dtype=np.uint64)]
+        assert metis.philox_block(ctr, key) == philox.block(ctr, key)
+
+
+def _expect(status, code):
+    assert status == code, metis.load().metis_last_error()
+
+
+def test_argument_errors_are_synchronous():
+    lib = metis.load()
+    cfg = metis.make_config(k=8, s=8, l_k=64)
+    f = metis._Factors(None, None, None, 256, 512, 8, -1)
+    # NULL operand
+    _expect(lib.metis_decompose(None, 0, 256, 512, 512, ctypes.byref(cfg), 1, 0, 0, ctypes.byref(f),
+                                None, 0, None), metis.E_INVALID)
+    # k + s too large for the sample
+    bad = metis.make_config(k=60, s=8, l_k=64)
+    dummy = ctypes.c_void_p(16)
+    f2 = metis._Factors(dummy, dummy, dummy, 256, 512, 60, -1)
+    _expect(lib.metis_decompose(dummy, 0, 256, 512, 512, ctypes.byref(bad), 1, 0, 0, ctypes.byref(f2),
+                                dummy, 1 << 30, None), metis.E_INVALID)
+    # rank beyond the supported width
+    huge = metis.make_config(k=120, s=8, l_k=4096)
+    _expect(lib.metis_decompose(dummy, 0, 8192, 512, 512, ctypes.byref(huge), 1, 0, 0,
+                                ctypes.byref(f2), dummy, 1 << 30, None), metis.E_INVALID)
+    # ld < cols
+    _expect(lib.metis_decompose(dummy, 0, 256, 512, 100, ctypes.byref(cfg), 1, 0, 0, ctypes.byref(f),
+                                dummy, 1 << 30, None), metis.E_INVALID)
+    # quantise along an axis whose length is not a multiple of 16
+    q = metis._QOperand(256, 24, 0, None)
+    _expect(lib.metis_quantize(dummy, 0, 256, 24, 24, None, ctypes.byref(cfg), 0, 0, metis.AXIS1,
+                               ctypes.byref(q), None, dummy, 1 << 30, None), metis.E_INVALID)
+    # undersized workspace
+    q4 = metis._Q4(dummy, dummy, dummy, 256, 512)
+    q = metis._QOperand(256, 512, 0, None, metis._Q4(), metis._Q4(), metis._Q4(), q4)
+    _expect(lib.metis_quantize(dummy, 0, 256, 512, 512, None, ctypes.byref(cfg), 0, 0, metis.AXIS1,
+                               ctypes.byref(q), None, dummy, 16, None), metis.E_WORKSPACE)
+    # GEMM with mismatched inner dimensions
+    x = metis._QOperand(64, 32, 0, None)
+    w = metis._QOperand(48, 16, 0, None)
+    _expect(lib.metis_gemm_fwd(ctypes.byref(x), ctypes.byref(w), dummy, 16, dummy, 1 << 20, None),
+            metis.E_INVALID)
+    assert b"inner" in lib.metis_last_error()
+
+
+def test_workspace_sizes_are_positive_and_monotone():
+    lib = metis.load()
+    cfg = metis.make_config(k=61, s=8, l_k=164)
+    a = lib.metis_decompose_workspace(16384, 4096, ctypes.byref(cfg), 1)
+    b = lib.metis_decompose_workspace(16384, 14336, ctypes.byref(cfg), 1)
+    assert 0 < a < b
+    assert lib.metis_quantize_workspace(4096, 4096, 61) > lib.metis_quantize_workspace(4096, 4096, 0) > 0
