@@ -1,0 +1,355 @@
+#!/usr/bin/env python
+"""Benchmark: Metis spectral-split NVFP4 forward + backward on one MI355X.
+
+Workload (the 8-step LLaMA-3-8B MLP case): 16384 tokens, hidden 4096, FFN
+14336; projections gate and up (4096 -> 14336, sharing X) and down
+(14336 -> 4096), bf16 inputs; rank k = 61, oversampling 8, 1% row sample
+(164 rows), stochastic rounding, factors sketched every 8 steps and reused in
+between.  Weights drift each step (W += 1e-3 ||W||_F / sqrt(numel) N(0,1));
+activations and gradients are redrawn each step with their dominant right
+subspace rotated by 0.01 rad per step.  A "step" is one pass of the whole
+path over all three projections: decompose (sketch on refresh steps,
+projection + rediag always), quantise (residual and factors, both K
+orientations), split GEMM forward, split GEMM backward (dX and dW).
+
+All inputs are synthetic and resident in HBM before the timed region starts.
+The printed JSON line reports algorithmic TFLOP/s of the whole step, the
+roofline of the dominant kernel (the main split-GEMM kernel, timed live with
+HIP events on its stream) and the CPU oracle timed on a bounded sample.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Metis fwd+bwd layer TFLOP/s (8B MLP, 16K tok); rSVD ms; % of roofline"
+PEAK_F16_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+TOKENS, HIDDEN, FFN = 16384, 4096, 14336
+K_RANK, OVERSAMPLE, L_K, REFRESH = 61, 8, 164, 8
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------- FLOP model --
+
+def split_gemm_flops(M, N, K, kL, kR):
+    """Algorithmic FLOP of one split product: the residual GEMM, the low-rank
+    terms (P' J^T and H G) and the skinny products that build P' and G."""
+    main = 2 * M * N * K
+    lowrank = 2 * M * N * (kL + kR)
+    skinny = 2 * M * K * kR + 2 * kL * K * N + 2 * kL * K * kR + 2 * kL * kR * N
+    return main + lowrank + skinny
+
+
+def decompose_flops(r, c, k, s, l_k, refresh):
+    """Projection P = M V, Gram P^T P, U = P R; the sketch on refresh steps."""
+    f = 2 * r * c * k + 2 * r * k * k + 2 * r * k * k
+    if refresh:
+        n = k + s
+        f += 2 * l_k * c * n * 2 + 2 * l_k * n * n * 3
+    return f
+
+
+def residual_flops(r, c, k):
+    return 2 * r * c * k
+
+
+# ---------------------------------------------------------------- workload --
+
+class Operand:
+    def __init__(self, name, kind, layer, rows, cols):
+        self.name, self.kind, self.layer = name, kind, layer
+        self.rows, self.cols = rows, cols
+        self.sample = kind != "W"
+
+
+def operands():
+    l, h, f = TOKENS, HIDDEN, FFN
+    return [Operand("W_gate", "W", 0, h, f), Operand("W_up", "W", 1, h, f),
+            Operand("W_down", "W", 2, f, h), Operand("X_gu", "X", 0, l, h),
+            Operand("X_down", "X", 2, l, f), Operand("D_gate", "D", 0, l, f),
+            Operand("D_up", "D", 1, l, f), Operand("D_down", "D", 2, l, h)]
+
+
+PROJECTIONS = [("gate", "X_gu", "W_gate", "D_gate"), ("up", "X_gu", "W_up", "D_up"),
+               ("down", "X_down", "W_down", "D_down")]
+
+
+def build_inputs(n_steps, device):
+    """Synthetic inputs for n_steps steps, all bf16 in HBM."""
+    import torch
+    from spectral_split_quantized_amd import synth
+    seqs = {}
+    for i, op in enumerate(operands()):
+        frac = synth.FRACS[op.kind]
+        base_seed = synth.gen_seed(3, op.kind) + 100 * op.layer
+        if op.kind == "W":
+            master, _ = synth.anisotropic_fast(op.rows, op.cols, frac, base_seed,
+                                               out_dtype=torch.float32, device=device)
+            seq = [master.to(torch.bfloat16)]
+            for t in range(1, n_steps):
+                master = synth.drift_weight(master, base_seed + 7919 * t)
+                seq.append(master.to(torch.bfloat16))
+            del master
+        else:
+            seq, basis = [], None
+            for t in range(n_steps):
+                m, basis = synth.anisotropic_fast(op.rows, op.cols, frac, base_seed + t,
+                                                  device=device, basis=basis, theta=0.01 * t)
+                seq.append(m)
+        seqs[op.name] = seq
+        torch.cuda.synchronize()
+        log("  inputs %-7s %s x %d steps" % (op.name, tuple(seq[0].shape), n_steps))
+    return seqs
+
+
+class MetisMLP:
+    """Persistent state of the path for the three projections: factor
+    caches, quantised operands, outputs and one shared workspace."""
+
+    def __init__(self, device):
+        import torch
+        from spectral_split_quantized_amd import metis
+        self.metis = metis
+        self.cfg = metis.make_config(k=K_RANK, s=OVERSAMPLE, l_k=L_K, refresh=REFRESH,
+                                     rounding=metis.SR, seed=0)
+        self.ops = {op.name: op for op in operands()}
+        self.factors, self.q = {}, {}
+        kind_id = {"W": metis.OPERAND_W, "X": metis.OPERAND_X, "D": metis.OPERAND_D}
+        need = 0
+        lib = metis.load()
+        import ctypes
+        for op in self.ops.values():
+            op.tag = metis.make_tag(op.layer, kind_id[op.kind])
+            self.factors[op.name] = metis.Factors(op.rows, op.cols, K_RANK, device)
+            self.q[op.name] = metis.QOperand(op.rows, op.cols, K_RANK, metis.AXIS0 | metis.AXIS1, device)
+            need = max(need, lib.metis_decompose_workspace(op.rows, op.cols, ctypes.byref(self.cfg),
+                                                           int(op.sample)),
+                       lib.metis_quantize_workspace(op.rows, op.cols, K_RANK))
+        self.out = {}
+        for name, x, w, d in PROJECTIONS:
+            X, W = self.ops[x], self.ops[w]
+            self.out[name] = (torch.empty(X.rows, W.cols, dtype=torch.float32, device=device),
+                              torch.empty(X.rows, W.rows, dtype=torch.float32, device=device),
+                              torch.empty(W.rows, W.cols, dtype=torch.float32, device=device))
+            xc, wc, dc = self.q[x]._c(), self.q[w]._c(), self.q[d]._c()
+            need = max(need, lib.metis_gemm_fwd_workspace(ctypes.byref(xc), ctypes.byref(wc)),
+                       lib.metis_gemm_bwd_workspace(ctypes.byref(dc), ctypes.byref(wc), ctypes.byref(xc)))
+        self.ws = torch.empty(need, dtype=torch.uint8, device=device)
+        log("  workspace %.1f MB" % (need / 1e6))
+
+    def decompose(self, name, M, t):
+        op = self.ops[name]
+        self.metis.decompose(M, self.cfg, op.sample, op.tag, t, self.factors[name], workspace=self.ws)
+
+    def step(self, t, inputs):
+        m = self.metis
+        for name, op in self.ops.items():
+            M = inputs[name][t % len(inputs[name])]
+            self.decompose(name, M, t)
+            m.quantize(M, self.cfg, op.tag, t, m.AXIS0 | m.AXIS1, factors=self.factors[name],
+                       out=self.q[name], workspace=self.ws)
+        for name, x, w, d in PROJECTIONS:
+            Y, dX, dW = self.out[name]
+            m.gemm_fwd(self.q[x], self.q[w], Y=Y, workspace=self.ws)
+            m.gemm_bwd(self.q[d], self.q[w], self.q[x], dX=dX, dW=dW, workspace=self.ws)
+
+    def step_flops(self, t):
+        refresh = (t % REFRESH) == 0
+        f = 0
+        for op in self.ops.values():
+            lk = L_K if op.sample else op.rows
+            f += decompose_flops(op.rows, op.cols, K_RANK, OVERSAMPLE, lk, refresh)
+            f += residual_flops(op.rows, op.cols, K_RANK)
+        for name, x, w, d in PROJECTIONS:
+            X, W = self.ops[x], self.ops[w]
+            l, mm, n = X.rows, X.cols, W.cols
+            f += split_gemm_flops(l, n, mm, K_RANK, K_RANK)      # Y
+            f += split_gemm_flops(l, mm, n, K_RANK, K_RANK)      # dX
+            f += split_gemm_flops(mm, n, l, K_RANK, K_RANK)      # dW
+        return f
+
+
+def dense_equiv_flops():
+    return 3 * 6 * TOKENS * HIDDEN * FFN
+
+
+# ------------------------------------------------------------ CPU baseline --
+
+def cpu_baseline(inputs_cpu, tokens, ncols):
+    """Time the float64 oracle on a bounded sample of the gate projection:
+    `tokens` rows of X and D and the first `ncols` output columns of W."""
+    import numpy as np
+    from oracle import philox, rsvd, split_gemm
+    X = inputs_cpu["X"][:tokens].astype(np.float64)
+    W = inputs_cpu["W"][:, :ncols].astype(np.float64)
+    D = inputs_cpu["D"][:tokens, :ncols].astype(np.float64)
+    cfg = rsvd.Config(k=K_RANK, s=OVERSAMPLE, l_k=L_K, refresh=REFRESH, rounding="sr", seed=0)
+    t0 = time.perf_counter()
+    q = {}
+    for name, M, sample, oid in (("X", X, True, 2), ("W", W, False, 1), ("D", D, True, 3)):
+        tag = philox.make_tag(0, oid, 0)
+        u, s, v, _ = rsvd.decompose(M, cfg, sample, tag, 0)
+        q[name] = split_gemm.quantize_operand(M, u.astype(np.float32), s.astype(np.float32),
+                                              v.astype(np.float32), "sr", 0, tag, 0)
+    split_gemm.gemm_fwd(q["X"], q["W"])
+    split_gemm.gemm_bwd(q["D"], q["W"], q["X"])
+    dt = time.perf_counter() - t0
+    l, h, n = tokens, X.shape[1], ncols
+    flops = 0
+    for r, c, lk in ((l, h, L_K), (h, n, h), (l, n, L_K)):
+        flops += decompose_flops(r, c, K_RANK, OVERSAMPLE, lk, True) + residual_flops(r, c, K_RANK)
+    flops += split_gemm_flops(l, n, h, K_RANK, K_RANK) + split_gemm_flops(l, h, n, K_RANK, K_RANK)
+    flops += split_gemm_flops(h, n, l, K_RANK, K_RANK)
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 0) for i in threadpool_info()), default=None)
+    except Exception:  # pragma: no cover
+        pass
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads or os.cpu_count(),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": "gate projection, first %d tokens x first %d output columns, refresh step "
+                      "(decompose + quantise + fwd + bwd), float64 numpy oracle" % (tokens, ncols)}
+
+
+# -------------------------------------------------------------------- main --
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=16)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=256)
+    ap.add_argument("--cpu-cols", type=int, default=2048)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from spectral_split_quantized_amd import metis
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    metis.load()
+
+    log("building inputs (8 steps, LLaMA-3-8B MLP shapes)")
+    t_build = time.time()
+    inputs = build_inputs(REFRESH, dev)
+    log("inputs built in %.1f s" % (time.time() - t_build))
+    mlp = MetisMLP(dev)
+
+    # warmup (untimed), then the timed steps; step index continues so the
+    # refresh schedule (every 8 steps) is the same in both
+    for t in range(args.warmup):
+        mlp.step(t, inputs)
+        if t == 0:
+            metis.status_sync()
+    torch.cuda.synchronize()
+    metis.status_sync()
+    log("warmup done (%d steps)" % args.warmup)
+
+    metis.timing_enable(4096)
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for t in range(args.warmup, args.warmup + args.steps):
+        mlp.step(t, inputs)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    recs = metis.timing_read(4096)
+    metis.timing_enable(0)
+    metis.status_sync()
+    ms_per_step = total_ms / args.steps
+    flops = sum(mlp.step_flops(t) for t in range(args.warmup, args.warmup + args.steps))
+    value = flops / (total_ms * 1e-3) / 1e12
+    log("timed %d steps: %.2f ms/step, %.1f TFLOP/s" % (args.steps, ms_per_step, value))
+
+    # roofline of the dominant kernel: the main split-GEMM kernel (kind 0)
+    g = [r for r in recs if r[0] == 0]
+    g_ms = sum(r[1] for r in g)
+    g_flops = sum(2 * r[2] * r[3] * r[4] + 2 * r[2] * r[3] * 2 * K_RANK for r in g)
+    g_tflops = g_flops / (g_ms * 1e-3) / 1e12 if g_ms > 0 else 0.0
+    roofline = {"bound": "mfma", "achieved": round(g_tflops, 1), "peak": PEAK_F16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(g_tflops / PEAK_F16_TFLOPS, 4), "traffic": None,
+                "kernel": "gemm_fp4_kernel (main split GEMM)", "launches": len(g),
+                "avg_ms": round(g_ms / max(len(g), 1), 4)}
+    # streaming: both quantiser sweeps (amax + quantise-on-store)
+    q1 = [r for r in recs if r[0] == 1]
+    q2 = [r for r in recs if r[0] == 2]
+    q_bytes = 0
+    for r in q2:
+        rows, cols, axes, kc = r[2], r[3], r[4], r[5]
+        in_b = 4 if cols == K_RANK else 2     # factors are fp32, operands bf16
+        naxes = bin(axes).count("1")
+        q_bytes += rows * cols * (2 * in_b + naxes * (0.5 + 1 / 16))
+        if kc:
+            q_bytes += 2 * (rows + cols) * K_RANK * 4
+    q_ms = sum(r[1] for r in q1) + sum(r[1] for r in q2)
+    q_gbs = q_bytes / (q_ms * 1e-3) / 1e9 if q_ms > 0 else 0.0
+    streaming = {"bound": "hbm", "achieved": round(q_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                 "frac": round(q_gbs / PEAK_HBM_GBS, 4), "kernel": "quant_kernel (amax + quantise sweeps)",
+                 "ms_per_step": round(q_ms / args.steps, 3)}
+
+    # rSVD timing at a refresh step and a cached step (outside the timed region)
+    rsvd_ms = {}
+    for name in ("W_gate", "X_gu", "D_gate"):
+        M = inputs[name][0]
+        op = mlp.ops[name]
+        f = metis.Factors(op.rows, op.cols, K_RANK, dev)
+        for label, t in (("refresh", 64), ("cached", 65)):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            metis.decompose(M, mlp.cfg, op.sample, op.tag, t, f, workspace=mlp.ws)
+            b.record(stream)
+            torch.cuda.synchronize()
+            rsvd_ms["%s_%s" % (name, label)] = round(a.elapsed_time(b), 3)
+    metis.status_sync()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        sample = {"X": inputs["X_gu"][0][:args.cpu_tokens].float().cpu().numpy(),
+                  "W": inputs["W_gate"][0][:, :args.cpu_cols].float().cpu().numpy(),
+                  "D": inputs["D_gate"][0][:args.cpu_tokens, :args.cpu_cols].float().cpu().numpy()}
+        cpu = cpu_baseline(sample, args.cpu_tokens, args.cpu_cols)
+        log("cpu oracle: %.3g TFLOP/s in %.1f s" % (cpu["value"], cpu["seconds"]))
+
+    out = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "nvfp4 operands, f16 mfma, f32 accumulate",
+           "data": "synthetic",
+           "config": {"workload": "llama3_8b_mlp_gate_up_down_16k_tokens_8step_factor_cache",
+                      "tokens": TOKENS, "hidden": HIDDEN, "ffn": FFN, "k": K_RANK, "s": OVERSAMPLE,
+                      "l_k": L_K, "refresh": REFRESH, "rounding": "sr"},
+           "dense_equiv_tflops": round(dense_equiv_flops() * args.steps / (total_ms * 1e-3) / 1e12, 2),
+           "algorithmic_flop_per_step": round(flops / args.steps),
+           "roofline": roofline, "streaming_roofline": streaming, "rsvd_ms": rsvd_ms,
+           "cpu_baseline": cpu}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

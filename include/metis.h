@@ -177,6 +177,18 @@ metis_status metis_gemm_bwd(const metis_qoperand *D, const metis_qoperand *W, co
  * failure flag (METIS_OK or METIS_E_NUMERIC). */
 metis_status metis_status_sync(void *stream);
 
+/* Kernel timing for benchmarks.  metis_timing_enable(capacity) creates
+ * capacity pairs of HIP events (0 disables timing and releases them); while
+ * enabled, each main split-GEMM kernel (kind 0; d = M, N, K, K-extension) and
+ * each quantiser sweep (kind 1: amax pass, kind 2: quantise pass; d = rows,
+ * cols, axes, K of the rank-k product) is bracketed by events recorded on the
+ * launching stream, until the capacity is used up.  metis_timing_read waits
+ * for the recorded events, writes up to max_records durations (ms) and
+ * 5-tuples (kind, d0, d1, d2, d3), resets the record list and returns the
+ * number written. */
+metis_status metis_timing_enable(int32_t capacity);
+int32_t metis_timing_read(float *ms, int64_t *shape, int32_t max_records);
+
 /* Host-only helpers (no GPU needed) exposing the library's own definitions
  * of its random draws, for verification against an independent model.
  * metis_omega_table: the 65536 bf16 bit patterns of the Gaussian quantile

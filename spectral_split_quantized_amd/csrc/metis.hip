@@ -12,6 +12,7 @@
 
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/metis.h"
 #include "common.hpp"
@@ -46,6 +47,39 @@ metis_status fail(metis_status st, const char* fmt, ...) {
     hipError_t e__ = hipGetLastError();                                                   \
     if (e__ != hipSuccess) return fail(METIS_E_HIP, "kernel launch: %s", hipGetErrorString(e__)); \
   } while (0)
+
+// ---------------------------------------------- benchmark instrumentation
+
+// When enabled, a pair of HIP events is recorded on the launching stream
+// around each main split-GEMM kernel (kind 0) and each quantiser sweep (kind
+// 1: amax pass, kind 2: quantise pass).  Events are created once, when timing
+// is enabled; recording them allocates nothing.
+struct TimingRec {
+  hipEvent_t a, b;
+  int64_t kind, d0, d1, d2, d3;
+};
+std::mutex g_tmu;
+std::vector<TimingRec> g_trecs;
+size_t g_tused = 0;
+bool g_timing = false;
+
+TimingRec* timing_begin(hipStream_t st, int64_t kind, int64_t d0, int64_t d1, int64_t d2, int64_t d3) {
+  if (!g_timing) return nullptr;
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (g_tused >= g_trecs.size()) return nullptr;
+  TimingRec* r = &g_trecs[g_tused++];
+  r->kind = kind;
+  r->d0 = d0;
+  r->d1 = d1;
+  r->d2 = d2;
+  r->d3 = d3;
+  hipEventRecord(r->a, st);
+  return r;
+}
+
+void timing_end(TimingRec* r, hipStream_t st) {
+  if (r) hipEventRecord(r->b, st);
+}
 
 // ------------------------------------------------------- Omega quantile table
 
@@ -232,16 +266,21 @@ metis_status run_quant(const QuantParams& qp, bool has_f, int64_t rows, int64_t 
                        hipStream_t st) {
   const dim3 grid((unsigned)ceil_div<int64_t>(cols, kQT_C), (unsigned)ceil_div<int64_t>(rows, kQT_R));
   if (grid.y > 65535u) return fail(METIS_E_UNSUPPORTED, "too many rows (%lld)", (long long)rows);
-  if (has_f) {
+  const int64_t kc = has_f ? qp.kc : 0;
+  TimingRec* t1 = timing_begin(st, 1, rows, cols, qp.axes, kc);
+  if (has_f)
     hipLaunchKernelGGL((quant_kernel<true, false>), grid, dim3(kQThreads), 0, st, qp);
-    LAUNCH_CHECK();
-    hipLaunchKernelGGL((quant_kernel<true, true>), grid, dim3(kQThreads), 0, st, qp);
-  } else {
+  else
     hipLaunchKernelGGL((quant_kernel<false, false>), grid, dim3(kQThreads), 0, st, qp);
-    LAUNCH_CHECK();
-    hipLaunchKernelGGL((quant_kernel<false, true>), grid, dim3(kQThreads), 0, st, qp);
-  }
   LAUNCH_CHECK();
+  timing_end(t1, st);
+  TimingRec* t2 = timing_begin(st, 2, rows, cols, qp.axes, kc);
+  if (has_f)
+    hipLaunchKernelGGL((quant_kernel<true, true>), grid, dim3(kQThreads), 0, st, qp);
+  else
+    hipLaunchKernelGGL((quant_kernel<false, true>), grid, dim3(kQThreads), 0, st, qp);
+  LAUNCH_CHECK();
+  timing_end(t2, st);
   return METIS_OK;
 }
 
@@ -369,7 +408,10 @@ metis_status split_product(const SideQ& L, const SideQ& R, int64_t M, int64_t N,
   }
   g = GemmParams{M, N, K, L.res->codes, L.res->scales, R.res->codes, R.res->scales,
                  L.res->tensor_scale, R.res->tensor_scale, kext, w.a_ext, w.b_ext, C, ldc};
-  return launch_gemm(g, st);
+  TimingRec* tr = timing_begin(st, 0, M, N, K, kext);
+  s = launch_gemm(g, st);
+  timing_end(tr, st);
+  return s;
 }
 
 size_t split_ws_size(int64_t M, int64_t N, int kL, int kR) {
@@ -694,6 +736,42 @@ metis_status metis_gemm_bwd(const metis_qoperand* D, const metis_qoperand* W, co
       return s;
   }
   return METIS_OK;
+}
+
+metis_status metis_timing_enable(int32_t capacity) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  for (auto& r : g_trecs) {
+    hipEventDestroy(r.a);
+    hipEventDestroy(r.b);
+  }
+  g_trecs.clear();
+  g_tused = 0;
+  g_timing = capacity > 0;
+  if (!g_timing) return METIS_OK;
+  g_trecs.resize((size_t)capacity);
+  for (auto& r : g_trecs) {
+    HIP_TRY(hipEventCreate(&r.a));
+    HIP_TRY(hipEventCreate(&r.b));
+  }
+  return METIS_OK;
+}
+
+int32_t metis_timing_read(float* ms, int64_t* shape, int32_t max_records) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  int32_t n = 0;
+  for (size_t i = 0; i < g_tused && n < max_records; ++i, ++n) {
+    TimingRec& r = g_trecs[i];
+    float t = -1.0f;
+    if (hipEventSynchronize(r.b) == hipSuccess) hipEventElapsedTime(&t, r.a, r.b);
+    ms[n] = t;
+    shape[5 * n + 0] = r.kind;
+    shape[5 * n + 1] = r.d0;
+    shape[5 * n + 2] = r.d1;
+    shape[5 * n + 3] = r.d2;
+    shape[5 * n + 4] = r.d3;
+  }
+  g_tused = 0;
+  return n;
 }
 
 metis_status metis_status_sync(void* stream) {

@@ -89,6 +89,10 @@ def load():
     lib.metis_status_sync.restype = i32
     lib.metis_omega_table.argtypes = [P]
     lib.metis_omega_table.restype = None
+    lib.metis_timing_enable.argtypes = [i32]
+    lib.metis_timing_enable.restype = i32
+    lib.metis_timing_read.argtypes = [P, P, i32]
+    lib.metis_timing_read.restype = i32
     lib.metis_philox4x32_10.argtypes = [ctypes.POINTER(ctypes.c_uint32)] * 3
     lib.metis_philox4x32_10.restype = None
     _lib = lib
@@ -262,3 +266,22 @@ def philox_block(ctr, key):
     o = (ctypes.c_uint32 * 4)()
     load().metis_philox4x32_10(c, k, o)
     return tuple(o)
+
+
+def timing_enable(capacity):
+    """Start recording HIP events around the main GEMM and quantiser kernels."""
+    _check(load().metis_timing_enable(int(capacity)))
+
+
+def timing_read(max_records=1 << 16):
+    """[(kind, ms, d0, d1, d2, d3), ...] for the recorded kernels (and reset)."""
+    import numpy as np
+    ms = np.zeros(max_records, dtype=np.float32)
+    shape = np.zeros(5 * max_records, dtype=np.int64)
+    n = load().metis_timing_read(ms.ctypes.data_as(ctypes.c_void_p),
+                                 shape.ctypes.data_as(ctypes.c_void_p), max_records)
+    out = []
+    for i in range(n):
+        k, d0, d1, d2, d3 = (int(v) for v in shape[5 * i:5 * i + 5])
+        out.append((k, float(ms[i]), d0, d1, d2, d3))
+    return out

@@ -82,6 +82,37 @@ def anisotropic(rows, cols, frac, seed, out_dtype=torch.bfloat16, device="cpu",
     return out
 
 
+def anisotropic_fast(rows, cols, frac, seed, out_dtype=torch.bfloat16, device="cuda",
+                     basis=None, theta=0.0, noise=0.01, work_dtype=torch.float32):
+    """Large-shape variant of :func:`anisotropic` (LLaMA-3-8B-sized operands).
+
+    The dominant part is exact: U_dom (rows x n_dom) is Haar and the right
+    basis comes from ``basis`` (cols x 2 n_dom, Haar; drawn when None), whose
+    first n_dom columns are turned towards the next n_dom by ``theta``
+    (the dominant subspace rotated by theta).  The tail sigma_i = i**-0.5 uses
+    Gaussian bases with unit expected column norm instead of exactly
+    orthonormal ones, which avoids full-width QRs; at these shapes the tail
+    lies below the 0.01 N(0,1) noise floor.  Returns (M, basis)."""
+    gen = _generator(seed, device)
+    rho = min(rows, cols)
+    n_dom = n_dominant(rows, cols, frac)
+    sigma = spectrum(rho, n_dom, gen, work_dtype)
+    u_dom = haar(rows, n_dom, gen, work_dtype)
+    if basis is None:
+        basis = haar(cols, 2 * n_dom, gen, work_dtype)
+    c, s = math.cos(theta), math.sin(theta)
+    v_dom = c * basis[:, :n_dom] + s * basis[:, n_dom:2 * n_dom]
+    m = (u_dom * sigma[:n_dom]) @ v_dom.T
+    nt = rho - n_dom
+    if nt > 0:
+        gu = torch.randn(rows, nt, generator=gen, dtype=work_dtype, device=device) / math.sqrt(rows)
+        gv = torch.randn(cols, nt, generator=gen, dtype=work_dtype, device=device) / math.sqrt(cols)
+        m.addmm_(gu * sigma[n_dom:], gv.T)
+        del gu, gv
+    m.add_(torch.randn(rows, cols, generator=gen, dtype=work_dtype, device=device), alpha=noise)
+    return m.to(out_dtype), basis
+
+
 def rotate_dominant(v, n_dom, theta):
     """Rotate each dominant right vector v_i in the plane (v_i, v_{n_dom+i})
     by angle theta; the partner turns the other way so V stays orthonormal."""
