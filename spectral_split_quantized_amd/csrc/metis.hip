@@ -170,7 +170,10 @@ struct DecompWs {
   uint2* cand;
   uint8_t* flags;
   int32_t* idx;
-  float *om, *y, *q, *bpart, *b, *p, *vn, *sign;
+  float *om, *y, *q, *bpart, *b, *p, *vn, *sign, *ppart;
+  uint16_t* vfrag;
+  bool proj_mfma;
+  int64_t proj_nkb, proj_kbps, proj_splits;
   double *gpart, *g, *rinv, *z, *theta, *ptp, *rot, *lam;
   int gblocks, slices;
   int64_t rows_per_gblock, rows_per_slice;
@@ -209,6 +212,16 @@ DecompWs carve_decompose(Carver& cv, int64_t rows, int64_t cols, int k, int n, i
   w.lam = cv.take<double>(kMaxN);
   w.vn = cv.take<float>(cols * k);
   w.sign = cv.take<float>(kMaxN);
+  // MFMA projection (bf16 operands, cols % 64 == 0, k <= 64): split-K plan
+  w.proj_nkb = cols / 64;
+  const int64_t row_blocks = (rows + 127) / 128;
+  int64_t splits = (1024 + row_blocks - 1) / row_blocks;
+  if (splits > w.proj_nkb) splits = w.proj_nkb;
+  if (splits < 1) splits = 1;
+  w.proj_kbps = (w.proj_nkb + splits - 1) / splits;
+  w.proj_splits = (w.proj_nkb + w.proj_kbps - 1) / w.proj_kbps;
+  w.vfrag = cv.take<uint16_t>((size_t)w.proj_nkb * kProjFragU4 * 8);
+  w.ppart = cv.take<float>((size_t)w.proj_splits * rows * 64);
   return w;
 }
 
@@ -570,9 +583,24 @@ metis_status metis_decompose(const void* M, int32_t dtype, int64_t rows, int64_t
   }
 
   // projection and rediagonalisation (every step)
-  hipLaunchKernelGGL(project_kernel, dim3(grid1(rows, 64)), dim3(256), 0, st, M, dtype, ld, rows, cols,
-                     f->V, k, w.p);
-  LAUNCH_CHECK();
+  const bool proj_mfma = dtype == METIS_BF16 && cols % 64 == 0 && ld % 8 == 0 &&
+                         ((uintptr_t)M & 15) == 0 && k <= 64;
+  if (proj_mfma) {
+    hipLaunchKernelGGL(proj_prep_kernel, dim3(grid1(w.proj_nkb * 4096, 256)), dim3(256), 0, st, f->V,
+                       cols, k, w.proj_nkb, w.vfrag);
+    LAUNCH_CHECK();
+    hipLaunchKernelGGL(project_mfma_kernel, dim3((unsigned)ceil_div<int64_t>(rows, 128), (unsigned)w.proj_splits),
+                       dim3(256), 0, st, (const uint16_t*)M, ld, rows, w.vfrag, w.proj_nkb, w.proj_kbps,
+                       w.ppart);
+    LAUNCH_CHECK();
+    hipLaunchKernelGGL(project_reduce_kernel, dim3(grid1(rows * k, 256)), dim3(256), 0, st, w.ppart,
+                       w.proj_splits, rows, k, w.p);
+    LAUNCH_CHECK();
+  } else {
+    hipLaunchKernelGGL(project_kernel, dim3(grid1(rows, 64)), dim3(256), 0, st, M, dtype, ld, rows, cols,
+                       f->V, k, w.p);
+    LAUNCH_CHECK();
+  }
   if ((s = launch_gram(w.p, rows, k, k, 1, w.gblocks, w.gpart, w.ptp, st)) != METIS_OK) return s;
   hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(1024), 0, st, w.ptp, k, w.lam, w.rot);
   LAUNCH_CHECK();

@@ -595,6 +595,115 @@ __global__ __launch_bounds__(256) void project_kernel(const void* __restrict__ M
     }
 }
 
+// ------------------------------------------- MFMA projection P = M V (bf16 M)
+//
+// M is exact in bf16; V (binary32) is carried as three bf16 terms
+// v = t0 + t1 + t2 (+ O(2^-24 |v|)), so P = sum_t M T_t is the fp32-accurate
+// product on bf16 MFMA with fp32 accumulation.  The reduction axis (cols of
+// M) is walked in blocks of 64; inside a block, lane half h of a wave owns K
+// indices 32h + 8j + i (j = MFMA step 0..3, i = 0..7) for both operands, so
+// each lane reads 64 contiguous bytes of its row of M.  V's fragments are
+// pre-arranged in exactly the order the waves read them from LDS.
+
+constexpr int kProjFragU4 = 3 * 2 * 4 * 64;  // uint4 slots per K block (24 KB)
+
+// vfrag[((kb*3 + t)*2 + n)*4 + j][lane] (uint4 of 8 bf16): column n*32 + lane%32,
+// K = kb*64 + 32*(lane/32) + 8*j + i.
+__global__ void proj_prep_kernel(const float* __restrict__ V, int64_t cols, int k, int64_t nkb,
+                                 uint16_t* __restrict__ vfrag) {
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // one element
+  const int64_t total = nkb * 2 * 4 * 64 * 8;
+  if (id >= total) return;
+  const int i = (int)(id & 7);
+  const int lane = (int)((id >> 3) & 63);
+  const int j = (int)((id >> 9) & 3);
+  const int n = (int)((id >> 11) & 1);
+  const int64_t kb = id >> 12;
+  const int col = n * 32 + (lane & 31);
+  const int64_t kk = kb * 64 + 32 * (lane >> 5) + 8 * j + i;
+  const float v = (col < k && kk < cols) ? V[kk * k + col] : 0.0f;
+  const __bf16 t0 = (__bf16)v;
+  const float r1 = v - (float)t0;
+  const __bf16 t1 = (__bf16)r1;
+  const __bf16 t2 = (__bf16)(r1 - (float)t1);
+  const __bf16 t[3] = {t0, t1, t2};
+#pragma unroll
+  for (int tt = 0; tt < 3; ++tt) {
+    const int64_t slot = (((kb * 3 + tt) * 2 + n) * 4 + j) * 64 + lane;
+    vfrag[slot * 8 + i] = __builtin_bit_cast(uint16_t, t[tt]);
+  }
+}
+
+// part[s][row][64] = sum over K blocks of split s of M[row] V (128 rows per
+// workgroup, one 32-row slab per wave, 64 output columns as two 32x32 tiles).
+__global__ __launch_bounds__(256) void project_mfma_kernel(const uint16_t* __restrict__ M, int64_t ld,
+                                                           int64_t rows,
+                                                           const uint16_t* __restrict__ vfrag,
+                                                           int64_t nkb, int64_t kb_per_split,
+                                                           float* __restrict__ part) {
+  __shared__ uint4 vs[2 * kProjFragU4];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t r0 = (int64_t)blockIdx.x * 128;
+  const int64_t s = blockIdx.y;
+  const int64_t kb0 = s * kb_per_split;
+  const int64_t kb1 = min(nkb, kb0 + kb_per_split);
+  const int64_t row = r0 + wave * 32 + (lane & 31);
+  const bool rv = row < rows;
+  const uint16_t* mrow = M + (rv ? row : 0) * ld + 32 * (lane >> 5);
+  f32x16_t acc0 = {}, acc1 = {};
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  for (int64_t kb = kb0; kb < kb1; kb += 2) {
+    const int nb = (int)min((int64_t)2, kb1 - kb);
+    uint4 a[2][4];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        a[b][j] = (rv && b < nb) ? *(const uint4*)(mrow + (kb + b) * 64 + 8 * j) : z;
+    __syncthreads();
+    const uint4* src = (const uint4*)vfrag + kb * kProjFragU4;
+    for (int e = tid; e < nb * kProjFragU4; e += 256) vs[e] = src[e];
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      if (b >= nb) break;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, a[b][j]);
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+          const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, vs[b * kProjFragU4 + ((t * 2 + 0) * 4 + j) * 64 + lane]);
+          const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, vs[b * kProjFragU4 + ((t * 2 + 1) * 4 + j) * 64 + lane]);
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b0, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b1, acc1, 0, 0, 0);
+        }
+      }
+    }
+  }
+  const int col = lane & 31;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int64_t ro = r0 + wave * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+    if (ro < rows) {
+      float* dst = part + (s * rows + ro) * 64;
+      dst[col] = acc0[v];
+      dst[32 + col] = acc1[v];
+    }
+  }
+}
+
+// P[row][j] = sum_s part[s][row][j], j < k (fixed order: deterministic).
+__global__ void project_reduce_kernel(const float* __restrict__ part, int64_t splits, int64_t rows,
+                                      int k, float* __restrict__ P) {
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= rows * k) return;
+  const int64_t r = id / k;
+  const int j = (int)(id % k);
+  float acc = 0.0f;
+  for (int64_t s = 0; s < splits; ++s) acc += part[(s * rows + r) * 64 + j];
+  P[id] = acc;
+}
+
 // Vn = V R (cols x k), fp64 accumulation.
 __global__ void rotate_kernel(const float* __restrict__ V, int64_t cols, int k,
                               const double* __restrict__ R, float* __restrict__ Vn) {
