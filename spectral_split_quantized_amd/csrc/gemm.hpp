@@ -13,11 +13,12 @@
 // the low-rank terms of the split as bf16 hi/lo pairs; it is accumulated
 // after alpha has been applied to the main sum.
 //
-// Tiling: BM x BN output tile per 256-thread workgroup, 4 waves in 2 x 2,
-// each wave (BM/2) x (BN/2) as 32 x 32 MFMA tiles; K step 64; FP4 codes are
-// loaded to registers one tile ahead, dequantised once per element and
-// stored to a double-buffered LDS area laid out in MFMA fragment order
-// (one barrier per K step).  Workgroup ids are remapped so that each XCD
+// Tiling: BM x BN output tile per workgroup of WM x WN waves, each wave
+// (BM/WM) x (BN/WN) as 32 x 32 MFMA tiles; K step 64; FP4 codes are loaded to
+// registers one tile ahead, dequantised once per element and stored to a
+// double-buffered LDS area laid out in MFMA fragment order (one barrier per
+// K step).  Skinny products (one side = the rank k) split K across
+// workgroups and reduce the partial sums in a fixed order.  Workgroup ids are remapped so that each XCD
 // (ids are dealt round-robin over 8 XCDs) walks a contiguous, row-grouped
 // range of tiles and so shares A and B panels in its own L2.
 #pragma once
@@ -42,41 +43,38 @@ struct GemmParams {
 };
 
 // 8 E2M1 codes (one dword, element 0 in the low nibble) -> 8 fp16 values
-// (exact grid values), by byte lookups: the fp16 high byte of magnitude m is
-// {00, 38, 3C, 3E, 40, 42, 44, 46}[m] | sign << 7 and the low byte is 0.
-__device__ inline uint4 e2m1x8_to_f16(uint32_t w) {
-  const uint32_t lut_lo = 0x3E3C3800u;
-  const uint32_t lut_hi = 0x46444240u;
-  const uint32_t me = w & 0x07070707u;
-  const uint32_t mo = (w >> 4) & 0x07070707u;
-  const uint32_t he = __builtin_amdgcn_perm(lut_hi, lut_lo, me) | ((w << 4) & 0x80808080u);
-  const uint32_t ho = __builtin_amdgcn_perm(lut_hi, lut_lo, mo) | (w & 0x80808080u);
+// grid(code) * s_b.  v_cvt_scalef32_pk_f16_fp4 applies only the exponent of
+// its scale operand, so it is used with scale 1 (exact grid values, low
+// nibble first) and the E4M3 block scale is applied by one packed fp16
+// multiply; the product is exact (<= 6 significant bits, in fp16 range).
+__device__ inline uint4 dequant8(uint32_t w, half2_t s) {
+  const half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
+  const half2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
+  const half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
+  const half2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
   uint4 o;
-  o.x = __builtin_amdgcn_perm(ho, he, 0x040C000Cu);
-  o.y = __builtin_amdgcn_perm(ho, he, 0x050C010Cu);
-  o.z = __builtin_amdgcn_perm(ho, he, 0x060C020Cu);
-  o.w = __builtin_amdgcn_perm(ho, he, 0x070C030Cu);
+  o.x = __builtin_bit_cast(uint32_t, h0);
+  o.y = __builtin_bit_cast(uint32_t, h1);
+  o.z = __builtin_bit_cast(uint32_t, h2);
+  o.w = __builtin_bit_cast(uint32_t, h3);
   return o;
 }
 
-__device__ inline uint32_t pk_mul_f16(uint32_t a, half2_t s) {
-  half2_t x = __builtin_bit_cast(half2_t, a);
-  x = x * s;
-  return __builtin_bit_cast(uint32_t, x);
-}
-
-template <int BM, int BN>
+// BM x BN tile, WM x WN waves; each wave owns (BM/WM) x (BN/WN) as 32 x 32
+// MFMA tiles.  K step 64.
+template <int BM, int BN, int WM, int WN>
 struct GemmCfg {
-  static constexpr int kThreads = 256;
+  static constexpr int kThreads = WM * WN * 64;
   static constexpr int BK = 64;
-  static constexpr int TM = BM / 64;  // 32-row MFMA tiles per wave
-  static constexpr int TN = BN / 64;
-  static constexpr int GA = BM / 32;  // 32-row groups in the tile
+  static constexpr int TM = BM / WM / 32;
+  static constexpr int TN = BN / WN / 32;
+  static constexpr int GA = BM / 32;
   static constexpr int GB = BN / 32;
   static constexpr int NCA = (BM * 2 + kThreads - 1) / kThreads;  // FP4 chunks / thread
   static constexpr int NCB = (BN * 2 + kThreads - 1) / kThreads;
   static constexpr int LDS_A = BM * BK;  // halfs per stage
   static constexpr int LDS_B = BN * BK;
+  static_assert(TM >= 1 && TN >= 1, "wave tile smaller than one MFMA tile");
 };
 
 // offset (in halfs) of the 8-half fragment slot for (kk, group, lane)
@@ -93,11 +91,11 @@ struct RawChunk {
 };
 
 __device__ inline RawChunk load_chunk(const uint8_t* codes, const uint8_t* scales, int64_t nrows,
-                                      int64_t K, int64_t row, int64_t kbase) {
+                                      int64_t K, int64_t row, int64_t kbase, int64_t kend) {
   RawChunk c;
   c.valid = row < nrows;
-  c.k0 = kbase < K;
-  c.k1 = kbase + 16 < K;
+  c.k0 = kbase < kend;
+  c.k1 = kbase + 16 < kend;
   c.codes = make_uint4(0, 0, 0, 0);
   c.sc = 0;
   if (c.valid && c.k0) {
@@ -133,12 +131,7 @@ __device__ inline void store_chunk(_Float16* lds, const RawChunk& c, int lrow, i
   const int g = lrow >> 5, r = lrow & 31;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    uint4 v = e2m1x8_to_f16(w[i]);
-    const half2_t s = (i < 2) ? s0 : s1;
-    v.x = pk_mul_f16(v.x, s);
-    v.y = pk_mul_f16(v.y, s);
-    v.z = pk_mul_f16(v.z, s);
-    v.w = pk_mul_f16(v.w, s);
+    uint4 v = dequant8(w[i], (i < 2) ? s0 : s1);
     const bool ok = c.valid && ((i < 2) ? c.k0 : c.k1);
     if (!ok) v = make_uint4(0, 0, 0, 0);
     const int kk = 2 * h + (i >> 1);
@@ -165,22 +158,30 @@ __device__ inline int64_t remap_tile(int64_t bid, int64_t tiles_m, int64_t tiles
 
 extern __shared__ __align__(16) _Float16 g_gemm_smem[];
 
-template <int BM, int BN>
-__global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmParams p) {
-  using Cfg = GemmCfg<BM, BN>;
+// gridDim.x = tiles, gridDim.y = K splits.  With splits > 1 the split's raw
+// partial sum goes to C + split * M * ldc (alpha and the K-extension are
+// not allowed then).
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_fp4_kernel(GemmParams p) {
+  using Cfg = GemmCfg<BM, BN, WM, WN>;
   constexpr int BK = Cfg::BK, TM = Cfg::TM, TN = Cfg::TN, GA = Cfg::GA, GB = Cfg::GB;
+  constexpr int NT = Cfg::kThreads;
   constexpr int kStage = Cfg::LDS_A + Cfg::LDS_B;
   auto lds_a = [&](int buf) { return g_gemm_smem + buf * kStage; };
   auto lds_b = [&](int buf) { return g_gemm_smem + buf * kStage + Cfg::LDS_A; };
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int64_t tiles_m = ceil_div<int64_t>(p.M, BM);
   const int64_t tiles_n = ceil_div<int64_t>(p.N, BN);
   const int64_t tile = remap_tile(blockIdx.x, tiles_m, tiles_n);
   const int64_t m0 = (tile / tiles_n) * BM;
   const int64_t n0 = (tile % tiles_n) * BN;
+  const int64_t nsplit = gridDim.y;
+  const int64_t kper = ceil_div<int64_t>(ceil_div<int64_t>(p.K, BK), nsplit) * BK;
+  const int64_t kbeg = (int64_t)blockIdx.y * kper;
+  const int64_t kend = min(p.K, kbeg + kper);
 
   f32x16_t acc[TM][TN];
 #pragma unroll
@@ -188,32 +189,33 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16_t{};
 
-  const int64_t nk = ceil_div<int64_t>(p.K, BK);
+  const int64_t nk = kend > kbeg ? ceil_div<int64_t>(kend - kbeg, BK) : 0;
   RawChunk ra[Cfg::NCA], rb[Cfg::NCB];
 
   auto load_tile = [&](int64_t kt) {
+    const int64_t kb = kbeg + kt * BK;
 #pragma unroll
     for (int i = 0; i < Cfg::NCA; ++i) {
-      const int c = tid + i * Cfg::kThreads;
+      const int c = tid + i * NT;
       if (c < BM * 2)
-        ra[i] = load_chunk(p.a_codes, p.a_scales, p.M, p.K, m0 + (c >> 1), kt * BK + (c & 1) * 32);
+        ra[i] = load_chunk(p.a_codes, p.a_scales, p.M, p.K, m0 + (c >> 1), kb + (c & 1) * 32, kend);
     }
 #pragma unroll
     for (int i = 0; i < Cfg::NCB; ++i) {
-      const int c = tid + i * Cfg::kThreads;
+      const int c = tid + i * NT;
       if (c < BN * 2)
-        rb[i] = load_chunk(p.b_codes, p.b_scales, p.N, p.K, n0 + (c >> 1), kt * BK + (c & 1) * 32);
+        rb[i] = load_chunk(p.b_codes, p.b_scales, p.N, p.K, n0 + (c >> 1), kb + (c & 1) * 32, kend);
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < Cfg::NCA; ++i) {
-      const int c = tid + i * Cfg::kThreads;
+      const int c = tid + i * NT;
       if (c < BM * 2) store_chunk<GA>(lds_a(buf), ra[i], c >> 1, c & 1);
     }
 #pragma unroll
     for (int i = 0; i < Cfg::NCB; ++i) {
-      const int c = tid + i * Cfg::kThreads;
+      const int c = tid + i * NT;
       if (c < BN * 2) store_chunk<GB>(lds_b(buf), rb[i], c >> 1, c & 1);
     }
   };
@@ -262,14 +264,14 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmParams p) {
     const int64_t ne = p.kext / BK;
     for (int64_t kt = 0; kt < ne; ++kt) {
       // 8 chunks of 8 bf16 per row and K step
-      for (int c = tid; c < BM * 8; c += Cfg::kThreads) {
+      for (int c = tid; c < BM * 8; c += NT) {
         const int lrow = c >> 3, c8 = c & 7;
         const int64_t row = m0 + lrow;
         uint4 v = make_uint4(0, 0, 0, 0);
         if (row < p.M) v = *(const uint4*)(p.a_ext + row * p.kext + kt * BK + c8 * 8);
         *(uint4*)(lds_a(0) + frag_off<GA>(c8 >> 1, lrow >> 5, (c8 & 1) * 32 + (lrow & 31))) = v;
       }
-      for (int c = tid; c < BN * 8; c += Cfg::kThreads) {
+      for (int c = tid; c < BN * 8; c += NT) {
         const int lrow = c >> 3, c8 = c & 7;
         const int64_t row = n0 + lrow;
         uint4 v = make_uint4(0, 0, 0, 0);
@@ -297,6 +299,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmParams p) {
   }
 
   // ---- epilogue: lane holds column lane%32 and rows 8(v/4) + 4(lane/32) + v%4
+  float* C = p.C + (int64_t)blockIdx.y * p.M * p.ldc;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -306,15 +309,26 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int64_t row = m0 + (wm * TM + i) * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (row < p.M) p.C[row * p.ldc + col] = acc[i][j][v];
+        if (row < p.M) C[row * p.ldc + col] = acc[i][j][v];
       }
     }
   }
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int WM, int WN>
 inline size_t gemm_lds_bytes() {
-  return 2 * (size_t)(GemmCfg<BM, BN>::LDS_A + GemmCfg<BM, BN>::LDS_B) * sizeof(_Float16);
+  using Cfg = GemmCfg<BM, BN, WM, WN>;
+  return 2 * (size_t)(Cfg::LDS_A + Cfg::LDS_B) * sizeof(_Float16);
+}
+
+// out[i] = sum over splits of part[s][i] (fixed order: deterministic)
+__global__ void reduce_splits_kernel(const float* __restrict__ part, int splits, int64_t count,
+                                     float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= count) return;
+  float s = 0.0f;
+  for (int k = 0; k < splits; ++k) s += part[(int64_t)k * count + i];
+  out[i] = s;
 }
 
 // --------------------------------------------------- split-term operand prep --

@@ -10,6 +10,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -304,30 +305,82 @@ bool q4_ok(const metis_q4& q, int64_t n_outer, int64_t k_len) {
 
 // ----------------------------------------------------------------- GEMMs --
 
-template <int BM, int BN>
-metis_status launch_gemm_cfg(const GemmParams& gp, hipStream_t st) {
+template <int BM, int BN, int WM, int WN>
+metis_status launch_gemm_cfg(const GemmParams& gp, int splits, hipStream_t st) {
   const int64_t tiles = ceil_div<int64_t>(gp.M, BM) * ceil_div<int64_t>(gp.N, BN);
   if (tiles <= 0) return METIS_OK;
-  const size_t lds = gemm_lds_bytes<BM, BN>();
+  const size_t lds = gemm_lds_bytes<BM, BN, WM, WN>();
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [&] {
-    attr_err = hipFuncSetAttribute((const void*)gemm_fp4_kernel<BM, BN>,
+    attr_err = hipFuncSetAttribute((const void*)gemm_fp4_kernel<BM, BN, WM, WN>,
                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   });
   if (attr_err != hipSuccess) return fail(METIS_E_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(attr_err));
-  hipLaunchKernelGGL((gemm_fp4_kernel<BM, BN>), dim3((unsigned)tiles), dim3(256), lds, st, gp);
+  hipLaunchKernelGGL((gemm_fp4_kernel<BM, BN, WM, WN>), dim3((unsigned)tiles, (unsigned)splits),
+                     dim3(WM * WN * 64), lds, st, gp);
   LAUNCH_CHECK();
   return METIS_OK;
 }
 
-metis_status launch_gemm(const GemmParams& gp, hipStream_t st) {
-  if (gp.M <= 0 || gp.N <= 0) return METIS_OK;
-  const int64_t t256 = ceil_div<int64_t>(gp.M, 256) * ceil_div<int64_t>(gp.N, 256);
-  const int64_t t128 = ceil_div<int64_t>(gp.M, 128) * ceil_div<int64_t>(gp.N, 128);
-  (void)t256;
-  if (gp.M >= 128 && gp.N >= 128 && t128 >= 256) return launch_gemm_cfg<128, 128>(gp, st);
-  return launch_gemm_cfg<64, 64>(gp, st);
+enum GemmShape { kGemmBig, kGemmMid, kGemmTall, kGemmWide, kGemmSmall };
+
+GemmShape gemm_shape(int64_t M, int64_t N) {
+  if (N <= 64 && M > 64) return kGemmTall;
+  if (M <= 64 && N > 64) return kGemmWide;
+  if (M <= 64 && N <= 64) return kGemmSmall;
+  const int64_t t256 = ceil_div<int64_t>(M, 256) * ceil_div<int64_t>(N, 256);
+  return t256 >= 256 ? kGemmBig : kGemmMid;
+}
+
+// K splits for a skinny product: enough workgroups to cover the GPU, at
+// least 4 K steps each.
+int gemm_splits(int64_t M, int64_t N, int64_t K) {
+  int64_t tiles;
+  switch (gemm_shape(M, N)) {
+    case kGemmTall: tiles = ceil_div<int64_t>(M, 256); break;
+    case kGemmWide: tiles = ceil_div<int64_t>(N, 256); break;
+    case kGemmSmall: tiles = 1; break;
+    default: return 1;
+  }
+  const int64_t nk = ceil_div<int64_t>(K, 64);
+  int64_t s = ceil_div<int64_t>(512, tiles);
+  const int64_t smax = nk / 4 > 1 ? nk / 4 : 1;
+  if (s > smax) s = smax;
+  if (s > 64) s = 64;
+  return (int)(s < 1 ? 1 : s);
+}
+
+// C = A B^T (+ alpha, K-extension).  Split-K products need a partial buffer
+// of splits * M * N floats (`part`) and are reduced into C (ldc == N).
+metis_status launch_gemm(const GemmParams& gp0, float* part, hipStream_t st) {
+  if (gp0.M <= 0 || gp0.N <= 0) return METIS_OK;
+  const int splits = gemm_splits(gp0.M, gp0.N, gp0.K);
+  GemmParams gp = gp0;
+  if (splits > 1) {
+    if (gp.kext > 0 || gp.sa || gp.sb || !part || gp.ldc != gp.N)
+      return fail(METIS_E_INVALID, "internal: split-K product with epilogue options");
+    gp.C = part;
+  }
+  metis_status s;
+  switch (gemm_shape(gp.M, gp.N)) {
+    case kGemmBig: s = launch_gemm_cfg<256, 256, 4, 2>(gp, splits, st); break;
+    case kGemmMid: s = launch_gemm_cfg<128, 128, 2, 2>(gp, splits, st); break;
+    case kGemmTall: s = launch_gemm_cfg<256, 64, 8, 1>(gp, splits, st); break;
+    case kGemmWide: s = launch_gemm_cfg<64, 256, 1, 8>(gp, splits, st); break;
+    default: s = launch_gemm_cfg<64, 64, 2, 2>(gp, splits, st); break;
+  }
+  if (s != METIS_OK || splits == 1) return s;
+  const int64_t count = gp.M * gp.N;
+  hipLaunchKernelGGL(reduce_splits_kernel, dim3(grid1(count, 256)), dim3(256), 0, st, part, splits,
+                     count, gp0.C);
+  LAUNCH_CHECK();
+  return METIS_OK;
+}
+
+size_t gemm_part_floats(int64_t M, int64_t N, int64_t K) {
+  const int s = gemm_splits(M, N, K);
+  return s > 1 ? (size_t)s * M * N : 0;
 }
 
 struct SideQ {
@@ -339,18 +392,23 @@ struct SideQ {
 };
 
 struct SplitWs {
-  float *praw, *t1, *t2, *ones;
+  float *praw, *t1, *t2, *ones, *part;
   uint16_t *a_ext, *b_ext;
   int64_t kext;
   int ksR, ksL;
 };
 
-SplitWs carve_split(Carver& cv, int64_t M, int64_t N, int kL, int kR) {
+SplitWs carve_split(Carver& cv, int64_t M, int64_t N, int64_t K, int kL, int kR) {
   SplitWs w{};
   w.ksR = round_up(kR, 16);
   w.ksL = round_up(kL, 16);
   w.kext = round_up(2 * w.ksR + 2 * w.ksL, 64);
   w.ones = cv.take<float>(4);
+  size_t part = 0;
+  if (kR > 0) part = std::max(part, gemm_part_floats(M, kR, K));
+  if (kL > 0) part = std::max(part, gemm_part_floats(kL, N, K));
+  if (kL > 0 && kR > 0) part = std::max(part, gemm_part_floats(kL, kR, K));
+  if (part) w.part = cv.take<float>(part);
   if (kR > 0) w.praw = cv.take<float>((size_t)M * kR);
   if (kL > 0) w.t1 = cv.take<float>((size_t)kL * N);
   if (kL > 0 && kR > 0) w.t2 = cv.take<float>((size_t)kL * kR);
@@ -366,7 +424,7 @@ SplitWs carve_split(Carver& cv, int64_t M, int64_t N, int kL, int kR) {
 metis_status split_product(const SideQ& L, const SideQ& R, int64_t M, int64_t N, int64_t K,
                            float* C, int64_t ldc, void* ws, size_t ws_bytes, hipStream_t st) {
   Carver cv(ws, ws_bytes);
-  SplitWs w = carve_split(cv, M, N, L.k, R.k);
+  SplitWs w = carve_split(cv, M, N, K, L.k, R.k);
   if (cv.used() > ws_bytes) return fail(METIS_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, cv.used());
   hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, st, (uint32_t*)w.ones, 0x3F800000u,
                      (int64_t)4);
@@ -376,17 +434,17 @@ metis_status split_product(const SideQ& L, const SideQ& R, int64_t M, int64_t N,
   if (R.k > 0) {  // P_raw = L_R . E   (M x kR)
     g = GemmParams{M, R.k, K, L.res->codes, L.res->scales, R.kf->codes, R.kf->scales,
                    nullptr, nullptr, 0, nullptr, nullptr, w.praw, R.k};
-    if ((s = launch_gemm(g, st)) != METIS_OK) return s;
+    if ((s = launch_gemm(g, w.part, st)) != METIS_OK) return s;
   }
   if (L.k > 0) {  // T1 = F . R_R   (kL x N)
     g = GemmParams{L.k, N, K, L.kf->codes, L.kf->scales, R.res->codes, R.res->scales,
                    nullptr, nullptr, 0, nullptr, nullptr, w.t1, N};
-    if ((s = launch_gemm(g, st)) != METIS_OK) return s;
+    if ((s = launch_gemm(g, w.part, st)) != METIS_OK) return s;
   }
   if (L.k > 0 && R.k > 0) {  // T2 = F . E   (kL x kR)
     g = GemmParams{L.k, R.k, K, L.kf->codes, L.kf->scales, R.kf->codes, R.kf->scales,
                    nullptr, nullptr, 0, nullptr, nullptr, w.t2, R.k};
-    if ((s = launch_gemm(g, st)) != METIS_OK) return s;
+    if ((s = launch_gemm(g, w.part, st)) != METIS_OK) return s;
   }
   int64_t kext = 0;
   if (L.k > 0 || R.k > 0) {
@@ -422,14 +480,14 @@ metis_status split_product(const SideQ& L, const SideQ& R, int64_t M, int64_t N,
   g = GemmParams{M, N, K, L.res->codes, L.res->scales, R.res->codes, R.res->scales,
                  L.res->tensor_scale, R.res->tensor_scale, kext, w.a_ext, w.b_ext, C, ldc};
   TimingRec* tr = timing_begin(st, 0, M, N, K, kext);
-  s = launch_gemm(g, st);
+  s = launch_gemm(g, nullptr, st);
   timing_end(tr, st);
   return s;
 }
 
-size_t split_ws_size(int64_t M, int64_t N, int kL, int kR) {
+size_t split_ws_size(int64_t M, int64_t N, int64_t K, int kL, int kR) {
   Carver cv(nullptr, 0);
-  carve_split(cv, M, N, kL, kR);
+  carve_split(cv, M, N, K, kL, kR);
   return cv.used();
 }
 
@@ -483,14 +541,14 @@ size_t metis_quantize_workspace(int64_t rows, int64_t cols, int32_t k) {
 
 size_t metis_gemm_fwd_workspace(const metis_qoperand* X, const metis_qoperand* W) {
   if (!X || !W) return 0;
-  return split_ws_size(X->rows, W->cols, X->k, W->k);
+  return split_ws_size(X->rows, W->cols, X->cols, X->k, W->k);
 }
 
 size_t metis_gemm_bwd_workspace(const metis_qoperand* D, const metis_qoperand* W,
                                 const metis_qoperand* X) {
   if (!D || !W || !X) return 0;
-  const size_t a = split_ws_size(D->rows, W->rows, D->k, W->k);
-  const size_t b = split_ws_size(X->cols, D->cols, X->k, D->k);
+  const size_t a = split_ws_size(D->rows, W->rows, D->cols, D->k, W->k);
+  const size_t b = split_ws_size(X->cols, D->cols, X->rows, X->k, D->k);
   return a > b ? a : b;
 }
 
