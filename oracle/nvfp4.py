@@ -30,8 +30,10 @@ along, i.e. the GEMM's reduction axis):
   s_g    float32 scalar
 For axis 1 (K = columns) n_outer is the row count; for axis 0 (K = rows) the
 tensor is taken transposed, so n_outer is the column count.  The stochastic
-rounding uniform of element (i, j) is drawn for the logical row-major index
-e = i * cols + j of the untransposed tensor, whatever the axis.
+rounding draw of an element is indexed by its position in the quantised
+orientation's own row-major layout (n_outer x K): e = i * cols + j along axis
+1 and e = j * rows + i along axis 0, so sixteen consecutive elements of a block
+always share two Philox blocks.
 """
 
 import numpy as np
@@ -101,10 +103,7 @@ def quantize(x, axis, rounding="rne", seed=0, tag=0, step=0):
     if rounding == "rne":
         m = formats.e2m1_rne(y)
     elif rounding == "sr":
-        ii = np.arange(rows, dtype=np.uint64)[:, None]
-        jj = np.arange(cols, dtype=np.uint64)[None, :]
-        e = ii * np.uint64(cols) + jj                     # logical index of x
-        et = e if axis == 1 else e.T
+        et = np.arange(n_outer * K, dtype=np.uint64)      # index in the (n_outer x K) layout
         u = philox.uniform_from_halves(philox.halves(et, seed, tag, step))
         m = formats.e2m1_sr(y, u.reshape(n_outer, K // BLOCK, BLOCK))
     else:

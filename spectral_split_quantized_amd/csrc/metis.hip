@@ -259,8 +259,8 @@ struct QuantWs {
   uint32_t* amax;  // 3 words: residual, U, V
   float* pre;
   float* pscale;
-  _Float16* acat;
-  _Float16* bcat;
+  _Float16* ucat;
+  _Float16* vcat;
 };
 
 QuantWs carve_quantize(Carver& cv, int64_t rows, int64_t cols, int k) {
@@ -270,32 +270,46 @@ QuantWs carve_quantize(Carver& cv, int64_t rows, int64_t cols, int k) {
   w.pscale = cv.take<float>(1);
   if (k > 0) {
     const int kc = 3 * round_up(k, 16);
-    w.acat = cv.take<_Float16>((size_t)rows * kc);
-    w.bcat = cv.take<_Float16>((size_t)cols * kc);
+    w.ucat = cv.take<_Float16>((size_t)((rows + 31) & ~(int64_t)31) * kc);
+    w.vcat = cv.take<_Float16>((size_t)((cols + 63) & ~(int64_t)63) * kc);
   }
   return w;
 }
 
-metis_status run_quant(const QuantParams& qp, bool has_f, int64_t rows, int64_t cols,
-                       hipStream_t st) {
-  const dim3 grid((unsigned)ceil_div<int64_t>(cols, kQT_C), (unsigned)ceil_div<int64_t>(rows, kQT_R));
-  if (grid.y > 65535u) return fail(METIS_E_UNSUPPORTED, "too many rows (%lld)", (long long)rows);
-  const int64_t kc = has_f ? qp.kc : 0;
+template <int NKK>
+metis_status launch_quant_pair(const QuantParams& qp, dim3 grid, int64_t rows, int64_t cols,
+                               hipStream_t st) {
+  const int64_t kc = NKK * 16;
   TimingRec* t1 = timing_begin(st, 1, rows, cols, qp.axes, kc);
-  if (has_f)
-    hipLaunchKernelGGL((quant_kernel<true, false>), grid, dim3(kQThreads), 0, st, qp);
-  else
-    hipLaunchKernelGGL((quant_kernel<false, false>), grid, dim3(kQThreads), 0, st, qp);
+  hipLaunchKernelGGL((quant_kernel<NKK, false>), grid, dim3(kQThreads), 0, st, qp);
   LAUNCH_CHECK();
   timing_end(t1, st);
   TimingRec* t2 = timing_begin(st, 2, rows, cols, qp.axes, kc);
-  if (has_f)
-    hipLaunchKernelGGL((quant_kernel<true, true>), grid, dim3(kQThreads), 0, st, qp);
-  else
-    hipLaunchKernelGGL((quant_kernel<false, true>), grid, dim3(kQThreads), 0, st, qp);
+  hipLaunchKernelGGL((quant_kernel<NKK, true>), grid, dim3(kQThreads), 0, st, qp);
   LAUNCH_CHECK();
   timing_end(t2, st);
   return METIS_OK;
+}
+
+metis_status run_quant(const QuantParams& qp0, bool has_f, int64_t rows, int64_t cols,
+                       hipStream_t st) {
+  QuantParams qp = qp0;
+  const int64_t panels = ceil_div<int64_t>(rows, kQT_R);
+  const int64_t ntc = ceil_div<int64_t>(cols, kQT_C);
+  int64_t tpw = panels * ntc / 2048;
+  if (tpw < 1) tpw = 1;
+  if (tpw > 16) tpw = 16;
+  qp.tiles_per_wg = (int)tpw;
+  const dim3 grid((unsigned)panels, (unsigned)ceil_div<int64_t>(ntc, tpw));
+  if (panels > INT32_MAX || grid.y > 65535u) return fail(METIS_E_UNSUPPORTED, "operand too large");
+  if (!has_f) return launch_quant_pair<0>(qp, grid, rows, cols, st);
+  switch (qp.kc / 16) {
+    case 3: return launch_quant_pair<3>(qp, grid, rows, cols, st);
+    case 6: return launch_quant_pair<6>(qp, grid, rows, cols, st);
+    case 9: return launch_quant_pair<9>(qp, grid, rows, cols, st);
+    case 12: return launch_quant_pair<12>(qp, grid, rows, cols, st);
+    default: return fail(METIS_E_UNSUPPORTED, "rank above 64 in the quantiser");
+  }
 }
 
 bool q4_ok(const metis_q4& q, int64_t n_outer, int64_t k_len) {
@@ -744,11 +758,12 @@ metis_status metis_quantize(const void* M, int32_t dtype, int64_t rows, int64_t 
     const int kp = round_up(k, 16);
     hipLaunchKernelGGL(resid_scale_kernel, dim3(1), dim3(64), 0, st, f->S, k, w.pre, w.pscale);
     LAUNCH_CHECK();
-    hipLaunchKernelGGL(resid_prep_kernel, dim3(grid1((rows + cols) * kp, 256)), dim3(256), 0, st, f->U,
-                       f->S, f->V, rows, cols, k, kp, w.pre, w.acat, w.bcat);
+    const int64_t rc_pad = ((rows + 31) & ~(int64_t)31) + ((cols + 63) & ~(int64_t)63);
+    hipLaunchKernelGGL(resid_prep_kernel, dim3(grid1(rc_pad * kp, 256)), dim3(256), 0, st, f->U,
+                       f->S, f->V, rows, cols, k, kp, w.pre, w.ucat, w.vcat);
     LAUNCH_CHECK();
-    qp.acat = w.acat;
-    qp.bcat = w.bcat;
+    qp.ucat = w.ucat;
+    qp.vcat = w.vcat;
     qp.kc = 3 * kp;
     qp.pscale = w.pscale;
   }

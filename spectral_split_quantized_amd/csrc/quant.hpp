@@ -26,16 +26,24 @@
 
 namespace metis {
 
-constexpr int kQT_R = 64;    // tile rows
-constexpr int kQT_C = 128;   // tile cols
+constexpr int kQT_R = 128;   // tile rows (4 waves x 32)
+constexpr int kQT_C = 64;    // tile cols (two 32-wide MFMA tiles)
 constexpr int kQThreads = 256;
+constexpr int kQMaxKK = 12;  // K of the rank-k product / 16 (k <= 64)
 
 // ---------------------------------------------------- residual operand prep --
 
-// acat[i][0:KP] = hi(U_i S pre), acat[i][KP:2KP] = hi(...), acat[i][2KP:3KP] = lo(...)
-// bcat[c][0:KP] = hi(V_c vpre),  bcat[c][KP:2KP] = lo(...),  bcat[c][2KP:3KP] = hi(...)
-// so that acat . bcat = hi hi + hi lo + lo hi.  pscale receives
-// 1 / (pre * vpre), a power of two.
+// The rank-k product of a tile is evaluated transposed, P^T = V (U S)^T, on
+// fp16 MFMA from hi/lo splits:
+//   vcat row (a column c of M) = [hi(V) | lo(V) | hi(V)],
+//   ucat row (a row r of M)    = [hi(US) | hi(US) | lo(US)],
+// so vcat . ucat = hi hi + lo hi + hi lo, each segment kp = round_up(k, 16)
+// wide (kc = 3 kp).  U S is pre-scaled by a power of two `pre` so its largest
+// entry is below 2^14, V by 256; pscale = 1 / (pre 256) undoes both.  Both
+// are stored fragment-major, rows padded to 32:
+//   (row, kidx) -> ((row/32 * kc/16 + kidx/16) * 64 + lane) * 8 + kidx%8,
+//   lane = (kidx%16)/8 * 32 + row%32,
+// so one wave's fragment load is 1 KB of contiguous memory.
 constexpr float kVPre = 256.0f;
 
 __global__ void resid_scale_kernel(const float* __restrict__ S, int k, float* __restrict__ pre_out,
@@ -49,35 +57,40 @@ __global__ void resid_scale_kernel(const float* __restrict__ S, int k, float* __
   pscale_out[0] = ldexpf(1.0f, ex - 14 - 8);  // 1 / (pre * kVPre)
 }
 
+__device__ inline int64_t frag_off(int64_t row, int kidx, int kc) {
+  const int lane = ((kidx & 15) >> 3) * 32 + (int)(row & 31);
+  return (((row >> 5) * (kc >> 4) + (kidx >> 4)) * 64 + lane) * 8 + (kidx & 7);
+}
+
+// one thread per (padded row, j < kp) of ucat and of vcat
 __global__ void resid_prep_kernel(const float* __restrict__ U, const float* __restrict__ S,
                                   const float* __restrict__ V, int64_t rows, int64_t cols, int k,
-                                  int kp, const float* __restrict__ pre_p, _Float16* __restrict__ acat,
-                                  _Float16* __restrict__ bcat) {
+                                  int kp, const float* __restrict__ pre_p, _Float16* __restrict__ ucat,
+                                  _Float16* __restrict__ vcat) {
   const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (rows + cols) * kp;
+  const int64_t rows_p = (rows + 31) & ~(int64_t)31, cols_p = (cols + 63) & ~(int64_t)63;
+  const int64_t total = (rows_p + cols_p) * kp;
   if (id >= total) return;
   const int64_t r = id / kp;
   const int j = (int)(id % kp);
   const int kc = 3 * kp;
-  if (r < rows) {
+  if (r < rows_p) {
     float x = 0.0f;
-    if (j < k) x = __fmul_rn(__fmul_rn(U[r * k + j], S[j]), pre_p[0]);
+    if (j < k && r < rows) x = __fmul_rn(__fmul_rn(U[r * k + j], S[j]), pre_p[0]);
     const _Float16 h = (_Float16)x;
     const _Float16 l = (_Float16)__fsub_rn(x, (float)h);
-    _Float16* a = acat + r * kc;
-    a[j] = h;
-    a[kp + j] = h;
-    a[2 * kp + j] = l;
+    ucat[frag_off(r, j, kc)] = h;
+    ucat[frag_off(r, kp + j, kc)] = h;
+    ucat[frag_off(r, 2 * kp + j, kc)] = l;
   } else {
-    const int64_t c = r - rows;
+    const int64_t c = r - rows_p;
     float v = 0.0f;
-    if (j < k) v = __fmul_rn(V[c * k + j], kVPre);
+    if (j < k && c < cols) v = __fmul_rn(V[c * k + j], kVPre);
     const _Float16 h = (_Float16)v;
     const _Float16 l = (_Float16)__fsub_rn(v, (float)h);
-    _Float16* b = bcat + c * kc;
-    b[j] = h;
-    b[kp + j] = l;
-    b[2 * kp + j] = h;
+    vcat[frag_off(c, j, kc)] = h;
+    vcat[frag_off(c, kp + j, kc)] = l;
+    vcat[frag_off(c, 2 * kp + j, kc)] = h;
   }
 }
 
@@ -87,8 +100,8 @@ struct QuantParams {
   const void* M;
   int dtype;  // 0 bf16, 1 f32
   int64_t rows, cols, ld;
-  const _Float16* acat;  // rows x kc (null: no factors)
-  const _Float16* bcat;  // cols x kc
+  const _Float16* ucat;  // fragment-major (null: no factors)
+  const _Float16* vcat;
   int kc;
   const float* pscale;
   uint32_t* amax;
@@ -103,6 +116,7 @@ struct QuantParams {
   int sr;
   uint64_t seed;
   uint32_t tag0, tag1, step;
+  int tiles_per_wg;  // column tiles walked by one workgroup
 };
 
 struct QuantBlockOut {
@@ -141,207 +155,245 @@ __device__ inline QuantBlockOut quant_block16(const float (&x)[16], const uint32
   return o;
 }
 
-// 16-bit draws of 16 consecutive logical elements e0 .. e0+15 (n valid).
-__device__ inline void draws16(uint64_t e0, int n, uint32_t tag, uint32_t step, uint64_t seed,
+// 16-bit draws of 16 consecutive indices e0 .. e0+15 with e0 % 8 == 0.
+__device__ inline void draws16(uint64_t e0, uint32_t tag, uint32_t step, uint64_t seed,
                                uint32_t (&h)[16]) {
-  if (n <= 0) return;
-  const uint64_t qa = e0 >> 3;
-  const uint64_t qb = (e0 + (uint64_t)(n - 1)) >> 3;
-  Philox4 b0 = philox_block(qa, tag, step, seed);
-  Philox4 b1 = (qb > qa) ? philox_block(qa + 1, tag, step, seed) : b0;
-  Philox4 b2 = (qb > qa + 1) ? philox_block(qa + 2, tag, step, seed) : b1;
+  const Philox4 b0 = philox_block(e0 >> 3, tag, step, seed);
+  const Philox4 b1 = philox_block((e0 >> 3) + 1, tag, step, seed);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint64_t e = e0 + (uint64_t)i;
-    const uint64_t q = e >> 3;
-    const Philox4& b = (q == qa) ? b0 : ((q == qa + 1) ? b1 : b2);
-    h[i] = (i < n) ? philox_half_of(b, (uint32_t)(e & 7)) : 0u;
+  for (int i = 0; i < 8; ++i) {
+    h[i] = philox_half_of(b0, (uint32_t)i);
+    h[8 + i] = philox_half_of(b1, (uint32_t)i);
   }
 }
 
-// Product tile (U S)(V)^T of the 64 x 128 tile at (r0, c0) into R (fp32,
-// unscaled).  4 waves in 2 x 2: each wave covers 32 rows x 64 cols.
-__device__ inline void resid_product_tile(const QuantParams& p, int64_t r0, int64_t c0,
-                                          float (*R)[kQT_C + 4]) {
+// 16 consecutive elements of row `row` starting at column `col` (n valid).
+__device__ inline void load_row16(const void* M, int dtype, int64_t base, int n, bool vec_ok,
+                                  float (&x)[16]) {
+  if (n == 16 && vec_ok && dtype == 0) {
+    const uint4 q0 = *(const uint4*)((const uint16_t*)M + base);
+    const uint4 q1 = *(const uint4*)((const uint16_t*)M + base + 8);
+    const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else if (n == 16 && vec_ok && dtype == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 f = *(const float4*)((const float*)M + base + 4 * i);
+      x[4 * i] = f.x;
+      x[4 * i + 1] = f.y;
+      x[4 * i + 2] = f.z;
+      x[4 * i + 3] = f.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = i < n ? load_as_float(M, dtype, base + i) : 0.0f;
+  }
+}
+
+// Bring the 16 accumulator values of one transposed 32x32 MFMA tile into
+// column order: lanes 0-31 end with columns 0-15, lanes 32-63 with columns
+// 16-31 of M row lane%32.  (The MFMA leaves lane l holding columns
+// 8(v/4) + 4(l/32) + v%4; v_permlane32_swap exchanges the upper half of its
+// first operand with the lower half of its second.)
+__device__ inline void gather_cols16(const f32x16_t& acc, float (&out)[16]) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[b]), __float_as_uint(acc[8 + b]),
+                                                    false, false);
+    const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[4 + b]),
+                                                    __float_as_uint(acc[12 + b]), false, false);
+    out[b] = __uint_as_float(s[0]);
+    out[4 + b] = __uint_as_float(s[1]);
+    out[8 + b] = __uint_as_float(t[0]);
+    out[12 + b] = __uint_as_float(t[1]);
+  }
+}
+
+// PASS2 = false: amax sweep.  PASS2 = true: quantise sweep.  NKK = kc / 16
+// of the rank-k product (0: no factors, direct quantisation).
+// A workgroup owns a 128-row panel and walks `tiles_per_wg` tiles of 64
+// columns.  Wave w owns rows 32w..32w+31; after gather_cols16 lane l holds
+// row 32w + l%32 at columns 16(l/32) .. +15 and 32 + 16(l/32) .. +15: two
+// axis-1 blocks, matching 32-byte row loads of M.  Both sweeps form the
+// residual with the same instructions, so they see bit-identical values.
+// Axis-0 blocks (16 rows of one column) go through an LDS transpose.
+template <int NKK, bool PASS2>
+__global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void quant_kernel(QuantParams p) {
+  constexpr bool HAS_F = NKK > 0;
+  __shared__ float R[PASS2 ? kQT_R : 1][PASS2 ? kQT_C + 4 : 1];
+  __shared__ uint4 Bf[HAS_F ? NKK * 2 * 64 : 1];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int wr = wave >> 1, wc = wave & 1;
-  const int64_t arow = r0 + wr * 32 + (lane & 31);
-  const int64_t bc0 = c0 + wc * 64 + (lane & 31);
-  const int64_t bc1 = bc0 + 32;
-  const bool av = arow < p.rows, bv0 = bc0 < p.cols, bv1 = bc1 < p.cols;
-  const int koff = (lane >> 5) * 8;
-  f32x16_t acc0 = {}, acc1 = {};
-  const half8_t z = {};
-  for (int kk = 0; kk < p.kc; kk += 16) {
-    const half8_t a = av ? *(const half8_t*)(p.acat + arow * p.kc + kk + koff) : z;
-    const half8_t b0 = bv0 ? *(const half8_t*)(p.bcat + bc0 * p.kc + kk + koff) : z;
-    const half8_t b1 = bv1 ? *(const half8_t*)(p.bcat + bc1 * p.kc + kk + koff) : z;
-    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b0, acc0, 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b1, acc1, 0, 0, 0);
+  const int hh = lane >> 5;
+  const int64_t r0 = (int64_t)blockIdx.x * kQT_R;
+  const int64_t ntc = ceil_div<int64_t>(p.cols, kQT_C);
+  const int64_t ct0 = (int64_t)blockIdx.y * p.tiles_per_wg;
+  const int64_t ct1 = min(ntc, ct0 + p.tiles_per_wg);
+  const int64_t row = r0 + wave * 32 + (lane & 31);
+  const bool row_ok = row < p.rows;
+  const bool vec_ok = ((p.ld & 7) == 0) && (((uintptr_t)p.M & 15) == 0);
+
+  half8_t uf[HAS_F ? NKK : 1];
+  if (HAS_F) {
+    const int64_t g = (r0 >> 5) + wave;
+    const int64_t gmax = (p.rows + 31) >> 5;
+    const half8_t z = {};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      uf[kk] = g < gmax ? *(const half8_t*)(p.ucat + ((g * NKK + kk) * 64 + lane) * 8) : z;
   }
-  const int col = wc * 64 + (lane & 31);
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int row = wr * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-    R[row][col] = acc0[v];
-    R[row][col + 32] = acc1[v];
-  }
-}
+  const float ps = HAS_F ? p.pscale[0] : 0.0f;
 
-// PASS2 = false: amax sweep.  PASS2 = true: quantise sweep.
-template <bool HAS_F, bool PASS2>
-__global__ __launch_bounds__(kQThreads) void quant_kernel(QuantParams p) {
-  __shared__ float R[kQT_R][kQT_C + 4];
-  __shared__ uint16_t H0[PASS2 ? kQT_R : 1][PASS2 ? kQT_C + 2 : 1];
-  const int tid = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.y * kQT_R;
-  const int64_t c0 = (int64_t)blockIdx.x * kQT_C;
-
-  if (HAS_F) resid_product_tile(p, r0, c0, R);
-
-  // this thread's two axis-1 blocks: rows tid/8 and tid/8 + 32, cols (tid%8)*16
-  const int lc = (tid & 7) * 16;
-  const int64_t gc = c0 + lc;
-  const int nvalid_c = (int)max((int64_t)0, min((int64_t)16, p.cols - gc));
-  float x[2][16];
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int lr = (tid >> 3) + 32 * b;
-    const int64_t gr = r0 + lr;
-    const bool rv = gr < p.rows;
-    const int64_t base = gr * p.ld + gc;
-    if (rv && nvalid_c == 16 && p.dtype == 0 && ((base & 7) == 0)) {
-      const uint4 q0 = *(const uint4*)((const uint16_t*)p.M + base);
-      const uint4 q1 = *(const uint4*)((const uint16_t*)p.M + base + 8);
-      const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        x[b][2 * i] = __uint_as_float(w[i] << 16);
-        x[b][2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-      }
-    } else if (rv && nvalid_c == 16 && p.dtype == 1 && ((base & 3) == 0)) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 f = *(const float4*)((const float*)p.M + base + 4 * i);
-        x[b][4 * i] = f.x;
-        x[b][4 * i + 1] = f.y;
-        x[b][4 * i + 2] = f.z;
-        x[b][4 * i + 3] = f.w;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        x[b][i] = (rv && i < nvalid_c) ? load_as_float(p.M, p.dtype, base + i) : 0.0f;
+  float s_g = 1.0f, d = 6.0f;
+  if (PASS2) {
+    const float at = __uint_as_float(p.amax[0]);
+    if (at > 0.0f) {
+      s_g = __fdiv_rn(at, 2688.0f);
+      d = __fmul_rn(6.0f, s_g);
+    }
+    if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
+      if (p.sg0) p.sg0[0] = s_g;
+      if (p.sg1) p.sg1[0] = s_g;
     }
   }
-  if (HAS_F) __syncthreads();
-  const float ps = HAS_F ? p.pscale[0] : 0.0f;
+  const bool sr = p.sr != 0;
+  const bool ax0 = PASS2 && (p.axes & 1);
+  const bool ax1 = PASS2 && (p.axes & 2);
+  float runmax = 0.0f;
+  bool bad = false;
+
+  for (int64_t ct = ct0; ct < ct1; ++ct) {
+    const int64_t c0 = ct * kQT_C;
+    // this lane's two 16-column blocks of row `row`
+    float x[2][16];
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int lr = (tid >> 3) + 32 * b;
-    const bool rv = r0 + lr < p.rows;
+    for (int b = 0; b < 2; ++b) {
+      const int64_t gc = c0 + 32 * b + 16 * hh;
+      const int n = (int)max((int64_t)0, min((int64_t)16, p.cols - gc));
+      if (row_ok && n > 0)
+        load_row16(p.M, p.dtype, row * p.ld + gc, n, vec_ok, x[b]);
+      else
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float v = x[b][i];
-      if (HAS_F) v = __fsub_rn(v, __fmul_rn(R[lr][lc + i], ps));
-      if (!(rv && i < nvalid_c)) v = 0.0f;
-      x[b][i] = v;
-      if (PASS2) R[lr][lc + i] = v;
+        for (int i = 0; i < 16; ++i) x[b][i] = 0.0f;
+    }
+    if (HAS_F) {
+      __syncthreads();  // the previous tile is done with Bf (and R)
+      const uint4* src = (const uint4*)p.vcat + (ct * 2) * (int64_t)NKK * 64;
+      for (int e = tid; e < 2 * NKK * 64; e += kQThreads) Bf[e] = src[e];
+      __syncthreads();
+      f32x16_t acc0 = {}, acc1 = {};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const half8_t v0 = __builtin_bit_cast(half8_t, Bf[kk * 64 + lane]);
+        const half8_t v1 = __builtin_bit_cast(half8_t, Bf[(NKK + kk) * 64 + lane]);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(v0, uf[kk], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(v1, uf[kk], acc1, 0, 0, 0);
+      }
+      float p0[16], p1[16];
+      gather_cols16(acc0, p0);
+      gather_cols16(acc1, p1);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        x[0][i] = __fsub_rn(x[0][i], __fmul_rn(p0[i], ps));
+        x[1][i] = __fsub_rn(x[1][i], __fmul_rn(p1[i], ps));
+      }
+    } else if (PASS2 && ax0) {
+      __syncthreads();  // the previous tile's axis-0 readers are done with R
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t gc = c0 + 32 * b + 16 * hh;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (!(row_ok && gc + i < p.cols)) x[b][i] = 0.0f;
+    }
+
+    if (!PASS2) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float a = fabsf(x[b][i]);
+          bad |= !(a <= 3.402823466e38f);
+          runmax = fmaxf(runmax, a);
+        }
+      continue;
+    }
+
+    // ---- axis 1 (and the export) from registers
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t gc = c0 + 32 * b + 16 * hh;
+      const int n = (int)max((int64_t)0, min((int64_t)16, p.cols - gc));
+      if (row_ok && n > 0) {
+        if (p.resid) {
+          float* dst = p.resid + row * p.cols + gc;
+          for (int i = 0; i < n; ++i) dst[i] = x[b][i];
+        }
+        if (ax1 && n == 16) {
+          uint32_t h[16];
+          if (sr) draws16((uint64_t)row * (uint64_t)p.cols + (uint64_t)gc, p.tag1, p.step, p.seed, h);
+          const QuantBlockOut o = quant_block16(x[b], h, s_g, d, sr);
+          *(uint2*)(p.codes1 + row * (p.cols >> 1) + (gc >> 1)) = make_uint2(o.lo, o.hi);
+          p.scales1[row * (p.cols >> 4) + (gc >> 4)] = (uint8_t)o.scale;
+        }
+      }
+      if (ax0) {
+        const int lr = wave * 32 + (lane & 31);
+        const int lc = 32 * b + 16 * hh;
+#pragma unroll
+        for (int i = 0; i < 16; i += 4)
+          *(float4*)&R[lr][lc + i] = make_float4(x[b][i], x[b][i + 1], x[b][i + 2], x[b][i + 3]);
+      }
+    }
+    if (!ax0) continue;
+    __syncthreads();
+    // ---- axis 0: column tid % 64, row blocks (tid/64)*2 + {0, 1}
+    const int lcol = tid & (kQT_C - 1);
+    const int64_t gcol = c0 + lcol;
+    if (gcol < p.cols) {
+      uint32_t packed[4];
+      uint32_t sc = 0;
+      int nb = 0;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int lr0 = (tid >> 6) * 32 + 16 * b;
+        const int64_t grow = r0 + lr0;
+        if (grow >= p.rows) break;
+        float xc[16];
+        uint32_t h[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xc[i] = R[lr0 + i][lcol];
+        if (sr) draws16((uint64_t)gcol * (uint64_t)p.rows + (uint64_t)grow, p.tag0, p.step, p.seed, h);
+        const QuantBlockOut o = quant_block16(xc, h, s_g, d, sr);
+        packed[2 * b] = o.lo;
+        packed[2 * b + 1] = o.hi;
+        sc |= o.scale << (8 * b);
+        ++nb;
+      }
+      const int64_t grow0 = r0 + (tid >> 6) * 32;
+      // rows % 16 == 0 makes every 8-byte code group 8-byte aligned; the
+      // pair is 16-byte aligned only when rows % 32 == 0
+      uint8_t* cdst = p.codes0 + gcol * (p.rows >> 1) + (grow0 >> 1);
+      uint8_t* sdst = p.scales0 + gcol * (p.rows >> 4) + (grow0 >> 4);
+      if (nb == 2 && (((uintptr_t)cdst & 15) == 0)) {
+        *(uint4*)cdst = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+      } else {
+        for (int b = 0; b < nb; ++b) *(uint2*)(cdst + 8 * b) = make_uint2(packed[2 * b], packed[2 * b + 1]);
+      }
+      for (int b = 0; b < nb; ++b) sdst[b] = (uint8_t)(sc >> (8 * b));
     }
   }
 
   if (!PASS2) {
-    float m = 0.0f;
-    bool bad = false;
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float a = fabsf(x[b][i]);
-        bad |= !(a <= 3.402823466e38f);
-        m = fmaxf(m, a);
-      }
     if (bad) raise_status(kStatusNonFinite);
-    m = wave_max(m);
-    if ((tid & 63) == 0) atomicMax(p.amax, __float_as_uint(m));
-    return;
+    runmax = wave_max(runmax);
+    if (lane == 0) atomicMax(p.amax, __float_as_uint(runmax));
   }
-
-  // ---- pass 2: tensor scale from the amax of pass 1
-  const float at = __uint_as_float(p.amax[0]);
-  float s_g = 1.0f, d = 6.0f;
-  if (at > 0.0f) {
-    s_g = __fdiv_rn(at, 2688.0f);
-    d = __fmul_rn(6.0f, s_g);
-  }
-  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
-    if (p.sg0) p.sg0[0] = s_g;
-    if (p.sg1) p.sg1[0] = s_g;
-  }
-  const bool sr = p.sr != 0;
-
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int lr = (tid >> 3) + 32 * b;
-    const int64_t gr = r0 + lr;
-    if (gr >= p.rows || nvalid_c <= 0) continue;
-    const uint64_t e0 = (uint64_t)gr * (uint64_t)p.cols + (uint64_t)gc;
-    if (p.resid) {
-      float* dst = p.resid + gr * p.cols + gc;
-      for (int i = 0; i < nvalid_c; ++i) dst[i] = x[b][i];
-    }
-    if ((p.axes & 2) && nvalid_c == 16) {
-      uint32_t h[16];
-      if (sr) draws16(e0, 16, p.tag1, p.step, p.seed, h);
-      const QuantBlockOut o = quant_block16(x[b], h, s_g, d, sr);
-      *(uint2*)(p.codes1 + gr * (p.cols >> 1) + (gc >> 1)) = make_uint2(o.lo, o.hi);
-      p.scales1[gr * (p.cols >> 4) + (gc >> 4)] = (uint8_t)o.scale;
-    }
-    if ((p.axes & 1) && sr) {
-      uint32_t h[16];
-      draws16(e0, nvalid_c, p.tag0, p.step, p.seed, h);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) H0[lr][lc + i] = (uint16_t)h[i];
-    }
-  }
-  if (!(p.axes & 1)) return;
-  __syncthreads();
-  // axis 0: column tid % 128, row blocks (tid/128)*2 + {0, 1}
-  const int lcol = tid & (kQT_C - 1);
-  const int64_t gcol = c0 + lcol;
-  if (gcol >= p.cols) return;
-  uint32_t packed[4];
-  uint32_t sc = 0;
-  int nb = 0;
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int lr0 = (tid >> 7) * 32 + 16 * b;
-    if (r0 + lr0 >= p.rows) break;
-    float xc[16];
-    uint32_t h[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      xc[i] = R[lr0 + i][lcol];
-      h[i] = sr ? (uint32_t)H0[lr0 + i][lcol] : 0u;
-    }
-    const QuantBlockOut o = quant_block16(xc, h, s_g, d, sr);
-    packed[2 * b] = o.lo;
-    packed[2 * b + 1] = o.hi;
-    sc |= o.scale << (8 * b);
-    ++nb;
-  }
-  const int64_t grow0 = r0 + (tid >> 7) * 32;
-  // rows % 16 == 0 makes every 8-byte code group 8-byte aligned; the pair is
-  // 16-byte aligned only when rows % 32 == 0
-  uint8_t* cdst = p.codes0 + gcol * (p.rows >> 1) + (grow0 >> 1);
-  uint8_t* sdst = p.scales0 + gcol * (p.rows >> 4) + (grow0 >> 4);
-  if (nb == 2 && (((uintptr_t)cdst & 15) == 0)) {
-    *(uint4*)cdst = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-  } else {
-    for (int b = 0; b < nb; ++b) *(uint2*)(cdst + 8 * b) = make_uint2(packed[2 * b], packed[2 * b + 1]);
-  }
-  for (int b = 0; b < nb; ++b) sdst[b] = (uint8_t)(sc >> (8 * b));
 }
 
 }  // namespace metis
