@@ -74,12 +74,12 @@ TimingRec* timing_begin(hipStream_t st, int64_t kind, int64_t d0, int64_t d1, in
   r->d1 = d1;
   r->d2 = d2;
   r->d3 = d3;
-  hipEventRecord(r->a, st);
+  if (hipEventRecord(r->a, st) != hipSuccess) return nullptr;  // record is skipped
   return r;
 }
 
 void timing_end(TimingRec* r, hipStream_t st) {
-  if (r) hipEventRecord(r->b, st);
+  if (r) (void)hipEventRecord(r->b, st);  // a failed record reads back as -1 ms
 }
 
 // ------------------------------------------------------- Omega quantile table
@@ -171,14 +171,58 @@ struct DecompWs {
   uint2* cand;
   uint8_t* flags;
   int32_t* idx;
-  float *om, *y, *q, *bpart, *b, *p, *vn, *sign, *ppart;
-  uint16_t* vfrag;
-  bool proj_mfma;
-  int64_t proj_nkb, proj_kbps, proj_splits;
+  float *om, *y, *q, *bpart, *b, *p, *vn, *sign, *ppart, *spart;
+  uint16_t *vfrag, *ofrag;
+  int64_t proj_nkb, proj_kbps, proj_splits, sk_kbps, sk_splits;
   double *gpart, *g, *rinv, *z, *theta, *ptp, *rot, *lam;
   int gblocks, slices;
   int64_t rows_per_gblock, rows_per_slice;
 };
+
+// Split-K plan of an MFMA product with nr output rows over nkb 64-wide K
+// blocks: about 1024 workgroups of 128 rows; returns the split count.
+int64_t split_plan(int64_t nr, int64_t nkb, int64_t* kbps) {
+  const int64_t row_blocks = (nr + 127) / 128;
+  int64_t splits = (1024 + row_blocks - 1) / row_blocks;
+  if (splits > nkb) splits = nkb;
+  if (splits < 1) splits = 1;
+  *kbps = (nkb + splits - 1) / splits;
+  return (nkb + *kbps - 1) / *kbps;
+}
+
+// out (nr x width, row-major) = scale * A[src rows] B on MFMA with B as NTERM
+// bf16 terms (width <= 96; A bf16, 16-byte aligned rows).
+template <int NTERM, int NSUB>
+metis_status mfma_product_n(const uint16_t* A, int64_t ld, int64_t nr, const int32_t* idx,
+                            const float* B, int64_t K, int width, int64_t ldb, int64_t nkb,
+                            int64_t kbps, int64_t splits, float scale, uint16_t* frag, float* part,
+                            float* out, hipStream_t st) {
+  hipLaunchKernelGGL((proj_prep_kernel<NTERM, NSUB>), dim3(grid1(nkb * NSUB * 2048, 256)), dim3(256), 0,
+                     st, B, K, width, ldb, nkb, frag);
+  LAUNCH_CHECK();
+  hipLaunchKernelGGL((project_mfma_kernel<NTERM, NSUB>),
+                     dim3((unsigned)ceil_div<int64_t>(nr, 128), (unsigned)splits), dim3(256), 0, st, A, ld,
+                     nr, idx, frag, nkb, kbps, part);
+  LAUNCH_CHECK();
+  hipLaunchKernelGGL(project_reduce_kernel, dim3(grid1(nr * width, 256)), dim3(256), 0, st, part, splits,
+                     nr, NSUB * 32, width, scale, out);
+  LAUNCH_CHECK();
+  return METIS_OK;
+}
+
+template <int NTERM>
+metis_status mfma_product(const uint16_t* A, int64_t ld, int64_t nr, const int32_t* idx, const float* B,
+                          int64_t K, int width, int64_t ldb, int64_t nkb, int64_t kbps, int64_t splits,
+                          float scale, uint16_t* frag, float* part, float* out, hipStream_t st) {
+  if (width <= 32)
+    return mfma_product_n<NTERM, 1>(A, ld, nr, idx, B, K, width, ldb, nkb, kbps, splits, scale, frag,
+                                    part, out, st);
+  if (width <= 64)
+    return mfma_product_n<NTERM, 2>(A, ld, nr, idx, B, K, width, ldb, nkb, kbps, splits, scale, frag,
+                                    part, out, st);
+  return mfma_product_n<NTERM, 3>(A, ld, nr, idx, B, K, width, ldb, nkb, kbps, splits, scale, frag, part,
+                                  out, st);
+}
 
 DecompWs carve_decompose(Carver& cv, int64_t rows, int64_t cols, int k, int n, int64_t lr,
                          bool sample) {
@@ -213,16 +257,15 @@ DecompWs carve_decompose(Carver& cv, int64_t rows, int64_t cols, int k, int n, i
   w.lam = cv.take<double>(kMaxN);
   w.vn = cv.take<float>(cols * k);
   w.sign = cv.take<float>(kMaxN);
-  // MFMA projection (bf16 operands, cols % 64 == 0, k <= 64): split-K plan
+  // MFMA products (bf16 operands, cols % 64 == 0): split-K plans for the
+  // projection P = M V (rows x k) and the sketch Y = M_s Omega (lr x n)
   w.proj_nkb = cols / 64;
-  const int64_t row_blocks = (rows + 127) / 128;
-  int64_t splits = (1024 + row_blocks - 1) / row_blocks;
-  if (splits > w.proj_nkb) splits = w.proj_nkb;
-  if (splits < 1) splits = 1;
-  w.proj_kbps = (w.proj_nkb + splits - 1) / splits;
-  w.proj_splits = (w.proj_nkb + w.proj_kbps - 1) / w.proj_kbps;
-  w.vfrag = cv.take<uint16_t>((size_t)w.proj_nkb * kProjFragU4 * 8);
-  w.ppart = cv.take<float>((size_t)w.proj_splits * rows * 64);
+  w.proj_splits = split_plan(rows, w.proj_nkb, &w.proj_kbps);
+  w.sk_splits = split_plan(lr, w.proj_nkb, &w.sk_kbps);
+  w.vfrag = cv.take<uint16_t>((size_t)w.proj_nkb * proj_frag_u4<3, 3>() * 8);
+  w.ofrag = cv.take<uint16_t>((size_t)w.proj_nkb * proj_frag_u4<1, 3>() * 8);
+  w.ppart = cv.take<float>((size_t)w.proj_splits * rows * 96);
+  w.spart = cv.take<float>((size_t)w.sk_splits * lr * 96);
   return w;
 }
 
@@ -596,6 +639,8 @@ metis_status metis_decompose(const void* M, int32_t dtype, int64_t rows, int64_t
   hipStream_t st = (hipStream_t)stream;
   const uint32_t ustep = (uint32_t)step;
   const bool refresh = f->refreshed_at < 0 || step - f->refreshed_at >= cfg->refresh;
+  // bf16 rows on 16-byte boundaries with whole 64-column K blocks take MFMA
+  const bool mfma_ok = dtype == METIS_BF16 && cols % 64 == 0 && ld % 8 == 0 && ((uintptr_t)M & 15) == 0;
 
   if (refresh) {
     const float scale = sample ? (float)sqrt((double)rows / (double)lr) : 1.0f;
@@ -623,9 +668,16 @@ metis_status metis_decompose(const void* M, int32_t dtype, int64_t rows, int64_t
     hipLaunchKernelGGL(omega_kernel, dim3(grid1(ceil_div<int64_t>(cols * n, 8), 256)), dim3(256), 0,
                        st, w.om, cols, n, tag_with_role(tag, kRoleOmega), ustep, cfg->seed);
     LAUNCH_CHECK();
-    hipLaunchKernelGGL(sketch_y_kernel, dim3(grid1(lr, 32)), dim3(256), 0, st, M, dtype, ld, w.idx,
-                       lr, cols, w.om, n, scale, w.y);
-    LAUNCH_CHECK();
+    if (mfma_ok) {
+      // Omega's entries are bf16 values: one term is exact
+      if ((s = mfma_product<1>((const uint16_t*)M, ld, lr, w.idx, w.om, cols, n, n, w.proj_nkb, w.sk_kbps,
+                               w.sk_splits, scale, w.ofrag, w.spart, w.y, st)) != METIS_OK)
+        return s;
+    } else {
+      hipLaunchKernelGGL(sketch_y_kernel, dim3(grid1(lr, 32)), dim3(256), 0, st, M, dtype, ld, w.idx,
+                         lr, cols, w.om, n, scale, w.y);
+      LAUNCH_CHECK();
+    }
     float* src = w.y;
     float* dst = w.q;
     for (int pass = 0; pass < 3; ++pass) {
@@ -654,20 +706,11 @@ metis_status metis_decompose(const void* M, int32_t dtype, int64_t rows, int64_t
     LAUNCH_CHECK();
   }
 
-  // projection and rediagonalisation (every step)
-  const bool proj_mfma = dtype == METIS_BF16 && cols % 64 == 0 && ld % 8 == 0 &&
-                         ((uintptr_t)M & 15) == 0 && k <= 64;
-  if (proj_mfma) {
-    hipLaunchKernelGGL(proj_prep_kernel, dim3(grid1(w.proj_nkb * 4096, 256)), dim3(256), 0, st, f->V,
-                       cols, k, w.proj_nkb, w.vfrag);
-    LAUNCH_CHECK();
-    hipLaunchKernelGGL(project_mfma_kernel, dim3((unsigned)ceil_div<int64_t>(rows, 128), (unsigned)w.proj_splits),
-                       dim3(256), 0, st, (const uint16_t*)M, ld, rows, w.vfrag, w.proj_nkb, w.proj_kbps,
-                       w.ppart);
-    LAUNCH_CHECK();
-    hipLaunchKernelGGL(project_reduce_kernel, dim3(grid1(rows * k, 256)), dim3(256), 0, st, w.ppart,
-                       w.proj_splits, rows, k, w.p);
-    LAUNCH_CHECK();
+  // projection and rediagonalisation (every step); V as three bf16 terms
+  if (mfma_ok) {
+    if ((s = mfma_product<3>((const uint16_t*)M, ld, rows, nullptr, f->V, cols, k, k, w.proj_nkb, w.proj_kbps,
+                             w.proj_splits, 1.0f, w.vfrag, w.ppart, w.p, st)) != METIS_OK)
+      return s;
   } else {
     hipLaunchKernelGGL(project_kernel, dim3(grid1(rows, 64)), dim3(256), 0, st, M, dtype, ld, rows, cols,
                        f->V, k, w.p);
@@ -842,8 +885,8 @@ metis_status metis_gemm_bwd(const metis_qoperand* D, const metis_qoperand* W, co
 metis_status metis_timing_enable(int32_t capacity) {
   std::lock_guard<std::mutex> lk(g_tmu);
   for (auto& r : g_trecs) {
-    hipEventDestroy(r.a);
-    hipEventDestroy(r.b);
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
   }
   g_trecs.clear();
   g_tused = 0;
@@ -863,7 +906,7 @@ int32_t metis_timing_read(float* ms, int64_t* shape, int32_t max_records) {
   for (size_t i = 0; i < g_tused && n < max_records; ++i, ++n) {
     TimingRec& r = g_trecs[i];
     float t = -1.0f;
-    if (hipEventSynchronize(r.b) == hipSuccess) hipEventElapsedTime(&t, r.a, r.b);
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) t = -1.0f;
     ms[n] = t;
     shape[5 * n + 0] = r.kind;
     shape[5 * n + 1] = r.d0;

@@ -394,46 +394,104 @@ __global__ __launch_bounds__(256) void apply_rinv_kernel(const float* __restrict
 
 // --------------------------------------------------------- Jacobi (one WG) --
 
-// Cyclic Jacobi with the Golub & Van Loan symmetric 2x2 Schur rotation, in a
-// parallel round-robin pair order; stops when off(A) <= 1e-15 ||A||_F (or 30
-// sweeps).  Output: eigenvalues descending (ties by index) and eigenvectors
-// (column-major in Z: Z[a * n + i] = component a of vector i) signed so the
-// largest-magnitude component is positive (lowest index on ties).
+// Pair kp of round r in the circle method over np players (np even; player
+// np-1 stays, the others rotate), as (p, q) with p < q.
+__device__ __forceinline__ int jacobi_pair(int kp, int r, int np) {
+  const int m = np - 1;
+  int a, b;
+  if (kp == 0) {
+    a = m;
+    b = r;
+  } else {
+    a = r + kp;
+    if (a >= m) a -= m;
+    b = r - kp;
+    if (b < 0) b += m;
+  }
+  return min(a, b) | (max(a, b) << 8);
+}
+
+// Symmetric 2x2 Schur rotation (Golub & Van Loan, section 8.5) that zeroes
+// a_pq: [c s; -s c]^T [app apq; apq aqq] [c s; -s c] is diagonal.
+__device__ __forceinline__ void jacobi_rot(double app, double aqq, double apq, double& c, double& s) {
+  c = 1.0;
+  s = 0.0;
+  if (apq == 0.0) return;
+  const double diff = aqq - app;
+  double t;
+  if (fabs(diff) > 1e300 * fabs(apq)) {
+    t = apq / diff;  // tau would overflow: t = 1 / (2 tau)
+  } else {
+    const double tau = diff / (2.0 * apq);
+    const double h = hypot(1.0, tau);
+    t = tau >= 0.0 ? 1.0 / (tau + h) : -1.0 / (-tau + h);
+  }
+  c = 1.0 / sqrt(1.0 + t * t);
+  s = t * c;
+}
+
+// Cyclic Jacobi with the symmetric Schur rotation in the parallel circle
+// order; stops when off(A) <= 1e-15 ||A||_F (or 30 sweeps).  Output:
+// eigenvalues descending (ties by index) and eigenvectors (column-major in
+// Z: Z[a * n + i] = component a of vector i) signed so the largest-magnitude
+// component is positive (lowest index on ties).
+//
+// One round applies its np/2 disjoint rotations as J^T A J on 2x2 blocks
+// (block (P, Q) of pairs P <= Q, mirrored below the diagonal), then wave 0
+// forms the next round's rotations while the other waves apply this round's
+// to V: two barriers per round.
 __global__ __launch_bounds__(1024) void jacobi_kernel(const double* __restrict__ Ain, int n,
                                                       double* __restrict__ w_out,
                                                       double* __restrict__ Z) {
+  constexpr int kHalf = kMaxN / 2;
   __shared__ double A[kMaxN][kMaxN + 1];
   __shared__ double V[kMaxN][kMaxN + 1];
-  __shared__ double cs[kMaxN / 2], sn[kMaxN / 2];
-  __shared__ int pp[kMaxN / 2], qq[kMaxN / 2];
-  __shared__ double red[32];
+  __shared__ double cs[2][kHalf], sn[2][kHalf];
+  __shared__ int pq[2][kHalf];
+  __shared__ uint16_t blk[kHalf * (kHalf + 1) / 2];
+  __shared__ double red[16];
   __shared__ int go;
   const int tid = threadIdx.x;
   const int np = (n + 1) & ~1;  // even, padded with a zero row/column
   const int half = np / 2;
-  for (int e = tid; e < np * np; e += blockDim.x) {
+  const int nblk = half * (half + 1) / 2;
+  for (int e = tid; e < np * np; e += 1024) {
     const int a = e / np, b = e % np;
     A[a][b] = (a < n && b < n) ? 0.5 * (Ain[a * n + b] + Ain[b * n + a]) : 0.0;
     V[a][b] = (a == b) ? 1.0 : 0.0;
   }
+  if (tid < half) {
+    const int base = tid * half - tid * (tid - 1) / 2;
+    for (int q = tid; q < half; ++q) blk[base + q - tid] = (uint16_t)(tid | (q << 8));
+  }
   __syncthreads();
-  // ||A||_F^2
   double loc = 0.0;
-  for (int e = tid; e < np * np; e += blockDim.x) {
+  for (int e = tid; e < np * np; e += 1024) {
     const double v = A[e / np][e % np];
     loc += v * v;
   }
   loc = wave_sum_d(loc);
   if ((tid & 63) == 0) red[tid >> 6] = loc;
+  if (tid < half) {
+    const int pr = jacobi_pair(tid, 0, np);
+    const int p = pr & 255, q = pr >> 8;
+    pq[0][tid] = pr;
+    jacobi_rot(A[p][p], A[q][q], A[p][q], cs[0][tid], sn[0][tid]);
+  }
   __syncthreads();
   double norm2 = 0.0;
-  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) norm2 += red[i];
+  for (int i = 0; i < 16; ++i) norm2 += red[i];
   const double tol2 = 1e-30 * norm2;
+  // V update: thread t of waves 1..15 owns pair t % half and rows t / half + g * G
+  const int vt = tid - 64;
+  const int G = 960 / half;
+  const bool vact = vt >= 0 && vt < G * half;
+  const int vk = vact ? vt % half : 0;
+  const int vi0 = vact ? vt / half : 0;
+  int par = 0;
   for (int sweep = 0; sweep < 30; ++sweep) {
-    // off(A)^2
-    __syncthreads();
     double o = 0.0;
-    for (int e = tid; e < np * np; e += blockDim.x) {
+    for (int e = tid; e < np * np; e += 1024) {
       const int a = e / np, b = e % np;
       if (a != b) o += A[a][b] * A[a][b];
     }
@@ -443,67 +501,56 @@ __global__ __launch_bounds__(1024) void jacobi_kernel(const double* __restrict__
     __syncthreads();
     if (tid == 0) {
       double off2 = 0.0;
-      for (int i = 0; i < (int)(blockDim.x >> 6); ++i) off2 += red[i];
+      for (int i = 0; i < 16; ++i) off2 += red[i];
       go = off2 > tol2;
     }
     __syncthreads();
     if (!go) break;
     for (int round = 0; round < np - 1; ++round) {
-      if (tid < half) {
-        // circle method: player np-1 fixed, others rotate
-        int a, b;
-        if (tid == 0) {
-          a = np - 1;
-          b = round;
-        } else {
-          a = (round + tid) % (np - 1);
-          b = (round - tid + (np - 1)) % (np - 1);
+      for (int e = tid; e < nblk; e += 1024) {
+        const int bq = blk[e];
+        const int P = bq & 255, Q = bq >> 8;
+        const int r1 = pq[par][P], r2 = pq[par][Q];
+        const int p1 = r1 & 255, q1 = r1 >> 8, p2 = r2 & 255, q2 = r2 >> 8;
+        const double c1 = cs[par][P], s1 = sn[par][P], c2 = cs[par][Q], s2 = sn[par][Q];
+        const double a = A[p1][p2], b = A[p1][q2], c = A[q1][p2], d = A[q1][q2];
+        // rows (J^T from the left), then columns (J from the right)
+        const double ra = c1 * a - s1 * c, rc = s1 * a + c1 * c;
+        const double rb = c1 * b - s1 * d, rd = s1 * b + c1 * d;
+        const double na = c2 * ra - s2 * rb, nb = s2 * ra + c2 * rb;
+        const double nc = c2 * rc - s2 * rd, nd = s2 * rc + c2 * rd;
+        A[p1][p2] = na;
+        A[p1][q2] = nb;
+        A[q1][p2] = nc;
+        A[q1][q2] = nd;
+        if (P != Q) {
+          A[p2][p1] = na;
+          A[q2][p1] = nb;
+          A[p2][q1] = nc;
+          A[q2][q1] = nd;
         }
-        const int p = min(a, b), q = max(a, b);
-        pp[tid] = p;
-        qq[tid] = q;
-        const double apq = A[p][q];
-        double c = 1.0, s = 0.0;
-        if (apq != 0.0) {
-          const double diff = A[q][q] - A[p][p];
-          double t;
-          if (fabs(diff) > 1e300 * fabs(apq)) {
-            t = apq / diff;
-          } else {
-            const double tau = diff / (2.0 * apq);
-            const double h = hypot(1.0, tau);
-            t = tau >= 0.0 ? 1.0 / (tau + h) : -1.0 / (-tau + h);
-          }
-          c = 1.0 / sqrt(1.0 + t * t);
-          s = t * c;
+      }
+      __syncthreads();
+      if (tid < 64) {
+        if (tid < half) {
+          const int nr = round + 1 < np - 1 ? round + 1 : 0;
+          const int pr = jacobi_pair(tid, nr, np);
+          const int p = pr & 255, q = pr >> 8;
+          pq[par ^ 1][tid] = pr;
+          jacobi_rot(A[p][p], A[q][q], A[p][q], cs[par ^ 1][tid], sn[par ^ 1][tid]);
         }
-        cs[tid] = c;
-        sn[tid] = s;
+      } else if (vact) {
+        const int r = pq[par][vk];
+        const int p = r & 255, q = r >> 8;
+        const double c = cs[par][vk], sv = sn[par][vk];
+        for (int i = vi0; i < np; i += G) {
+          const double vp = V[i][p], vq = V[i][q];
+          V[i][p] = c * vp - sv * vq;
+          V[i][q] = sv * vp + c * vq;
+        }
       }
       __syncthreads();
-      // rows: A <- J^T A
-      for (int e = tid; e < half * np; e += blockDim.x) {
-        const int k = e / np, j = e % np;
-        const int p = pp[k], q = qq[k];
-        const double c = cs[k], s = sn[k];
-        const double ap = A[p][j], aq = A[q][j];
-        A[p][j] = c * ap - s * aq;
-        A[q][j] = s * ap + c * aq;
-      }
-      __syncthreads();
-      // columns: A <- A J, V <- V J
-      for (int e = tid; e < half * np; e += blockDim.x) {
-        const int k = e / np, i = e % np;
-        const int p = pp[k], q = qq[k];
-        const double c = cs[k], s = sn[k];
-        const double ap = A[i][p], aq = A[i][q];
-        A[i][p] = c * ap - s * aq;
-        A[i][q] = s * ap + c * aq;
-        const double vp = V[i][p], vq = V[i][q];
-        V[i][p] = c * vp - s * vq;
-        V[i][q] = s * vp + c * vq;
-      }
-      __syncthreads();
+      par ^= 1;
     }
   }
   __syncthreads();
@@ -605,43 +652,49 @@ __global__ __launch_bounds__(256) void project_kernel(const void* __restrict__ M
 // each lane reads 64 contiguous bytes of its row of M.  V's fragments are
 // pre-arranged in exactly the order the waves read them from LDS.
 
-constexpr int kProjFragU4 = 3 * 2 * 4 * 64;  // uint4 slots per K block (24 KB)
+// uint4 slots of one K block of B fragments: NTERM terms x NSUB 32-column
+// tiles x 4 MFMA steps x 64 lanes.
+template <int NTERM, int NSUB>
+constexpr int proj_frag_u4() { return NTERM * NSUB * 4 * 64; }
 
-// vfrag[((kb*3 + t)*2 + n)*4 + j][lane] (uint4 of 8 bf16): column n*32 + lane%32,
-// K = kb*64 + 32*(lane/32) + 8*j + i.
-__global__ void proj_prep_kernel(const float* __restrict__ V, int64_t cols, int k, int64_t nkb,
-                                 uint16_t* __restrict__ vfrag) {
+// B (K x width, binary32, row-major with leading dimension ldb) as NTERM bf16
+// terms in fragment order: bfrag[((kb*NTERM + t)*NSUB + n)*4 + j][lane] (uint4
+// of 8 bf16) holds column n*32 + lane%32 at K = kb*64 + 32*(lane/32) + 8*j + i.
+template <int NTERM, int NSUB>
+__global__ void proj_prep_kernel(const float* __restrict__ B, int64_t K, int width, int64_t ldb,
+                                 int64_t nkb, uint16_t* __restrict__ bfrag) {
   const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // one element
-  const int64_t total = nkb * 2 * 4 * 64 * 8;
+  const int64_t total = nkb * NSUB * 4 * 64 * 8;
   if (id >= total) return;
   const int i = (int)(id & 7);
   const int lane = (int)((id >> 3) & 63);
   const int j = (int)((id >> 9) & 3);
-  const int n = (int)((id >> 11) & 1);
-  const int64_t kb = id >> 12;
+  const int64_t rest = id >> 11;
+  const int n = (int)(rest % NSUB);
+  const int64_t kb = rest / NSUB;
   const int col = n * 32 + (lane & 31);
   const int64_t kk = kb * 64 + 32 * (lane >> 5) + 8 * j + i;
-  const float v = (col < k && kk < cols) ? V[kk * k + col] : 0.0f;
-  const __bf16 t0 = (__bf16)v;
-  const float r1 = v - (float)t0;
-  const __bf16 t1 = (__bf16)r1;
-  const __bf16 t2 = (__bf16)(r1 - (float)t1);
-  const __bf16 t[3] = {t0, t1, t2};
+  float v = (col < width && kk < K) ? B[kk * ldb + col] : 0.0f;
 #pragma unroll
-  for (int tt = 0; tt < 3; ++tt) {
-    const int64_t slot = (((kb * 3 + tt) * 2 + n) * 4 + j) * 64 + lane;
-    vfrag[slot * 8 + i] = __builtin_bit_cast(uint16_t, t[tt]);
+  for (int t = 0; t < NTERM; ++t) {
+    const __bf16 b = (__bf16)v;
+    v = v - (float)b;
+    const int64_t slot = (((kb * NTERM + t) * NSUB + n) * 4 + j) * 64 + lane;
+    bfrag[slot * 8 + i] = __builtin_bit_cast(uint16_t, b);
   }
 }
 
-// part[s][row][64] = sum over K blocks of split s of M[row] V (128 rows per
-// workgroup, one 32-row slab per wave, 64 output columns as two 32x32 tiles).
-__global__ __launch_bounds__(256) void project_mfma_kernel(const uint16_t* __restrict__ M, int64_t ld,
-                                                           int64_t rows,
-                                                           const uint16_t* __restrict__ vfrag,
+// part[s][r][NSUB*32] = sum over the K blocks of split s of A[src(r)] B, with
+// src(r) = idx[r] (gathered rows) or r; A is bf16 with leading dimension ld.
+// 128 output rows per workgroup, one 32-row slab per wave.
+template <int NTERM, int NSUB>
+__global__ __launch_bounds__(256) void project_mfma_kernel(const uint16_t* __restrict__ A, int64_t ld,
+                                                           int64_t rows, const int32_t* __restrict__ idx,
+                                                           const uint16_t* __restrict__ bfrag,
                                                            int64_t nkb, int64_t kb_per_split,
                                                            float* __restrict__ part) {
-  __shared__ uint4 vs[2 * kProjFragU4];
+  constexpr int FU = proj_frag_u4<NTERM, NSUB>();
+  __shared__ uint4 vs[2 * FU];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t r0 = (int64_t)blockIdx.x * 128;
   const int64_t s = blockIdx.y;
@@ -649,8 +702,11 @@ __global__ __launch_bounds__(256) void project_mfma_kernel(const uint16_t* __res
   const int64_t kb1 = min(nkb, kb0 + kb_per_split);
   const int64_t row = r0 + wave * 32 + (lane & 31);
   const bool rv = row < rows;
-  const uint16_t* mrow = M + (rv ? row : 0) * ld + 32 * (lane >> 5);
-  f32x16_t acc0 = {}, acc1 = {};
+  const int64_t src = rv ? (idx ? (int64_t)idx[row] : row) : 0;
+  const uint16_t* mrow = A + src * ld + 32 * (lane >> 5);
+  f32x16_t acc[NSUB];
+#pragma unroll
+  for (int n = 0; n < NSUB; ++n) acc[n] = f32x16_t{};
   const uint4 z = make_uint4(0, 0, 0, 0);
   for (int64_t kb = kb0; kb < kb1; kb += 2) {
     const int nb = (int)min((int64_t)2, kb1 - kb);
@@ -661,8 +717,8 @@ __global__ __launch_bounds__(256) void project_mfma_kernel(const uint16_t* __res
       for (int j = 0; j < 4; ++j)
         a[b][j] = (rv && b < nb) ? *(const uint4*)(mrow + (kb + b) * 64 + 8 * j) : z;
     __syncthreads();
-    const uint4* src = (const uint4*)vfrag + kb * kProjFragU4;
-    for (int e = tid; e < nb * kProjFragU4; e += 256) vs[e] = src[e];
+    const uint4* srcf = (const uint4*)bfrag + kb * FU;
+    for (int e = tid; e < nb * FU; e += 256) vs[e] = srcf[e];
     __syncthreads();
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -671,37 +727,38 @@ __global__ __launch_bounds__(256) void project_mfma_kernel(const uint16_t* __res
       for (int j = 0; j < 4; ++j) {
         const bf16x8_t af = __builtin_bit_cast(bf16x8_t, a[b][j]);
 #pragma unroll
-        for (int t = 0; t < 3; ++t) {
-          const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, vs[b * kProjFragU4 + ((t * 2 + 0) * 4 + j) * 64 + lane]);
-          const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, vs[b * kProjFragU4 + ((t * 2 + 1) * 4 + j) * 64 + lane]);
-          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b0, acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b1, acc1, 0, 0, 0);
-        }
+        for (int t = 0; t < NTERM; ++t)
+#pragma unroll
+          for (int n = 0; n < NSUB; ++n) {
+            const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, vs[b * FU + ((t * NSUB + n) * 4 + j) * 64 + lane]);
+            acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, acc[n], 0, 0, 0);
+          }
       }
     }
   }
   const int col = lane & 31;
+  constexpr int W = NSUB * 32;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int64_t ro = r0 + wave * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
     if (ro < rows) {
-      float* dst = part + (s * rows + ro) * 64;
-      dst[col] = acc0[v];
-      dst[32 + col] = acc1[v];
+      float* dst = part + (s * rows + ro) * W;
+#pragma unroll
+      for (int n = 0; n < NSUB; ++n) dst[n * 32 + col] = acc[n][v];
     }
   }
 }
 
-// P[row][j] = sum_s part[s][row][j], j < k (fixed order: deterministic).
+// out[row][j] = scale * sum_s part[s][row][j], j < width (fixed order).
 __global__ void project_reduce_kernel(const float* __restrict__ part, int64_t splits, int64_t rows,
-                                      int k, float* __restrict__ P) {
+                                      int pw, int width, float scale, float* __restrict__ out) {
   const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (id >= rows * k) return;
-  const int64_t r = id / k;
-  const int j = (int)(id % k);
+  if (id >= rows * width) return;
+  const int64_t r = id / width;
+  const int j = (int)(id % width);
   float acc = 0.0f;
-  for (int64_t s = 0; s < splits; ++s) acc += part[(s * rows + r) * 64 + j];
-  P[id] = acc;
+  for (int64_t s = 0; s < splits; ++s) acc += part[(s * rows + r) * pw + j];
+  out[id] = acc * scale;
 }
 
 // Vn = V R (cols x k), fp64 accumulation.
