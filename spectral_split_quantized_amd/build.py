@@ -8,15 +8,24 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "csrc", "metis.hip")
+CSRC = os.path.join(HERE, "csrc")
+OBJ = os.path.join(HERE, "_build")
 OUT = os.path.join(HERE, "libmetis.so")
+
+# translation units and their extra flags: the register-dequant GEMM is
+# scheduled for instruction-level parallelism (its expansion instructions
+# must interleave with the matrix instructions of the same wave); the rest
+# keeps the default strategy
+UNITS = [
+    ("metis.hip", []),
+    ("gemm_big.hip", ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]),
+]
 
 FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # keep every binary32 rounding of the quantiser explicit
     "-ffp-contract=off",
     # packed FP32 instructions are avoided on this target
@@ -25,13 +34,22 @@ FLAGS = [
 ]
 
 
-def build(verbose=False):
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = OUT + ".tmp"
-    cmd = [hipcc] + FLAGS + [SRC, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
+
+
+def build(verbose=False):
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    os.makedirs(OBJ, exist_ok=True)
+    objs = []
+    for src, extra in UNITS:
+        obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+        _run([hipcc] + FLAGS + extra + ["-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    tmp = OUT + ".tmp"
+    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
     os.replace(tmp, OUT)
     return OUT
 

@@ -146,17 +146,6 @@ __host__ __device__ inline uint32_t e2m1_sr(float y, uint32_t h) {
   return (u < p) ? lo + 1 : lo;
 }
 
-// ----------------------------------------------------------- status flag --
-
-// Per-device numeric failure flag (bit 0: non-finite input, bit 1: Cholesky
-// breakdown, bit 2: row-sample selection overflow).
-__device__ int g_metis_status;
-
-__device__ inline void raise_status(int bits) { atomicOr(&g_metis_status, bits); }
-
-constexpr int kStatusNonFinite = 1;
-constexpr int kStatusCholesky = 2;
-constexpr int kStatusSample = 4;
 
 // ------------------------------------------------------------------- misc --
 
@@ -185,9 +174,5 @@ __device__ inline double wave_sum_d(double v) {
   return v;
 }
 
-__global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = v;
-}
 
 }  // namespace metis

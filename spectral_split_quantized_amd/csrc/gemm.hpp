@@ -23,42 +23,9 @@
 // range of tiles and so shares A and B panels in its own L2.
 #pragma once
 
-#include "common.hpp"
+#include "gemm_common.hpp"
 
 namespace metis {
-
-struct GemmParams {
-  int64_t M, N, K;
-  const uint8_t* a_codes;
-  const uint8_t* a_scales;
-  const uint8_t* b_codes;
-  const uint8_t* b_scales;
-  const float* sa;  // tensor scales (device) or null
-  const float* sb;
-  int64_t kext;     // multiple of 64; 0 = none
-  const uint16_t* a_ext;  // bf16 [M][kext]
-  const uint16_t* b_ext;  // bf16 [N][kext]
-  float* C;
-  int64_t ldc;
-};
-
-// 8 E2M1 codes (one dword, element 0 in the low nibble) -> 8 fp16 values
-// grid(code) * s_b.  v_cvt_scalef32_pk_f16_fp4 applies only the exponent of
-// its scale operand, so it is used with scale 1 (exact grid values, low
-// nibble first) and the E4M3 block scale is applied by one packed fp16
-// multiply; the product is exact (<= 6 significant bits, in fp16 range).
-__device__ inline uint4 dequant8(uint32_t w, half2_t s) {
-  const half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
-  const half2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
-  const half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
-  const half2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
-  uint4 o;
-  o.x = __builtin_bit_cast(uint32_t, h0);
-  o.y = __builtin_bit_cast(uint32_t, h1);
-  o.z = __builtin_bit_cast(uint32_t, h2);
-  o.w = __builtin_bit_cast(uint32_t, h3);
-  return o;
-}
 
 // BM x BN tile, WM x WN waves; each wave owns (BM/WM) x (BN/WN) as 32 x 32
 // MFMA tiles.  K step 64.
@@ -140,23 +107,6 @@ __device__ inline void store_chunk(_Float16* lds, const RawChunk& c, int lrow, i
   }
 }
 
-__device__ inline int64_t remap_tile(int64_t bid, int64_t tiles_m, int64_t tiles_n) {
-  const int64_t total = tiles_m * tiles_n;
-  int64_t pid = bid;
-  if (total % 8 == 0) pid = (bid % 8) * (total / 8) + bid / 8;  // XCD-contiguous
-  // group 8 tile-rows together (column-major inside a group)
-  const int64_t group = 8;
-  const int64_t per_group = group * tiles_n;
-  const int64_t gid = pid / per_group;
-  const int64_t first_m = gid * group;
-  const int64_t gsize = min(tiles_m - first_m, group);
-  const int64_t in = pid % per_group;
-  const int64_t tm = first_m + in % gsize;
-  const int64_t tn = in / gsize;
-  return tm * tiles_n + tn;
-}
-
-extern __shared__ __align__(16) _Float16 g_gemm_smem[];
 
 // gridDim.x = tiles, gridDim.y = K splits.  With splits > 1 the split's raw
 // partial sum goes to C + split * M * ldc (alpha and the K-extension are
@@ -268,14 +218,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp4_kernel(GemmParams p) {
         const int lrow = c >> 3, c8 = c & 7;
         const int64_t row = m0 + lrow;
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (row < p.M) v = *(const uint4*)(p.a_ext + row * p.kext + kt * BK + c8 * 8);
+        if (row < p.M) v = *(const uint4*)(p.a_ext + ext_off(row, kt * BK + c8 * 8, p.kext));
         *(uint4*)(lds_a(0) + frag_off<GA>(c8 >> 1, lrow >> 5, (c8 & 1) * 32 + (lrow & 31))) = v;
       }
       for (int c = tid; c < BN * 8; c += NT) {
         const int lrow = c >> 3, c8 = c & 7;
         const int64_t row = n0 + lrow;
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (row < p.N) v = *(const uint4*)(p.b_ext + row * p.kext + kt * BK + c8 * 8);
+        if (row < p.N) v = *(const uint4*)(p.b_ext + ext_off(row, kt * BK + c8 * 8, p.kext));
         *(uint4*)(lds_b(0) + frag_off<GB>(c8 >> 1, lrow >> 5, (c8 & 1) * 32 + (lrow & 31))) = v;
       }
       __syncthreads();
@@ -314,6 +264,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp4_kernel(GemmParams p) {
     }
   }
 }
+
+
 
 template <int BM, int BN, int WM, int WN>
 inline size_t gemm_lds_bytes() {
@@ -382,13 +334,15 @@ struct ExtParams {
 };
 
 // A_ext[i] = [hi(P'' s_J) | lo(..) | H_bar | H_bar | 0 ...]
+// (rows past e.rows up to the next multiple of 32 are written as zeros)
 __global__ void ext_prep_a_kernel(ExtParams e) {
   const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t i = id / e.kext;
   const int col = (int)(id % e.kext);
-  if (i >= e.rows) return;
+  if (i >= ((e.rows + 31) & ~(int64_t)31)) return;
   uint16_t out = 0;
-  if (col < 2 * e.ksR) {
+  if (i >= e.rows) {
+  } else if (col < 2 * e.ksR) {
     const int p = col % e.ksR;
     if (p < e.kR) {
       const float v = e.praw[i * e.kR + p] * (e.s_LR[0] * e.s_E[0]) * e.S_R[p] * e.J.ts[0];
@@ -399,7 +353,7 @@ __global__ void ext_prep_a_kernel(ExtParams e) {
     const int q = (col - 2 * e.ksR) % e.ksL;
     if (q < e.kL) out = bf16_rn_bits(factor_val(e.H, q, i));
   }
-  e.a_ext[i * e.kext + col] = out;
+  e.a_ext[ext_off(i, col, e.kext)] = out;
 }
 
 // B_ext[j] = [J_bar | J_bar | hi(s_H G) | lo(..) | 0 ...]; one workgroup per 64
@@ -424,7 +378,7 @@ __global__ __launch_bounds__(256) void ext_prep_b_kernel(ExtParams e) {
     const int p = col % e.ksR;
     if (j0 + jj >= e.cols) continue;
     const uint16_t v = (p < e.kR) ? bf16_rn_bits(jb[jj][p]) : (uint16_t)0;
-    e.b_ext[(j0 + jj) * e.kext + col] = v;
+    e.b_ext[ext_off(j0 + jj, col, e.kext)] = v;
   }
   // G rows
   const float sFE = e.s_F[0] * e.s_E[0];
@@ -455,17 +409,23 @@ __global__ __launch_bounds__(256) void ext_prep_b_kernel(ExtParams e) {
         const uint16_t hi = bf16_rn_bits(g);
         const uint16_t v = (tid < 64) ? hi : bf16_rn_bits(g - bf16_bits_to_float(hi));
         const int col = 2 * e.ksR + ((tid < 64) ? 0 : e.ksL) + q;
-        e.b_ext[j * e.kext + col] = v;
+        e.b_ext[ext_off(j, col, e.kext)] = v;
       }
     }
   }
-  // zero tail of the K-extension
+  // zero tail of the K-extension, and whole rows past e.cols up to the next
+  // multiple of 32
   const int used = 2 * e.ksR + 2 * e.ksL;
   const int tail = (int)(e.kext - used);
   for (int idx = tid; idx < 64 * tail; idx += blockDim.x) {
     const int jj = idx / tail;
     const int col = used + idx % tail;
-    if (j0 + jj < e.cols) e.b_ext[(j0 + jj) * e.kext + col] = 0;
+    if (j0 + jj < e.cols) e.b_ext[ext_off(j0 + jj, col, e.kext)] = 0;
+  }
+  const int64_t padded = (e.cols + 31) & ~(int64_t)31;
+  for (int64_t idx = tid; idx < 64 * e.kext; idx += blockDim.x) {
+    const int64_t j = j0 + idx / e.kext;
+    if (j >= e.cols && j < padded) e.b_ext[ext_off(j, idx % e.kext, e.kext)] = 0;
   }
 }
 

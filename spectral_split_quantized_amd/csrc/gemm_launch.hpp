@@ -1,0 +1,15 @@
+// gemm_launch.hpp -- host entry of the register-dequant GEMM translation unit.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace metis {
+
+struct GemmParams;
+
+// C = alpha A B^T (+ K-extension) with 256 x 256 tiles; requires K % 64 == 0,
+// 16-byte aligned code rows and extension rows, 4-byte aligned scale rows.
+// splits > 1 writes raw partial sums per split (see gemm_fp4_kernel).
+hipError_t launch_gemm_big(const GemmParams& gp, int splits, hipStream_t st);
+
+}  // namespace metis

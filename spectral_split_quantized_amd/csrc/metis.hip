@@ -18,6 +18,7 @@
 #include "../../include/metis.h"
 #include "common.hpp"
 #include "gemm.hpp"
+#include "gemm_launch.hpp"
 #include "quant.hpp"
 #include "rsvd.hpp"
 
@@ -159,6 +160,7 @@ struct Carver {
 };
 
 inline int round_up(int a, int b) { return (a + b - 1) / b * b; }
+inline int64_t round_up64(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
 inline unsigned grid1(int64_t n, int block) { return (unsigned)((n + block - 1) / block); }
 
@@ -380,6 +382,14 @@ metis_status launch_gemm_cfg(const GemmParams& gp, int splits, hipStream_t st) {
   return METIS_OK;
 }
 
+// The register-dequant kernel needs whole 64-wide K steps, 16-byte aligned
+// code rows and 4-byte aligned scale rows.
+bool gemm_reg_ok(const GemmParams& gp) {
+  return gp.K % 64 == 0 && ((uintptr_t)gp.a_codes & 15) == 0 && ((uintptr_t)gp.b_codes & 15) == 0 &&
+         ((uintptr_t)gp.a_scales & 3) == 0 && ((uintptr_t)gp.b_scales & 3) == 0 &&
+         ((uintptr_t)gp.a_ext & 15) == 0 && ((uintptr_t)gp.b_ext & 15) == 0;
+}
+
 enum GemmShape { kGemmBig, kGemmMid, kGemmTall, kGemmWide, kGemmSmall };
 
 GemmShape gemm_shape(int64_t M, int64_t N) {
@@ -421,7 +431,14 @@ metis_status launch_gemm(const GemmParams& gp0, float* part, hipStream_t st) {
   }
   metis_status s;
   switch (gemm_shape(gp.M, gp.N)) {
-    case kGemmBig: s = launch_gemm_cfg<256, 256, 4, 2>(gp, splits, st); break;
+    case kGemmBig:
+      if (gemm_reg_ok(gp)) {
+        const hipError_t e = launch_gemm_big(gp, splits, st);
+        s = e == hipSuccess ? METIS_OK : fail(METIS_E_HIP, "gemm launch: %s", hipGetErrorString(e));
+      } else {
+        s = launch_gemm_cfg<256, 256, 4, 2>(gp, splits, st);
+      }
+      break;
     case kGemmMid: s = launch_gemm_cfg<128, 128, 2, 2>(gp, splits, st); break;
     case kGemmTall: s = launch_gemm_cfg<256, 64, 8, 1>(gp, splits, st); break;
     case kGemmWide: s = launch_gemm_cfg<64, 256, 1, 8>(gp, splits, st); break;
@@ -470,8 +487,8 @@ SplitWs carve_split(Carver& cv, int64_t M, int64_t N, int64_t K, int kL, int kR)
   if (kL > 0) w.t1 = cv.take<float>((size_t)kL * N);
   if (kL > 0 && kR > 0) w.t2 = cv.take<float>((size_t)kL * kR);
   if (w.kext > 0) {
-    w.a_ext = cv.take<uint16_t>((size_t)M * w.kext);
-    w.b_ext = cv.take<uint16_t>((size_t)N * w.kext);
+    w.a_ext = cv.take<uint16_t>((size_t)round_up64(M, 32) * w.kext);
+    w.b_ext = cv.take<uint16_t>((size_t)round_up64(N, 32) * w.kext);
   }
   return w;
 }
@@ -529,7 +546,7 @@ metis_status split_product(const SideQ& L, const SideQ& R, int64_t M, int64_t N,
                     R.k > 0 ? R.out->tensor_scale : w.ones, R.k, N};
     e.a_ext = w.a_ext;
     e.b_ext = w.b_ext;
-    hipLaunchKernelGGL(ext_prep_a_kernel, dim3(grid1(M * kext, 256)), dim3(256), 0, st, e);
+    hipLaunchKernelGGL(ext_prep_a_kernel, dim3(grid1(round_up64(M, 32) * kext, 256)), dim3(256), 0, st, e);
     LAUNCH_CHECK();
     hipLaunchKernelGGL(ext_prep_b_kernel, dim3(grid1(N, 64)), dim3(256), 0, st, e);
     LAUNCH_CHECK();

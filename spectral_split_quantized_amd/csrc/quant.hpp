@@ -23,6 +23,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "status.hpp"
 
 namespace metis {
 

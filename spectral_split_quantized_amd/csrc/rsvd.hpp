@@ -18,6 +18,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "status.hpp"
 
 namespace metis {
 
