@@ -117,33 +117,39 @@ __host__ __device__ inline uint32_t e4m3_encode_rne_sat(float t) {
 
 // E2M1 magnitude index of y >= 0, nearest with ties to the even mantissa,
 // saturating at 6 (index 7).
-__host__ __device__ inline uint32_t e2m1_rne(float y) {
-  if (y <= 0.25f) return 0;
-  if (y < 0.75f) return 1;
-  if (y <= 1.25f) return 2;
-  if (y < 1.75f) return 3;
-  if (y <= 2.5f) return 4;
-  if (y < 3.5f) return 5;
-  if (y <= 5.0f) return 6;
-  return 7;
+// E2M1 rounding without comparisons.  On y >= 0 the grid is three uniform
+// segments: steps of 0.5 on [0, 2] (codes 0..4), 1 on [2, 4] (4..6), 2 on
+// [4, 6] (6..7).  a1 = min(2y, 4), a2 = clamp(y - 2, 0, 2) and
+// a3 = clamp((y - 4) / 2, 0, 1) are exact (power-of-two scalings; y - 2 and
+// y - 4 by Sterbenz wherever they are not clamped), and the code is the sum
+// of the three segment codes.  NaN gives an unspecified code.
+__host__ __device__ inline float e2m1_seg_clamp(float x, float lo, float hi) {
+  return fminf(fmaxf(x, lo), hi);
 }
 
-// Stochastic E2M1 rounding of y >= 0 with a 16-bit draw h (u = h 2^-16):
-// hi iff u < (y - lo) / (hi - lo); the quotient is exact (power-of-two step).
+// Round to nearest with ties to the even code: rint (ties to even) within a
+// segment gives exactly the ties 0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2,
+// 2.5 -> 2, 3.5 -> 4, 5 -> 4 of the grid; y >= 6 saturates to code 7.
+__host__ __device__ inline uint32_t e2m1_rne(float y) {
+  const float a1 = fminf(2.0f * y, 4.0f);
+  const float a2 = e2m1_seg_clamp(y - 2.0f, 0.0f, 2.0f);
+  const float a3 = e2m1_seg_clamp((y - 4.0f) * 0.5f, 0.0f, 1.0f);
+  return (uint32_t)(rintf(a1) + rintf(a2) + rintf(a3));
+}
+
+// Stochastic rounding with a 16-bit draw h (u = h 2^-16): the floor code is
+// lo = sum floor(a_i) and p = sum (a_i - floor(a_i)) = (y - grid[lo]) / step,
+// both exact; the code is lo + 1 iff u < p, i.e. lo + ceil(p - u) (p - u is
+// zero only when p == u and keeps the sign of the exact difference;
+// |p - u| < 1).  y >= 6 gives a3 = 1, p = 0 and code 7.
 __host__ __device__ inline uint32_t e2m1_sr(float y, uint32_t h) {
-  if (!(y < 6.0f)) return 7;
-  uint32_t lo;
-  float glo, inv_step;
-  if (y < 0.5f) { lo = 0; glo = 0.0f; inv_step = 2.0f; }
-  else if (y < 1.0f) { lo = 1; glo = 0.5f; inv_step = 2.0f; }
-  else if (y < 1.5f) { lo = 2; glo = 1.0f; inv_step = 2.0f; }
-  else if (y < 2.0f) { lo = 3; glo = 1.5f; inv_step = 2.0f; }
-  else if (y < 3.0f) { lo = 4; glo = 2.0f; inv_step = 1.0f; }
-  else if (y < 4.0f) { lo = 5; glo = 3.0f; inv_step = 1.0f; }
-  else { lo = 6; glo = 4.0f; inv_step = 0.5f; }
-  const float p = (y - glo) * inv_step;
+  const float a1 = fminf(2.0f * y, 4.0f);
+  const float a2 = e2m1_seg_clamp(y - 2.0f, 0.0f, 2.0f);
+  const float a3 = e2m1_seg_clamp((y - 4.0f) * 0.5f, 0.0f, 1.0f);
+  const float f1 = floorf(a1), f2 = floorf(a2), f3 = floorf(a3);
+  const float p = (a1 - f1) + (a2 - f2) + (a3 - f3);
   const float u = (float)h * (1.0f / 65536.0f);
-  return (u < p) ? lo + 1 : lo;
+  return (uint32_t)(f1 + f2 + f3 + ceilf(p - u));
 }
 
 

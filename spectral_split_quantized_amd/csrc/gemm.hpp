@@ -356,77 +356,80 @@ __global__ void ext_prep_a_kernel(ExtParams e) {
   e.a_ext[ext_off(i, col, e.kext)] = out;
 }
 
-// B_ext[j] = [J_bar | J_bar | hi(s_H G) | lo(..) | 0 ...]; one workgroup per 64
-// output columns: J_bar (64 x kR) and the folded T2 (kL x kR) live in LDS.
-constexpr int kExtMaxK = 128;
+// B_ext[j] = [J_bar | J_bar | hi(s_H G) | lo(..) | 0 ...]: one thread per
+// output column j (rows past e.cols up to the next multiple of 32 are zero).
+// The column's J_bar entries stay in registers and the folded T2 (kL x kR)
+// in LDS; the row is written in 8-element chunks of the fragment layout.
+__device__ inline uint4 pack8_bf16(const float* v) {
+  uint4 o;
+  o.x = (uint32_t)bf16_rn_bits(v[0]) | ((uint32_t)bf16_rn_bits(v[1]) << 16);
+  o.y = (uint32_t)bf16_rn_bits(v[2]) | ((uint32_t)bf16_rn_bits(v[3]) << 16);
+  o.z = (uint32_t)bf16_rn_bits(v[4]) | ((uint32_t)bf16_rn_bits(v[5]) << 16);
+  o.w = (uint32_t)bf16_rn_bits(v[6]) | ((uint32_t)bf16_rn_bits(v[7]) << 16);
+  return o;
+}
+
+constexpr int kExtMaxK = 96;
 __global__ __launch_bounds__(256) void ext_prep_b_kernel(ExtParams e) {
-  __shared__ float jb[64][kExtMaxK + 1];
-  __shared__ float t2s[kExtMaxK];  // one row of folded T2 at a time
-  __shared__ float gq[64];
+  __shared__ float t2f[kExtMaxK][kExtMaxK + 1];
   const int tid = threadIdx.x;
-  const int64_t j0 = (int64_t)blockIdx.x * 64;
-  for (int idx = tid; idx < 64 * e.kR; idx += blockDim.x) {
-    const int jj = idx / e.kR, pp = idx % e.kR;
-    jb[jj][pp] = (j0 + jj < e.cols) ? factor_val(e.J, pp, j0 + jj) : 0.0f;
-  }
-  __syncthreads();
+  const int64_t j = (int64_t)blockIdx.x * 256 + tid;
   const float sJ = e.J.ts[0];
-  // J_bar segments
-  for (int idx = tid; idx < 64 * 2 * e.ksR; idx += blockDim.x) {
-    const int jj = idx / (2 * e.ksR);
-    const int col = idx % (2 * e.ksR);
-    const int p = col % e.ksR;
-    if (j0 + jj >= e.cols) continue;
-    const uint16_t v = (p < e.kR) ? bf16_rn_bits(jb[jj][p]) : (uint16_t)0;
-    e.b_ext[ext_off(j0 + jj, col, e.kext)] = v;
-  }
-  // G rows
   const float sFE = e.s_F[0] * e.s_E[0];
   const float sFR = e.s_F[0] * e.s_RR[0];
   const float sH = e.H.ts[0];
-  for (int q = 0; q < e.ksL; ++q) {
-    __syncthreads();
-    if (q < e.kL)
-      for (int pp = tid; pp < e.kR; pp += blockDim.x)
-        t2s[pp] = sFE * e.t2[(int64_t)q * e.kR + pp] * e.S_R[pp] * sJ;
-    __syncthreads();
-    if (tid < 64) {
+  for (int idx = tid; idx < e.kL * e.kR; idx += 256) {
+    const int q = idx / e.kR, pp = idx - q * e.kR;
+    t2f[q][pp] = sFE * e.t2[(int64_t)q * e.kR + pp] * e.S_R[pp] * sJ;
+  }
+  __syncthreads();
+  if (j >= ((e.cols + 31) & ~(int64_t)31)) return;
+  uint16_t* out = e.b_ext;
+  if (j >= e.cols) {
+    for (int64_t c = 0; c < e.kext; c += 8) *(uint4*)(out + ext_off(j, c, e.kext)) = make_uint4(0, 0, 0, 0);
+    return;
+  }
+  float jr[kExtMaxK];
+#pragma unroll
+  for (int pp = 0; pp < kExtMaxK; ++pp) jr[pp] = (pp < e.kR) ? factor_val(e.J, pp, j) : 0.0f;
+  // J_bar, twice
+  for (int c = 0; c < e.ksR; c += 8) {
+    float v[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      float x = 0.0f;
+#pragma unroll
+      for (int pp = 0; pp < kExtMaxK; pp += 8)
+        if (pp == (c & ~7)) x = jr[pp + t];  // static register index
+      v[t] = x;
+    }
+    const uint4 w = pack8_bf16(v);
+    *(uint4*)(out + ext_off(j, c, e.kext)) = w;
+    *(uint4*)(out + ext_off(j, e.ksR + c, e.kext)) = w;
+  }
+  // G = s_H S_L[q] (s_F s_RR T1[q][j] + sum_p T2f[q][p] J[j][p]) as hi / lo
+  for (int q0 = 0; q0 < e.ksL; q0 += 8) {
+    float hi[8], lo[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int q = q0 + t;
       float g = 0.0f;
-      const int64_t j = j0 + tid;
-      if (q < e.kL && j < e.cols) {
+      if (q < e.kL) {
         float acc = sFR * e.t1[(int64_t)q * e.cols + j];
-        for (int pp = 0; pp < e.kR; ++pp) acc += t2s[pp] * jb[tid][pp];
+#pragma unroll
+        for (int pp = 0; pp < kExtMaxK; ++pp)
+          if (pp < e.kR) acc += t2f[q][pp] * jr[pp];
         g = sH * e.S_L[q] * acc;
       }
-      gq[tid] = g;
+      const uint16_t h = bf16_rn_bits(g);
+      hi[t] = bf16_bits_to_float(h);
+      lo[t] = g - hi[t];
     }
-    __syncthreads();
-    if (tid < 128) {
-      const int jj = tid & 63;
-      const int64_t j = j0 + jj;
-      if (j < e.cols) {
-        const float g = gq[jj];
-        const uint16_t hi = bf16_rn_bits(g);
-        const uint16_t v = (tid < 64) ? hi : bf16_rn_bits(g - bf16_bits_to_float(hi));
-        const int col = 2 * e.ksR + ((tid < 64) ? 0 : e.ksL) + q;
-        e.b_ext[ext_off(j, col, e.kext)] = v;
-      }
-    }
+    *(uint4*)(out + ext_off(j, 2 * e.ksR + q0, e.kext)) = pack8_bf16(hi);
+    *(uint4*)(out + ext_off(j, 2 * e.ksR + e.ksL + q0, e.kext)) = pack8_bf16(lo);
   }
-  // zero tail of the K-extension, and whole rows past e.cols up to the next
-  // multiple of 32
-  const int used = 2 * e.ksR + 2 * e.ksL;
-  const int tail = (int)(e.kext - used);
-  for (int idx = tid; idx < 64 * tail; idx += blockDim.x) {
-    const int jj = idx / tail;
-    const int col = used + idx % tail;
-    if (j0 + jj < e.cols) e.b_ext[ext_off(j0 + jj, col, e.kext)] = 0;
-  }
-  const int64_t padded = (e.cols + 31) & ~(int64_t)31;
-  for (int64_t idx = tid; idx < 64 * e.kext; idx += blockDim.x) {
-    const int64_t j = j0 + idx / e.kext;
-    if (j >= e.cols && j < padded) e.b_ext[ext_off(j, idx % e.kext, e.kext)] = 0;
-  }
+  for (int64_t c = 2 * e.ksR + 2 * e.ksL; c < e.kext; c += 8)
+    *(uint4*)(out + ext_off(j, c, e.kext)) = make_uint4(0, 0, 0, 0);
 }
 
 }  // namespace metis

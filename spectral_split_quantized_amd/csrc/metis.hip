@@ -275,10 +275,17 @@ metis_status launch_gram(const float* X, int64_t nr, int n, int64_t rs, int64_t 
                          double* part, double* G, hipStream_t st) {
   int64_t per = (nr + maxblocks - 1) / maxblocks;
   per = (per + 31) / 32 * 32;
-  if (per < 32) per = 32;
+  if (per < 64) per = 64;
   const int blocks = (int)((nr + per - 1) / per);
-  hipLaunchKernelGGL(gram_partial_kernel, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, st, X, nr, n,
-                     rs, cs, per, part);
+  const dim3 grid(blocks > 0 ? blocks : 1);
+  switch ((n + 15) / 16) {
+    case 1: hipLaunchKernelGGL(gram_partial_kernel<1>, grid, dim3(256), 0, st, X, nr, n, rs, cs, per, part); break;
+    case 2: hipLaunchKernelGGL(gram_partial_kernel<2>, grid, dim3(256), 0, st, X, nr, n, rs, cs, per, part); break;
+    case 3: hipLaunchKernelGGL(gram_partial_kernel<3>, grid, dim3(256), 0, st, X, nr, n, rs, cs, per, part); break;
+    case 4: hipLaunchKernelGGL(gram_partial_kernel<4>, grid, dim3(256), 0, st, X, nr, n, rs, cs, per, part); break;
+    case 5: hipLaunchKernelGGL(gram_partial_kernel<5>, grid, dim3(256), 0, st, X, nr, n, rs, cs, per, part); break;
+    default: hipLaunchKernelGGL(gram_partial_kernel<6>, grid, dim3(256), 0, st, X, nr, n, rs, cs, per, part); break;
+  }
   LAUNCH_CHECK();
   hipLaunchKernelGGL(reduce_gram_kernel, dim3(grid1(n * n, 256)), dim3(256), 0, st, part,
                      blocks > 0 ? blocks : 1, n * n, G);
@@ -548,7 +555,7 @@ metis_status split_product(const SideQ& L, const SideQ& R, int64_t M, int64_t N,
     e.b_ext = w.b_ext;
     hipLaunchKernelGGL(ext_prep_a_kernel, dim3(grid1(round_up64(M, 32) * kext, 256)), dim3(256), 0, st, e);
     LAUNCH_CHECK();
-    hipLaunchKernelGGL(ext_prep_b_kernel, dim3(grid1(N, 64)), dim3(256), 0, st, e);
+    hipLaunchKernelGGL(ext_prep_b_kernel, dim3(grid1(round_up64(N, 32), 256)), dim3(256), 0, st, e);
     LAUNCH_CHECK();
   }
   g = GemmParams{M, N, K, L.res->codes, L.res->scales, R.res->codes, R.res->scales,

@@ -134,19 +134,17 @@ __device__ inline QuantBlockOut quant_block16(const float (&x)[16], const uint32
   const uint32_t sb = e4m3_encode_rne_sat(t);
   const float s_b = e4m3_decode(sb);
   const float s_eff = __fmul_rn(s_b, s_g);
-  const float inv = __fdiv_rn(1.0f, s_eff);
+  // a zero block scale gives inv = 0, hence y = 0 and magnitude code 0 for
+  // every (finite) element of the block
+  const float inv = sb != 0u ? __fdiv_rn(1.0f, s_eff) : 0.0f;
   QuantBlockOut o;
   o.lo = 0;
   o.hi = 0;
   o.scale = sb;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const float ax = fabsf(x[i]);
-    uint32_t m = 0;
-    if (sb != 0u && ax != 0.0f) {
-      const float y = __fmul_rn(ax, inv);
-      m = sr ? e2m1_sr(y, h[i]) : e2m1_rne(y);
-    }
+    const float y = __fmul_rn(fabsf(x[i]), inv);
+    const uint32_t m = sr ? e2m1_sr(y, h[i]) : e2m1_rne(y);
     const uint32_t code = ((__float_as_uint(x[i]) >> 31) << 3) | m;
     if (i < 8)
       o.lo |= code << (4 * i);

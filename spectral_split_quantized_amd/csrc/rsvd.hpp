@@ -262,41 +262,60 @@ __global__ void reduce_slices_kernel(const float* __restrict__ part, int slices,
 
 // --------------------------------------------------------------- fp64 Grams --
 
-// Partial Gram of an nr x n matrix X (element (r, j) at X[r*rs + j*cs]):
-// part[block][a][b] = sum over this block's rows of X[r][a] X[r][b].
-__global__ __launch_bounds__(256) void gram_partial_kernel(const float* __restrict__ X, int64_t nr,
-                                                           int n, int64_t rs, int64_t cs,
-                                                           int64_t rows_per_block,
+// Partial Gram of an nr x n matrix X (element (r, j) at X[r*rs + j*cs]),
+// n <= 16 T: part[block][a][b] = sum over this block's rows (in row order)
+// of X[r][a] X[r][b], in fp64 (each product of two binary32 values is exact).
+// Thread (ti, tj) of a 16 x 16 grid owns entries a = ti + 16 u, b = tj + 16 v.
+template <int T>
+__global__ __launch_bounds__(256) void gram_partial_kernel(const float* __restrict__ X, int64_t nr, int n,
+                                                           int64_t rs, int64_t cs, int64_t rows_per_block,
                                                            double* __restrict__ part) {
-  __shared__ float xs[32][kMaxN + 1];
+  constexpr int W = 16 * T;
+  __shared__ float xs[32][W + 1];
   const int tid = threadIdx.x;
+  const int ti = tid & 15, tj = tid >> 4;
   const int64_t rb = (int64_t)blockIdx.x * rows_per_block;
   const int64_t re = min(nr, rb + rows_per_block);
-  const int nn = n * n;
-  double acc[(kMaxN * kMaxN + 255) / 256];
-  const int per = (nn + 255) / 256;
-  for (int t = 0; t < per; ++t) acc[t] = 0.0;
+  double acc[T][T];
+#pragma unroll
+  for (int u = 0; u < T; ++u)
+#pragma unroll
+    for (int v = 0; v < T; ++v) acc[u][v] = 0.0;
   for (int64_t r0 = rb; r0 < re; r0 += 32) {
     __syncthreads();
-    for (int e = tid; e < 32 * n; e += 256) {
-      const int r = e / n, j = e % n;
-      xs[r][j] = (r0 + r < re) ? X[(r0 + r) * rs + (int64_t)j * cs] : 0.0f;
-    }
-    __syncthreads();
-    for (int t = 0; t < per; ++t) {
-      const int e = tid + 256 * t;
-      if (e < nn) {
-        const int a = e / n, b = e % n;
-        double s = 0.0;
-        for (int r = 0; r < 32; ++r) s += (double)xs[r][a] * (double)xs[r][b];
-        acc[t] += s;
+    if (cs == 1) {  // rows contiguous: walk the columns fastest
+      for (int e = tid; e < 32 * n; e += 256) {
+        const int r = e / n, j = e - r * n;
+        xs[r][j] = (r0 + r < re) ? X[(r0 + r) * rs + j] : 0.0f;
+      }
+    } else {        // columns contiguous: walk the rows fastest
+      for (int e = tid; e < 32 * n; e += 256) {
+        const int r = e & 31, j = e >> 5;
+        xs[r][j] = (r0 + r < re) ? X[(r0 + r) * rs + (int64_t)j * cs] : 0.0f;
       }
     }
+    __syncthreads();
+#pragma unroll 4
+    for (int r = 0; r < 32; ++r) {
+      double xa[T], xb[T];
+#pragma unroll
+      for (int u = 0; u < T; ++u) xa[u] = (double)xs[r][ti + 16 * u];
+#pragma unroll
+      for (int v = 0; v < T; ++v) xb[v] = (double)xs[r][tj + 16 * v];
+#pragma unroll
+      for (int u = 0; u < T; ++u)
+#pragma unroll
+        for (int v = 0; v < T; ++v) acc[u][v] += xa[u] * xb[v];
+    }
   }
-  for (int t = 0; t < per; ++t) {
-    const int e = tid + 256 * t;
-    if (e < nn) part[(int64_t)blockIdx.x * nn + e] = acc[t];
-  }
+  const int nn = n * n;
+#pragma unroll
+  for (int u = 0; u < T; ++u)
+#pragma unroll
+    for (int v = 0; v < T; ++v) {
+      const int a = ti + 16 * u, b = tj + 16 * v;
+      if (a < n && b < n) part[(int64_t)blockIdx.x * nn + a * n + b] = acc[u][v];
+    }
 }
 
 __global__ void reduce_gram_kernel(const double* __restrict__ part, int blocks, int nn,
