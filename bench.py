@@ -116,12 +116,22 @@ def build_inputs(n_steps, device):
 
 class MetisMLP:
     """Persistent state of the path for the three projections: factor
-    caches, quantised operands, outputs and one shared workspace."""
+    caches, quantised operands, outputs and one workspace per stream.
 
-    def __init__(self, device):
+    One step follows the layer's data dependencies on up to three HIP
+    streams: the weights (known when the step starts) are decomposed and
+    quantised on a side stream while the main stream handles X_gu; the
+    forward GEMMs wait for their weight; X_down follows the gate/up GEMMs
+    and D_down the down GEMM (in a real layer they are computed from them);
+    D_gate and D_up, which both come from the down projection's dX, are
+    processed concurrently.  With streams=1 everything runs in that order
+    on one stream."""
+
+    def __init__(self, device, streams=3):
         import torch
         from spectral_split_quantized_amd import metis
         self.metis = metis
+        self.torch = torch
         self.cfg = metis.make_config(k=K_RANK, s=OVERSAMPLE, l_k=L_K, refresh=REFRESH,
                                      rounding=metis.SR, seed=0)
         self.ops = {op.name: op for op in operands()}
@@ -146,24 +156,73 @@ class MetisMLP:
             xc, wc, dc = self.q[x]._c(), self.q[w]._c(), self.q[d]._c()
             need = max(need, lib.metis_gemm_fwd_workspace(ctypes.byref(xc), ctypes.byref(wc)),
                        lib.metis_gemm_bwd_workspace(ctypes.byref(dc), ctypes.byref(wc), ctypes.byref(xc)))
-        self.ws = torch.empty(need, dtype=torch.uint8, device=device)
-        log("  workspace %.1f MB" % (need / 1e6))
+        self.nstreams = max(1, min(3, int(streams)))
+        # default-priority streams only
+        self.streams = [torch.cuda.current_stream(device)] + \
+            [torch.cuda.Stream(device=device) for _ in range(self.nstreams - 1)]
+        self.ws = [torch.empty(need, dtype=torch.uint8, device=device) for _ in self.streams]
+        self.step_done = None
+        log("  workspace %.1f MB x %d streams" % (need / 1e6, self.nstreams))
 
     def decompose(self, name, M, t):
         op = self.ops[name]
-        self.metis.decompose(M, self.cfg, op.sample, op.tag, t, self.factors[name], workspace=self.ws)
+        self.metis.decompose(M, self.cfg, op.sample, op.tag, t, self.factors[name], workspace=self.ws[0])
+
+    def _prep(self, name, t, inputs, si):
+        """Decompose and quantise one operand (both K orientations) on stream si."""
+        m = self.metis
+        op = self.ops[name]
+        M = inputs[name][t % len(inputs[name])]
+        with self.torch.cuda.stream(self.streams[si]):
+            m.decompose(M, self.cfg, op.sample, op.tag, t, self.factors[name], workspace=self.ws[si])
+            m.quantize(M, self.cfg, op.tag, t, m.AXIS0 | m.AXIS1, factors=self.factors[name],
+                       out=self.q[name], workspace=self.ws[si])
+
+    def _event(self, si):
+        e = self.torch.cuda.Event()
+        e.record(self.streams[si])
+        return e
+
+    def _gemms(self, name, fwd):
+        m = self.metis
+        _, x, w, d = next(p for p in PROJECTIONS if p[0] == name)
+        Y, dX, dW = self.out[name]
+        if fwd:
+            m.gemm_fwd(self.q[x], self.q[w], Y=Y, workspace=self.ws[0])
+        else:
+            m.gemm_bwd(self.q[d], self.q[w], self.q[x], dX=dX, dW=dW, workspace=self.ws[0])
 
     def step(self, t, inputs):
-        m = self.metis
-        for name, op in self.ops.items():
-            M = inputs[name][t % len(inputs[name])]
-            self.decompose(name, M, t)
-            m.quantize(M, self.cfg, op.tag, t, m.AXIS0 | m.AXIS1, factors=self.factors[name],
-                       out=self.q[name], workspace=self.ws)
-        for name, x, w, d in PROJECTIONS:
-            Y, dX, dW = self.out[name]
-            m.gemm_fwd(self.q[x], self.q[w], Y=Y, workspace=self.ws)
-            m.gemm_bwd(self.q[d], self.q[w], self.q[x], dX=dX, dW=dW, workspace=self.ws)
+        main = self.streams[0]
+        sw = 1 if self.nstreams > 1 else 0
+        sd = 2 if self.nstreams > 2 else 0
+        # the side streams overwrite quantised operands the previous step read
+        if self.step_done is not None:
+            for s in self.streams[1:]:
+                s.wait_event(self.step_done)
+        ev = {}
+        for w in ("W_gate", "W_up", "W_down"):
+            self._prep(w, t, inputs, sw)
+            ev[w] = self._event(sw)
+        self._prep("X_gu", t, inputs, 0)
+        main.wait_event(ev["W_gate"])
+        self._gemms("gate", True)
+        main.wait_event(ev["W_up"])
+        self._gemms("up", True)
+        self._prep("X_down", t, inputs, 0)
+        main.wait_event(ev["W_down"])
+        self._gemms("down", True)
+        self._prep("D_down", t, inputs, 0)
+        self._gemms("down", False)
+        dx_ready = self._event(0)
+        self.streams[sd].wait_event(dx_ready)
+        self._prep("D_up", t, inputs, sd)
+        e_up = self._event(sd)
+        self._prep("D_gate", t, inputs, 0)
+        self._gemms("gate", False)
+        main.wait_event(e_up)
+        self._gemms("up", False)
+        self.step_done = self._event(0)
 
     def step_flops(self, t):
         refresh = (t % REFRESH) == 0
@@ -234,6 +293,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=256)
     ap.add_argument("--cpu-cols", type=int, default=2048)
+    ap.add_argument("--streams", type=int, default=3,
+                    help="HIP streams per step (1: every call in order on one stream)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -255,7 +316,7 @@ def main():
     t_build = time.time()
     inputs = build_inputs(REFRESH, dev)
     log("inputs built in %.1f s" % (time.time() - t_build))
-    mlp = MetisMLP(dev)
+    mlp = MetisMLP(dev, streams=args.streams)
 
     # warmup (untimed), then the timed steps; step index continues so the
     # refresh schedule (every 8 steps) is the same in both
@@ -320,7 +381,7 @@ def main():
         for label, t in (("refresh", 64), ("cached", 65)):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            metis.decompose(M, mlp.cfg, op.sample, op.tag, t, f, workspace=mlp.ws)
+            metis.decompose(M, mlp.cfg, op.sample, op.tag, t, f, workspace=mlp.ws[0])
             b.record(stream)
             torch.cuda.synchronize()
             rsvd_ms["%s_%s" % (name, label)] = round(a.elapsed_time(b), 3)
@@ -341,6 +402,7 @@ def main():
            "dtype": "nvfp4 operands, f16 mfma, f32 accumulate",
            "data": "synthetic",
            "config": {"workload": "llama3_8b_mlp_gate_up_down_16k_tokens_8step_factor_cache",
+                      "streams": mlp.nstreams,
                       "tokens": TOKENS, "hidden": HIDDEN, "ffn": FFN, "k": K_RANK, "s": OVERSAMPLE,
                       "l_k": L_K, "refresh": REFRESH, "rounding": "sr"},
            "dense_equiv_tflops": round(dense_equiv_flops() * args.steps / (total_ms * 1e-3) / 1e12, 2),
