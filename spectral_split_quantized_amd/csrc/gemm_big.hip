@@ -8,11 +8,11 @@
 namespace metis {
 
 hipError_t launch_gemm_big(const GemmParams& gp, int splits, hipStream_t st) {
-  using Cfg = RegCfg<2, 2, 4, 4, 3>;
+  using Cfg = RegCfg<2, 2, 4, 4>;
   const int64_t tiles = ceil_div<int64_t>(gp.M, Cfg::BM) * ceil_div<int64_t>(gp.N, Cfg::BN);
   if (tiles <= 0) return hipSuccess;
   // LDS is static (one array per pipeline stage)
-  hipLaunchKernelGGL((gemm_fp4_reg_kernel<2, 2, 4, 4, 3>), dim3((unsigned)tiles, (unsigned)splits), dim3(Cfg::NT),
+  hipLaunchKernelGGL((gemm_fp4_reg_kernel<2, 2, 4, 4>), dim3((unsigned)tiles, (unsigned)splits), dim3(Cfg::NT),
                      0, st, gp);
   return hipGetLastError();
 }

@@ -7,8 +7,8 @@ namespace metis {
 
 struct GemmParams;
 
-// C = alpha A B^T (+ K-extension) with 256 x 256 tiles; requires K % 64 == 0,
-// 16-byte aligned code rows and extension rows, 4-byte aligned scale rows.
+// C = alpha A B^T (+ K-extension) with 256 x 256 tiles; requires K % 256 == 0
+// and 16-byte aligned code, scale and extension rows.
 // splits > 1 writes raw partial sums per split (see gemm_fp4_kernel).
 hipError_t launch_gemm_big(const GemmParams& gp, int splits, hipStream_t st);
 

@@ -389,11 +389,11 @@ metis_status launch_gemm_cfg(const GemmParams& gp, int splits, hipStream_t st) {
   return METIS_OK;
 }
 
-// The register-dequant kernel needs whole 64-wide K steps, 16-byte aligned
-// code rows and 4-byte aligned scale rows.
+// The register-dequant kernel needs whole 256-wide K stages and 16-byte
+// aligned code, scale and extension rows.
 bool gemm_reg_ok(const GemmParams& gp) {
-  return gp.K % 64 == 0 && ((uintptr_t)gp.a_codes & 15) == 0 && ((uintptr_t)gp.b_codes & 15) == 0 &&
-         ((uintptr_t)gp.a_scales & 3) == 0 && ((uintptr_t)gp.b_scales & 3) == 0 &&
+  return gp.K % 256 == 0 && ((uintptr_t)gp.a_codes & 15) == 0 && ((uintptr_t)gp.b_codes & 15) == 0 &&
+         ((uintptr_t)gp.a_scales & 15) == 0 && ((uintptr_t)gp.b_scales & 15) == 0 &&
          ((uintptr_t)gp.a_ext & 15) == 0 && ((uintptr_t)gp.b_ext & 15) == 0;
 }
 
