@@ -70,10 +70,17 @@ def tensor_scale(amax):
     return s_g, d
 
 
-def quantize(x, axis, rounding="rne", seed=0, tag=0, step=0):
+def quantize(x, axis, rounding="rne", seed=0, tag=0, step=0, amax=None, origin=None):
     """Quantise a 2-D binary32 tensor along ``axis``; returns a QTensor.
 
-    ``rounding`` is "rne" or "sr" (Philox uniforms with seed/tag/step)."""
+    ``rounding`` is "rne" or "sr" (Philox uniforms with seed/tag/step).
+
+    To quantise part of a larger tensor, pass the larger tensor's ``amax``
+    (its exact max |x|, Q1) and ``origin = (outer0, k0, K_full)``: the part's
+    first element sits at row outer0, column k0 of the larger tensor's
+    quantised orientation (n_outer x K_full), which fixes the Philox index of
+    every element.  K blocks of the part must be whole blocks of the larger
+    tensor (k0 % 16 == 0)."""
     x = np.asarray(x, dtype=np.float32)
     if x.ndim != 2:
         raise ValueError("2-D input expected")
@@ -84,7 +91,12 @@ def quantize(x, axis, rounding="rne", seed=0, tag=0, step=0):
     n_outer, K = xt.shape
     if K % BLOCK:
         raise ValueError("K must be a multiple of 16")
-    amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0)
+    if amax is None:
+        amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0)
+    amax = np.float32(amax)
+    outer0, k0, k_full = (0, 0, K) if origin is None else (int(origin[0]), int(origin[1]), int(origin[2]))
+    if k0 % BLOCK or k0 + K > k_full:
+        raise ValueError("origin must place whole blocks inside the larger tensor")
     s_g, d = tensor_scale(amax)
     ax = np.abs(xt).astype(np.float64).reshape(n_outer, K // BLOCK, BLOCK)
     a_b = ax.max(axis=2)
@@ -103,7 +115,9 @@ def quantize(x, axis, rounding="rne", seed=0, tag=0, step=0):
     if rounding == "rne":
         m = formats.e2m1_rne(y)
     elif rounding == "sr":
-        et = np.arange(n_outer * K, dtype=np.uint64)      # index in the (n_outer x K) layout
+        # index in the (n_outer x K_full) layout of the whole tensor
+        et = ((np.arange(n_outer, dtype=np.uint64) + np.uint64(outer0))[:, None] * np.uint64(k_full)
+              + (np.arange(K, dtype=np.uint64) + np.uint64(k0))[None, :]).ravel()
         u = philox.uniform_from_halves(philox.halves(et, seed, tag, step))
         m = formats.e2m1_sr(y, u.reshape(n_outer, K // BLOCK, BLOCK))
     else:

@@ -133,6 +133,53 @@ def drift_weight(w_master, seed, scale=1e-3):
                                          dtype=w_master.dtype, device=w_master.device)
 
 
+# ------------------------------------------------- seeded quantised operands --
+# Random but valid NVFP4 operands (codes, E4M3 block scales, tensor scales,
+# singular values) used as GEMM inputs by both the HIP path and the oracle.
+
+def q4_arrays(n_outer, k_len, seed, zero_block_frac=0.02):
+    """One quantised orientation as numpy arrays: codes uint8 [n_outer,
+    k_len/2] (uniform random bytes), E4M3 scale bytes uint8 [n_outer,
+    k_len/16] (normal values 2^-6 .. 2^5, plus a few zero blocks) and a
+    binary32 tensor scale."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, size=(n_outer, k_len // 2), dtype=np.uint8)
+    scales = rng.integers(0x08, 0x60, size=(n_outer, k_len // 16), dtype=np.uint8)
+    scales[rng.random(scales.shape) < zero_block_frac] = 0
+    ts = np.float32(2.0 ** rng.uniform(-6, -2))
+    return codes, scales, ts
+
+
+def qoperand_arrays(rows, cols, k, seed):
+    """A quantised operand (rows x cols, rank k) as numpy arrays: residual
+    orientations 'R0' (K = rows) and 'R1' (K = cols); for k > 0 factors 'U'
+    (k x rows, blocked along rows), 'V' (k x cols) and descending binary32 'S'."""
+    import numpy as np
+    out = {"R0": q4_arrays(cols, rows, seed + 1), "R1": q4_arrays(rows, cols, seed + 2)}
+    if k > 0:
+        out["U"] = q4_arrays(k, rows, seed + 3)
+        out["V"] = q4_arrays(k, cols, seed + 4)
+        rng = np.random.default_rng(seed + 5)
+        out["S"] = np.sort(rng.uniform(0.5, 40.0, size=k)).astype(np.float32)[::-1].copy()
+    return out
+
+
+def exact_factors(rows, cols, k, seed):
+    """Factors whose product U diag(S) V^T is exact in binary32 (and in any
+    wider format): U = a/16, V = b/16 with integers |a|, |b| <= 8, and S
+    powers of two 2^3 .. 2^-2 (descending); every partial sum is a multiple
+    of 2^-10 below 2^8.  Returns float32 numpy arrays U (rows x k), S (k),
+    V (cols x k)."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    u = (rng.integers(-8, 9, size=(rows, k)) / 16.0).astype(np.float32)
+    v = (rng.integers(-8, 9, size=(cols, k)) / 16.0).astype(np.float32)
+    e = np.sort(rng.integers(-2, 4, size=k))[::-1]
+    s = (2.0 ** e).astype(np.float32)
+    return u, s, v
+
+
 # ---------------------------------------------------------------- configs ---
 
 C0 = dict(name="c0_fwd_256x512", X=(256, 512), W=(512, 512), k=8, s=8, l_k=64,

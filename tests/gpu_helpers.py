@@ -1,5 +1,6 @@
-"""Helpers shared by the GPU parity tests: run the HIP path on one layer and
-convert its outputs into the oracle's types."""
+"""Helpers shared by the GPU parity tests: run the HIP path on one layer, and
+build identical HIP-side and oracle-side operands from seeded arrays.  Nothing
+here feeds an output of the HIP path into the oracle."""
 
 import math
 import sys
@@ -20,23 +21,41 @@ def to_np(t):
     return t.detach().float().cpu().numpy() if t.dtype == torch.bfloat16 else t.detach().cpu().numpy()
 
 
-def qt_from_gpu(q4, rows, cols, axis):
-    """oracle QTensor holding the GPU's codes, scales and tensor scale."""
-    return nvfp4.QTensor(q4.codes.cpu().numpy(), q4.scales.cpu().numpy(),
-                         np.float32(q4.tensor_scale.cpu().item()), rows, cols, axis)
+def gpu_qop(arr, rows, cols, k, device="cuda"):
+    """HIP-side quantised operand filled with the seeded arrays of
+    synth.qoperand_arrays (the oracle side gets the same arrays)."""
+    q = metis.QOperand(rows, cols, k, metis.AXIS0 | metis.AXIS1, device)
+    for name, q4 in (("R0", q.R_ax0), ("R1", q.R_ax1), ("U", q.U), ("V", q.V)):
+        if q4 is None:
+            continue
+        codes, scales, ts = arr[name]
+        q4.codes.copy_(torch.from_numpy(codes))
+        q4.scales.copy_(torch.from_numpy(scales))
+        q4.tensor_scale.fill_(float(ts))
+    if k:
+        q.S = torch.from_numpy(arr["S"]).to(device)
+    return q
 
 
-def qop_from_gpu(q):
-    op = split_gemm.QOperand(q.rows, q.cols)
-    if q.k:
-        op.s = q.S.cpu().numpy().astype(np.float32)
-        op.u_q = qt_from_gpu(q.U, q.rows, q.k, 0)
-        op.v_q = qt_from_gpu(q.V, q.cols, q.k, 0)
-    if q.R_ax0 is not None:
-        op.r_ax0 = qt_from_gpu(q.R_ax0, q.rows, q.cols, 0)
-    if q.R_ax1 is not None:
-        op.r_ax1 = qt_from_gpu(q.R_ax1, q.rows, q.cols, 1)
+def oracle_qop(arr, rows, cols, k):
+    """Oracle quantised operand holding the same seeded arrays."""
+    op = split_gemm.QOperand(rows, cols)
+    op.r_ax0 = nvfp4.QTensor(arr["R0"][0], arr["R0"][1], arr["R0"][2], rows, cols, 0)
+    op.r_ax1 = nvfp4.QTensor(arr["R1"][0], arr["R1"][1], arr["R1"][2], rows, cols, 1)
+    if k:
+        op.s = np.asarray(arr["S"], np.float32)
+        op.u_q = nvfp4.QTensor(arr["U"][0], arr["U"][1], arr["U"][2], rows, k, 0)
+        op.v_q = nvfp4.QTensor(arr["V"][0], arr["V"][1], arr["V"][2], cols, k, 0)
     return op
+
+
+def gpu_factors(u, s, v, device="cuda"):
+    """metis.Factors holding given (seeded) binary32 U, S, V."""
+    f = metis.Factors(u.shape[0], v.shape[0], u.shape[1], device)
+    f.U.copy_(torch.from_numpy(np.ascontiguousarray(u)))
+    f.S.copy_(torch.from_numpy(np.ascontiguousarray(s)))
+    f.V.copy_(torch.from_numpy(np.ascontiguousarray(v)))
+    return f
 
 
 def assert_qtensor_equal(gpu_q4, oracle_q, what):

@@ -151,3 +151,22 @@ def test_sr_uses_element_index_and_role():
 def test_k_not_multiple_of_16_rejected():
     with pytest.raises(ValueError):
         nvfp4.quantize(np.ones((4, 24), np.float32), 1)
+
+
+@pytest.mark.parametrize("rounding", ["rne", "sr"])
+def test_part_quantisation_matches_whole(rounding):
+    # a panel quantised with the whole tensor's amax and its origin equals the
+    # corresponding rows (axis 1) / outer rows (axis 0) of the whole result
+    x = (np.random.default_rng(21).standard_normal((96, 80)) * 3).astype(np.float32)
+    amax = np.float32(np.max(np.abs(x)))
+    full1 = nvfp4.quantize(x, 1, rounding, seed=3, tag=77, step=2)
+    part1 = nvfp4.quantize(x[32:64], 1, rounding, seed=3, tag=77, step=2, amax=amax, origin=(32, 0, 80))
+    assert np.array_equal(part1.codes, full1.codes[32:64])
+    assert np.array_equal(part1.scales, full1.scales[32:64])
+    assert part1.s_g == full1.s_g
+    full0 = nvfp4.quantize(x, 0, rounding, seed=3, tag=77, step=2)
+    # columns 16..31, rows 48..95 (whole 16-row blocks along K = rows)
+    part0 = nvfp4.quantize(x[48:96, 16:32], 0, rounding, seed=3, tag=77, step=2, amax=amax,
+                           origin=(16, 48, 96))
+    assert np.array_equal(part0.codes, full0.codes[16:32, 24:48])
+    assert np.array_equal(part0.scales, full0.scales[16:32, 3:6])
