@@ -357,9 +357,11 @@ __global__ void ext_prep_a_kernel(ExtParams e) {
 }
 
 // B_ext[j] = [J_bar | J_bar | hi(s_H G) | lo(..) | 0 ...]: one thread per
-// output column j (rows past e.cols up to the next multiple of 32 are zero).
-// The column's J_bar entries stay in registers and the folded T2 (kL x kR)
-// in LDS; the row is written in 8-element chunks of the fragment layout.
+// output column j (rows past e.cols up to the next multiple of 32 are zero)
+// and, along blockIdx.y, one group of 8 rows q of G; the group-0 workgroups
+// also write J_bar and the zero tail.  The column's J_bar entries stay in
+// registers and the group's 8 rows of the folded T2 in LDS; the row is
+// written in 8-element chunks.
 __device__ inline uint4 pack8_bf16(const float* v) {
   uint4 o;
   o.x = (uint32_t)bf16_rn_bits(v[0]) | ((uint32_t)bf16_rn_bits(v[1]) << 16);
@@ -371,65 +373,69 @@ __device__ inline uint4 pack8_bf16(const float* v) {
 
 constexpr int kExtMaxK = 96;
 __global__ __launch_bounds__(256) void ext_prep_b_kernel(ExtParams e) {
-  __shared__ float t2f[kExtMaxK][kExtMaxK + 1];
+  __shared__ float t2f[8][kExtMaxK + 1];
   const int tid = threadIdx.x;
   const int64_t j = (int64_t)blockIdx.x * 256 + tid;
+  const int q0 = 8 * blockIdx.y;  // this workgroup's rows of G
   const float sJ = e.J.ts[0];
   const float sFE = e.s_F[0] * e.s_E[0];
   const float sFR = e.s_F[0] * e.s_RR[0];
   const float sH = e.H.ts[0];
-  for (int idx = tid; idx < e.kL * e.kR; idx += 256) {
-    const int q = idx / e.kR, pp = idx - q * e.kR;
-    t2f[q][pp] = sFE * e.t2[(int64_t)q * e.kR + pp] * e.S_R[pp] * sJ;
+  for (int idx = tid; idx < 8 * e.kR; idx += 256) {
+    const int t = idx / e.kR, pp = idx - t * e.kR;
+    const int q = q0 + t;
+    t2f[t][pp] = q < e.kL ? sFE * e.t2[(int64_t)q * e.kR + pp] * e.S_R[pp] * sJ : 0.0f;
   }
   __syncthreads();
   if (j >= ((e.cols + 31) & ~(int64_t)31)) return;
   uint16_t* out = e.b_ext;
   if (j >= e.cols) {
-    for (int64_t c = 0; c < e.kext; c += 8) *(uint4*)(out + ext_off(j, c, e.kext)) = make_uint4(0, 0, 0, 0);
+    if (blockIdx.y == 0)
+      for (int64_t c = 0; c < e.kext; c += 8) *(uint4*)(out + ext_off(j, c, e.kext)) = make_uint4(0, 0, 0, 0);
     return;
   }
   float jr[kExtMaxK];
 #pragma unroll
   for (int pp = 0; pp < kExtMaxK; ++pp) jr[pp] = (pp < e.kR) ? factor_val(e.J, pp, j) : 0.0f;
-  // J_bar, twice
-  for (int c = 0; c < e.ksR; c += 8) {
-    float v[8];
+  if (blockIdx.y == 0) {
+    // J_bar, twice, and the zero tail
+    for (int c = 0; c < e.ksR; c += 8) {
+      float v[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      float x = 0.0f;
+      for (int t = 0; t < 8; ++t) {
+        float x = 0.0f;
 #pragma unroll
-      for (int pp = 0; pp < kExtMaxK; pp += 8)
-        if (pp == (c & ~7)) x = jr[pp + t];  // static register index
-      v[t] = x;
-    }
-    const uint4 w = pack8_bf16(v);
-    *(uint4*)(out + ext_off(j, c, e.kext)) = w;
-    *(uint4*)(out + ext_off(j, e.ksR + c, e.kext)) = w;
-  }
-  // G = s_H S_L[q] (s_F s_RR T1[q][j] + sum_p T2f[q][p] J[j][p]) as hi / lo
-  for (int q0 = 0; q0 < e.ksL; q0 += 8) {
-    float hi[8], lo[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int q = q0 + t;
-      float g = 0.0f;
-      if (q < e.kL) {
-        float acc = sFR * e.t1[(int64_t)q * e.cols + j];
-#pragma unroll
-        for (int pp = 0; pp < kExtMaxK; ++pp)
-          if (pp < e.kR) acc += t2f[q][pp] * jr[pp];
-        g = sH * e.S_L[q] * acc;
+        for (int pp = 0; pp < kExtMaxK; pp += 8)
+          if (pp == c) x = jr[pp + t];  // static register index
+        v[t] = x;
       }
-      const uint16_t h = bf16_rn_bits(g);
-      hi[t] = bf16_bits_to_float(h);
-      lo[t] = g - hi[t];
+      const uint4 w = pack8_bf16(v);
+      *(uint4*)(out + ext_off(j, c, e.kext)) = w;
+      *(uint4*)(out + ext_off(j, e.ksR + c, e.kext)) = w;
     }
-    *(uint4*)(out + ext_off(j, 2 * e.ksR + q0, e.kext)) = pack8_bf16(hi);
-    *(uint4*)(out + ext_off(j, 2 * e.ksR + e.ksL + q0, e.kext)) = pack8_bf16(lo);
+    for (int64_t c = 2 * e.ksR + 2 * e.ksL; c < e.kext; c += 8)
+      *(uint4*)(out + ext_off(j, c, e.kext)) = make_uint4(0, 0, 0, 0);
   }
-  for (int64_t c = 2 * e.ksR + 2 * e.ksL; c < e.kext; c += 8)
-    *(uint4*)(out + ext_off(j, c, e.kext)) = make_uint4(0, 0, 0, 0);
+  if (q0 >= e.ksL) return;
+  // G[q] = s_H S_L[q] (s_F s_RR T1[q][j] + sum_p T2f[q][p] J[j][p]) as hi / lo
+  float hi[8], lo[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int q = q0 + t;
+    float g = 0.0f;
+    if (q < e.kL) {
+      float acc = sFR * e.t1[(int64_t)q * e.cols + j];
+#pragma unroll
+      for (int pp = 0; pp < kExtMaxK; ++pp)
+        if (pp < e.kR) acc += t2f[t][pp] * jr[pp];
+      g = sH * e.S_L[q] * acc;
+    }
+    const uint16_t h = bf16_rn_bits(g);
+    hi[t] = bf16_bits_to_float(h);
+    lo[t] = g - hi[t];
+  }
+  *(uint4*)(out + ext_off(j, 2 * e.ksR + q0, e.kext)) = pack8_bf16(hi);
+  *(uint4*)(out + ext_off(j, 2 * e.ksR + e.ksL + q0, e.kext)) = pack8_bf16(lo);
 }
 
 }  // namespace metis

@@ -555,7 +555,8 @@ metis_status split_product(const SideQ& L, const SideQ& R, int64_t M, int64_t N,
     e.b_ext = w.b_ext;
     hipLaunchKernelGGL(ext_prep_a_kernel, dim3(grid1(round_up64(M, 32) * kext, 256)), dim3(256), 0, st, e);
     LAUNCH_CHECK();
-    hipLaunchKernelGGL(ext_prep_b_kernel, dim3(grid1(round_up64(N, 32), 256)), dim3(256), 0, st, e);
+    hipLaunchKernelGGL(ext_prep_b_kernel, dim3(grid1(round_up64(N, 32), 256), (unsigned)std::max(1, w.ksL / 8)), dim3(256), 0,
+                       st, e);
     LAUNCH_CHECK();
   }
   g = GemmParams{M, N, K, L.res->codes, L.res->scales, R.res->codes, R.res->scales,

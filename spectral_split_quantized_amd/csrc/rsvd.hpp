@@ -332,15 +332,23 @@ __global__ void reduce_gram_kernel(const double* __restrict__ part, int blocks, 
 // Rinv = R^-1 with R^T R = G + shift I.  pass 0: shift = c u32 tr(G);
 // passes 1, 2: no shift unless the factorisation breaks down, then the
 // guard shift c u64 tr(G).  c = 11 (p n + n (n + 1)).
+// Right-looking Cholesky (column j: pivot square root, column scaling,
+// rank-1 update of the trailing lower triangle, all threads sharing each
+// phase), then X = L^-1 by right-looking forward elimination of L X = I.
 __global__ __launch_bounds__(256) void cholinv_kernel(const double* __restrict__ G, int n,
                                                       int64_t p, int pass,
                                                       double* __restrict__ Rinv) {
   __shared__ double L[kMaxN][kMaxN + 1];
-  __shared__ double Li[kMaxN][kMaxN + 1];
+  __shared__ double X[kMaxN][kMaxN + 1];
+  __shared__ double red[4];
   __shared__ int fail;
   const int tid = threadIdx.x;
-  double tr = 0.0;
-  for (int i = 0; i < n; ++i) tr += G[i * n + i];
+  double t = 0.0;
+  for (int i = tid; i < n; i += 256) t += G[i * n + i];
+  t = wave_sum_d(t);
+  if ((tid & 63) == 0) red[tid >> 6] = t;
+  __syncthreads();
+  const double tr = red[0] + red[1] + red[2] + red[3];
   const double c = 11.0 * ((double)p * n + (double)n * (n + 1));
   const int attempts = pass == 0 ? 1 : 2;
   for (int att = 0; att < attempts; ++att) {
@@ -348,48 +356,57 @@ __global__ __launch_bounds__(256) void cholinv_kernel(const double* __restrict__
     if (pass == 0) shift = c * ldexp(1.0, -24) * tr;
     else if (att == 1) shift = c * ldexp(1.0, -53) * tr;
     __syncthreads();
-    for (int e = tid; e < n * n; e += blockDim.x) {
-      const int a = e / n, b = e % n;
+    for (int e = tid; e < n * n; e += 256) {
+      const int a = e / n, b = e - a * n;
       L[a][b] = G[e] + (a == b ? shift : 0.0);
     }
     if (tid == 0) fail = 0;
     __syncthreads();
     for (int j = 0; j < n; ++j) {
-      if (tid == 0) {
-        double d = L[j][j];
-        for (int k = 0; k < j; ++k) d -= L[j][k] * L[j][k];
-        if (!(d > 0.0)) {
-          fail = 1;
-          d = 1.0;
-        }
-        L[j][j] = sqrt(d);
+      // pivot (every thread reads it; thread 0 records a breakdown)
+      double d = L[j][j];
+      if (!(d > 0.0)) {
+        if (tid == 0) fail = 1;
+        d = 1.0;
       }
+      const double piv = sqrt(d);
+      // column j below the pivot
+      for (int i = j + 1 + tid; i < n; i += 256) L[i][j] /= piv;
       __syncthreads();
-      for (int i = j + 1 + tid; i < n; i += blockDim.x) {
-        double s = L[i][j];
-        for (int k = 0; k < j; ++k) s -= L[i][k] * L[j][k];
-        L[i][j] = s / L[j][j];
+      if (tid == 0) L[j][j] = piv;
+      // trailing lower triangle: L[i][k] -= L[i][j] L[k][j], j < k <= i
+      const int m = n - j - 1;
+      for (int e = tid; e < m * m; e += 256) {
+        const int i = j + 1 + e / m, k = j + 1 + e % m;
+        if (k <= i) L[i][k] -= L[i][j] * L[k][j];
       }
       __syncthreads();
     }
     if (!fail) break;
   }
   if (fail && tid == 0) raise_status(kStatusCholesky);
-  // Li = L^-1 (lower): column j by forward substitution
-  for (int j = tid; j < n; j += blockDim.x) {
-    for (int i = 0; i < n; ++i) Li[i][j] = 0.0;
-    Li[j][j] = 1.0 / L[j][j];
-    for (int i = j + 1; i < n; ++i) {
-      double s = 0.0;
-      for (int k = j; k < i; ++k) s += L[i][k] * Li[k][j];
-      Li[i][j] = -s / L[i][i];
-    }
+  // X = L^-1: start from I, eliminate column by column
+  for (int e = tid; e < n * n; e += 256) {
+    const int a = e / n, b = e - a * n;
+    X[a][b] = a == b ? 1.0 : 0.0;
   }
   __syncthreads();
+  for (int k = 0; k < n; ++k) {
+    // row k: X[k][:] /= L[k][k] (only columns <= k are nonzero)
+    for (int b = tid; b <= k; b += 256) X[k][b] /= L[k][k];
+    __syncthreads();
+    // rows below: X[i][b] -= L[i][k] X[k][b]
+    const int m = n - k - 1;
+    for (int e = tid; e < m * (k + 1); e += 256) {
+      const int i = k + 1 + e / (k + 1), b = e % (k + 1);
+      X[i][b] -= L[i][k] * X[k][b];
+    }
+    __syncthreads();
+  }
   // R^-1 = (L^-1)^T
-  for (int e = tid; e < n * n; e += blockDim.x) {
-    const int a = e / n, b = e % n;
-    Rinv[e] = Li[b][a];
+  for (int e = tid; e < n * n; e += 256) {
+    const int a = e / n, b = e - a * n;
+    Rinv[e] = X[b][a];
   }
 }
 

@@ -203,6 +203,7 @@ def test_residual_quant_bit_exact(shape, k, dtype, rounding):
     (8192, 768, 3072, 12, 12, 12),   # GPT-2 MLP-up shapes
     (96, 80, 64, 0, 0, 0),           # direct NVFP4, ragged tiles
     (304, 272, 208, 5, 3, 7),        # several tiles and ragged tails, unequal ranks
+    (160, 96, 128, 0, 6, 4),         # one side plain NVFP4 (rank 0), the other factored
     (1024, 2048, 512, 61, 61, 61),   # rank 61 (K-extension width 256)
     (4096, 1024, 4096, 61, 61, 61),  # Y on the large-product kernel (256 tiles)
     (4000, 1024, 4112, 61, 61, 61),  # the same with ragged rows and columns
