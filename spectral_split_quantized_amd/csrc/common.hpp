@@ -168,6 +168,24 @@ __device__ inline float load_as_float(const void* p, int dtype, int64_t idx) {
   return ((const float*)p)[idx];
 }
 
+// 16-byte direct global -> LDS load: lane L writes lds + 16 L (the LDS
+// address must be wave-uniform).
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ inline void dma16(const void* g, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 16, 0, 0);
+}
+
+// Workgroup barrier for an LDS-DMA ring.  Every wave first waits for its own
+// DMAs into the stage about to be read (s_waitcnt vmcnt(0)); the LDS is
+// written only by those DMAs, so no release fence is needed.  The empty asm
+// keeps the compiler from moving LDS reads above the barrier.
+__device__ inline void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));  // vmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ inline float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

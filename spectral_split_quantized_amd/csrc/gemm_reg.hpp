@@ -53,22 +53,6 @@ struct RegCfg {
   static_assert(DCA % NW == 0 && DCB % NW == 0 && DSA % NW == 0 && DSB % NW == 0, "DMA split");
 };
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-__device__ inline void dma16(const void* g, uint8_t* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 16, 0, 0);
-}
-
-// Workgroup barrier for the DMA ring.  Every wave first waits for its own
-// DMAs into the stage about to be read (s_waitcnt vmcnt(0)); the LDS is
-// written only by those DMAs, so no release fence is needed.  The empty asm
-// keeps the compiler from moving LDS reads above the barrier.
-__device__ inline void ring_barrier() {
-  __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));  // vmcnt(0) only
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 __device__ inline uint32_t u4_get(const uint4& v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }

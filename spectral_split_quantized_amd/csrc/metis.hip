@@ -333,11 +333,11 @@ metis_status launch_quant_pair(const QuantParams& qp, dim3 grid, int64_t rows, i
                                hipStream_t st) {
   const int64_t kc = NKK * 16;
   TimingRec* t1 = timing_begin(st, 1, rows, cols, qp.axes, kc);
-  hipLaunchKernelGGL((quant_kernel<NKK, false>), grid, dim3(kQThreads), 0, st, qp);
+  hipLaunchKernelGGL((quant_amax_kernel<NKK>), grid, dim3(kQThreads), 0, st, qp);
   LAUNCH_CHECK();
   timing_end(t1, st);
   TimingRec* t2 = timing_begin(st, 2, rows, cols, qp.axes, kc);
-  hipLaunchKernelGGL((quant_kernel<NKK, true>), grid, dim3(kQThreads), 0, st, qp);
+  hipLaunchKernelGGL((quant_kernel<NKK>), grid, dim3(kQThreads), 0, st, qp);
   LAUNCH_CHECK();
   timing_end(t2, st);
   return METIS_OK;

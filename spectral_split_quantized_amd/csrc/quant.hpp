@@ -2,12 +2,13 @@
 // M_R = M - U diag(S) V^T ("Metis: Training LLMs with FP4 Quantization",
 // 关键设计 1; NVFP4 format from section 研究背景与动机).
 //
-// Two sweeps over M, both HBM-bound:
-//   pass 1: residual tile -> |max| -> one atomicMax per wave (float bits of a
-//           non-negative value order like unsigned ints, so the result is
-//           independent of arrival order);
-//   pass 2: residual tile again (bit-identical: same instruction sequence),
-//           quantised on store in both K orientations.
+// Two sweeps over M:
+//   pass 1 (quant_amax_kernel): residual tile -> |max| -> one atomicMax per
+//           wave (float bits of a non-negative value order like unsigned
+//           ints, so the result is independent of arrival order);
+//   pass 2 (quant_kernel): residual tile again (bit-identical: the same MFMA
+//           chain and the same binary32 operations), quantised on store in
+//           both K orientations.
 // The rank-k product (U S)(V)^T of a tile runs on MFMA: U S and V are split
 // into fp16 hi + lo parts (pre-scaled by powers of two into fp16 range) and
 // the three significant cross terms are concatenated along K, so one
@@ -212,18 +213,157 @@ __device__ inline void gather_cols16(const f32x16_t& acc, float (&out)[16]) {
   }
 }
 
-// PASS2 = false: amax sweep.  PASS2 = true: quantise sweep.  NKK = kc / 16
-// of the rank-k product (0: no factors, direct quantisation).
+// This lane's two 16-column blocks of row `row` in the 64-column tile at c0
+// (zero outside the operand); the bf16 fast path takes four 16-byte loads.
+__device__ inline void load_tile_x(const QuantParams& p, int64_t row, bool row_ok, int64_t c0, int hh,
+                                   bool vec_ok, float (&x)[2][16]) {
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int64_t gc = c0 + 32 * b + 16 * hh;
+    const int n = (int)max((int64_t)0, min((int64_t)16, p.cols - gc));
+    if (row_ok && n > 0)
+      load_row16(p.M, p.dtype, row * p.ld + gc, n, vec_ok, x[b]);
+    else
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[b][i] = 0.0f;
+  }
+}
+
+__device__ inline void unpack_bf16x16(const uint4& q0, const uint4& q1, float (&x)[16]) {
+  const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+// x -= (V (U S)^T)^T of this wave's 32 rows x the tile's 64 columns; Bf holds
+// the tile's vcat fragments, uf this wave's ucat fragments.
+template <int NKK>
+__device__ inline void subtract_lowrank(const uint4* Bf, const half8_t (&uf)[NKK], float ps, int lane,
+                                        float (&x)[2][16]) {
+  f32x16_t acc0 = {}, acc1 = {};
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    const half8_t v0 = __builtin_bit_cast(half8_t, Bf[kk * 64 + lane]);
+    const half8_t v1 = __builtin_bit_cast(half8_t, Bf[(NKK + kk) * 64 + lane]);
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(v0, uf[kk], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(v1, uf[kk], acc1, 0, 0, 0);
+  }
+  float p0[16], p1[16];
+  gather_cols16(acc0, p0);
+  gather_cols16(acc1, p1);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    x[0][i] = __fsub_rn(x[0][i], __fmul_rn(p0[i], ps));
+    x[1][i] = __fsub_rn(x[1][i], __fmul_rn(p1[i], ps));
+  }
+}
+
+// Pass 1: tensor |max| of the residual (or of M when NKK == 0).  A workgroup
+// owns a 128-row panel and walks `tiles_per_wg` 64-column tiles; while tile t
+// is formed, tile t+1's vcat fragments stream into the other LDS buffer by
+// direct global->LDS loads and its M rows into registers, so one barrier per
+// tile and no exposed load latency.  The two buffers are distinct arrays and
+// the loop is unrolled by two so every LDS access names its buffer statically.
+template <int NKK>
+__global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void quant_amax_kernel(QuantParams p) {
+  constexpr bool HAS_F = NKK > 0;
+  constexpr int BFU = HAS_F ? NKK * 2 * 64 : 1;  // uint4 per tile
+  __shared__ uint4 Bf0[BFU];
+  __shared__ uint4 Bf1[BFU];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int hh = lane >> 5;
+  const int64_t r0 = (int64_t)blockIdx.x * kQT_R;
+  const int64_t ntc = ceil_div<int64_t>(p.cols, kQT_C);
+  const int64_t ct0 = (int64_t)blockIdx.y * p.tiles_per_wg;
+  const int64_t ct1 = min(ntc, ct0 + p.tiles_per_wg);
+  const int64_t row = r0 + wave * 32 + (lane & 31);
+  const bool row_ok = row < p.rows;
+  const bool vec_ok = ((p.ld & 7) == 0) && (((uintptr_t)p.M & 15) == 0);
+  // whole 16-byte-aligned bf16 tiles go through the register prefetch
+  const bool fast = p.dtype == 0 && vec_ok && row_ok;
+  const int64_t full_tiles = p.cols / kQT_C;
+
+  half8_t uf[HAS_F ? NKK : 1];
+  if (HAS_F) {
+    const int64_t g = (r0 >> 5) + wave;
+    const int64_t gmax = (p.rows + 31) >> 5;
+    const half8_t z = {};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      uf[kk] = g < gmax ? *(const half8_t*)(p.ucat + ((g * NKK + kk) * 64 + lane) * 8) : z;
+  }
+  const float ps = HAS_F ? p.pscale[0] : 0.0f;
+
+  auto issue = [&](int64_t ct, uint4* buf, uint4 (&raw)[4]) {
+    if (HAS_F) {
+      const uint4* src = (const uint4*)p.vcat + ct * BFU;
+      for (int i = wave; i < 2 * NKK; i += 4) dma16(src + i * 64 + lane, (uint8_t*)(buf + i * 64));
+    }
+    if (fast && ct < full_tiles) {
+      const uint16_t* m = (const uint16_t*)p.M + row * p.ld + ct * kQT_C + 16 * hh;
+      raw[0] = *(const uint4*)m;
+      raw[1] = *(const uint4*)(m + 8);
+      raw[2] = *(const uint4*)(m + 32);
+      raw[3] = *(const uint4*)(m + 40);
+    }
+  };
+  float runmax = 0.0f;
+  bool bad = false;
+  auto body = [&](int64_t ct, const uint4* buf, const uint4 (&raw)[4]) {
+    const int64_t c0 = ct * kQT_C;
+    float x[2][16];
+    if (fast && ct < full_tiles) {
+      unpack_bf16x16(raw[0], raw[1], x[0]);
+      unpack_bf16x16(raw[2], raw[3], x[1]);
+    } else {
+      load_tile_x(p, row, row_ok, c0, hh, vec_ok, x);
+    }
+    if (HAS_F) subtract_lowrank<HAS_F ? NKK : 1>(buf, uf, ps, lane, x);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t gc = c0 + 32 * b + 16 * hh;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float a = (row_ok && gc + i < p.cols) ? fabsf(x[b][i]) : 0.0f;
+        bad |= !(a <= 3.402823466e38f);
+        runmax = fmaxf(runmax, a);
+      }
+    }
+  };
+
+  uint4 rawA[4] = {}, rawB[4] = {};
+  if (ct0 < ct1) issue(ct0, Bf0, rawA);
+  for (int64_t ct = ct0; ct < ct1; ct += 2) {
+    ring_barrier();  // tile ct has landed in Bf0; every wave is done with Bf1
+    if (ct + 1 < ct1) issue(ct + 1, Bf1, rawB);
+    body(ct, Bf0, rawA);
+    if (ct + 1 >= ct1) break;
+    ring_barrier();  // tile ct+1 has landed in Bf1; every wave is done with Bf0
+    if (ct + 2 < ct1) issue(ct + 2, Bf0, rawA);
+    body(ct + 1, Bf1, rawB);
+  }
+  if (bad) raise_status(kStatusNonFinite);
+  runmax = wave_max(runmax);
+  if (lane == 0) atomicMax(p.amax, __float_as_uint(runmax));
+}
+
+// Pass 2: quantise the residual in the orientations `axes` asks for.  NKK =
+// kc / 16 of the rank-k product (0: no factors, direct quantisation).
 // A workgroup owns a 128-row panel and walks `tiles_per_wg` tiles of 64
 // columns.  Wave w owns rows 32w..32w+31; after gather_cols16 lane l holds
 // row 32w + l%32 at columns 16(l/32) .. +15 and 32 + 16(l/32) .. +15: two
-// axis-1 blocks, matching 32-byte row loads of M.  Both sweeps form the
-// residual with the same instructions, so they see bit-identical values.
-// Axis-0 blocks (16 rows of one column) go through an LDS transpose.
-template <int NKK, bool PASS2>
+// axis-1 blocks, matching 32-byte row loads of M.  The residual is formed by
+// the same subtract_lowrank as in pass 1, so both sweeps see bit-identical
+// values.  Axis-0 blocks (16 rows of one column) go through an LDS transpose.
+template <int NKK>
 __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void quant_kernel(QuantParams p) {
   constexpr bool HAS_F = NKK > 0;
-  __shared__ float R[PASS2 ? kQT_R : 1][PASS2 ? kQT_C + 4 : 1];
+  __shared__ float R[kQT_R][kQT_C + 4];
   __shared__ uint4 Bf[HAS_F ? NKK * 2 * 64 : 1];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -248,7 +388,7 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 8)
   const float ps = HAS_F ? p.pscale[0] : 0.0f;
 
   float s_g = 1.0f, d = 6.0f;
-  if (PASS2) {
+  {
     const float at = __uint_as_float(p.amax[0]);
     if (at > 0.0f) {
       s_g = __fdiv_rn(at, 2688.0f);
@@ -260,47 +400,20 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 8)
     }
   }
   const bool sr = p.sr != 0;
-  const bool ax0 = PASS2 && (p.axes & 1);
-  const bool ax1 = PASS2 && (p.axes & 2);
-  float runmax = 0.0f;
-  bool bad = false;
+  const bool ax0 = (p.axes & 1) != 0;
+  const bool ax1 = (p.axes & 2) != 0;
 
   for (int64_t ct = ct0; ct < ct1; ++ct) {
     const int64_t c0 = ct * kQT_C;
-    // this lane's two 16-column blocks of row `row`
     float x[2][16];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int64_t gc = c0 + 32 * b + 16 * hh;
-      const int n = (int)max((int64_t)0, min((int64_t)16, p.cols - gc));
-      if (row_ok && n > 0)
-        load_row16(p.M, p.dtype, row * p.ld + gc, n, vec_ok, x[b]);
-      else
-#pragma unroll
-        for (int i = 0; i < 16; ++i) x[b][i] = 0.0f;
-    }
+    load_tile_x(p, row, row_ok, c0, hh, vec_ok, x);
     if (HAS_F) {
       __syncthreads();  // the previous tile is done with Bf (and R)
       const uint4* src = (const uint4*)p.vcat + (ct * 2) * (int64_t)NKK * 64;
       for (int e = tid; e < 2 * NKK * 64; e += kQThreads) Bf[e] = src[e];
       __syncthreads();
-      f32x16_t acc0 = {}, acc1 = {};
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const half8_t v0 = __builtin_bit_cast(half8_t, Bf[kk * 64 + lane]);
-        const half8_t v1 = __builtin_bit_cast(half8_t, Bf[(NKK + kk) * 64 + lane]);
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(v0, uf[kk], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(v1, uf[kk], acc1, 0, 0, 0);
-      }
-      float p0[16], p1[16];
-      gather_cols16(acc0, p0);
-      gather_cols16(acc1, p1);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        x[0][i] = __fsub_rn(x[0][i], __fmul_rn(p0[i], ps));
-        x[1][i] = __fsub_rn(x[1][i], __fmul_rn(p1[i], ps));
-      }
-    } else if (PASS2 && ax0) {
+      subtract_lowrank<HAS_F ? NKK : 1>(Bf, uf, ps, lane, x);
+    } else if (ax0) {
       __syncthreads();  // the previous tile's axis-0 readers are done with R
     }
 #pragma unroll
@@ -309,18 +422,6 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 8)
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         if (!(row_ok && gc + i < p.cols)) x[b][i] = 0.0f;
-    }
-
-    if (!PASS2) {
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float a = fabsf(x[b][i]);
-          bad |= !(a <= 3.402823466e38f);
-          runmax = fmaxf(runmax, a);
-        }
-      continue;
     }
 
     // ---- axis 1 (and the export) from registers
@@ -388,11 +489,6 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 8)
     }
   }
 
-  if (!PASS2) {
-    if (bad) raise_status(kStatusNonFinite);
-    runmax = wave_max(runmax);
-    if (lane == 0) atomicMax(p.amax, __float_as_uint(runmax));
-  }
 }
 
 }  // namespace metis
