@@ -124,8 +124,9 @@ class MetisMLP:
     forward GEMMs wait for their weight; X_down follows the gate/up GEMMs
     and D_down the down GEMM (in a real layer they are computed from them);
     D_gate and D_up, which both come from the down projection's dX, are
-    processed concurrently.  With streams=1 everything runs in that order
-    on one stream."""
+    processed concurrently on the two side streams while the down
+    projection's dW GEMM runs on the main stream.  With streams=1
+    everything runs in that order on one stream."""
 
     def __init__(self, device, streams=3):
         import torch
@@ -183,14 +184,15 @@ class MetisMLP:
         e.record(self.streams[si])
         return e
 
-    def _gemms(self, name, fwd):
+    def _gemms(self, name, fwd, want_dx=True, want_dw=True):
         m = self.metis
         _, x, w, d = next(p for p in PROJECTIONS if p[0] == name)
         Y, dX, dW = self.out[name]
         if fwd:
             m.gemm_fwd(self.q[x], self.q[w], Y=Y, workspace=self.ws[0])
         else:
-            m.gemm_bwd(self.q[d], self.q[w], self.q[x], dX=dX, dW=dW, workspace=self.ws[0])
+            m.gemm_bwd(self.q[d], self.q[w], self.q[x], dX=dX, dW=dW, want_dx=want_dx, want_dw=want_dw,
+                       workspace=self.ws[0])
 
     def step(self, t, inputs):
         main = self.streams[0]
@@ -213,12 +215,19 @@ class MetisMLP:
         main.wait_event(ev["W_down"])
         self._gemms("down", True)
         self._prep("D_down", t, inputs, 0)
-        self._gemms("down", False)
+        # dX of the down projection first: D_gate and D_up (computed from it
+        # in a real layer) are prepared on the side streams while the down
+        # projection's dW runs on the main stream
+        self._gemms("down", False, want_dw=False)
         dx_ready = self._event(0)
         self.streams[sd].wait_event(dx_ready)
-        self._prep("D_up", t, inputs, sd)
-        e_up = self._event(sd)
-        self._prep("D_gate", t, inputs, 0)
+        self._prep("D_gate", t, inputs, sd)
+        e_gate = self._event(sd)
+        self.streams[sw].wait_event(dx_ready)
+        self._prep("D_up", t, inputs, sw)
+        e_up = self._event(sw)
+        self._gemms("down", False, want_dx=False)
+        main.wait_event(e_gate)
         self._gemms("gate", False)
         main.wait_event(e_up)
         self._gemms("up", False)
