@@ -407,61 +407,21 @@ GemmShape gemm_shape(int64_t M, int64_t N) {
   return t256 >= 256 ? kGemmBig : kGemmMid;
 }
 
-// K splits for a skinny product: enough workgroups to cover the GPU, at
-// least 4 K steps each.
-int gemm_splits(int64_t M, int64_t N, int64_t K) {
-  int64_t tiles;
-  switch (gemm_shape(M, N)) {
-    case kGemmTall: tiles = ceil_div<int64_t>(M, 256); break;
-    case kGemmWide: tiles = ceil_div<int64_t>(N, 256); break;
-    case kGemmSmall: tiles = 1; break;
-    default: return 1;
-  }
-  const int64_t nk = ceil_div<int64_t>(K, 64);
-  int64_t s = ceil_div<int64_t>(512, tiles);
-  const int64_t smax = nk / 4 > 1 ? nk / 4 : 1;
-  if (s > smax) s = smax;
-  if (s > 64) s = 64;
-  return (int)(s < 1 ? 1 : s);
-}
-
-// C = A B^T (+ alpha, K-extension).  Split-K products need a partial buffer
-// of splits * M * N floats (`part`) and are reduced into C (ldc == N).
-metis_status launch_gemm(const GemmParams& gp0, float* part, hipStream_t st) {
-  if (gp0.M <= 0 || gp0.N <= 0) return METIS_OK;
-  const int splits = gemm_splits(gp0.M, gp0.N, gp0.K);
-  GemmParams gp = gp0;
-  if (splits > 1) {
-    if (gp.kext > 0 || gp.sa || gp.sb || !part || gp.ldc != gp.N)
-      return fail(METIS_E_INVALID, "internal: split-K product with epilogue options");
-    gp.C = part;
-  }
-  metis_status s;
+// C = alpha A B^T (+ K-extension), one workgroup per output tile.
+metis_status launch_gemm(const GemmParams& gp, hipStream_t st) {
+  if (gp.M <= 0 || gp.N <= 0) return METIS_OK;
   switch (gemm_shape(gp.M, gp.N)) {
     case kGemmBig:
       if (gemm_reg_ok(gp)) {
-        const hipError_t e = launch_gemm_big(gp, splits, st);
-        s = e == hipSuccess ? METIS_OK : fail(METIS_E_HIP, "gemm launch: %s", hipGetErrorString(e));
-      } else {
-        s = launch_gemm_cfg<256, 256, 4, 2>(gp, splits, st);
+        const hipError_t e = launch_gemm_big(gp, 1, st);
+        return e == hipSuccess ? METIS_OK : fail(METIS_E_HIP, "gemm launch: %s", hipGetErrorString(e));
       }
-      break;
-    case kGemmMid: s = launch_gemm_cfg<128, 128, 2, 2>(gp, splits, st); break;
-    case kGemmTall: s = launch_gemm_cfg<256, 64, 8, 1>(gp, splits, st); break;
-    case kGemmWide: s = launch_gemm_cfg<64, 256, 1, 8>(gp, splits, st); break;
-    default: s = launch_gemm_cfg<64, 64, 2, 2>(gp, splits, st); break;
+      return launch_gemm_cfg<256, 256, 4, 2>(gp, 1, st);
+    case kGemmMid: return launch_gemm_cfg<128, 128, 2, 2>(gp, 1, st);
+    case kGemmTall: return launch_gemm_cfg<256, 64, 8, 1>(gp, 1, st);
+    case kGemmWide: return launch_gemm_cfg<64, 256, 1, 8>(gp, 1, st);
+    default: return launch_gemm_cfg<64, 64, 2, 2>(gp, 1, st);
   }
-  if (s != METIS_OK || splits == 1) return s;
-  const int64_t count = gp.M * gp.N;
-  hipLaunchKernelGGL(reduce_splits_kernel, dim3(grid1(count, 256)), dim3(256), 0, st, part, splits,
-                     count, gp0.C);
-  LAUNCH_CHECK();
-  return METIS_OK;
-}
-
-size_t gemm_part_floats(int64_t M, int64_t N, int64_t K) {
-  const int s = gemm_splits(M, N, K);
-  return s > 1 ? (size_t)s * M * N : 0;
 }
 
 struct SideQ {
@@ -473,11 +433,24 @@ struct SideQ {
 };
 
 struct SplitWs {
-  float *praw, *t1, *t2, *ones, *part;
+  float *pa, *p1, *p2, *t2, *ones;  // thin-product partial sums; T2 summed
+  uint4 *bf_E, *bf_F;             // thin operands as fp16 MFMA fragments
   uint16_t *a_ext, *b_ext;
   int64_t kext;
-  int ksR, ksL;
+  int ksR, ksL, sa, s1, s2;
 };
+
+// K splits of a thin product with m rows: about 512 workgroups, at least two
+// K steps each.
+int thin_splits(int64_t m, int64_t K) {
+  const int64_t wg = ceil_div<int64_t>(m, kThinRows);
+  const int64_t nks = ceil_div<int64_t>(K, 64);
+  int64_t s = ceil_div<int64_t>(512, wg);
+  const int64_t smax = std::max<int64_t>(1, nks / 2);
+  if (s > smax) s = smax;
+  if (s > 64) s = 64;
+  return (int)std::max<int64_t>(1, s);
+}
 
 SplitWs carve_split(Carver& cv, int64_t M, int64_t N, int64_t K, int kL, int kR) {
   SplitWs w{};
@@ -485,14 +458,22 @@ SplitWs carve_split(Carver& cv, int64_t M, int64_t N, int64_t K, int kL, int kR)
   w.ksL = round_up(kL, 16);
   w.kext = round_up(2 * w.ksR + 2 * w.ksL, 64);
   w.ones = cv.take<float>(4);
-  size_t part = 0;
-  if (kR > 0) part = std::max(part, gemm_part_floats(M, kR, K));
-  if (kL > 0) part = std::max(part, gemm_part_floats(kL, N, K));
-  if (kL > 0 && kR > 0) part = std::max(part, gemm_part_floats(kL, kR, K));
-  if (part) w.part = cv.take<float>(part);
-  if (kR > 0) w.praw = cv.take<float>((size_t)M * kR);
-  if (kL > 0) w.t1 = cv.take<float>((size_t)kL * N);
-  if (kL > 0 && kR > 0) w.t2 = cv.take<float>((size_t)kL * kR);
+  const size_t frag = (size_t)ceil_div<int64_t>(K, 64) * 512;
+  if (kR > 0) {
+    w.sa = thin_splits(M, K);
+    w.pa = cv.take<float>((size_t)w.sa * M * 64);
+    w.bf_E = cv.take<uint4>(frag);
+  }
+  if (kL > 0) {
+    w.s1 = thin_splits(N, K);
+    w.p1 = cv.take<float>((size_t)w.s1 * N * 64);
+    w.bf_F = cv.take<uint4>(frag);
+  }
+  if (kL > 0 && kR > 0) {
+    w.s2 = thin_splits(kL, K);
+    w.p2 = cv.take<float>((size_t)w.s2 * kL * 64);
+    w.t2 = cv.take<float>((size_t)kL * 64);
+  }
   if (w.kext > 0) {
     w.a_ext = cv.take<uint16_t>((size_t)round_up64(M, 32) * w.kext);
     w.b_ext = cv.take<uint16_t>((size_t)round_up64(N, 32) * w.kext);
@@ -500,10 +481,31 @@ SplitWs carve_split(Carver& cv, int64_t M, int64_t N, int64_t K, int kL, int kR)
   return w;
 }
 
+// Thin product part[s][m][64] = A (m x K) B^T, B = the nb <= 64 rows in bfrag.
+metis_status thin_product(const metis_q4& A, int64_t m, int64_t K, const uint4* bfrag, int splits,
+                          float* part, hipStream_t st) {
+  ThinParams tp{A.codes, A.scales, bfrag, m, K, 0, part};
+  const int64_t nks = ceil_div<int64_t>(K, 64);
+  tp.steps = ceil_div<int64_t>(nks, splits);
+  const dim3 grid((unsigned)ceil_div<int64_t>(m, kThinRows), (unsigned)splits);
+  if (K % 32 == 0) hipLaunchKernelGGL(gemm_thin_kernel<true>, grid, dim3(256), 0, st, tp);
+  else hipLaunchKernelGGL(gemm_thin_kernel<false>, grid, dim3(256), 0, st, tp);
+  LAUNCH_CHECK();
+  return METIS_OK;
+}
+
+metis_status thin_operand(const metis_q4& B, int nb, int64_t K, uint4* bfrag, hipStream_t st) {
+  const int64_t n = ceil_div<int64_t>(K, 64) * 512;
+  hipLaunchKernelGGL(thin_bfrag_kernel, dim3(grid1(n, 256)), dim3(256), 0, st, B.codes, B.scales, nb, K, bfrag);
+  LAUNCH_CHECK();
+  return METIS_OK;
+}
+
 // out (M x N) = L-hat R-hat with L = H S_L F^T + L_R, R^T = E S_R J^T + R_R^T
 // along K.
 metis_status split_product(const SideQ& L, const SideQ& R, int64_t M, int64_t N, int64_t K,
                            float* C, int64_t ldc, void* ws, size_t ws_bytes, hipStream_t st) {
+  if (L.k > 64 || R.k > 64) return fail(METIS_E_UNSUPPORTED, "split product rank above 64");
   Carver cv(ws, ws_bytes);
   SplitWs w = carve_split(cv, M, N, K, L.k, R.k);
   if (cv.used() > ws_bytes) return fail(METIS_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, cv.used());
@@ -511,21 +513,19 @@ metis_status split_product(const SideQ& L, const SideQ& R, int64_t M, int64_t N,
                      (int64_t)4);
   LAUNCH_CHECK();
   metis_status s;
-  GemmParams g{};
   if (R.k > 0) {  // P_raw = L_R . E   (M x kR)
-    g = GemmParams{M, R.k, K, L.res->codes, L.res->scales, R.kf->codes, R.kf->scales,
-                   nullptr, nullptr, 0, nullptr, nullptr, w.praw, R.k};
-    if ((s = launch_gemm(g, w.part, st)) != METIS_OK) return s;
+    if ((s = thin_operand(*R.kf, R.k, K, w.bf_E, st)) != METIS_OK) return s;
+    if ((s = thin_product(*L.res, M, K, w.bf_E, w.sa, w.pa, st)) != METIS_OK) return s;
   }
-  if (L.k > 0) {  // T1 = F . R_R   (kL x N)
-    g = GemmParams{L.k, N, K, L.kf->codes, L.kf->scales, R.res->codes, R.res->scales,
-                   nullptr, nullptr, 0, nullptr, nullptr, w.t1, N};
-    if ((s = launch_gemm(g, w.part, st)) != METIS_OK) return s;
+  if (L.k > 0) {  // T1^T = R_R . F^T   (N x kL)
+    if ((s = thin_operand(*L.kf, L.k, K, w.bf_F, st)) != METIS_OK) return s;
+    if ((s = thin_product(*R.res, N, K, w.bf_F, w.s1, w.p1, st)) != METIS_OK) return s;
   }
   if (L.k > 0 && R.k > 0) {  // T2 = F . E   (kL x kR)
-    g = GemmParams{L.k, R.k, K, L.kf->codes, L.kf->scales, R.kf->codes, R.kf->scales,
-                   nullptr, nullptr, 0, nullptr, nullptr, w.t2, R.k};
-    if ((s = launch_gemm(g, w.part, st)) != METIS_OK) return s;
+    if ((s = thin_product(*L.kf, L.k, K, w.bf_E, w.s2, w.p2, st)) != METIS_OK) return s;
+    const int64_t n2 = (int64_t)L.k * 64;
+    hipLaunchKernelGGL(sum_parts_kernel, dim3(grid1(n2 / 8, 256)), dim3(256), 0, st, w.p2, w.s2, n2, w.t2);
+    LAUNCH_CHECK();
   }
   int64_t kext = 0;
   if (L.k > 0 || R.k > 0) {
@@ -538,9 +538,11 @@ metis_status split_product(const SideQ& L, const SideQ& R, int64_t M, int64_t N,
     e.ksR = w.ksR;
     e.ksL = w.ksL;
     e.kext = kext;
-    e.praw = w.praw;
-    e.t1 = w.t1;
+    e.praw = w.pa;
+    e.t1 = w.p1;
     e.t2 = w.t2;
+    e.sa = w.sa;
+    e.s1 = w.s1;
     e.S_R = R.k > 0 ? R.S : w.ones;
     e.S_L = L.k > 0 ? L.S : w.ones;
     e.s_LR = L.res->tensor_scale;
@@ -553,16 +555,16 @@ metis_status split_product(const SideQ& L, const SideQ& R, int64_t M, int64_t N,
                     R.k > 0 ? R.out->tensor_scale : w.ones, R.k, N};
     e.a_ext = w.a_ext;
     e.b_ext = w.b_ext;
-    hipLaunchKernelGGL(ext_prep_a_kernel, dim3(grid1(round_up64(M, 32) * kext, 256)), dim3(256), 0, st, e);
+    hipLaunchKernelGGL(ext_prep_a_kernel, dim3(grid1(round_up64(M, 32) * (kext / 8), 256)), dim3(256), 0, st, e);
     LAUNCH_CHECK();
-    hipLaunchKernelGGL(ext_prep_b_kernel, dim3(grid1(round_up64(N, 32), 256), (unsigned)std::max(1, w.ksL / 8)), dim3(256), 0,
+    hipLaunchKernelGGL(ext_prep_b_kernel, dim3((unsigned)ceil_div<int64_t>(round_up64(N, 32), 64)), dim3(256), 0,
                        st, e);
     LAUNCH_CHECK();
   }
-  g = GemmParams{M, N, K, L.res->codes, L.res->scales, R.res->codes, R.res->scales,
-                 L.res->tensor_scale, R.res->tensor_scale, kext, w.a_ext, w.b_ext, C, ldc};
+  GemmParams g{M, N, K, L.res->codes, L.res->scales, R.res->codes, R.res->scales,
+               L.res->tensor_scale, R.res->tensor_scale, kext, w.a_ext, w.b_ext, C, ldc};
   TimingRec* tr = timing_begin(st, 0, M, N, K, kext);
-  s = launch_gemm(g, nullptr, st);
+  s = launch_gemm(g, st);
   timing_end(tr, st);
   return s;
 }
