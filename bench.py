@@ -145,9 +145,8 @@ class MetisMLP:
             op.tag = metis.make_tag(op.layer, kind_id[op.kind])
             self.factors[op.name] = metis.Factors(op.rows, op.cols, K_RANK, device)
             self.q[op.name] = metis.QOperand(op.rows, op.cols, K_RANK, metis.AXIS0 | metis.AXIS1, device)
-            need = max(need, lib.metis_decompose_workspace(op.rows, op.cols, ctypes.byref(self.cfg),
-                                                           int(op.sample)),
-                       lib.metis_quantize_workspace(op.rows, op.cols, K_RANK))
+            need = max(need, lib.metis_prepare_operand_workspace(op.rows, op.cols, ctypes.byref(self.cfg),
+                                                                 int(op.sample)))
         self.out = {}
         for name, x, w, d in PROJECTIONS:
             X, W = self.ops[x], self.ops[w]
@@ -161,6 +160,9 @@ class MetisMLP:
         # default-priority streams only
         self.streams = [torch.cuda.current_stream(device)] + \
             [torch.cuda.Stream(device=device) for _ in range(self.nstreams - 1)]
+        # companion of the main stream: the rediagonalisation of operands on
+        # the critical path runs there while their residual is quantised
+        self.side = torch.cuda.Stream(device=device) if self.nstreams > 1 else None
         self.ws = [torch.empty(need, dtype=torch.uint8, device=device) for _ in self.streams]
         self.step_done = None
         log("  workspace %.1f MB x %d streams" % (need / 1e6, self.nstreams))
@@ -174,10 +176,10 @@ class MetisMLP:
         m = self.metis
         op = self.ops[name]
         M = inputs[name][t % len(inputs[name])]
+        side = self.side if si == 0 else None
         with self.torch.cuda.stream(self.streams[si]):
-            m.decompose(M, self.cfg, op.sample, op.tag, t, self.factors[name], workspace=self.ws[si])
-            m.quantize(M, self.cfg, op.tag, t, m.AXIS0 | m.AXIS1, factors=self.factors[name],
-                       out=self.q[name], workspace=self.ws[si])
+            m.prepare_operand(M, self.cfg, op.sample, op.tag, t, self.factors[name], m.AXIS0 | m.AXIS1,
+                              out=self.q[name], workspace=self.ws[si], side_stream=side)
 
     def _event(self, si):
         e = self.torch.cuda.Event()
@@ -411,7 +413,7 @@ def main():
            "dtype": "nvfp4 operands, f16 mfma, f32 accumulate",
            "data": "synthetic",
            "config": {"workload": "llama3_8b_mlp_gate_up_down_16k_tokens_8step_factor_cache",
-                      "streams": mlp.nstreams,
+                      "streams": mlp.nstreams + (1 if mlp.side is not None else 0),
                       "tokens": TOKENS, "hidden": HIDDEN, "ffn": FFN, "k": K_RANK, "s": OVERSAMPLE,
                       "l_k": L_K, "refresh": REFRESH, "rounding": "sr"},
            "dense_equiv_tflops": round(dense_equiv_flops() * args.steps / (total_ms * 1e-3) / 1e12, 2),

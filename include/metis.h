@@ -123,6 +123,8 @@ size_t metis_quantize_workspace(int64_t rows, int64_t cols, int32_t k);
 size_t metis_gemm_fwd_workspace(const metis_qoperand *X, const metis_qoperand *W);
 size_t metis_gemm_bwd_workspace(const metis_qoperand *D, const metis_qoperand *W,
                                 const metis_qoperand *X);
+size_t metis_prepare_operand_workspace(int64_t rows, int64_t cols, const metis_config *cfg,
+                                       int32_t sample_rows);
 
 /* metis_decompose -- spectral split of one operand (关键设计 1-3).
  * M: rows x cols (dtype metis_dtype, leading dimension ld >= cols).
@@ -155,6 +157,24 @@ metis_status metis_quantize(const void *M, int32_t dtype, int64_t rows, int64_t 
                             const metis_factors *f, const metis_config *cfg, uint32_t tag,
                             int64_t step, int32_t axes, metis_qoperand *out, float *residual_out,
                             void *ws, size_t ws_bytes, void *stream);
+
+/* metis_prepare_operand -- metis_decompose followed by metis_quantize with
+ * the new factors (关键设计 1-3), as one call.  After the projection
+ * P = M V_old the residual M_R = M - P V_old^T is quantised on `stream` while
+ * the rediagonalisation (Jacobi, V <- V R, U, S) runs on `side_stream`; the
+ * two are equal in exact arithmetic because the rotation R is orthogonal
+ * (U diag(S) V^T = P R R^T V_old^T), and in binary32 they differ by rounding
+ * only.  The factors are then quantised on `stream`, which on return has
+ * everything ordered after it.  side_stream may be NULL or equal to stream
+ * (then everything runs on stream).  Arguments, requirements and outputs are
+ * those of metis_decompose and metis_quantize (f non-NULL; out->k == cfg->k);
+ * ws holds at least metis_prepare_operand_workspace(rows, cols, cfg,
+ * sample_rows) bytes. */
+metis_status metis_prepare_operand(const void *M, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                                   const metis_config *cfg, int32_t sample_rows, uint32_t tag,
+                                   int64_t step, metis_factors *f, int32_t axes, metis_qoperand *out,
+                                   float *residual_out, void *ws, size_t ws_bytes, void *stream,
+                                   void *side_stream);
 
 /* metis_gemm_fwd -- Y = X-hat W-hat (关键设计 1, the split forward GEMM).
  * X: l x m with R_ax1 (K = m); W: m x n with R_ax0 (K = m).  Y: l x n

@@ -311,6 +311,7 @@ struct QuantWs {
   uint32_t* amax;  // 3 words: residual, U, V
   float* pre;
   float* pscale;
+  float* ones;     // kMaxN ones (S of a residual formed from the projection)
   _Float16* ucat;
   _Float16* vcat;
 };
@@ -320,6 +321,7 @@ QuantWs carve_quantize(Carver& cv, int64_t rows, int64_t cols, int k) {
   w.amax = cv.take<uint32_t>(4);
   w.pre = cv.take<float>(1);
   w.pscale = cv.take<float>(1);
+  w.ones = cv.take<float>(kMaxN);
   if (k > 0) {
     const int kc = 3 * round_up(k, 16);
     w.ucat = cv.take<_Float16>((size_t)((rows + 31) & ~(int64_t)31) * kc);
@@ -588,58 +590,25 @@ bool qop_factors_ok(const metis_qoperand* q) {
   return q4_ok(q->U, q->k, q->rows) && q4_ok(q->V, q->k, q->cols);
 }
 
-}  // namespace
+// One decomposition call, checked and with its workspace carved.
+struct DecompCall {
+  const void* M;
+  int32_t dtype;
+  int64_t rows, cols, ld;
+  const metis_config* cfg;
+  bool sample;
+  uint32_t tag;
+  int64_t step;
+  metis_factors* f;
+  int k, n;
+  int64_t lr;
+  bool refresh;
+  DecompWs w;
+};
 
-// =================================================================== ABI ===
-
-extern "C" {
-
-int32_t metis_abi_version(void) { return METIS_ABI_VERSION; }
-
-const char* metis_last_error(void) { return g_last_error.c_str(); }
-
-void metis_omega_table(uint16_t* out65536) {
-  if (out65536) memcpy(out65536, host_omega_table(), 65536 * sizeof(uint16_t));
-}
-
-void metis_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
-  const Philox4 b = philox4x32_10(ctr[0], ctr[1], ctr[2], ctr[3], key[0], key[1]);
-  for (int i = 0; i < 4; ++i) out[i] = b.v[i];
-}
-
-size_t metis_decompose_workspace(int64_t rows, int64_t cols, const metis_config* cfg,
-                                 int32_t sample_rows) {
-  if (!cfg || rows <= 0 || cols <= 0 || cfg->k < 1) return 0;
-  const int n = cfg->k + cfg->s;
-  const int64_t lr = sample_rows ? cfg->l_k : rows;
-  Carver cv(nullptr, 0);
-  carve_decompose(cv, rows, cols, cfg->k, n, lr, sample_rows != 0);
-  return cv.used();
-}
-
-size_t metis_quantize_workspace(int64_t rows, int64_t cols, int32_t k) {
-  Carver cv(nullptr, 0);
-  carve_quantize(cv, rows, cols, k);
-  return cv.used();
-}
-
-size_t metis_gemm_fwd_workspace(const metis_qoperand* X, const metis_qoperand* W) {
-  if (!X || !W) return 0;
-  return split_ws_size(X->rows, W->cols, X->cols, X->k, W->k);
-}
-
-size_t metis_gemm_bwd_workspace(const metis_qoperand* D, const metis_qoperand* W,
-                                const metis_qoperand* X) {
-  if (!D || !W || !X) return 0;
-  const size_t a = split_ws_size(D->rows, W->rows, D->cols, D->k, W->k);
-  const size_t b = split_ws_size(X->cols, D->cols, X->rows, X->k, D->k);
-  return a > b ? a : b;
-}
-
-metis_status metis_decompose(const void* M, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
-                             const metis_config* cfg, int32_t sample_rows, uint32_t tag,
-                             int64_t step, metis_factors* f, void* ws, size_t ws_bytes,
-                             void* stream) {
+metis_status decompose_check(const void* M, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                             const metis_config* cfg, int32_t sample_rows, uint32_t tag, int64_t step,
+                             metis_factors* f, DecompCall* c) {
   metis_status s = validate_config(cfg);
   if (s != METIS_OK) return s;
   if (!M || !f || !f->U || !f->S || !f->V) return fail(METIS_E_INVALID, "NULL pointer argument");
@@ -650,7 +619,7 @@ metis_status metis_decompose(const void* M, int32_t dtype, int64_t rows, int64_t
   if (f->rows != rows || f->cols != cols || f->k != cfg->k)
     return fail(METIS_E_INVALID, "factors describe %lldx%lld k=%d, operand %lldx%lld k=%d",
                 (long long)f->rows, (long long)f->cols, f->k, (long long)rows, (long long)cols, cfg->k);
-  const int k = cfg->k, n = cfg->k + cfg->s;
+  const int n = cfg->k + cfg->s;
   const bool sample = sample_rows != 0;
   const int64_t lr = sample ? cfg->l_k : rows;
   if (sample && (cfg->l_k <= 0 || cfg->l_k > rows))
@@ -658,18 +627,30 @@ metis_status metis_decompose(const void* M, int32_t dtype, int64_t rows, int64_t
   if (n > lr || n > cols)
     return fail(METIS_E_INVALID, "k + s = %d exceeds min(l_k or rows, cols)", n);
   if (step < 0 || step > UINT32_MAX) return fail(METIS_E_INVALID, "step=%lld", (long long)step);
-  Carver cv(ws, ws_bytes);
-  DecompWs w = carve_decompose(cv, rows, cols, k, n, lr, sample);
-  if (!ws || cv.used() > ws_bytes)
-    return fail(METIS_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, cv.used());
-  if ((s = ensure_device_tables()) != METIS_OK) return s;
-  hipStream_t st = (hipStream_t)stream;
-  const uint32_t ustep = (uint32_t)step;
-  const bool refresh = f->refreshed_at < 0 || step - f->refreshed_at >= cfg->refresh;
+  *c = DecompCall{M, dtype, rows, cols, ld, cfg, sample, tag, step, f, cfg->k, n, lr,
+                  f->refreshed_at < 0 || step - f->refreshed_at >= cfg->refresh, DecompWs{}};
+  return METIS_OK;
+}
+
+// The sketch on refresh steps (V from the range of a row sample of M), then
+// the projection P = M V and its Gram matrix G = P^T P.
+metis_status decompose_project(DecompCall& c, hipStream_t st) {
+  metis_status s;
+  const void* M = c.M;
+  const int32_t dtype = c.dtype;
+  const int64_t rows = c.rows, cols = c.cols, ld = c.ld;
+  const metis_config* cfg = c.cfg;
+  const bool sample = c.sample;
+  const uint32_t tag = c.tag;
+  metis_factors* f = c.f;
+  const int k = c.k, n = c.n;
+  const int64_t lr = c.lr;
+  DecompWs& w = c.w;
+  const uint32_t ustep = (uint32_t)c.step;
   // bf16 rows on 16-byte boundaries with whole 64-column K blocks take MFMA
   const bool mfma_ok = dtype == METIS_BF16 && cols % 64 == 0 && ld % 8 == 0 && ((uintptr_t)M & 15) == 0;
 
-  if (refresh) {
+  if (c.refresh) {
     const float scale = sample ? (float)sqrt((double)rows / (double)lr) : 1.0f;
     if (sample) {
       const uint32_t tag_s = tag_with_role(tag, kRoleSample);
@@ -744,6 +725,17 @@ metis_status metis_decompose(const void* M, int32_t dtype, int64_t rows, int64_t
     LAUNCH_CHECK();
   }
   if ((s = launch_gram(w.p, rows, k, k, 1, w.gblocks, w.gpart, w.ptp, st)) != METIS_OK) return s;
+  return METIS_OK;
+}
+
+// Rediagonalisation: eig(G) = R Lambda R^T, V <- V R, U = P R Lambda^-1/2,
+// S = Lambda^1/2 (columns signed, descending).
+metis_status decompose_rediag(DecompCall& c, hipStream_t st) {
+  metis_status s = METIS_OK;
+  const int64_t rows = c.rows, cols = c.cols;
+  const int k = c.k;
+  metis_factors* f = c.f;
+  DecompWs& w = c.w;
   hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(1024), 0, st, w.ptp, k, w.lam, w.rot);
   LAUNCH_CHECK();
   hipLaunchKernelGGL(rotate_kernel, dim3(grid1(cols * k, 256)), dim3(256), 0, st, f->V, cols, k, w.rot,
@@ -759,14 +751,14 @@ metis_status metis_decompose(const void* M, int32_t dtype, int64_t rows, int64_t
   hipLaunchKernelGGL(finalize_u_kernel, dim3(grid1(rows, 64)), dim3(256), 0, st, w.p, rows, k, w.rot,
                      w.lam, w.sign, f->U);
   LAUNCH_CHECK();
-  if (refresh) f->refreshed_at = step;
+  (void)s;
   return METIS_OK;
 }
 
-metis_status metis_quantize(const void* M, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
-                            const metis_factors* f, const metis_config* cfg, uint32_t tag,
-                            int64_t step, int32_t axes, metis_qoperand* out, float* residual_out,
-                            void* ws, size_t ws_bytes, void* stream) {
+// Arguments of one quantisation, checked.
+metis_status quantize_check(const void* M, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                            const metis_factors* f, const metis_config* cfg, int64_t step, int32_t axes,
+                            const metis_qoperand* out) {
   if (!M || !out || !cfg) return fail(METIS_E_INVALID, "NULL pointer argument");
   if (!dtype_ok(dtype)) return fail(METIS_E_INVALID, "dtype=%d", dtype);
   if (rows <= 0 || cols <= 0 || ld < cols) return fail(METIS_E_INVALID, "bad shape");
@@ -791,15 +783,13 @@ metis_status metis_quantize(const void* M, int32_t dtype, int64_t rows, int64_t 
   } else if (out->k != 0) {
     return fail(METIS_E_INVALID, "out->k must be 0 for direct quantisation");
   }
-  Carver cv(ws, ws_bytes);
-  QuantWs w = carve_quantize(cv, rows, cols, k);
-  if (!ws || cv.used() > ws_bytes) return fail(METIS_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, cv.used());
-  metis_status s;
-  if ((s = ensure_device_tables()) != METIS_OK) return s;
-  hipStream_t st = (hipStream_t)stream;
-  hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, st, w.amax, 0u, (int64_t)4);
-  LAUNCH_CHECK();
+  return METIS_OK;
+}
 
+// Quantiser parameters of the residual (or direct) sweeps.
+QuantParams resid_params(const void* M, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                         const metis_config* cfg, uint32_t tag, int64_t step, int32_t axes,
+                         metis_qoperand* out, float* residual_out, const QuantWs& w) {
   QuantParams qp{};
   qp.M = M;
   qp.dtype = dtype;
@@ -824,22 +814,19 @@ metis_status metis_quantize(const void* M, int32_t dtype, int64_t rows, int64_t 
     qp.scales1 = out->R_ax1.scales;
     qp.sg1 = out->R_ax1.tensor_scale;
   }
-  if (f) {
-    const int kp = round_up(k, 16);
-    hipLaunchKernelGGL(resid_scale_kernel, dim3(1), dim3(64), 0, st, f->S, k, w.pre, w.pscale);
-    LAUNCH_CHECK();
-    const int64_t rc_pad = ((rows + 31) & ~(int64_t)31) + ((cols + 63) & ~(int64_t)63);
-    hipLaunchKernelGGL(resid_prep_kernel, dim3(grid1(rc_pad * kp, 256)), dim3(256), 0, st, f->U,
-                       f->S, f->V, rows, cols, k, kp, w.pre, w.ucat, w.vcat);
-    LAUNCH_CHECK();
-    qp.ucat = w.ucat;
-    qp.vcat = w.vcat;
-    qp.kc = 3 * kp;
-    qp.pscale = w.pscale;
-  }
-  if ((s = run_quant(qp, f != nullptr, rows, cols, st)) != METIS_OK) return s;
+  return qp;
+}
 
-  if (f) {
+// NVFP4 codes of the factors U (rows x k) and V (cols x k), blocked along
+// their rows; out->S = f->S.
+metis_status quantize_factors(const metis_factors* f, int64_t rows, int64_t cols, const metis_config* cfg,
+                              uint32_t tag, int64_t step, metis_qoperand* out, const QuantWs& w,
+                              hipStream_t st) {
+  metis_status s;
+  const int k = f->k;
+  QuantParams qp{};
+  qp.sr = cfg->rounding == METIS_SR;
+  {
     // factors: U (rows x k) and V (cols x k), blocked along their rows
     for (int which = 0; which < 2; ++which) {
       QuantParams fq{};
@@ -863,6 +850,215 @@ metis_status metis_quantize(const void* M, int32_t dtype, int64_t rows, int64_t 
     }
     out->S = f->S;
   }
+  return METIS_OK;
+}
+
+// Reusable events for the fork/join of metis_prepare_operand (an event may
+// be recorded again once the waits on its previous record are enqueued).
+std::mutex g_evmu;
+std::vector<hipEvent_t> g_evpool;
+
+metis_status take_event(hipEvent_t* e) {
+  {
+    std::lock_guard<std::mutex> lk(g_evmu);
+    if (!g_evpool.empty()) {
+      *e = g_evpool.back();
+      g_evpool.pop_back();
+      return METIS_OK;
+    }
+  }
+  const hipError_t err = hipEventCreateWithFlags(e, hipEventDisableTiming);
+  return err == hipSuccess ? METIS_OK : fail(METIS_E_HIP, "hipEventCreate: %s", hipGetErrorString(err));
+}
+
+void give_event(hipEvent_t e) {
+  std::lock_guard<std::mutex> lk(g_evmu);
+  g_evpool.push_back(e);
+}
+
+// `waiter` waits for everything issued to `from` so far.
+metis_status stream_after(hipStream_t waiter, hipStream_t from, hipEvent_t e) {
+  hipError_t err = hipEventRecord(e, from);
+  if (err == hipSuccess) err = hipStreamWaitEvent(waiter, e, 0);
+  return err == hipSuccess ? METIS_OK : fail(METIS_E_HIP, "stream order: %s", hipGetErrorString(err));
+}
+
+}  // namespace
+
+// =================================================================== ABI ===
+
+extern "C" {
+
+int32_t metis_abi_version(void) { return METIS_ABI_VERSION; }
+
+const char* metis_last_error(void) { return g_last_error.c_str(); }
+
+void metis_omega_table(uint16_t* out65536) {
+  if (out65536) memcpy(out65536, host_omega_table(), 65536 * sizeof(uint16_t));
+}
+
+void metis_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  const Philox4 b = philox4x32_10(ctr[0], ctr[1], ctr[2], ctr[3], key[0], key[1]);
+  for (int i = 0; i < 4; ++i) out[i] = b.v[i];
+}
+
+size_t metis_decompose_workspace(int64_t rows, int64_t cols, const metis_config* cfg,
+                                 int32_t sample_rows) {
+  if (!cfg || rows <= 0 || cols <= 0 || cfg->k < 1) return 0;
+  const int n = cfg->k + cfg->s;
+  const int64_t lr = sample_rows ? cfg->l_k : rows;
+  Carver cv(nullptr, 0);
+  carve_decompose(cv, rows, cols, cfg->k, n, lr, sample_rows != 0);
+  return cv.used();
+}
+
+size_t metis_quantize_workspace(int64_t rows, int64_t cols, int32_t k) {
+  Carver cv(nullptr, 0);
+  carve_quantize(cv, rows, cols, k);
+  return cv.used();
+}
+
+size_t metis_gemm_fwd_workspace(const metis_qoperand* X, const metis_qoperand* W) {
+  if (!X || !W) return 0;
+  return split_ws_size(X->rows, W->cols, X->cols, X->k, W->k);
+}
+
+size_t metis_gemm_bwd_workspace(const metis_qoperand* D, const metis_qoperand* W,
+                                const metis_qoperand* X) {
+  if (!D || !W || !X) return 0;
+  const size_t a = split_ws_size(D->rows, W->rows, D->cols, D->k, W->k);
+  const size_t b = split_ws_size(X->cols, D->cols, X->rows, X->k, D->k);
+  return a > b ? a : b;
+}
+
+metis_status metis_decompose(const void* M, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                             const metis_config* cfg, int32_t sample_rows, uint32_t tag,
+                             int64_t step, metis_factors* f, void* ws, size_t ws_bytes,
+                             void* stream) {
+  DecompCall c;
+  metis_status s = decompose_check(M, dtype, rows, cols, ld, cfg, sample_rows, tag, step, f, &c);
+  if (s != METIS_OK) return s;
+  Carver cv(ws, ws_bytes);
+  c.w = carve_decompose(cv, rows, cols, c.k, c.n, c.lr, c.sample);
+  if (!ws || cv.used() > ws_bytes)
+    return fail(METIS_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, cv.used());
+  if ((s = ensure_device_tables()) != METIS_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  if ((s = decompose_project(c, st)) != METIS_OK) return s;
+  if ((s = decompose_rediag(c, st)) != METIS_OK) return s;
+  if (c.refresh) f->refreshed_at = step;
+  return METIS_OK;
+}
+
+metis_status metis_quantize(const void* M, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                            const metis_factors* f, const metis_config* cfg, uint32_t tag,
+                            int64_t step, int32_t axes, metis_qoperand* out, float* residual_out,
+                            void* ws, size_t ws_bytes, void* stream) {
+  metis_status s = quantize_check(M, dtype, rows, cols, ld, f, cfg, step, axes, out);
+  if (s != METIS_OK) return s;
+  const int k = f ? f->k : 0;
+  Carver cv(ws, ws_bytes);
+  QuantWs w = carve_quantize(cv, rows, cols, k);
+  if (!ws || cv.used() > ws_bytes) return fail(METIS_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, cv.used());
+  if ((s = ensure_device_tables()) != METIS_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, st, w.amax, 0u, (int64_t)4);
+  LAUNCH_CHECK();
+  QuantParams qp = resid_params(M, dtype, rows, cols, ld, cfg, tag, step, axes, out, residual_out, w);
+  if (f) {
+    const int kp = round_up(k, 16);
+    hipLaunchKernelGGL(resid_scale_kernel, dim3(1), dim3(64), 0, st, f->S, k, w.pre, w.pscale);
+    LAUNCH_CHECK();
+    const int64_t rc_pad = ((rows + 31) & ~(int64_t)31) + ((cols + 63) & ~(int64_t)63);
+    hipLaunchKernelGGL(resid_prep_kernel, dim3(grid1(rc_pad * kp, 256)), dim3(256), 0, st, f->U,
+                       f->S, f->V, rows, cols, k, kp, w.pre, w.ucat, w.vcat);
+    LAUNCH_CHECK();
+    qp.ucat = w.ucat;
+    qp.vcat = w.vcat;
+    qp.kc = 3 * kp;
+    qp.pscale = w.pscale;
+  }
+  if ((s = run_quant(qp, f != nullptr, rows, cols, st)) != METIS_OK) return s;
+  if (f) return quantize_factors(f, rows, cols, cfg, tag, step, out, w, st);
+  return METIS_OK;
+}
+
+size_t metis_prepare_operand_workspace(int64_t rows, int64_t cols, const metis_config* cfg,
+                                       int32_t sample_rows) {
+  if (!cfg || rows <= 0 || cols <= 0 || cfg->k < 1 || cfg->k > kMaxN || cfg->s < 0) return 0;
+  const int n = cfg->k + cfg->s;
+  const int64_t lr = sample_rows ? cfg->l_k : rows;
+  Carver cv(nullptr, 0);
+  carve_decompose(cv, rows, cols, cfg->k, n, lr, sample_rows != 0);
+  carve_quantize(cv, rows, cols, cfg->k);
+  return cv.used();
+}
+
+metis_status metis_prepare_operand(const void* M, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                                   const metis_config* cfg, int32_t sample_rows, uint32_t tag, int64_t step,
+                                   metis_factors* f, int32_t axes, metis_qoperand* out, float* residual_out,
+                                   void* ws, size_t ws_bytes, void* stream, void* side_stream) {
+  DecompCall c;
+  metis_status s = decompose_check(M, dtype, rows, cols, ld, cfg, sample_rows, tag, step, f, &c);
+  if (s != METIS_OK) return s;
+  if ((s = quantize_check(M, dtype, rows, cols, ld, f, cfg, step, axes, out)) != METIS_OK) return s;
+  const int k = c.k;
+  Carver cv(ws, ws_bytes);
+  c.w = carve_decompose(cv, rows, cols, k, c.n, c.lr, c.sample);
+  QuantWs qw = carve_quantize(cv, rows, cols, k);
+  if (!ws || cv.used() > ws_bytes)
+    return fail(METIS_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, cv.used());
+  if ((s = ensure_device_tables()) != METIS_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  hipStream_t st2 = side_stream ? (hipStream_t)side_stream : st;
+  const bool fork = st2 != st;
+
+  // P = M V_old and G = P^T P (the sketch first on refresh steps)
+  if ((s = decompose_project(c, st)) != METIS_OK) return s;
+  // the residual's rank-k product from P and V_old, before V is rotated
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, st, qw.amax, 0u, (int64_t)4);
+  LAUNCH_CHECK();
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(128), 0, st, (uint32_t*)qw.ones, 0x3F800000u,
+                     (int64_t)kMaxN);
+  LAUNCH_CHECK();
+  hipLaunchKernelGGL(resid_scale_gram_kernel, dim3(1), dim3(64), 0, st, c.w.ptp, k, qw.pre, qw.pscale);
+  LAUNCH_CHECK();
+  const int kp = round_up(k, 16);
+  const int64_t rc_pad = ((rows + 31) & ~(int64_t)31) + ((cols + 63) & ~(int64_t)63);
+  hipLaunchKernelGGL(resid_prep_kernel, dim3(grid1(rc_pad * kp, 256)), dim3(256), 0, st, c.w.p, qw.ones,
+                     f->V, rows, cols, k, kp, qw.pre, qw.ucat, qw.vcat);
+  LAUNCH_CHECK();
+  QuantParams qp = resid_params(M, dtype, rows, cols, ld, cfg, tag, step, axes, out, residual_out, qw);
+  qp.ucat = qw.ucat;
+  qp.vcat = qw.vcat;
+  qp.kc = 3 * kp;
+  qp.pscale = qw.pscale;
+
+  hipEvent_t e_fork = nullptr, e_join = nullptr;
+  if (fork) {
+    if ((s = take_event(&e_fork)) != METIS_OK) return s;
+    if ((s = take_event(&e_join)) != METIS_OK) {
+      give_event(e_fork);
+      return s;
+    }
+    if ((s = stream_after(st2, st, e_fork)) != METIS_OK) {
+      give_event(e_fork);
+      give_event(e_join);
+      return s;
+    }
+  }
+  // rediagonalisation on the side stream, residual sweeps on the main stream
+  s = decompose_rediag(c, st2);
+  if (s == METIS_OK) s = run_quant(qp, true, rows, cols, st);
+  if (fork) {
+    const metis_status sj = stream_after(st, st2, e_join);
+    if (s == METIS_OK) s = sj;
+    give_event(e_fork);
+    give_event(e_join);
+  }
+  if (s != METIS_OK) return s;
+  if ((s = quantize_factors(f, rows, cols, cfg, tag, step, out, qw, st)) != METIS_OK) return s;
+  if (c.refresh) f->refreshed_at = step;
   return METIS_OK;
 }
 

@@ -59,6 +59,22 @@ __global__ void resid_scale_kernel(const float* __restrict__ S, int k, float* __
   pscale_out[0] = ldexpf(1.0f, ex - 14 - 8);  // 1 / (pre * kVPre)
 }
 
+// pre / pscale when the rank-k product is formed as P V^T from the
+// projection P = M V (equal to U S V^T after the rediagonalisation, whose
+// rotation is orthogonal): every |P_ij| <= sqrt(G_jj) with G = P^T P, so the
+// largest Gram diagonal entry bounds P as S[0] bounds U S.
+__global__ void resid_scale_gram_kernel(const double* __restrict__ G, int k, float* __restrict__ pre_out,
+                                        float* __restrict__ pscale_out) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  double g = 0.0;
+  for (int j = 0; j < k; ++j) g = fmax(g, G[j * k + j]);
+  const float s0 = (float)sqrt(g);
+  int ex = 0;
+  if (s0 > 0.0f) frexpf(s0, &ex);  // s0 < 2^ex
+  pre_out[0] = ldexpf(1.0f, 14 - ex);
+  pscale_out[0] = ldexpf(1.0f, ex - 14 - 8);  // 1 / (pre * kVPre)
+}
+
 __device__ inline int64_t frag_off(int64_t row, int kidx, int kc) {
   const int lane = ((kidx & 15) >> 3) * 32 + (int)(row & 31);
   return (((row >> 5) * (kc >> 4) + (kidx >> 4)) * 64 + lane) * 8 + (kidx & 7);

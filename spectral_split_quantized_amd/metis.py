@@ -80,6 +80,12 @@ def load():
                                    ctypes.POINTER(Config), u32, i64, i32,
                                    ctypes.POINTER(_QOperand), P, P, sz, P]
     lib.metis_quantize.restype = i32
+    lib.metis_prepare_operand_workspace.argtypes = [i64, i64, ctypes.POINTER(Config), i32]
+    lib.metis_prepare_operand_workspace.restype = sz
+    lib.metis_prepare_operand.argtypes = [P, i32, i64, i64, i64, ctypes.POINTER(Config), i32, u32, i64,
+                                          ctypes.POINTER(_Factors), i32, ctypes.POINTER(_QOperand), P, P,
+                                          sz, P, P]
+    lib.metis_prepare_operand.restype = i32
     lib.metis_gemm_fwd.argtypes = [ctypes.POINTER(_QOperand), ctypes.POINTER(_QOperand), P, i64, P,
                                    sz, P]
     lib.metis_gemm_fwd.restype = i32
@@ -212,6 +218,27 @@ def quantize(M, cfg, tag, step, axes, factors=None, out=None, residual_out=None,
                               tag, step, axes, ctypes.byref(oc), _ptr(residual_out), _ptr(ws),
                               ws.numel(), _stream()))
     out.S = factors.S if factors is not None else None
+    return out
+
+
+def prepare_operand(M, cfg, sample_rows, tag, step, factors, axes, out=None, residual_out=None,
+                    workspace=None, side_stream=None):
+    """Decompose and quantise M in one call (metis_prepare_operand): the
+    residual sweeps run on the current stream while the rediagonalisation runs
+    on ``side_stream`` (a torch.cuda.Stream; None: the current stream)."""
+    lib = load()
+    rows, cols = M.shape
+    if out is None:
+        out = QOperand(rows, cols, factors.k, axes, M.device)
+    need = lib.metis_prepare_operand_workspace(rows, cols, ctypes.byref(cfg), int(sample_rows))
+    ws = workspace if workspace is not None and workspace.numel() >= need else _workspace(need, M.device)
+    fc, oc = factors._c(), out._c()
+    side = ctypes.c_void_p(side_stream.cuda_stream) if side_stream is not None else None
+    _check(lib.metis_prepare_operand(_ptr(M), _dtype_code(M), rows, cols, M.stride(0), ctypes.byref(cfg),
+                                     int(sample_rows), tag, step, ctypes.byref(fc), axes, ctypes.byref(oc),
+                                     _ptr(residual_out), _ptr(ws), ws.numel(), _stream(), side))
+    factors.refreshed_at = fc.refreshed_at
+    out.S = factors.S
     return out
 
 
