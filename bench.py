@@ -176,7 +176,9 @@ class MetisMLP:
         m = self.metis
         op = self.ops[name]
         M = inputs[name][t % len(inputs[name])]
-        side = self.side if si == 0 else None
+        # the weights (off the critical path, prepared while X_gu is) keep
+        # their rediagonalisation on their own stream
+        side = self.side if op.kind != "W" else None
         with self.torch.cuda.stream(self.streams[si]):
             m.prepare_operand(M, self.cfg, op.sample, op.tag, t, self.factors[name], m.AXIS0 | m.AXIS1,
                               out=self.q[name], workspace=self.ws[si], side_stream=side)

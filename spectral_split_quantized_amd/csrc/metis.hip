@@ -738,8 +738,8 @@ metis_status decompose_rediag(DecompCall& c, hipStream_t st) {
   DecompWs& w = c.w;
   hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(1024), 0, st, w.ptp, k, w.lam, w.rot);
   LAUNCH_CHECK();
-  hipLaunchKernelGGL(rotate_kernel, dim3(grid1(cols * k, 256)), dim3(256), 0, st, f->V, cols, k, w.rot,
-                     w.vn);
+  hipLaunchKernelGGL(apply_rot_kernel<true>, dim3((unsigned)ceil_div<int64_t>(cols, 64)), dim3(256), 0, st,
+                     f->V, cols, k, w.rot, nullptr, nullptr, w.vn);
   LAUNCH_CHECK();
   hipLaunchKernelGGL(column_sign_kernel, dim3(k), dim3(256), 0, st, w.vn, cols, k, w.sign);
   LAUNCH_CHECK();
@@ -748,8 +748,8 @@ metis_status decompose_rediag(DecompCall& c, hipStream_t st) {
   LAUNCH_CHECK();
   hipLaunchKernelGGL(finalize_s_kernel, dim3(1), dim3(128), 0, st, w.lam, k, f->S);
   LAUNCH_CHECK();
-  hipLaunchKernelGGL(finalize_u_kernel, dim3(grid1(rows, 64)), dim3(256), 0, st, w.p, rows, k, w.rot,
-                     w.lam, w.sign, f->U);
+  hipLaunchKernelGGL(apply_rot_kernel<false>, dim3((unsigned)ceil_div<int64_t>(rows, 64)), dim3(256), 0, st,
+                     w.p, rows, k, w.rot, w.lam, w.sign, f->U);
   LAUNCH_CHECK();
   (void)s;
   return METIS_OK;

@@ -798,16 +798,64 @@ __global__ void project_reduce_kernel(const float* __restrict__ part, int64_t sp
   out[id] = acc * scale;
 }
 
-// Vn = V R (cols x k), fp64 accumulation.
-__global__ void rotate_kernel(const float* __restrict__ V, int64_t cols, int k,
-                              const double* __restrict__ R, float* __restrict__ Vn) {
-  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (id >= cols * k) return;
-  const int64_t c = id / k;
-  const int j = (int)(id % k);
-  double s = 0.0;
-  for (int p = 0; p < k; ++p) s += (double)V[c * k + p] * R[p * k + j];
-  Vn[id] = (float)s;
+// Out (n x k) = In R D for In binary32 (n x k), R binary64 (k x k) and a
+// column scaling D: D = I (ROT: V <- V R) or D = diag(sign_j lambda_j^-1/2,
+// 0 below the eigenvalue threshold) (U = P R Lambda^-1/2 with the column
+// signs).  binary64 accumulation.  A workgroup stages 64 rows of In and the
+// scaled R in LDS; thread item (row, 4-column group) keeps four sums.
+template <bool ROT>
+__global__ __launch_bounds__(256) void apply_rot_kernel(const float* __restrict__ In, int64_t n, int k,
+                                                        const double* __restrict__ R,
+                                                        const double* __restrict__ lam,
+                                                        const float* __restrict__ sign,
+                                                        float* __restrict__ Out) {
+  constexpr int kRs = kMaxN + 4;  // row pitch: 4-column groups stay 16-byte aligned
+  __shared__ __align__(16) double rs[kMaxN][kRs];
+  __shared__ float ins[64][kMaxN + 1];
+  const int tid = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  const double l0 = ROT ? 0.0 : lam[0];
+  for (int e = tid; e < k * k; e += blockDim.x) {
+    const int p = e / k, j = e - p * k;
+    double v = R[e];
+    if (!ROT) {
+      const double lj = lam[j];
+      v = (l0 > 0.0 && lj > kEigZero * l0) ? v * (double)sign[j] / sqrt(lj) : 0.0;
+    }
+    rs[p][j] = v;
+  }
+  const int kg = (k + 3) >> 2;
+  for (int e = tid; e < k * kg * 4; e += blockDim.x) {  // zero the tail of the last group
+    const int p = e / (kg * 4), j = e - p * kg * 4;
+    if (j >= k) rs[p][j] = 0.0;
+  }
+  for (int e = tid; e < 64 * k; e += blockDim.x) {
+    const int rl = e / k, p = e - rl * k;
+    const int64_t r = r0 + rl;
+    ins[rl][p] = r < n ? In[r * k + p] : 0.0f;
+  }
+  __syncthreads();
+  for (int item = tid; item < 64 * kg; item += blockDim.x) {
+    const int rl = item / kg, jg = item - rl * kg;
+    const int64_t r = r0 + rl;
+    if (r >= n) continue;
+    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+    for (int p = 0; p < k; ++p) {
+      const double x = (double)ins[rl][p];
+      const double2 q0 = *(const double2*)&rs[p][4 * jg];
+      const double2 q1 = *(const double2*)&rs[p][4 * jg + 2];
+      a0 += x * q0.x;
+      a1 += x * q0.y;
+      a2 += x * q1.x;
+      a3 += x * q1.y;
+    }
+    const int j = 4 * jg;
+    float* o = Out + r * k + j;
+    o[0] = (float)a0;
+    if (j + 1 < k) o[1] = (float)a1;
+    if (j + 2 < k) o[2] = (float)a2;
+    if (j + 3 < k) o[3] = (float)a3;
+  }
 }
 
 // sign[j] = -1 if the largest-magnitude entry of column j of Vn (lowest row
@@ -859,30 +907,5 @@ __global__ void finalize_s_kernel(const double* __restrict__ lam, int k, float* 
   S[j] = (l0 > 0.0 && lj > kEigZero * l0) ? (float)sqrt(lj) : 0.0f;
 }
 
-__global__ __launch_bounds__(256) void finalize_u_kernel(const float* __restrict__ P, int64_t rows,
-                                                         int k, const double* __restrict__ R,
-                                                         const double* __restrict__ lam,
-                                                         const float* __restrict__ sign,
-                                                         float* __restrict__ U) {
-  __shared__ double rs[kMaxN][kMaxN + 1];
-  const int tid = threadIdx.x;
-  const double l0 = lam[0];
-  for (int e = tid; e < k * k; e += blockDim.x) {
-    const int p = e / k, j = e % k;
-    const double lj = lam[j];
-    const bool keep = l0 > 0.0 && lj > kEigZero * l0;
-    rs[p][j] = keep ? R[e] * (double)sign[j] / sqrt(lj) : 0.0;
-  }
-  __syncthreads();
-  const int64_t r0 = (int64_t)blockIdx.x * 64;
-  for (int e = tid; e < 64 * k; e += blockDim.x) {
-    const int rl = e / k, j = e % k;
-    const int64_t r = r0 + rl;
-    if (r >= rows) continue;
-    double s = 0.0;
-    for (int p = 0; p < k; ++p) s += (double)P[r * k + p] * rs[p][j];
-    U[r * k + j] = (float)s;
-  }
-}
 
 }  // namespace metis
