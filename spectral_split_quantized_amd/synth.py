@@ -44,12 +44,14 @@ def spectrum(rho, n_dom, gen, dtype=torch.float64):
 
 
 def haar(rows, cols, gen, dtype=torch.float32):
-    """rows x cols matrix with Haar-distributed orthonormal columns."""
+    """rows x cols matrix with Haar-distributed orthonormal columns.  The
+    Gaussian draw stays on the generator's device; the QR runs on the host in
+    float64 (no device solver library is involved)."""
     g = torch.randn(rows, cols, generator=gen, dtype=dtype, device=gen.device)
-    q, r = torch.linalg.qr(g, mode="reduced")
+    q, r = torch.linalg.qr(g.to(dtype=torch.float64, device="cpu"), mode="reduced")
     d = torch.sign(torch.diagonal(r))
     d[d == 0] = 1
-    return q * d
+    return (q * d).to(dtype=dtype, device=gen.device)
 
 
 def _generator(seed, device):

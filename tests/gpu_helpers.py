@@ -120,3 +120,33 @@ class Layer:
             self.q[n] = metis.quantize(M, self.cfg, self.tags[n], step, metis.AXIS0 | metis.AXIS1,
                                        factors=f, residual_out=res)
             self.resid[n] = res
+
+
+# End to end, the HIP path (binary32 factors) and the oracle (binary64
+# factors) quantise factors and residuals that agree to ~1e-7 relative, so a
+# code whose value sits on a rounding boundary may be decided differently on
+# the two sides (each side decides in binary32, as the quantiser defines).
+# One flipped factor code moves a whole rank-one term's entry by an E2M1 step
+# times its singular value: two flips among D's U codes give ~1e-3 relative
+# Frobenius error on dX and dW.  The end-to-end bar therefore checks the flip
+# rates (residual and factor codes) and bounds the outputs at E2E_TOL, which
+# allows about ten such flips; the split GEMM's own parity on shared operands
+# keeps the 1e-3 bar.
+E2E_TOL = 3e-3
+E2E_RESID_FLIPS = 1e-4   # fraction of residual codes / block scales that may differ
+E2E_FACTOR_FLIPS = 1e-3  # fraction of factor codes that may differ
+
+
+def assert_e2e_codes(gq, oq, what):
+    """Flip rates of one operand's quantised parts, HIP vs oracle."""
+    rates = []
+    for name, g, o, lim in (("R_ax0", gq.R_ax0, oq.r_ax0, E2E_RESID_FLIPS),
+                            ("R_ax1", gq.R_ax1, oq.r_ax1, E2E_RESID_FLIPS),
+                            ("U", gq.U, oq.u_q, E2E_FACTOR_FLIPS), ("V", gq.V, oq.v_q, E2E_FACTOR_FLIPS)):
+        if g is None or o is None:
+            continue
+        fc = float((g.codes.cpu().numpy() != o.codes).mean())
+        fs = float((g.scales.cpu().numpy() != o.scales).mean())
+        rates.append("%s %.1e/%.1e" % (name, fc, fs))
+        assert fc <= lim and fs <= lim, "%s %s: %.2e of codes, %.2e of scales differ" % (what, name, fc, fs)
+    say("  %s flips (codes/scales): %s" % (what, ", ".join(rates)))

@@ -7,7 +7,8 @@ their codes are the same computation and must match bit for bit; the
 residual is formed as M - P V_old^T instead of M - U diag(S) V^T (equal in
 exact arithmetic, the rotation being orthogonal), so the two binary32
 residuals agree to rounding and only codes at a rounding boundary may
-differ.  Against the float64 oracle: the whole pipeline, to the GEMM bar."""
+differ.  Against the float64 oracle: the whole pipeline, with the flip-rate
+and output bounds of the end-to-end comparison (gpu_helpers.E2E_TOL)."""
 
 import numpy as np
 import pytest
@@ -16,11 +17,10 @@ import torch
 from oracle import rsvd, split_gemm
 from spectral_split_quantized_amd import metis, synth
 
-from gpu_helpers import Layer, rel_fro, say, to_np
+from gpu_helpers import E2E_TOL, Layer, assert_e2e_codes, rel_fro, say, to_np
 
 pytestmark = pytest.mark.gpu
 
-GEMM_TOL = 1e-3
 RESID_TOL = 1e-5       # |residual difference| / max |M|
 CODE_DIFF_FRAC = 1e-3  # residual codes allowed to differ (rounding boundaries)
 
@@ -99,6 +99,7 @@ def test_prepare_end_to_end_matches_oracle(config):
         v0 = rsvd.rsvd_sketch(m, L.ocfg, L.sample[n], L.tags[n], 0)
         u, s, v, _ = rsvd.project_rediag(m, v0)
         oq[n] = split_gemm.quantize_operand(m, u, s, v, L.rounding, L.seed, L.tags[n], 0)
+        assert_e2e_codes(q[n], oq[n], n)
     Y = metis.gemm_fwd(q["X"], q["W"])
     metis.status_sync()
     errs = [rel_fro(Y.cpu().double().numpy(), split_gemm.gemm_fwd(oq["X"], oq["W"]))]
@@ -108,4 +109,4 @@ def test_prepare_end_to_end_matches_oracle(config):
         wdx, wdw = split_gemm.gemm_bwd(oq["D"], oq["W"], oq["X"])
         errs += [rel_fro(dX.cpu().double().numpy(), wdx), rel_fro(dW.cpu().double().numpy(), wdw)]
     say("prepare end-to-end rel Frobenius errors: %s" % ", ".join("%.2e" % e for e in errs))
-    assert max(errs) <= GEMM_TOL
+    assert max(errs) <= E2E_TOL
