@@ -37,6 +37,39 @@ TOKENS, HIDDEN, FFN = 16384, 4096, 14336
 K_RANK, OVERSAMPLE, L_K, REFRESH = 61, 8, 164, 8
 
 
+# HBM traffic of the main split-GEMM kernel, bytes per launch averaged over
+# the 18 launches of one step (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE,
+# on ``bench.py --steps 1 --warmup 1 --no-cpu-baseline``; each counter scaled
+# by what it reads for a plain 256 MiB copy, ``bench.py --copy-calibration``).
+# The figure belongs to the kernel source it was taken on: if any file below
+# changes, the stored figure no longer applies and ``traffic`` is reported null.
+GEMM_TRAFFIC_BYTES = 1835941043
+GEMM_TRAFFIC_SHA = "121102e81c9dc36e"
+GEMM_SOURCES = ("common.hpp", "gemm_common.hpp", "gemm_reg.hpp", "gemm_launch.hpp", "gemm_big.hip")
+
+
+def gemm_source_sha():
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "spectral_split_quantized_amd", "csrc")
+    for name in GEMM_SOURCES:
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def copy_calibration():
+    """Three plain device-to-device copies of 256 MiB: the reference the PMC
+    byte counters are scaled by."""
+    import torch
+    a = torch.empty(1 << 28, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": 1 << 28, "copy_bytes_written": 1 << 28, "launches": 3}))
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -308,7 +341,12 @@ def main():
     ap.add_argument("--cpu-cols", type=int, default=2048)
     ap.add_argument("--streams", type=int, default=3,
                     help="HIP streams per step (1: every call in order on one stream)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy three times (PMC byte-counter scale)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -364,8 +402,9 @@ def main():
     g_ms = sum(r[1] for r in g)
     g_flops = sum(2 * r[2] * r[3] * r[4] + 2 * r[2] * r[3] * 2 * K_RANK for r in g)
     g_tflops = g_flops / (g_ms * 1e-3) / 1e12 if g_ms > 0 else 0.0
+    traffic = GEMM_TRAFFIC_BYTES if GEMM_TRAFFIC_SHA is not None and gemm_source_sha() == GEMM_TRAFFIC_SHA else None
     roofline = {"bound": "mfma", "achieved": round(g_tflops, 1), "peak": PEAK_F16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(g_tflops / PEAK_F16_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(g_tflops / PEAK_F16_TFLOPS, 4), "traffic": traffic,
                 "kernel": "gemm_fp4_kernel (main split GEMM)", "launches": len(g),
                 "avg_ms": round(g_ms / max(len(g), 1), 4)}
     # streaming: both quantiser sweeps (amax + quantise-on-store)
