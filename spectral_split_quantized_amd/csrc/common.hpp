@@ -115,42 +115,43 @@ __host__ __device__ inline uint32_t e4m3_encode_rne_sat(float t) {
   return (uint32_t)(((e + 7) << 3) | mq);
 }
 
-// E2M1 magnitude index of y >= 0, nearest with ties to the even mantissa,
-// saturating at 6 (index 7).
-// E2M1 rounding without comparisons.  On y >= 0 the grid is three uniform
-// segments: steps of 0.5 on [0, 2] (codes 0..4), 1 on [2, 4] (4..6), 2 on
-// [4, 6] (6..7).  a1 = min(2y, 4), a2 = clamp(y - 2, 0, 2) and
-// a3 = clamp((y - 4) / 2, 0, 1) are exact (power-of-two scalings; y - 2 and
-// y - 4 by Sterbenz wherever they are not clamped), and the code is the sum
-// of the three segment codes.  NaN gives an unspecified code.
-__host__ __device__ inline float e2m1_seg_clamp(float x, float lo, float hi) {
-  return fminf(fmaxf(x, lo), hi);
+// E2M1 magnitude index of y >= 0.  On y >= 0 the grid is three uniform
+// segments: steps of 0.5 on [0, 2) (codes 0..4), 1 on [2, 4) (codes 4..6) and
+// 2 on [4, 6] (codes 6..7).  With j = clamp(floor(log2 y), 0, 2) the segment
+// index (read from the exponent field), the position of y in code units is
+// y 2^(1-j) + 2j: a power-of-two scaling, exact in binary32, plus an even
+// integer.  y is first clamped to 6, whose position is code 7, so y >= 6
+// saturates.  NaN gives an unspecified code.  e2m1_segment_biased returns
+// 127 + j.
+__host__ __device__ inline uint32_t e2m1_segment_biased(float yc) {  // 127 + j
+  const uint32_t e = __builtin_bit_cast(uint32_t, yc) >> 23;  // biased exponent (yc >= 0)
+  return e < 127u ? 127u : (e > 129u ? 129u : e);
 }
 
-// Round to nearest with ties to the even code: rint (ties to even) within a
-// segment gives exactly the ties 0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2,
-// 2.5 -> 2, 3.5 -> 4, 5 -> 4 of the grid; y >= 6 saturates to code 7.
+// Round to nearest with ties to the even code: rint (ties to even) of the
+// scaled position gives exactly the ties 0.25 -> 0, 0.75 -> 1, 1.25 -> 1,
+// 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4 of the grid (adding the even 2j
+// keeps the parity).
 __host__ __device__ inline uint32_t e2m1_rne(float y) {
-  const float a1 = fminf(2.0f * y, 4.0f);
-  const float a2 = e2m1_seg_clamp(y - 2.0f, 0.0f, 2.0f);
-  const float a3 = e2m1_seg_clamp((y - 4.0f) * 0.5f, 0.0f, 1.0f);
-  return (uint32_t)(rintf(a1) + rintf(a2) + rintf(a3));
+  const float yc = fminf(y, 6.0f);
+  const uint32_t m = e2m1_segment_biased(yc);
+  return (uint32_t)rintf(ldexpf(yc, 128 - (int)m)) + 2u * (m - 127u);
 }
 
-// Stochastic rounding with a 16-bit draw h (u = h 2^-16): the floor code is
-// lo = sum floor(a_i) and p = sum (a_i - floor(a_i)) = (y - grid[lo]) / step,
-// both exact; the code is lo + 1 iff u < p, i.e. lo + ceil(p - u) (p - u is
-// zero only when p == u and keeps the sign of the exact difference;
-// |p - u| < 1).  y >= 6 gives a3 = 1, p = 0 and code 7.
-__host__ __device__ inline uint32_t e2m1_sr(float y, uint32_t h) {
-  const float a1 = fminf(2.0f * y, 4.0f);
-  const float a2 = e2m1_seg_clamp(y - 2.0f, 0.0f, 2.0f);
-  const float a3 = e2m1_seg_clamp((y - 4.0f) * 0.5f, 0.0f, 1.0f);
-  const float f1 = floorf(a1), f2 = floorf(a2), f3 = floorf(a3);
-  const float p = (a1 - f1) + (a2 - f2) + (a3 - f3);
-  const float u = (float)h * (1.0f / 65536.0f);
-  return (uint32_t)(f1 + f2 + f3 + ceilf(p - u));
+// Stochastic rounding with a 16-bit draw h (u = h 2^-16), given as its
+// complement hc = 0xFFFF - h: with position n + p (n its integer part, p in
+// [0, 1)) the code is n + 1 iff u < p, i.e. iff h < ceil(p 2^16).
+// z = y 2^(17-j) is exact, so C = ceil(z) + 2j 2^16 = ceil((n + p) 2^16), and
+// (C + hc) >> 16 equals n + [h < ceil(p 2^16)] for every h in [0, 0xFFFF]
+// (ceil(p 2^16) is at most 2^16).
+__host__ __device__ inline uint32_t e2m1_sr_c(float y, uint32_t hc) {
+  const float yc = fminf(y, 6.0f);
+  const uint32_t m = e2m1_segment_biased(yc);
+  const uint32_t c = (uint32_t)ceilf(ldexpf(yc, 144 - (int)m));
+  return (c + (m << 17) + hc - (127u << 17)) >> 16;  // 2j 2^16 = (m - 127) 2^17
 }
+
+__host__ __device__ inline uint32_t e2m1_sr(float y, uint32_t h) { return e2m1_sr_c(y, 0xFFFFu - h); }
 
 
 // ------------------------------------------------------------------- misc --

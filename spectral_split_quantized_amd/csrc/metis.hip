@@ -339,7 +339,10 @@ metis_status launch_quant_pair(const QuantParams& qp, dim3 grid, int64_t rows, i
   LAUNCH_CHECK();
   timing_end(t1, st);
   TimingRec* t2 = timing_begin(st, 2, rows, cols, qp.axes, kc);
-  hipLaunchKernelGGL((quant_kernel<NKK>), grid, dim3(kQThreads), 0, st, qp);
+  if (qp.sr)
+    hipLaunchKernelGGL((quant_kernel<NKK, true>), grid, dim3(kQThreads), 0, st, qp);
+  else
+    hipLaunchKernelGGL((quant_kernel<NKK, false>), grid, dim3(kQThreads), 0, st, qp);
   LAUNCH_CHECK();
   timing_end(t2, st);
   return METIS_OK;

@@ -142,7 +142,8 @@ struct QuantBlockOut {
   uint32_t scale;   // E4M3 byte
 };
 
-__device__ inline QuantBlockOut quant_block16(const float (&x)[16], const uint32_t (&h)[16],
+// hc: complemented 16-bit draws (0xFFFF - h) of the 16 elements (SR only).
+__device__ inline QuantBlockOut quant_block16(const float (&x)[16], const uint32_t (&hc)[16],
                                               float s_g, float d, bool sr) {
   float a = 0.0f;
 #pragma unroll
@@ -161,7 +162,7 @@ __device__ inline QuantBlockOut quant_block16(const float (&x)[16], const uint32
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const float y = __fmul_rn(fabsf(x[i]), inv);
-    const uint32_t m = sr ? e2m1_sr(y, h[i]) : e2m1_rne(y);
+    const uint32_t m = sr ? e2m1_sr_c(y, hc[i]) : e2m1_rne(y);
     const uint32_t code = ((__float_as_uint(x[i]) >> 31) << 3) | m;
     if (i < 8)
       o.lo |= code << (4 * i);
@@ -171,15 +172,21 @@ __device__ inline QuantBlockOut quant_block16(const float (&x)[16], const uint32
   return o;
 }
 
-// 16-bit draws of 16 consecutive indices e0 .. e0+15 with e0 % 8 == 0.
+// Complemented 16-bit draws (0xFFFF - h) of 16 consecutive indices
+// e0 .. e0+15 with e0 % 8 == 0.
 __device__ inline void draws16(uint64_t e0, uint32_t tag, uint32_t step, uint64_t seed,
-                               uint32_t (&h)[16]) {
-  const Philox4 b0 = philox_block(e0 >> 3, tag, step, seed);
-  const Philox4 b1 = philox_block((e0 >> 3) + 1, tag, step, seed);
+                               uint32_t (&hc)[16]) {
+  Philox4 b0 = philox_block(e0 >> 3, tag, step, seed);
+  Philox4 b1 = philox_block((e0 >> 3) + 1, tag, step, seed);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    b0.v[w] = ~b0.v[w];
+    b1.v[w] = ~b1.v[w];
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    h[i] = philox_half_of(b0, (uint32_t)i);
-    h[8 + i] = philox_half_of(b1, (uint32_t)i);
+    hc[i] = philox_half_of(b0, (uint32_t)i);
+    hc[8 + i] = philox_half_of(b1, (uint32_t)i);
   }
 }
 
@@ -369,18 +376,29 @@ void quant_amax_kernel(QuantParams p) {
 }
 
 // Pass 2: quantise the residual in the orientations `axes` asks for.  NKK =
-// kc / 16 of the rank-k product (0: no factors, direct quantisation).
-// A workgroup owns a 128-row panel and walks `tiles_per_wg` tiles of 64
-// columns.  Wave w owns rows 32w..32w+31; after gather_cols16 lane l holds
-// row 32w + l%32 at columns 16(l/32) .. +15 and 32 + 16(l/32) .. +15: two
-// axis-1 blocks, matching 32-byte row loads of M.  The residual is formed by
-// the same subtract_lowrank as in pass 1, so both sweeps see bit-identical
-// values.  Axis-0 blocks (16 rows of one column) go through an LDS transpose.
-template <int NKK>
-__global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void quant_kernel(QuantParams p) {
+// kc / 16 of the rank-k product (0: no factors, direct quantisation); SR
+// selects stochastic rounding.  A workgroup owns a 128-row panel and walks
+// `tiles_per_wg` tiles of 64 columns.  Wave w owns rows 32w..32w+31; after
+// gather_cols16 lane l holds row 32w + l%32 at columns 16(l/32) .. +15 and
+// 32 + 16(l/32) .. +15: two axis-1 blocks, matching 32-byte row loads of M.
+// The residual is formed by the same subtract_lowrank as in pass 1, so both
+// sweeps see bit-identical values.  Axis-0 blocks (16 rows of one column) go
+// through an LDS transpose inside the wave's own 32-row slab of R, so only the
+// vcat fragments need workgroup barriers: they land by LDS-DMA, and the next
+// tile's fragments (and its M rows, into registers) are requested as soon as
+// every wave has finished its MFMAs, so they arrive while this tile is
+// quantised.
+//
+// Positions outside the operand are never stored: an axis-1 block is written
+// only for a valid row and 16 valid columns (cols % 16 == 0 for axis 1), an
+// axis-0 block only for a valid column and 16 valid rows (rows % 16 == 0 for
+// axis 0), so the values computed there need no masking.
+template <int NKK, bool SR>
+__global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void quant_kernel(QuantParams p) {
   constexpr bool HAS_F = NKK > 0;
+  constexpr int BFU = HAS_F ? NKK * 2 * 64 : 1;  // uint4 per tile
   __shared__ float R[kQT_R][kQT_C + 4];
-  __shared__ uint4 Bf[HAS_F ? NKK * 2 * 64 : 1];
+  __shared__ uint4 Bf[BFU];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5;
@@ -391,6 +409,8 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 8)
   const int64_t row = r0 + wave * 32 + (lane & 31);
   const bool row_ok = row < p.rows;
   const bool vec_ok = ((p.ld & 7) == 0) && (((uintptr_t)p.M & 15) == 0);
+  const bool fast = p.dtype == 0 && vec_ok && row_ok;
+  const int64_t full_tiles = p.cols / kQT_C;
 
   half8_t uf[HAS_F ? NKK : 1];
   if (HAS_F) {
@@ -415,96 +435,118 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 8)
       if (p.sg1) p.sg1[0] = s_g;
     }
   }
-  const bool sr = p.sr != 0;
   const bool ax0 = (p.axes & 1) != 0;
   const bool ax1 = (p.axes & 2) != 0;
 
+  // tile ct's vcat fragments -> Bf (LDS-DMA) and, on the fast path, its two
+  // 16-column blocks of this lane's row -> raw
+  auto issue = [&](int64_t ct, uint4 (&raw)[4]) {
+    if (HAS_F) {
+      const uint4* src = (const uint4*)p.vcat + ct * BFU;
+      for (int i = wave; i < 2 * NKK; i += 4) dma16(src + i * 64 + lane, (uint8_t*)(Bf + i * 64));
+    }
+    if (fast && ct < full_tiles) {
+      const uint16_t* m = (const uint16_t*)p.M + row * p.ld + ct * kQT_C + 16 * hh;
+      raw[0] = *(const uint4*)m;
+      raw[1] = *(const uint4*)(m + 8);
+      raw[2] = *(const uint4*)(m + 32);
+      raw[3] = *(const uint4*)(m + 40);
+    }
+  };
+
+  uint4 raw[4] = {};
+  if (ct0 < ct1) issue(ct0, raw);
   for (int64_t ct = ct0; ct < ct1; ++ct) {
     const int64_t c0 = ct * kQT_C;
     float x[2][16];
-    load_tile_x(p, row, row_ok, c0, hh, vec_ok, x);
+    if (fast && ct < full_tiles) {
+      unpack_bf16x16(raw[0], raw[1], x[0]);
+      unpack_bf16x16(raw[2], raw[3], x[1]);
+    } else {
+      load_tile_x(p, row, row_ok, c0, hh, vec_ok, x);
+    }
     if (HAS_F) {
-      __syncthreads();  // the previous tile is done with Bf (and R)
-      const uint4* src = (const uint4*)p.vcat + (ct * 2) * (int64_t)NKK * 64;
-      for (int e = tid; e < 2 * NKK * 64; e += kQThreads) Bf[e] = src[e];
-      __syncthreads();
+      ring_barrier();  // tile ct's fragments have landed in Bf
       subtract_lowrank<HAS_F ? NKK : 1>(Bf, uf, ps, lane, x);
-    } else if (ax0) {
-      __syncthreads();  // the previous tile's axis-0 readers are done with R
+      // every wave has read Bf (its MFMAs consumed the reads) before the
+      // next tile's DMA overwrites it
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
     }
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int64_t gc = c0 + 32 * b + 16 * hh;
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (!(row_ok && gc + i < p.cols)) x[b][i] = 0.0f;
-    }
+    if (ct + 1 < ct1) issue(ct + 1, raw);
 
     // ---- axis 1 (and the export) from registers
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int64_t gc = c0 + 32 * b + 16 * hh;
-      const int n = (int)max((int64_t)0, min((int64_t)16, p.cols - gc));
-      if (row_ok && n > 0) {
-        if (p.resid) {
-          float* dst = p.resid + row * p.cols + gc;
-          for (int i = 0; i < n; ++i) dst[i] = x[b][i];
-        }
-        if (ax1 && n == 16) {
-          uint32_t h[16];
-          if (sr) draws16((uint64_t)row * (uint64_t)p.cols + (uint64_t)gc, p.tag1, p.step, p.seed, h);
-          const QuantBlockOut o = quant_block16(x[b], h, s_g, d, sr);
-          *(uint2*)(p.codes1 + row * (p.cols >> 1) + (gc >> 1)) = make_uint2(o.lo, o.hi);
-          p.scales1[row * (p.cols >> 4) + (gc >> 4)] = (uint8_t)o.scale;
-        }
+      if (!row_ok || gc >= p.cols) continue;
+      if (p.resid) {
+        const int n = (int)min((int64_t)16, p.cols - gc);
+        float* dst = p.resid + row * p.cols + gc;
+        for (int i = 0; i < n; ++i) dst[i] = x[b][i];
       }
-      if (ax0) {
-        const int lr = wave * 32 + (lane & 31);
-        const int lc = 32 * b + 16 * hh;
-#pragma unroll
-        for (int i = 0; i < 16; i += 4)
-          *(float4*)&R[lr][lc + i] = make_float4(x[b][i], x[b][i + 1], x[b][i + 2], x[b][i + 3]);
+      if (ax1) {
+        uint32_t hc[16];
+        if (SR) draws16((uint64_t)row * (uint64_t)p.cols + (uint64_t)gc, p.tag1, p.step, p.seed, hc);
+        const QuantBlockOut o = quant_block16(x[b], hc, s_g, d, SR);
+        *(uint2*)(p.codes1 + row * (p.cols >> 1) + (gc >> 1)) = make_uint2(o.lo, o.hi);
+        p.scales1[row * (p.cols >> 4) + (gc >> 4)] = (uint8_t)o.scale;
       }
     }
     if (!ax0) continue;
-    __syncthreads();
-    // ---- axis 0: column tid % 64, row blocks (tid/64)*2 + {0, 1}
-    const int lcol = tid & (kQT_C - 1);
-    const int64_t gcol = c0 + lcol;
-    if (gcol < p.cols) {
-      uint32_t packed[4];
+
+    // ---- axis 0: transpose through this wave's slab of R (rows 32w..32w+31);
+    // LDS operations of one wave complete in order, so the slab needs no
+    // barrier, only a compiler fence
+    const int lr = wave * 32 + (lane & 31);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int lc = 32 * b + 16 * hh;
+#pragma unroll
+      for (int i = 0; i < 16; i += 4)
+        *(float4*)&R[lr][lc + i] = make_float4(x[b][i], x[b][i + 1], x[b][i + 2], x[b][i + 3]);
+    }
+    asm volatile("" ::: "memory");
+    const int64_t gcol = c0 + lane;
+    const int64_t grow0 = r0 + wave * 32;
+    if (gcol < p.cols && grow0 < p.rows) {
+      const bool two = grow0 + 16 < p.rows;  // rows % 16 == 0: blocks are whole
+      uint32_t packed[4] = {0u, 0u, 0u, 0u};
       uint32_t sc = 0;
-      int nb = 0;
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        const int lr0 = (tid >> 6) * 32 + 16 * b;
-        const int64_t grow = r0 + lr0;
-        if (grow >= p.rows) break;
+        if (b == 1 && !two) break;
+        const int lr0 = wave * 32 + 16 * b;
         float xc[16];
-        uint32_t h[16];
+        uint32_t hc[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) xc[i] = R[lr0 + i][lcol];
-        if (sr) draws16((uint64_t)gcol * (uint64_t)p.rows + (uint64_t)grow, p.tag0, p.step, p.seed, h);
-        const QuantBlockOut o = quant_block16(xc, h, s_g, d, sr);
+        for (int i = 0; i < 16; ++i) xc[i] = R[lr0 + i][lane];
+        if (SR) draws16((uint64_t)gcol * (uint64_t)p.rows + (uint64_t)(grow0 + 16 * b), p.tag0, p.step, p.seed, hc);
+        const QuantBlockOut o = quant_block16(xc, hc, s_g, d, SR);
         packed[2 * b] = o.lo;
         packed[2 * b + 1] = o.hi;
         sc |= o.scale << (8 * b);
-        ++nb;
       }
-      const int64_t grow0 = r0 + (tid >> 6) * 32;
       // rows % 16 == 0 makes every 8-byte code group 8-byte aligned; the
       // pair is 16-byte aligned only when rows % 32 == 0
       uint8_t* cdst = p.codes0 + gcol * (p.rows >> 1) + (grow0 >> 1);
       uint8_t* sdst = p.scales0 + gcol * (p.rows >> 4) + (grow0 >> 4);
-      if (nb == 2 && (((uintptr_t)cdst & 15) == 0)) {
+      if (two && (((uintptr_t)cdst & 15) == 0)) {
         *(uint4*)cdst = make_uint4(packed[0], packed[1], packed[2], packed[3]);
       } else {
-        for (int b = 0; b < nb; ++b) *(uint2*)(cdst + 8 * b) = make_uint2(packed[2 * b], packed[2 * b + 1]);
+        *(uint2*)cdst = make_uint2(packed[0], packed[1]);
+        if (two) *(uint2*)(cdst + 8) = make_uint2(packed[2], packed[3]);
       }
-      for (int b = 0; b < nb; ++b) sdst[b] = (uint8_t)(sc >> (8 * b));
+      if (two && (((uintptr_t)sdst & 1) == 0)) {
+        *(uint16_t*)sdst = (uint16_t)sc;
+      } else {
+        sdst[0] = (uint8_t)sc;
+        if (two) sdst[1] = (uint8_t)(sc >> 8);
+      }
     }
+    asm volatile("" ::: "memory");  // the slab is rewritten by the next tile
   }
-
 }
 
 }  // namespace metis
