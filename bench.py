@@ -149,19 +149,23 @@ def build_inputs(n_steps, device):
 
 class MetisMLP:
     """Persistent state of the path for the three projections: factor
-    caches, quantised operands, outputs and one workspace per stream.
+    caches, quantised operands, outputs, one workspace per stream and one per
+    split product.
 
-    One step follows the layer's data dependencies on up to three HIP
-    streams: the weights (known when the step starts) are decomposed and
-    quantised on a side stream while the main stream handles X_gu; the
-    forward GEMMs wait for their weight; X_down follows the gate/up GEMMs
-    and D_down the down GEMM (in a real layer they are computed from them);
-    D_gate and D_up, which both come from the down projection's dX, are
-    processed concurrently on the two side streams while the down
-    projection's dW GEMM runs on the main stream.  With streams=1
-    everything runs in that order on one stream."""
+    One step follows the layer's data dependencies on the main stream, a
+    side stream and the main stream's companion: the weights (known when
+    the step starts) are decomposed and quantised on the side stream while
+    the main stream handles X_gu; the forward GEMMs wait for their weight;
+    X_down follows the gate/up GEMMs and D_down the down GEMM (in a real
+    layer they are computed from them); D_gate and D_up both come from the
+    down projection's dX: D_gate is prepared on the main stream, D_up beside
+    it on the side stream; the down projection's dW runs last.  Operands on
+    the main stream rediagonalise on the companion while their residual is
+    quantised, and the K-extension of every split product whose operands are
+    ready early is built on the companion beside an earlier GEMM.  With
+    streams=1 everything runs in that order on one stream."""
 
-    def __init__(self, device, streams=3):
+    def __init__(self, device, streams=2):
         import torch
         from spectral_split_quantized_amd import metis
         self.metis = metis
@@ -180,16 +184,21 @@ class MetisMLP:
             self.q[op.name] = metis.QOperand(op.rows, op.cols, K_RANK, metis.AXIS0 | metis.AXIS1, device)
             need = max(need, lib.metis_prepare_operand_workspace(op.rows, op.cols, ctypes.byref(self.cfg),
                                                                  int(op.sample)))
-        self.out = {}
+        self.out, self.gws = {}, {}
         for name, x, w, d in PROJECTIONS:
             X, W = self.ops[x], self.ops[w]
             self.out[name] = (torch.empty(X.rows, W.cols, dtype=torch.float32, device=device),
                               torch.empty(X.rows, W.rows, dtype=torch.float32, device=device),
                               torch.empty(W.rows, W.cols, dtype=torch.float32, device=device))
             xc, wc, dc = self.q[x]._c(), self.q[w]._c(), self.q[d]._c()
-            need = max(need, lib.metis_gemm_fwd_workspace(ctypes.byref(xc), ctypes.byref(wc)),
-                       lib.metis_gemm_bwd_workspace(ctypes.byref(dc), ctypes.byref(wc), ctypes.byref(xc)))
-        self.nstreams = max(1, min(3, int(streams)))
+            # one workspace per split product: its K-extension stays there
+            # from the prepare call to the GEMM
+            self.gws[name] = (
+                torch.empty(lib.metis_gemm_fwd_workspace(ctypes.byref(xc), ctypes.byref(wc)), dtype=torch.uint8,
+                            device=device),
+                torch.empty(lib.metis_gemm_bwd_workspace(ctypes.byref(dc), ctypes.byref(wc), ctypes.byref(xc)),
+                            dtype=torch.uint8, device=device))
+        self.nstreams = max(1, min(2, int(streams)))
         # default-priority streams only
         self.streams = [torch.cuda.current_stream(device)] + \
             [torch.cuda.Stream(device=device) for _ in range(self.nstreams - 1)]
@@ -198,20 +207,21 @@ class MetisMLP:
         self.side = torch.cuda.Stream(device=device) if self.nstreams > 1 else None
         self.ws = [torch.empty(need, dtype=torch.uint8, device=device) for _ in self.streams]
         self.step_done = None
-        log("  workspace %.1f MB x %d streams" % (need / 1e6, self.nstreams))
+        log("  workspace %.1f MB x %d streams, %.1f MB for the split products"
+            % (need / 1e6, self.nstreams, sum(a.numel() + b.numel() for a, b in self.gws.values()) / 1e6))
 
     def decompose(self, name, M, t):
         op = self.ops[name]
         self.metis.decompose(M, self.cfg, op.sample, op.tag, t, self.factors[name], workspace=self.ws[0])
 
-    def _prep(self, name, t, inputs, si):
-        """Decompose and quantise one operand (both K orientations) on stream si."""
+    def _prep(self, name, t, inputs, si, companion=True):
+        """Decompose and quantise one operand (both K orientations) on stream
+        si; with ``companion`` the rediagonalisation runs on the main
+        stream's companion (for operands on the critical path)."""
         m = self.metis
         op = self.ops[name]
         M = inputs[name][t % len(inputs[name])]
-        # the weights (off the critical path, prepared while X_gu is) keep
-        # their rediagonalisation on their own stream
-        side = self.side if op.kind != "W" else None
+        side = self.side if companion else None
         with self.torch.cuda.stream(self.streams[si]):
             m.prepare_operand(M, self.cfg, op.sample, op.tag, t, self.factors[name], m.AXIS0 | m.AXIS1,
                               out=self.q[name], workspace=self.ws[si], side_stream=side)
@@ -221,53 +231,107 @@ class MetisMLP:
         e.record(self.streams[si])
         return e
 
-    def _gemms(self, name, fwd, want_dx=True, want_dw=True):
-        m = self.metis
+    def _names(self, name):
         _, x, w, d = next(p for p in PROJECTIONS if p[0] == name)
+        return self.q[x], self.q[w], self.q[d]
+
+    def _ext(self, name, kind, stream):
+        """Build the K-extension of one split product ("fwd", "dx" or "dw")
+        on ``stream``; returns an event that follows it."""
+        m = self.metis
+        X, W, D = self._names(name)
+        wsf, wsb = self.gws[name]
+        with self.torch.cuda.stream(stream):
+            if kind == "fwd":
+                m.gemm_fwd_prepare(X, W, wsf)
+            else:
+                m.gemm_bwd_prepare(D, W, X, wsb, which=m.GRAD_DX if kind == "dx" else m.GRAD_DW)
+            e = self.torch.cuda.Event()
+            e.record(stream)
+        return e
+
+    def _gemm(self, name, kind):
+        """The main GEMM of one split product on the main stream, from the
+        K-extension built by _ext."""
+        m = self.metis
+        X, W, D = self._names(name)
         Y, dX, dW = self.out[name]
-        if fwd:
-            m.gemm_fwd(self.q[x], self.q[w], Y=Y, workspace=self.ws[0])
+        wsf, wsb = self.gws[name]
+        if kind == "fwd":
+            m.gemm_fwd_prepared(X, W, wsf, Y=Y)
+        elif kind == "dx":
+            m.gemm_bwd_prepared(D, W, X, wsb, dX=dX, want_dw=False)
         else:
-            m.gemm_bwd(self.q[d], self.q[w], self.q[x], dX=dX, dW=dW, want_dx=want_dx, want_dw=want_dw,
-                       workspace=self.ws[0])
+            m.gemm_bwd_prepared(D, W, X, wsb, dW=dW, want_dx=False)
+
+    def _ahead(self, name, kind, after):
+        """The K-extension of a product whose GEMM comes later, built on the
+        companion stream once the events ``after`` have fired (on the main
+        stream when there is no companion)."""
+        st = self.side if self.side is not None else self.streams[0]
+        for e in after:
+            st.wait_event(e)
+        return self._ext(name, kind, st)
 
     def step(self, t, inputs):
         main = self.streams[0]
         sw = 1 if self.nstreams > 1 else 0
-        sd = 2 if self.nstreams > 2 else 0
-        # the side streams overwrite quantised operands the previous step read
+        # the side stream overwrites quantised operands the previous step read
         if self.step_done is not None:
             for s in self.streams[1:]:
                 s.wait_event(self.step_done)
         ev = {}
+        # the weights (known when the step starts, off the critical path)
+        # keep their rediagonalisation on their own stream
         for w in ("W_gate", "W_up", "W_down"):
-            self._prep(w, t, inputs, sw)
+            self._prep(w, t, inputs, sw, companion=False)
             ev[w] = self._event(sw)
         self._prep("X_gu", t, inputs, 0)
+        x_ready = self._event(0)
+        # forward: the up projection's K-extension is built beside the gate
+        # projection's GEMM
         main.wait_event(ev["W_gate"])
-        self._gemms("gate", True)
-        main.wait_event(ev["W_up"])
-        self._gemms("up", True)
+        self._ext("gate", "fwd", main)
+        self._gemm("gate", "fwd")
+        e_up = self._ahead("up", "fwd", [x_ready, ev["W_up"]])
+        main.wait_event(e_up)
+        self._gemm("up", "fwd")
         self._prep("X_down", t, inputs, 0)
         main.wait_event(ev["W_down"])
-        self._gemms("down", True)
+        self._ext("down", "fwd", main)
+        self._gemm("down", "fwd")
         self._prep("D_down", t, inputs, 0)
-        # dX of the down projection first: D_gate and D_up (computed from it
-        # in a real layer) are prepared on the side streams while the down
-        # projection's dW runs on the main stream
-        self._gemms("down", False, want_dw=False)
+        d_ready = self._event(0)
+        # backward: dX of the down projection first (D_gate and D_up are
+        # computed from it in a real layer); D_gate is prepared on the main
+        # stream and D_up beside it on the side stream (both are chains of
+        # small kernels that leave room for each other, whereas a chain
+        # running beside a GEMM waits for its tiles); every K-extension that
+        # can be built ahead is built on the companion stream beside an
+        # earlier GEMM; the down projection's dW, needed by nothing in the
+        # step, runs last
+        self._ext("down", "dx", main)
+        e_down_dw = self._ahead("down", "dw", [d_ready])
+        self._gemm("down", "dx")
         dx_ready = self._event(0)
-        self.streams[sd].wait_event(dx_ready)
-        self._prep("D_gate", t, inputs, sd)
-        e_gate = self._event(sd)
         self.streams[sw].wait_event(dx_ready)
-        self._prep("D_up", t, inputs, sw)
-        e_up = self._event(sw)
-        self._gemms("down", False, want_dx=False)
-        main.wait_event(e_gate)
-        self._gemms("gate", False)
-        main.wait_event(e_up)
-        self._gemms("up", False)
+        self._prep("D_up", t, inputs, sw, companion=False)
+        self._prep("D_gate", t, inputs, 0)
+        g_ready = self._event(0)
+        u_ready = self._event(sw)
+        self._ext("gate", "dx", main)
+        e_gate_dw = self._ahead("gate", "dw", [g_ready])
+        self._gemm("gate", "dx")
+        e_up_dx = self._ahead("up", "dx", [u_ready])
+        e_up_dw = self._ahead("up", "dw", [])
+        main.wait_event(e_gate_dw)
+        self._gemm("gate", "dw")
+        main.wait_event(e_up_dx)
+        self._gemm("up", "dx")
+        main.wait_event(e_up_dw)
+        self._gemm("up", "dw")
+        main.wait_event(e_down_dw)
+        self._gemm("down", "dw")
         self.step_done = self._event(0)
 
     def step_flops(self, t):
@@ -339,7 +403,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=256)
     ap.add_argument("--cpu-cols", type=int, default=2048)
-    ap.add_argument("--streams", type=int, default=3,
+    ap.add_argument("--streams", type=int, default=2,
                     help="HIP streams per step (1: every call in order on one stream)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy three times (PMC byte-counter scale)")

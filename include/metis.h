@@ -187,11 +187,38 @@ metis_status metis_gemm_fwd(const metis_qoperand *X, const metis_qoperand *W, fl
 
 /* metis_gemm_bwd -- dX = D-hat W-hat^T (K = n: D needs R_ax1, W needs R_ax1)
  * and dW = X-hat^T D-hat (K = l: X needs R_ax0, D needs R_ax0), the same
- * split embedded in the backward GEMMs (W4A4G4).  dX: l x m, dW: m x n,
- * binary32.  Either output pointer may be NULL to skip that product. */
+ * split embedded in the backward GEMMs (W4A4G4, 整体框架).  dX: l x m,
+ * dW: m x n, binary32.  Either output pointer may be NULL to skip that
+ * product.  The dW product uses the part of ws after the dX product's
+ * region, so ws holds metis_gemm_bwd_workspace(D, W, X) bytes even when only
+ * dW is asked for. */
 metis_status metis_gemm_bwd(const metis_qoperand *D, const metis_qoperand *W, const metis_qoperand *X,
                             float *dX, int64_t lddx, float *dW, int64_t lddw, void *ws,
                             size_t ws_bytes, void *stream);
+
+/* Two-phase form of the split GEMMs.  The low-rank terms of a split product
+ * (P' and G of the forward equation of 关键设计 1, and their counterparts in
+ * dX and dW) ride along K as bf16 hi/lo operands; building them needs only
+ * the quantised operands.  *_prepare builds them into ws on `stream` and
+ * *_prepared runs the main GEMM, reading them from the same ws, so a caller
+ * can build one product's terms on another stream while an earlier GEMM
+ * runs.  Arguments are those of metis_gemm_fwd / metis_gemm_bwd; `which`
+ * selects the backward products (METIS_GRAD_DX | METIS_GRAD_DW).  Contract:
+ * the prepared call names the same operands, ws and ws_bytes as the prepare
+ * call, is ordered after it (same stream or an event), and neither ws nor the
+ * operands change in between; the results then equal those of
+ * metis_gemm_fwd / metis_gemm_bwd bit for bit.  Argument errors return
+ * synchronously as in the one-call form. */
+enum { METIS_GRAD_DX = 1, METIS_GRAD_DW = 2 };
+metis_status metis_gemm_fwd_prepare(const metis_qoperand *X, const metis_qoperand *W, void *ws,
+                                    size_t ws_bytes, void *stream);
+metis_status metis_gemm_fwd_prepared(const metis_qoperand *X, const metis_qoperand *W, float *Y, int64_t ldy,
+                                     void *ws, size_t ws_bytes, void *stream);
+metis_status metis_gemm_bwd_prepare(const metis_qoperand *D, const metis_qoperand *W, const metis_qoperand *X,
+                                    int32_t which, void *ws, size_t ws_bytes, void *stream);
+metis_status metis_gemm_bwd_prepared(const metis_qoperand *D, const metis_qoperand *W, const metis_qoperand *X,
+                                     float *dX, int64_t lddx, float *dW, int64_t lddw, void *ws,
+                                     size_t ws_bytes, void *stream);
 
 /* Waits for `stream`, then returns and clears the current device's numeric
  * failure flag (METIS_OK or METIS_E_NUMERIC). */

@@ -506,14 +506,12 @@ metis_status thin_operand(const metis_q4& B, int nb, int64_t K, uint4* bfrag, hi
   return METIS_OK;
 }
 
-// out (M x N) = L-hat R-hat with L = H S_L F^T + L_R, R^T = E S_R J^T + R_R^T
-// along K.
-metis_status split_product(const SideQ& L, const SideQ& R, int64_t M, int64_t N, int64_t K,
-                           float* C, int64_t ldc, void* ws, size_t ws_bytes, hipStream_t st) {
-  if (L.k > 64 || R.k > 64) return fail(METIS_E_UNSUPPORTED, "split product rank above 64");
-  Carver cv(ws, ws_bytes);
-  SplitWs w = carve_split(cv, M, N, K, L.k, R.k);
-  if (cv.used() > ws_bytes) return fail(METIS_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, cv.used());
+// The K-extension of a split product: P_raw = L_R E, T1^T = R_R F^T and
+// T2 = F E on the thin-product kernel, then the bf16 hi/lo operands
+// a_ext / b_ext of the extra K columns (with S, Lambda and the tensor scales
+// folded in).
+metis_status split_ext(const SideQ& L, const SideQ& R, int64_t M, int64_t N, int64_t K, const SplitWs& w,
+                       hipStream_t st) {
   hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, st, (uint32_t*)w.ones, 0x3F800000u,
                      (int64_t)4);
   LAUNCH_CHECK();
@@ -532,9 +530,8 @@ metis_status split_product(const SideQ& L, const SideQ& R, int64_t M, int64_t N,
     hipLaunchKernelGGL(sum_parts_kernel, dim3(grid1(n2 / 8, 256)), dim3(256), 0, st, w.p2, w.s2, n2, w.t2);
     LAUNCH_CHECK();
   }
-  int64_t kext = 0;
   if (L.k > 0 || R.k > 0) {
-    kext = w.kext;
+    const int64_t kext = w.kext;
     ExtParams e{};
     e.rows = M;
     e.cols = N;
@@ -566,6 +563,29 @@ metis_status split_product(const SideQ& L, const SideQ& R, int64_t M, int64_t N,
                        st, e);
     LAUNCH_CHECK();
   }
+  return METIS_OK;
+}
+
+// Phases of a split product: the K-extension (written into the workspace)
+// and the main GEMM that reads it.  Both phases carve the workspace alike,
+// so they can be issued by separate calls.
+enum SplitPhase { kPhaseExt = 1, kPhaseMain = 2, kPhaseAll = 3 };
+
+// out (M x N) = L-hat R-hat with L = H S_L F^T + L_R, R^T = E S_R J^T + R_R^T
+// along K.
+metis_status split_product(const SideQ& L, const SideQ& R, int64_t M, int64_t N, int64_t K,
+                           float* C, int64_t ldc, void* ws, size_t ws_bytes, hipStream_t st,
+                           int phase = kPhaseAll) {
+  if (L.k > 64 || R.k > 64) return fail(METIS_E_UNSUPPORTED, "split product rank above 64");
+  Carver cv(ws, ws_bytes);
+  SplitWs w = carve_split(cv, M, N, K, L.k, R.k);
+  if (cv.used() > ws_bytes) return fail(METIS_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, cv.used());
+  const int64_t kext = (L.k > 0 || R.k > 0) ? w.kext : 0;
+  metis_status s;
+  if (phase & kPhaseExt) {
+    if ((s = split_ext(L, R, M, N, K, w, st)) != METIS_OK) return s;
+  }
+  if (!(phase & kPhaseMain)) return METIS_OK;
   GemmParams g{M, N, K, L.res->codes, L.res->scales, R.res->codes, R.res->scales,
                L.res->tensor_scale, R.res->tensor_scale, kext, w.a_ext, w.b_ext, C, ldc};
   TimingRec* tr = timing_begin(st, 0, M, N, K, kext);
@@ -825,14 +845,16 @@ QuantParams resid_params(const void* M, int32_t dtype, int64_t rows, int64_t col
 metis_status quantize_factors(const metis_factors* f, int64_t rows, int64_t cols, const metis_config* cfg,
                               uint32_t tag, int64_t step, metis_qoperand* out, const QuantWs& w,
                               hipStream_t st) {
-  metis_status s;
   const int k = f->k;
   QuantParams qp{};
   qp.sr = cfg->rounding == METIS_SR;
   {
-    // factors: U (rows x k) and V (cols x k), blocked along their rows
+    // factors: U (rows x k) and V (cols x k), blocked along their rows, both
+    // in one launch per sweep
+    QuantParams fqs[2];
     for (int which = 0; which < 2; ++which) {
-      QuantParams fq{};
+      QuantParams& fq = fqs[which];
+      fq = QuantParams{};
       const int64_t fr = which == 0 ? rows : cols;
       const metis_q4& o = which == 0 ? out->U : out->V;
       fq.M = which == 0 ? (const void*)f->U : (const void*)f->V;
@@ -849,8 +871,22 @@ metis_status quantize_factors(const metis_factors* f, int64_t rows, int64_t cols
       fq.codes0 = o.codes;
       fq.scales0 = o.scales;
       fq.sg0 = o.tensor_scale;
-      if ((s = run_quant(fq, false, fr, k, st)) != METIS_OK) return s;
+      fq.tiles_per_wg = 1;
     }
+    const int64_t pu = ceil_div<int64_t>(rows, kQT_R), pv = ceil_div<int64_t>(cols, kQT_R);
+    const dim3 grid((unsigned)(pu + pv), (unsigned)ceil_div<int64_t>(k, kQT_C));
+    if (pu + pv > INT32_MAX) return fail(METIS_E_UNSUPPORTED, "operand too large");
+    TimingRec* t1 = timing_begin(st, 1, rows + cols, k, METIS_AXIS0, 0);
+    hipLaunchKernelGGL(quant_amax_pair_kernel, grid, dim3(kQThreads), 0, st, fqs[0], fqs[1], (int)pu);
+    LAUNCH_CHECK();
+    timing_end(t1, st);
+    TimingRec* t2 = timing_begin(st, 2, rows + cols, k, METIS_AXIS0, 0);
+    if (qp.sr)
+      hipLaunchKernelGGL(quant_pair_kernel<true>, grid, dim3(kQThreads), 0, st, fqs[0], fqs[1], (int)pu);
+    else
+      hipLaunchKernelGGL(quant_pair_kernel<false>, grid, dim3(kQThreads), 0, st, fqs[0], fqs[1], (int)pu);
+    LAUNCH_CHECK();
+    timing_end(t2, st);
     out->S = f->S;
   }
   return METIS_OK;
@@ -889,6 +925,61 @@ metis_status stream_after(hipStream_t waiter, hipStream_t from, hipEvent_t e) {
 }  // namespace
 
 // =================================================================== ABI ===
+
+// Y = X-hat W-hat, whole or one phase (the main phase reads the K-extension
+// an earlier extension phase wrote into the same workspace).
+metis_status gemm_fwd_call(const metis_qoperand* X, const metis_qoperand* W, float* Y, int64_t ldy, void* ws,
+                           size_t ws_bytes, void* stream, int phase) {
+  if (!X || !W || ((phase & kPhaseMain) && !Y)) return fail(METIS_E_INVALID, "NULL pointer argument");
+  if (X->cols != W->rows) return fail(METIS_E_INVALID, "inner dimensions differ (%lld vs %lld)",
+                                      (long long)X->cols, (long long)W->rows);
+  if ((phase & kPhaseMain) && ldy < W->cols) return fail(METIS_E_INVALID, "ldy < n");
+  if (!qop_has(X, 1)) return fail(METIS_E_INVALID, "X lacks its residual along m (R_ax1)");
+  if (!qop_has(W, 0)) return fail(METIS_E_INVALID, "W lacks its residual along m (R_ax0)");
+  if (!qop_factors_ok(X) || !qop_factors_ok(W)) return fail(METIS_E_INVALID, "bad factor descriptors");
+  const SideQ L{&X->R_ax1, &X->U, &X->V, X->S, X->k};
+  const SideQ R{&W->R_ax0, &W->V, &W->U, W->S, W->k};
+  return split_product(L, R, X->rows, W->cols, X->cols, Y, ldy, ws, ws_bytes, (hipStream_t)stream, phase);
+}
+
+// Workspace bytes of the dX product; the dW product's region follows it.
+size_t bwd_dx_region(const metis_qoperand* D, const metis_qoperand* W) {
+  return round_up64((int64_t)split_ws_size(D->rows, W->rows, D->cols, D->k, W->k), 256);
+}
+
+// dX = D-hat W-hat^T and dW = X-hat^T D-hat, whole or one phase.
+metis_status gemm_bwd_call(const metis_qoperand* D, const metis_qoperand* W, const metis_qoperand* X, bool do_dx,
+                           float* dX, int64_t lddx, bool do_dw, float* dW, int64_t lddw, void* ws,
+                           size_t ws_bytes, void* stream, int phase) {
+  if (!D || !W || !X) return fail(METIS_E_INVALID, "NULL pointer argument");
+  if (D->cols != W->cols || D->rows != X->rows || X->cols != W->rows)
+    return fail(METIS_E_INVALID, "shapes of D, W, X do not form a linear layer");
+  if (!qop_factors_ok(D) || !qop_factors_ok(W) || !qop_factors_ok(X))
+    return fail(METIS_E_INVALID, "bad factor descriptors");
+  hipStream_t st = (hipStream_t)stream;
+  const bool main = (phase & kPhaseMain) != 0;
+  const size_t off = bwd_dx_region(D, W);
+  metis_status s;
+  if (do_dx) {
+    if (main && lddx < W->rows) return fail(METIS_E_INVALID, "lddx < m");
+    if (!qop_has(D, 1) || !qop_has(W, 1)) return fail(METIS_E_INVALID, "dX needs D and W along n (R_ax1)");
+    const SideQ L{&D->R_ax1, &D->U, &D->V, D->S, D->k};
+    const SideQ R{&W->R_ax1, &W->U, &W->V, W->S, W->k};
+    if ((s = split_product(L, R, D->rows, W->rows, D->cols, dX, lddx, ws, ws_bytes, st, phase)) != METIS_OK)
+      return s;
+  }
+  if (do_dw) {
+    if (main && lddw < D->cols) return fail(METIS_E_INVALID, "lddw < n");
+    if (!qop_has(X, 0) || !qop_has(D, 0)) return fail(METIS_E_INVALID, "dW needs X and D along l (R_ax0)");
+    if (ws_bytes < off) return fail(METIS_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, off);
+    const SideQ L{&X->R_ax0, &X->V, &X->U, X->S, X->k};
+    const SideQ R{&D->R_ax0, &D->V, &D->U, D->S, D->k};
+    if ((s = split_product(L, R, X->cols, D->cols, X->rows, dW, lddw, (uint8_t*)ws + off, ws_bytes - off, st,
+                           phase)) != METIS_OK)
+      return s;
+  }
+  return METIS_OK;
+}
 
 extern "C" {
 
@@ -929,9 +1020,7 @@ size_t metis_gemm_fwd_workspace(const metis_qoperand* X, const metis_qoperand* W
 size_t metis_gemm_bwd_workspace(const metis_qoperand* D, const metis_qoperand* W,
                                 const metis_qoperand* X) {
   if (!D || !W || !X) return 0;
-  const size_t a = split_ws_size(D->rows, W->rows, D->cols, D->k, W->k);
-  const size_t b = split_ws_size(X->cols, D->cols, X->rows, X->k, D->k);
-  return a > b ? a : b;
+  return bwd_dx_region(D, W) + split_ws_size(X->cols, D->cols, X->rows, X->k, D->k);
 }
 
 metis_status metis_decompose(const void* M, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
@@ -1067,45 +1156,38 @@ metis_status metis_prepare_operand(const void* M, int32_t dtype, int64_t rows, i
 
 metis_status metis_gemm_fwd(const metis_qoperand* X, const metis_qoperand* W, float* Y, int64_t ldy,
                             void* ws, size_t ws_bytes, void* stream) {
-  if (!X || !W || !Y) return fail(METIS_E_INVALID, "NULL pointer argument");
-  if (X->cols != W->rows) return fail(METIS_E_INVALID, "inner dimensions differ (%lld vs %lld)",
-                                      (long long)X->cols, (long long)W->rows);
-  if (ldy < W->cols) return fail(METIS_E_INVALID, "ldy < n");
-  if (!qop_has(X, 1)) return fail(METIS_E_INVALID, "X lacks its residual along m (R_ax1)");
-  if (!qop_has(W, 0)) return fail(METIS_E_INVALID, "W lacks its residual along m (R_ax0)");
-  if (!qop_factors_ok(X) || !qop_factors_ok(W)) return fail(METIS_E_INVALID, "bad factor descriptors");
-  const SideQ L{&X->R_ax1, &X->U, &X->V, X->S, X->k};
-  const SideQ R{&W->R_ax0, &W->V, &W->U, W->S, W->k};
-  return split_product(L, R, X->rows, W->cols, X->cols, Y, ldy, ws, ws_bytes, (hipStream_t)stream);
+  return gemm_fwd_call(X, W, Y, ldy, ws, ws_bytes, stream, kPhaseAll);
+}
+
+metis_status metis_gemm_fwd_prepare(const metis_qoperand* X, const metis_qoperand* W, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  return gemm_fwd_call(X, W, nullptr, 0, ws, ws_bytes, stream, kPhaseExt);
+}
+
+metis_status metis_gemm_fwd_prepared(const metis_qoperand* X, const metis_qoperand* W, float* Y, int64_t ldy,
+                                     void* ws, size_t ws_bytes, void* stream) {
+  return gemm_fwd_call(X, W, Y, ldy, ws, ws_bytes, stream, kPhaseMain);
 }
 
 metis_status metis_gemm_bwd(const metis_qoperand* D, const metis_qoperand* W, const metis_qoperand* X,
                             float* dX, int64_t lddx, float* dW, int64_t lddw, void* ws,
                             size_t ws_bytes, void* stream) {
-  if (!D || !W || !X) return fail(METIS_E_INVALID, "NULL pointer argument");
-  if (D->cols != W->cols || D->rows != X->rows || X->cols != W->rows)
-    return fail(METIS_E_INVALID, "shapes of D, W, X do not form a linear layer");
-  if (!qop_factors_ok(D) || !qop_factors_ok(W) || !qop_factors_ok(X))
-    return fail(METIS_E_INVALID, "bad factor descriptors");
-  hipStream_t st = (hipStream_t)stream;
-  metis_status s;
-  if (dX) {
-    if (lddx < W->rows) return fail(METIS_E_INVALID, "lddx < m");
-    if (!qop_has(D, 1) || !qop_has(W, 1)) return fail(METIS_E_INVALID, "dX needs D and W along n (R_ax1)");
-    const SideQ L{&D->R_ax1, &D->U, &D->V, D->S, D->k};
-    const SideQ R{&W->R_ax1, &W->U, &W->V, W->S, W->k};
-    if ((s = split_product(L, R, D->rows, W->rows, D->cols, dX, lddx, ws, ws_bytes, st)) != METIS_OK)
-      return s;
-  }
-  if (dW) {
-    if (lddw < D->cols) return fail(METIS_E_INVALID, "lddw < n");
-    if (!qop_has(X, 0) || !qop_has(D, 0)) return fail(METIS_E_INVALID, "dW needs X and D along l (R_ax0)");
-    const SideQ L{&X->R_ax0, &X->V, &X->U, X->S, X->k};
-    const SideQ R{&D->R_ax0, &D->V, &D->U, D->S, D->k};
-    if ((s = split_product(L, R, X->cols, D->cols, X->rows, dW, lddw, ws, ws_bytes, st)) != METIS_OK)
-      return s;
-  }
-  return METIS_OK;
+  return gemm_bwd_call(D, W, X, dX != nullptr, dX, lddx, dW != nullptr, dW, lddw, ws, ws_bytes, stream,
+                       kPhaseAll);
+}
+
+metis_status metis_gemm_bwd_prepare(const metis_qoperand* D, const metis_qoperand* W, const metis_qoperand* X,
+                                    int32_t which, void* ws, size_t ws_bytes, void* stream) {
+  if (which <= 0 || which > (METIS_GRAD_DX | METIS_GRAD_DW)) return fail(METIS_E_INVALID, "which=%d", which);
+  return gemm_bwd_call(D, W, X, (which & METIS_GRAD_DX) != 0, nullptr, 0, (which & METIS_GRAD_DW) != 0, nullptr,
+                       0, ws, ws_bytes, stream, kPhaseExt);
+}
+
+metis_status metis_gemm_bwd_prepared(const metis_qoperand* D, const metis_qoperand* W, const metis_qoperand* X,
+                                     float* dX, int64_t lddx, float* dW, int64_t lddw, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  return gemm_bwd_call(D, W, X, dX != nullptr, dX, lddx, dW != nullptr, dW, lddw, ws, ws_bytes, stream,
+                       kPhaseMain);
 }
 
 metis_status metis_timing_enable(int32_t capacity) {

@@ -291,8 +291,7 @@ __device__ inline void subtract_lowrank(const uint4* Bf, const half8_t (&uf)[NKK
 // tile and no exposed load latency.  The two buffers are distinct arrays and
 // the loop is unrolled by two so every LDS access names its buffer statically.
 template <int NKK>
-__global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
-void quant_amax_kernel(QuantParams p) {
+__device__ __forceinline__ void quant_amax_body(const QuantParams& p, int64_t bx, int64_t by) {
   constexpr bool HAS_F = NKK > 0;
   constexpr int BFU = HAS_F ? NKK * 2 * 64 : 1;  // uint4 per tile
   __shared__ uint4 Bf0[BFU];
@@ -300,9 +299,9 @@ void quant_amax_kernel(QuantParams p) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5;
-  const int64_t r0 = (int64_t)blockIdx.x * kQT_R;
+  const int64_t r0 = bx * kQT_R;
   const int64_t ntc = ceil_div<int64_t>(p.cols, kQT_C);
-  const int64_t ct0 = (int64_t)blockIdx.y * p.tiles_per_wg;
+  const int64_t ct0 = by * p.tiles_per_wg;
   const int64_t ct1 = min(ntc, ct0 + p.tiles_per_wg);
   const int64_t row = r0 + wave * 32 + (lane & 31);
   const bool row_ok = row < p.rows;
@@ -375,6 +374,22 @@ void quant_amax_kernel(QuantParams p) {
   if (lane == 0) atomicMax(p.amax, __float_as_uint(runmax));
 }
 
+template <int NKK>
+__global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void quant_amax_kernel(QuantParams p) {
+  quant_amax_body<NKK>(p, blockIdx.x, blockIdx.y);
+}
+
+// Two operands in one launch (the factors U and V, quantised directly):
+// workgroups [0, na) take a, the others b.
+__global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void quant_amax_pair_kernel(QuantParams a, QuantParams b, int na) {
+  if ((int)blockIdx.x < na)
+    quant_amax_body<0>(a, blockIdx.x, blockIdx.y);
+  else
+    quant_amax_body<0>(b, (int64_t)blockIdx.x - na, blockIdx.y);
+}
+
 // Pass 2: quantise the residual in the orientations `axes` asks for.  NKK =
 // kc / 16 of the rank-k product (0: no factors, direct quantisation); SR
 // selects stochastic rounding.  A workgroup owns a 128-row panel and walks
@@ -394,7 +409,7 @@ void quant_amax_kernel(QuantParams p) {
 // axis-0 block only for a valid column and 16 valid rows (rows % 16 == 0 for
 // axis 0), so the values computed there need no masking.
 template <int NKK, bool SR>
-__global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void quant_kernel(QuantParams p) {
+__device__ __forceinline__ void quant_body(const QuantParams& p, int64_t bx, int64_t by) {
   constexpr bool HAS_F = NKK > 0;
   constexpr int BFU = HAS_F ? NKK * 2 * 64 : 1;  // uint4 per tile
   __shared__ float R[kQT_R][kQT_C + 4];
@@ -402,9 +417,9 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5;
-  const int64_t r0 = (int64_t)blockIdx.x * kQT_R;
+  const int64_t r0 = bx * kQT_R;
   const int64_t ntc = ceil_div<int64_t>(p.cols, kQT_C);
-  const int64_t ct0 = (int64_t)blockIdx.y * p.tiles_per_wg;
+  const int64_t ct0 = by * p.tiles_per_wg;
   const int64_t ct1 = min(ntc, ct0 + p.tiles_per_wg);
   const int64_t row = r0 + wave * 32 + (lane & 31);
   const bool row_ok = row < p.rows;
@@ -430,7 +445,7 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
       s_g = __fdiv_rn(at, 2688.0f);
       d = __fmul_rn(6.0f, s_g);
     }
-    if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
+    if (bx == 0 && by == 0 && tid == 0) {
       if (p.sg0) p.sg0[0] = s_g;
       if (p.sg1) p.sg1[0] = s_g;
     }
@@ -547,6 +562,21 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     }
     asm volatile("" ::: "memory");  // the slab is rewritten by the next tile
   }
+}
+
+template <int NKK, bool SR>
+__global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void quant_kernel(QuantParams p) {
+  quant_body<NKK, SR>(p, blockIdx.x, blockIdx.y);
+}
+
+// Two operands in one launch, as quant_amax_pair_kernel.
+template <bool SR>
+__global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void quant_pair_kernel(QuantParams a, QuantParams b, int na) {
+  if ((int)blockIdx.x < na)
+    quant_body<0, SR>(a, blockIdx.x, blockIdx.y);
+  else
+    quant_body<0, SR>(b, (int64_t)blockIdx.x - na, blockIdx.y);
 }
 
 }  // namespace metis

@@ -723,7 +723,11 @@ __global__ void proj_prep_kernel(const float* __restrict__ B, int64_t K, int wid
 
 // part[s][r][NSUB*32] = sum over the K blocks of split s of A[src(r)] B, with
 // src(r) = idx[r] (gathered rows) or r; A is bf16 with leading dimension ld.
-// 128 output rows per workgroup, one 32-row slab per wave.
+// 128 output rows per workgroup, one 32-row slab per wave.  The K blocks are
+// software-pipelined: while block kb is multiplied, block kb+1's B fragments
+// land in the other LDS buffer by LDS-DMA and its A rows in registers.  The
+// two buffers are distinct arrays and the loop is unrolled by two, so every
+// LDS access names its buffer statically.
 template <int NTERM, int NSUB>
 __global__ __launch_bounds__(256) void project_mfma_kernel(const uint16_t* __restrict__ A, int64_t ld,
                                                            int64_t rows, const int32_t* __restrict__ idx,
@@ -731,7 +735,8 @@ __global__ __launch_bounds__(256) void project_mfma_kernel(const uint16_t* __res
                                                            int64_t nkb, int64_t kb_per_split,
                                                            float* __restrict__ part) {
   constexpr int FU = proj_frag_u4<NTERM, NSUB>();
-  __shared__ uint4 vs[2 * FU];
+  __shared__ uint4 vs0[FU];
+  __shared__ uint4 vs1[FU];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t r0 = (int64_t)blockIdx.x * 128;
   const int64_t s = blockIdx.y;
@@ -744,34 +749,37 @@ __global__ __launch_bounds__(256) void project_mfma_kernel(const uint16_t* __res
   f32x16_t acc[NSUB];
 #pragma unroll
   for (int n = 0; n < NSUB; ++n) acc[n] = f32x16_t{};
-  const uint4 z = make_uint4(0, 0, 0, 0);
-  for (int64_t kb = kb0; kb < kb1; kb += 2) {
-    const int nb = (int)min((int64_t)2, kb1 - kb);
-    uint4 a[2][4];
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        a[b][j] = (rv && b < nb) ? *(const uint4*)(mrow + (kb + b) * 64 + 8 * j) : z;
-    __syncthreads();
+
+  auto issue = [&](int64_t kb, uint4* buf, uint4 (&a)[4]) {
     const uint4* srcf = (const uint4*)bfrag + kb * FU;
-    for (int e = tid; e < nb * FU; e += 256) vs[e] = srcf[e];
-    __syncthreads();
+    for (int i = wave; i < FU / 64; i += 4) dma16(srcf + i * 64 + lane, (uint8_t*)(buf + i * 64));
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      if (b >= nb) break;
+    for (int j = 0; j < 4; ++j) a[j] = rv ? *(const uint4*)(mrow + kb * 64 + 8 * j) : make_uint4(0, 0, 0, 0);
+  };
+  auto body = [&](const uint4* buf, const uint4 (&a)[4]) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, a[b][j]);
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8_t af = __builtin_bit_cast(bf16x8_t, a[j]);
 #pragma unroll
-        for (int t = 0; t < NTERM; ++t)
+      for (int t = 0; t < NTERM; ++t)
 #pragma unroll
-          for (int n = 0; n < NSUB; ++n) {
-            const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, vs[b * FU + ((t * NSUB + n) * 4 + j) * 64 + lane]);
-            acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, acc[n], 0, 0, 0);
-          }
-      }
+        for (int n = 0; n < NSUB; ++n) {
+          const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, buf[((t * NSUB + n) * 4 + j) * 64 + lane]);
+          acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, acc[n], 0, 0, 0);
+        }
     }
+  };
+
+  uint4 aA[4], aB[4];
+  if (kb0 < kb1) issue(kb0, vs0, aA);
+  for (int64_t kb = kb0; kb < kb1; kb += 2) {
+    ring_barrier();  // block kb has landed in vs0; every wave is done with vs1
+    if (kb + 1 < kb1) issue(kb + 1, vs1, aB);
+    body(vs0, aA);
+    if (kb + 1 >= kb1) break;
+    ring_barrier();  // block kb+1 has landed in vs1; every wave is done with vs0
+    if (kb + 2 < kb1) issue(kb + 2, vs0, aA);
+    body(vs1, aB);
   }
   const int col = lane & 31;
   constexpr int W = NSUB * 32;

@@ -91,6 +91,14 @@ def load():
     lib.metis_gemm_fwd.restype = i32
     lib.metis_gemm_bwd.argtypes = [ctypes.POINTER(_QOperand)] * 3 + [P, i64, P, i64, P, sz, P]
     lib.metis_gemm_bwd.restype = i32
+    lib.metis_gemm_fwd_prepare.argtypes = [ctypes.POINTER(_QOperand)] * 2 + [P, sz, P]
+    lib.metis_gemm_fwd_prepare.restype = i32
+    lib.metis_gemm_fwd_prepared.argtypes = [ctypes.POINTER(_QOperand)] * 2 + [P, i64, P, sz, P]
+    lib.metis_gemm_fwd_prepared.restype = i32
+    lib.metis_gemm_bwd_prepare.argtypes = [ctypes.POINTER(_QOperand)] * 3 + [i32, P, sz, P]
+    lib.metis_gemm_bwd_prepare.restype = i32
+    lib.metis_gemm_bwd_prepared.argtypes = [ctypes.POINTER(_QOperand)] * 3 + [P, i64, P, i64, P, sz, P]
+    lib.metis_gemm_bwd_prepared.restype = i32
     lib.metis_status_sync.argtypes = [P]
     lib.metis_status_sync.restype = i32
     lib.metis_omega_table.argtypes = [P]
@@ -270,6 +278,65 @@ def gemm_bwd(dq, wq, xq, dX=None, dW=None, want_dx=True, want_dw=True, workspace
                               _ptr(dX) if want_dx else None, dX.stride(0) if want_dx else 0,
                               _ptr(dW) if want_dw else None, dW.stride(0) if want_dw else 0,
                               _ptr(ws), ws.numel(), _stream()))
+    return dX, dW
+
+
+GRAD_DX, GRAD_DW = 1, 2
+
+
+def _gemm_ws(need, workspace):
+    if workspace is None or workspace.numel() < need:
+        raise ValueError("the two-phase GEMM needs a workspace of at least %d bytes, shared by both calls" % need)
+    return workspace
+
+
+def gemm_fwd_prepare(xq, wq, workspace):
+    """Build the low-rank K-extension of Y = X-hat W-hat into ``workspace``
+    (metis_gemm_fwd_prepare) on the current stream."""
+    lib = load()
+    xc, wc = xq._c(), wq._c()
+    ws = _gemm_ws(lib.metis_gemm_fwd_workspace(ctypes.byref(xc), ctypes.byref(wc)), workspace)
+    _check(lib.metis_gemm_fwd_prepare(ctypes.byref(xc), ctypes.byref(wc), _ptr(ws), ws.numel(), _stream()))
+
+
+def gemm_fwd_prepared(xq, wq, workspace, Y=None):
+    """Y = X-hat W-hat from a K-extension built by gemm_fwd_prepare into the
+    same workspace (metis_gemm_fwd_prepared)."""
+    lib = load()
+    if Y is None:
+        Y = torch.empty(xq.rows, wq.cols, dtype=torch.float32, device=xq.R_ax1.codes.device)
+    xc, wc = xq._c(), wq._c()
+    ws = _gemm_ws(lib.metis_gemm_fwd_workspace(ctypes.byref(xc), ctypes.byref(wc)), workspace)
+    _check(lib.metis_gemm_fwd_prepared(ctypes.byref(xc), ctypes.byref(wc), _ptr(Y), Y.stride(0), _ptr(ws),
+                                       ws.numel(), _stream()))
+    return Y
+
+
+def gemm_bwd_prepare(dq, wq, xq, workspace, which=GRAD_DX | GRAD_DW):
+    """Build the K-extensions of the backward products selected by ``which``
+    into ``workspace`` (metis_gemm_bwd_prepare) on the current stream."""
+    lib = load()
+    dc, wc, xc = dq._c(), wq._c(), xq._c()
+    ws = _gemm_ws(lib.metis_gemm_bwd_workspace(ctypes.byref(dc), ctypes.byref(wc), ctypes.byref(xc)), workspace)
+    _check(lib.metis_gemm_bwd_prepare(ctypes.byref(dc), ctypes.byref(wc), ctypes.byref(xc), int(which), _ptr(ws),
+                                      ws.numel(), _stream()))
+
+
+def gemm_bwd_prepared(dq, wq, xq, workspace, dX=None, dW=None, want_dx=True, want_dw=True):
+    """(dX, dW) from K-extensions built by gemm_bwd_prepare into the same
+    workspace (metis_gemm_bwd_prepared)."""
+    lib = load()
+    dev = (dq.R_ax1 or dq.R_ax0).codes.device
+    if want_dx and dX is None:
+        dX = torch.empty(dq.rows, wq.rows, dtype=torch.float32, device=dev)
+    if want_dw and dW is None:
+        dW = torch.empty(xq.cols, dq.cols, dtype=torch.float32, device=dev)
+    dc, wc, xc = dq._c(), wq._c(), xq._c()
+    ws = _gemm_ws(lib.metis_gemm_bwd_workspace(ctypes.byref(dc), ctypes.byref(wc), ctypes.byref(xc)), workspace)
+    _check(lib.metis_gemm_bwd_prepared(ctypes.byref(dc), ctypes.byref(wc), ctypes.byref(xc),
+                                       _ptr(dX) if want_dx else None, dX.stride(0) if want_dx else 0,
+                                       _ptr(dW) if want_dw else None, dW.stride(0) if want_dw else 0,
+                                       _ptr(ws), ws.numel(), _stream()))
     return dX, dW
 
 

@@ -84,6 +84,17 @@ def test_argument_errors_are_synchronous():
     _expect(lib.metis_gemm_fwd(ctypes.byref(x), ctypes.byref(w), dummy, 16, dummy, 1 << 20, None),
             metis.E_INVALID)
     assert b"inner" in lib.metis_last_error()
+    # the two-phase GEMM: same checks, plus the product selector
+    _expect(lib.metis_gemm_fwd_prepare(ctypes.byref(x), ctypes.byref(w), dummy, 1 << 20, None), metis.E_INVALID)
+    _expect(lib.metis_gemm_fwd_prepared(ctypes.byref(x), ctypes.byref(w), dummy, 16, dummy, 1 << 20, None),
+            metis.E_INVALID)
+    d = metis._QOperand(64, 16, 0, None)
+    w2 = metis._QOperand(32, 16, 0, None)
+    for which in (0, 4, -1):
+        _expect(lib.metis_gemm_bwd_prepare(ctypes.byref(d), ctypes.byref(w2), ctypes.byref(x), which, dummy,
+                                           1 << 20, None), metis.E_INVALID)
+    _expect(lib.metis_gemm_bwd_prepare(None, ctypes.byref(w2), ctypes.byref(x), metis.GRAD_DX, dummy, 1 << 20,
+                                       None), metis.E_INVALID)
 
 
 def test_workspace_sizes_are_positive_and_monotone():

@@ -9,6 +9,8 @@ subspaces to a largest principal-angle sine <= 1e-3 and singular values to
 relative Frobenius error on seeded quantised operands; the whole pipeline
 from seeded X, W, D is compared end to end."""
 
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -227,6 +229,40 @@ def test_split_gemm_matches_oracle(l, m, n, kx, kw, kd):
             rel_fro(dW.cpu().double().numpy(), wdw))
     say("rel Frobenius errors Y %.2e dX %.2e dW %.2e" % errs)
     assert max(errs) <= GEMM_TOL
+
+
+@pytest.mark.parametrize("l,m,n,k", [(304, 272, 208, 5), (4000, 1024, 4112, 61)])
+def test_two_phase_gemm_equals_one_call(l, m, n, k):
+    """The K-extension built on a second stream by the prepare calls, then
+    the main GEMMs on the first stream: bit-identical to the one-call form,
+    for both products together and for dW alone."""
+    say("two-phase split GEMM l=%d m=%d n=%d k=%d" % (l, m, n, k))
+    X = gpu_qop(synth.qoperand_arrays(l, m, k, seed=11), l, m, k)
+    W = gpu_qop(synth.qoperand_arrays(m, n, k, seed=12), m, n, k)
+    D = gpu_qop(synth.qoperand_arrays(l, n, k, seed=13), l, n, k)
+    Y = metis.gemm_fwd(X, W)
+    dX, dW = metis.gemm_bwd(D, W, X)
+    lib = metis.load()
+    xc, wc, dc = X._c(), W._c(), D._c()
+    wsf = torch.empty(lib.metis_gemm_fwd_workspace(ctypes.byref(xc), ctypes.byref(wc)), dtype=torch.uint8,
+                      device="cuda")
+    wsb = torch.empty(lib.metis_gemm_bwd_workspace(ctypes.byref(dc), ctypes.byref(wc), ctypes.byref(xc)),
+                      dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        metis.gemm_fwd_prepare(X, W, wsf)
+        metis.gemm_bwd_prepare(D, W, X, wsb)
+    torch.cuda.current_stream().wait_stream(side)
+    Y2 = metis.gemm_fwd_prepared(X, W, wsf)
+    dX2, dW2 = metis.gemm_bwd_prepared(D, W, X, wsb)
+    metis.status_sync()
+    assert torch.equal(Y, Y2) and torch.equal(dX, dX2) and torch.equal(dW, dW2)
+    wsb.zero_()
+    metis.gemm_bwd_prepare(D, W, X, wsb, which=metis.GRAD_DW)
+    _, dW3 = metis.gemm_bwd_prepared(D, W, X, wsb, want_dx=False)
+    metis.status_sync()
+    assert torch.equal(dW, dW3)
 
 
 def test_exact_rank_k_recovery_gpu():
