@@ -16,6 +16,10 @@ All inputs are synthetic and resident in HBM before the timed region starts.
 The printed JSON line reports algorithmic TFLOP/s of the whole step, the
 roofline of the dominant kernel (the main split-GEMM kernel, timed live with
 HIP events on its stream) and the CPU oracle timed on a bounded sample.
+Outside the timed region it also measures (unless --no-extras): the copy and
+vendor bf16 GEMM ceilings of the GPU, plain NVFP4 (k = 0) through the same
+kernels on the same workload (step time and quantisation error against
+Metis), and the 1M x 4096 activation (decompose and quantise).
 """
 
 import argparse
@@ -354,6 +358,188 @@ def dense_equiv_flops():
     return 3 * 6 * TOKENS * HIDDEN * FFN
 
 
+# ------------------------------------------------- measurements beside it --
+
+def _median_ms(fn, reps):
+    """Median wall time of fn() on the current stream (HIP events), after one
+    untimed call."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in evs)
+    return ts[len(ts) // 2]
+
+
+def measure_ceilings(dev):
+    """Practical ceilings on this GPU: a plain 1 GiB device copy (GB/s of
+    bytes read + written) and the vendor library's dense bf16 GEMM at the
+    gate projection's shape (torch.matmul -> hipBLASLt)."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    t_copy = _median_ms(lambda: dst.copy_(src), 10)
+    del src, dst
+    a = torch.randn(TOKENS, HIDDEN, device=dev).to(torch.bfloat16)
+    b = torch.randn(HIDDEN, FFN, device=dev).to(torch.bfloat16)
+    t_gemm = _median_ms(lambda: torch.matmul(a, b), 10)
+    del a, b
+    torch.cuda.empty_cache()
+    return {"copy_GBps": round(2 * n / (t_copy * 1e-3) / 1e9, 1),
+            "hipblaslt_bf16_TFLOPs": round(2 * TOKENS * HIDDEN * FFN / (t_gemm * 1e-3) / 1e12, 1),
+            "hipblaslt_bf16_ms": round(t_gemm, 4), "gemm_shape_MNK": [TOKENS, FFN, HIDDEN]}
+
+
+_E2M1 = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def dequant_q4(q4):
+    """Dense binary32 values of one quantised orientation (n_outer x K): the
+    E2M1 code (low nibble = even K index) times its E4M3 block scale times
+    the tensor scale.  Measurement only."""
+    import torch
+    dev = q4.codes.device
+    lut = torch.tensor(_E2M1 + tuple(-v for v in _E2M1), device=dev)
+    c = q4.codes.to(torch.int64)
+    vals = torch.stack((lut[c & 15], lut[c >> 4]), dim=-1).reshape(q4.codes.shape[0], -1)
+    b = q4.scales.to(torch.int64)
+    e, m = (b >> 3) & 15, (b & 7).to(torch.float32)
+    sc = torch.where(e == 0, m * 2.0 ** -9, (8 + m) * torch.pow(2.0, (e - 10).to(torch.float32)))
+    return vals * sc.repeat_interleave(16, dim=1) * q4.tensor_scale.float()
+
+
+def operand_errors(M, qm, qd, V):
+    """Quantisation error of one operand for Metis (qm: factors + residual)
+    and for plain NVFP4 (qd), in the K-along-columns orientation: over the
+    whole matrix, and inside the residual subspace (the orthogonal
+    complement of span(V), V = the cached right factor), where the pages
+    place the small components that one block scale per 16 values flushes."""
+    import torch
+    Mf = M.float()
+    U = dequant_q4(qm.U).T
+    Vq = dequant_q4(qm.V).T
+    metis_hat = (U * qm.S) @ Vq.T + dequant_q4(qm.R_ax1)
+    plain_hat = dequant_q4(qd.R_ax1)
+
+    def perp(A):
+        return A - (A @ V) @ V.T
+    ref_all, ref_perp = torch.linalg.norm(Mf), torch.linalg.norm(perp(Mf))
+    # small values: below 1/8 of their 16-block's largest magnitude
+    a = Mf.abs()
+    small = a < a.reshape(a.shape[0], -1, 16).amax(dim=2).repeat_interleave(16, dim=1) / 8
+    out = {}
+    for name, hat in (("metis", metis_hat), ("nvfp4", plain_hat)):
+        E = hat - Mf
+        out[name] = {"all": round(float(torch.linalg.norm(E) / ref_all), 6),
+                     "residual_subspace": round(float(torch.linalg.norm(perp(E)) / ref_perp), 6),
+                     "small_values_to_zero": round(float(((hat == 0) & small & (Mf != 0)).sum() / small.sum()), 6)}
+    return out
+
+
+def measure_direct(mlp, inputs, t_last, mlp_ms=None, steps=4, warmup=2, sample_rows=256):
+    """The pages' comparison point: plain NVFP4 (k = 0) through the same
+    quantiser and GEMM kernels.  Times whole steps (eight operands quantised
+    in both orientations, the nine GEMMs) on one stream, and compares the
+    forward outputs of both paths on the last timed step's inputs with the
+    exact product X W on sampled rows."""
+    import torch
+    m = mlp.metis
+    dev = mlp.streams[0].device
+    q = {name: m.QOperand(op.rows, op.cols, 0, m.AXIS0 | m.AXIS1, dev) for name, op in mlp.ops.items()}
+    out = {name: tuple(torch.empty_like(t) for t in mlp.out[name]) for name in mlp.out}
+    ws = torch.empty(max(max(a.numel(), b.numel()) for a, b in mlp.gws.values()), dtype=torch.uint8, device=dev)
+
+    def step(t):
+        for name, op in mlp.ops.items():
+            M = inputs[name][t % len(inputs[name])]
+            m.quantize(M, mlp.cfg, op.tag, t, m.AXIS0 | m.AXIS1, out=q[name], workspace=mlp.ws[0])
+        for name, x, w, d in PROJECTIONS:
+            Y, dX, dW = out[name]
+            m.gemm_fwd(q[x], q[w], Y=Y, workspace=ws)
+            m.gemm_bwd(q[d], q[w], q[x], dX=dX, dW=dW, workspace=ws)
+
+    for t in range(warmup):
+        step(t)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for t in range(warmup, warmup + steps):
+        step(t)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    step(t_last)
+    m.status_sync()
+    err = {}
+    for name, x, w, d in PROJECTIONS:
+        X = inputs[x][t_last % len(inputs[x])]
+        W = inputs[w][t_last % len(inputs[w])]
+        idx = torch.arange(0, X.shape[0], X.shape[0] // sample_rows, device=dev)
+        exact = X[idx].float() @ W.float()
+
+        def rel(Y):
+            return float(torch.linalg.norm(Y[idx] - exact) / torch.linalg.norm(exact))
+        err[name] = {"metis": round(rel(mlp.out[name][0]), 6), "nvfp4": round(rel(out[name][0]), 6)}
+    ops = {}
+    for name in ("X_gu", "W_gate", "D_gate"):
+        M = inputs[name][t_last % len(inputs[name])]
+        ops[name] = operand_errors(M, mlp.q[name], q[name], mlp.factors[name].V)
+    return {"ms_per_step": round(ms, 3), "streams": 1, "metis_over_nvfp4_time": round(mlp_ms / ms, 4) if mlp_ms else None,
+            "y_rel_fro_err_vs_exact": err,
+            "y_sample": "forward Y of each projection on %d evenly spaced token rows of the step-%d inputs"
+                        % (sample_rows, t_last),
+            "operand_rel_err": ops,
+            "operand_note": "||M-hat - M|| / ||M|| over the matrix; the same ratio inside the orthogonal "
+                            "complement of the cached right factor V (residual subspace); the fraction of values "
+                            "below 1/8 of their 16-block's largest magnitude that dequantise to 0"}
+
+
+def measure_c4(dev, copy_gbps):
+    """The 1M x 4096 activation (4.3e9 elements, l_k = 10486): decompose at a
+    refresh and at a cached step, and the residual quantisation in both
+    orientations, each timed alone."""
+    import torch
+    from spectral_split_quantized_amd import metis, synth
+    c4 = synth.CONFIGS[4]
+    rows, cols = c4["X"]
+    k = c4["k"]
+    M, _ = synth.anisotropic_fast(rows, cols, synth.FRAC_X, synth.gen_seed(4, "X"), device=dev)
+    torch.cuda.synchronize()
+    cfg = metis.make_config(k=k, s=c4["s"], l_k=c4["l_k"], refresh=REFRESH, rounding=metis.SR, seed=0)
+    tag = metis.make_tag(0, metis.OPERAND_X)
+    f = metis.Factors(rows, cols, k, dev)
+    q = metis.QOperand(rows, cols, k, metis.AXIS0 | metis.AXIS1, dev)
+    res = {}
+    for label, t in (("decompose_refresh_ms", 0), ("decompose_cached_ms", 1)):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        metis.decompose(M, cfg, True, tag, t, f)
+        b.record()
+        torch.cuda.synchronize()
+        res[label] = round(a.elapsed_time(b), 3)
+    t_q = _median_ms(lambda: metis.quantize(M, cfg, tag, 1, metis.AXIS0 | metis.AXIS1, factors=f, out=q), 5)
+    metis.status_sync()
+    # algorithmic bytes per element: M read twice (bf16), codes and scales of
+    # two orientations, and the rank-k reconstruction operands
+    per_elem = 2 * 2 + 2 * (0.5 + 1 / 16) + 2 * 4 * k / cols
+    gbs = rows * cols * per_elem / (t_q * 1e-3) / 1e9
+    res.update({"quantize_ms": round(t_q, 3), "quantize_GBps": round(gbs, 1),
+                "quantize_frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                "quantize_frac_copy": round(gbs / copy_gbps, 4) if copy_gbps else None,
+                "bytes_per_elem": round(per_elem, 4), "shape": [rows, cols], "k": k, "l_k": c4["l_k"]})
+    del M, f, q
+    torch.cuda.empty_cache()
+    return res
+
+
 # ------------------------------------------------------------ CPU baseline --
 
 def cpu_baseline(inputs_cpu, tokens, ncols):
@@ -401,10 +587,12 @@ def main():
     ap.add_argument("--steps", type=int, default=16)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=256)
-    ap.add_argument("--cpu-cols", type=int, default=2048)
+    ap.add_argument("--cpu-tokens", type=int, default=512)
+    ap.add_argument("--cpu-cols", type=int, default=4096)
     ap.add_argument("--streams", type=int, default=2,
                     help="HIP streams per step (1: every call in order on one stream)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the ceilings, the plain-NVFP4 comparison and the 1M x 4096 activation")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy three times (PMC byte-counter scale)")
     args = ap.parse_args()
@@ -503,6 +691,18 @@ def main():
             rsvd_ms["%s_%s" % (name, label)] = round(a.elapsed_time(b), 3)
     metis.status_sync()
 
+    extras = {}
+    if not args.no_extras:
+        log("measuring the copy and vendor-GEMM ceilings")
+        extras["ceilings"] = measure_ceilings(dev)
+        log("plain NVFP4 (k = 0) on the same workload")
+        extras["direct_nvfp4"] = measure_direct(mlp, inputs, args.warmup + args.steps - 1, ms_per_step)
+        log("1M x 4096 activation")
+        extras["c4_activation"] = measure_c4(dev, extras["ceilings"]["copy_GBps"])
+        ceil_tf = extras["ceilings"]["hipblaslt_bf16_TFLOPs"]
+        roofline["frac_vs_hipblaslt_bf16"] = round(g_tflops / ceil_tf, 4) if ceil_tf else None
+        streaming["frac_vs_copy"] = round(streaming["achieved"] / extras["ceilings"]["copy_GBps"], 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
@@ -525,6 +725,7 @@ def main():
            "algorithmic_flop_per_step": round(flops / args.steps),
            "roofline": roofline, "streaming_roofline": streaming, "rsvd_ms": rsvd_ms,
            "cpu_baseline": cpu}
+    out.update(extras)
     print(json.dumps(out), flush=True)
     return 0
 
