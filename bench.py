@@ -156,9 +156,9 @@ class MetisMLP:
     caches, quantised operands, outputs, one workspace per stream and one per
     split product.
 
-    One step follows the layer's data dependencies on the main stream, a
-    side stream and the main stream's companion: the weights (known when
-    the step starts) are decomposed and quantised on the side stream while
+    One step follows the layer's data dependencies on the main stream, two
+    side streams and the main stream's companion: the weights (known when
+    the step starts) are decomposed and quantised on the side streams while
     the main stream handles X_gu; the forward GEMMs wait for their weight;
     X_down follows the gate/up GEMMs and D_down the down GEMM (in a real
     layer they are computed from them); D_gate and D_up both come from the
@@ -169,7 +169,7 @@ class MetisMLP:
     ready early is built on the companion beside an earlier GEMM.  With
     streams=1 everything runs in that order on one stream."""
 
-    def __init__(self, device, streams=2):
+    def __init__(self, device, streams=3):
         import torch
         from spectral_split_quantized_amd import metis
         self.metis = metis
@@ -202,7 +202,7 @@ class MetisMLP:
                             device=device),
                 torch.empty(lib.metis_gemm_bwd_workspace(ctypes.byref(dc), ctypes.byref(wc), ctypes.byref(xc)),
                             dtype=torch.uint8, device=device))
-        self.nstreams = max(1, min(2, int(streams)))
+        self.nstreams = max(1, min(3, int(streams)))
         # default-priority streams only
         self.streams = [torch.cuda.current_stream(device)] + \
             [torch.cuda.Stream(device=device) for _ in range(self.nstreams - 1)]
@@ -287,9 +287,12 @@ class MetisMLP:
         ev = {}
         # the weights (known when the step starts, off the critical path)
         # keep their rediagonalisation on their own stream
-        for w in ("W_gate", "W_up", "W_down"):
-            self._prep(w, t, inputs, sw, companion=False)
-            ev[w] = self._event(sw)
+        # (W_up on a second side stream, so that at a refresh step its
+        # sketch runs beside W_gate's instead of after it)
+        sw2 = 2 if self.nstreams > 2 else sw
+        for w, si in (("W_gate", sw), ("W_up", sw2), ("W_down", sw)):
+            self._prep(w, t, inputs, si, companion=False)
+            ev[w] = self._event(si)
         self._prep("X_gu", t, inputs, 0)
         x_ready = self._event(0)
         # forward: the up projection's K-extension is built beside the gate
@@ -589,7 +592,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=512)
     ap.add_argument("--cpu-cols", type=int, default=4096)
-    ap.add_argument("--streams", type=int, default=2,
+    ap.add_argument("--streams", type=int, default=3,
                     help="HIP streams per step (1: every call in order on one stream)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the ceilings, the plain-NVFP4 comparison and the 1M x 4096 activation")
