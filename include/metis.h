@@ -235,6 +235,10 @@ metis_status metis_status_sync(void *stream);
  * number written. */
 metis_status metis_timing_enable(int32_t capacity);
 int32_t metis_timing_read(float *ms, int64_t *shape, int32_t max_records);
+/* Restricts the recorded kinds to the bits of mask (bit k: kind k; all kinds
+ * by default).  Each record adds two event packets to the stream, so a caller
+ * timing a whole step records only the kinds it needs. */
+metis_status metis_timing_kinds(int32_t mask);
 
 /* Host-only helpers (no GPU needed) exposing the library's own definitions
  * of its random draws, for verification against an independent model.

@@ -64,9 +64,10 @@ std::mutex g_tmu;
 std::vector<TimingRec> g_trecs;
 size_t g_tused = 0;
 bool g_timing = false;
+uint32_t g_tkinds = ~0u;  // kinds recorded while timing is enabled
 
 TimingRec* timing_begin(hipStream_t st, int64_t kind, int64_t d0, int64_t d1, int64_t d2, int64_t d3) {
-  if (!g_timing) return nullptr;
+  if (!g_timing || kind < 0 || kind > 31 || !((g_tkinds >> kind) & 1u)) return nullptr;
   std::lock_guard<std::mutex> lk(g_tmu);
   if (g_tused >= g_trecs.size()) return nullptr;
   TimingRec* r = &g_trecs[g_tused++];
@@ -1188,6 +1189,12 @@ metis_status metis_gemm_bwd_prepared(const metis_qoperand* D, const metis_qopera
                                      size_t ws_bytes, void* stream) {
   return gemm_bwd_call(D, W, X, dX != nullptr, dX, lddx, dW != nullptr, dW, lddw, ws, ws_bytes, stream,
                        kPhaseMain);
+}
+
+metis_status metis_timing_kinds(int32_t mask) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_tkinds = (uint32_t)mask;
+  return METIS_OK;
 }
 
 metis_status metis_timing_enable(int32_t capacity) {

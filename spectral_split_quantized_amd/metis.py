@@ -104,6 +104,8 @@ def load():
     lib.metis_omega_table.argtypes = [P]
     lib.metis_omega_table.restype = None
     lib.metis_timing_enable.argtypes = [i32]
+    lib.metis_timing_kinds.argtypes = [i32]
+    lib.metis_timing_kinds.restype = i32
     lib.metis_timing_enable.restype = i32
     lib.metis_timing_read.argtypes = [P, P, i32]
     lib.metis_timing_read.restype = i32
@@ -365,6 +367,12 @@ def philox_block(ctr, key):
 def timing_enable(capacity):
     """Start recording HIP events around the main GEMM and quantiser kernels."""
     _check(load().metis_timing_enable(int(capacity)))
+
+
+def timing_kinds(mask):
+    """Record only the kernel kinds whose bits are set (bit 0: main GEMM,
+    1: amax sweep, 2: quantise sweep)."""
+    _check(load().metis_timing_kinds(int(mask)))
 
 
 def timing_read(max_records=1 << 16):
