@@ -680,8 +680,9 @@ def main():
     qrecs = metis.timing_read(64)
     metis.timing_enable(0)
     metis.timing_kinds(-1)
-    q1 = [r[1] for r in qrecs if r[0] == 1][1:]
-    q2 = [r[1] for r in qrecs if r[0] == 2][1:]
+    # the residual sweeps only (the factor sweeps are recorded too)
+    q1 = [r[1] for r in qrecs if r[0] == 1 and r[2] == xd.rows and r[3] == xd.cols][1:]
+    q2 = [r[1] for r in qrecs if r[0] == 2 and r[2] == xd.rows and r[3] == xd.cols][1:]
     q_ms = sorted(a + b for a, b in zip(q1, q2))[len(q2) // 2]
     # M read by both sweeps (bf16), codes and scales of two orientations, and
     # the rank-k reconstruction operands

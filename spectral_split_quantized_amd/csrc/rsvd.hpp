@@ -374,11 +374,11 @@ __global__ __launch_bounds__(256) void cholinv_kernel(const double* __restrict__
       for (int i = j + 1 + tid; i < n; i += 256) L[i][j] /= piv;
       __syncthreads();
       if (tid == 0) L[j][j] = piv;
-      // trailing lower triangle: L[i][k] -= L[i][j] L[k][j], j < k <= i
-      const int m = n - j - 1;
-      for (int e = tid; e < m * m; e += 256) {
-        const int i = j + 1 + e / m, k = j + 1 + e % m;
-        if (k <= i) L[i][k] -= L[i][j] * L[k][j];
+      // trailing lower triangle: L[i][k] -= L[i][j] L[k][j], j < k <= i;
+      // thread (tid / 16, tid % 16) strides rows and columns by 16
+      for (int i = j + 1 + (tid >> 4); i < n; i += 16) {
+        const double lij = L[i][j];
+        for (int k = j + 1 + (tid & 15); k <= i; k += 16) L[i][k] -= lij * L[k][j];
       }
       __syncthreads();
     }
@@ -395,11 +395,11 @@ __global__ __launch_bounds__(256) void cholinv_kernel(const double* __restrict__
     // row k: X[k][:] /= L[k][k] (only columns <= k are nonzero)
     for (int b = tid; b <= k; b += 256) X[k][b] /= L[k][k];
     __syncthreads();
-    // rows below: X[i][b] -= L[i][k] X[k][b]
-    const int m = n - k - 1;
-    for (int e = tid; e < m * (k + 1); e += 256) {
-      const int i = k + 1 + e / (k + 1), b = e % (k + 1);
-      X[i][b] -= L[i][k] * X[k][b];
+    // rows below: X[i][b] -= L[i][k] X[k][b], thread (tid / 16, tid % 16)
+    // striding rows and columns by 16
+    for (int i = k + 1 + (tid >> 4); i < n; i += 16) {
+      const double lik = L[i][k];
+      for (int b = tid & 15; b <= k; b += 16) X[i][b] -= lik * X[k][b];
     }
     __syncthreads();
   }
