@@ -210,7 +210,7 @@ class MetisMLP:
         # the critical path runs there while their residual is quantised
         self.side = torch.cuda.Stream(device=device) if self.nstreams > 1 else None
         self.ws = [torch.empty(need, dtype=torch.uint8, device=device) for _ in self.streams]
-        self.step_done = None
+        self.free_gate = self.free_up = None
         log("  workspace %.1f MB x %d streams, %.1f MB for the split products"
             % (need / 1e6, self.nstreams, sum(a.numel() + b.numel() for a, b in self.gws.values()) / 1e6))
 
@@ -280,16 +280,20 @@ class MetisMLP:
     def step(self, t, inputs):
         main = self.streams[0]
         sw = 1 if self.nstreams > 1 else 0
-        # the side stream overwrites quantised operands the previous step read
-        if self.step_done is not None:
-            for s in self.streams[1:]:
-                s.wait_event(self.step_done)
-        ev = {}
-        # the weights (known when the step starts, off the critical path)
-        # keep their rediagonalisation on their own stream
-        # (W_up on a second side stream, so that at a refresh step its
-        # sketch runs beside W_gate's instead of after it)
         sw2 = 2 if self.nstreams > 2 else sw
+        # a side stream overwrites a weight's quantised operand once the
+        # previous step's last GEMM reading it is done: the gate projection's
+        # dW for W_gate (and the down projection's dX before it for W_down),
+        # the up projection's dW for W_up.  The weights of a step are thus
+        # prepared beside the previous step's last GEMMs, as an optimizer
+        # updates each weight as soon as its gradient is ready.
+        if self.free_gate is not None:
+            self.streams[sw].wait_event(self.free_gate)
+            self.streams[sw2].wait_event(self.free_up)
+        ev = {}
+        # the weights keep their rediagonalisation on their own stream (W_up
+        # on the second side stream, so that at a refresh step its sketch
+        # runs beside W_gate's instead of after it)
         for w, si in (("W_gate", sw), ("W_up", sw2), ("W_down", sw)):
             self._prep(w, t, inputs, si, companion=False)
             ev[w] = self._event(si)
@@ -333,13 +337,14 @@ class MetisMLP:
         e_up_dw = self._ahead("up", "dw", [])
         main.wait_event(e_gate_dw)
         self._gemm("gate", "dw")
+        self.free_gate = self._event(0)
         main.wait_event(e_up_dx)
         self._gemm("up", "dx")
         main.wait_event(e_up_dw)
         self._gemm("up", "dw")
+        self.free_up = self._event(0)
         main.wait_event(e_down_dw)
         self._gemm("down", "dw")
-        self.step_done = self._event(0)
 
     def step_flops(self, t):
         refresh = (t % REFRESH) == 0
