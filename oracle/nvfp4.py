@@ -29,11 +29,18 @@ along, i.e. the GEMM's reduction axis):
   scales uint8 [n_outer, K/16] E4M3 bytes
   s_g    float32 scalar
 For axis 1 (K = columns) n_outer is the row count; for axis 0 (K = rows) the
-tensor is taken transposed, so n_outer is the column count.  The stochastic
-rounding draw of an element is indexed by its position in the quantised
-orientation's own row-major layout (n_outer x K): e = i * cols + j along axis
-1 and e = j * rows + i along axis 0, so sixteen consecutive elements of a block
-always share two Philox blocks.
+tensor is taken transposed, so n_outer is the column count.
+
+Stochastic rounding draws (readings; the pages name no random stream):
+  draws="own"     an element's draw is indexed by its position in the
+                  quantised orientation's own row-major layout (n_outer x K):
+                  e = i * cols + j along axis 1, e = j * rows + i along axis 0
+                  (the factors U and V, quantised along one axis only);
+  draws="matrix"  by its position in the tensor's row-major layout,
+                  e = i * cols + j along either axis, so an operand's two
+                  orientations round each element with the same uniform.
+                  Each orientation's rounding stays unbiased on its own; the
+                  Philox work per element of an operand halves.
 """
 
 import numpy as np
@@ -70,17 +77,20 @@ def tensor_scale(amax):
     return s_g, d
 
 
-def quantize(x, axis, rounding="rne", seed=0, tag=0, step=0, amax=None, origin=None):
+def quantize(x, axis, rounding="rne", seed=0, tag=0, step=0, amax=None, origin=None, draws="own"):
     """Quantise a 2-D binary32 tensor along ``axis``; returns a QTensor.
 
-    ``rounding`` is "rne" or "sr" (Philox uniforms with seed/tag/step).
+    ``rounding`` is "rne" or "sr" (Philox uniforms with seed/tag/step, laid
+    out as ``draws`` says: "own" or "matrix", see the module docstring).
 
     To quantise part of a larger tensor, pass the larger tensor's ``amax``
-    (its exact max |x|, Q1) and ``origin = (outer0, k0, K_full)``: the part's
-    first element sits at row outer0, column k0 of the larger tensor's
-    quantised orientation (n_outer x K_full), which fixes the Philox index of
-    every element.  K blocks of the part must be whole blocks of the larger
-    tensor (k0 % 16 == 0)."""
+    (its exact max |x|, Q1) and ``origin``, which fixes the Philox index of
+    every element.  With draws="own", origin = (outer0, k0, K_full): the
+    part's first element sits at row outer0, column k0 of the larger tensor's
+    quantised orientation (n_outer x K_full).  With draws="matrix", origin =
+    (row0, col0, cols_full): it sits at row row0, column col0 of the larger
+    tensor itself.  K blocks of the part must be whole blocks of the larger
+    tensor."""
     x = np.asarray(x, dtype=np.float32)
     if x.ndim != 2:
         raise ValueError("2-D input expected")
@@ -94,9 +104,16 @@ def quantize(x, axis, rounding="rne", seed=0, tag=0, step=0, amax=None, origin=N
     if amax is None:
         amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0)
     amax = np.float32(amax)
-    outer0, k0, k_full = (0, 0, K) if origin is None else (int(origin[0]), int(origin[1]), int(origin[2]))
-    if k0 % BLOCK or k0 + K > k_full:
-        raise ValueError("origin must place whole blocks inside the larger tensor")
+    if draws not in ("own", "matrix"):
+        raise ValueError("draws must be 'own' or 'matrix'")
+    if draws == "own":
+        outer0, k0, k_full = (0, 0, K) if origin is None else (int(origin[0]), int(origin[1]), int(origin[2]))
+        if k0 % BLOCK or k0 + K > k_full:
+            raise ValueError("origin must place whole blocks inside the larger tensor")
+    else:
+        row0, col0, cols_full = (0, 0, cols) if origin is None else (int(origin[0]), int(origin[1]), int(origin[2]))
+        if (row0 if axis == 0 else col0) % BLOCK or col0 + cols > cols_full:
+            raise ValueError("origin must place whole blocks inside the larger tensor")
     s_g, d = tensor_scale(amax)
     ax = np.abs(xt).astype(np.float64).reshape(n_outer, K // BLOCK, BLOCK)
     a_b = ax.max(axis=2)
@@ -115,9 +132,16 @@ def quantize(x, axis, rounding="rne", seed=0, tag=0, step=0, amax=None, origin=N
     if rounding == "rne":
         m = formats.e2m1_rne(y)
     elif rounding == "sr":
-        # index in the (n_outer x K_full) layout of the whole tensor
-        et = ((np.arange(n_outer, dtype=np.uint64) + np.uint64(outer0))[:, None] * np.uint64(k_full)
-              + (np.arange(K, dtype=np.uint64) + np.uint64(k0))[None, :]).ravel()
+        if draws == "own":
+            # index in the (n_outer x K_full) layout of the whole tensor
+            et = ((np.arange(n_outer, dtype=np.uint64) + np.uint64(outer0))[:, None] * np.uint64(k_full)
+                  + (np.arange(K, dtype=np.uint64) + np.uint64(k0))[None, :])
+        else:
+            # index in the tensor's own row-major layout, in xt's order
+            e = ((np.arange(rows, dtype=np.uint64) + np.uint64(row0))[:, None] * np.uint64(cols_full)
+                 + (np.arange(cols, dtype=np.uint64) + np.uint64(col0))[None, :])
+            et = e if axis == 1 else e.T
+        et = np.ascontiguousarray(et).ravel()
         u = philox.uniform_from_halves(philox.halves(et, seed, tag, step))
         m = formats.e2m1_sr(y, u.reshape(n_outer, K // BLOCK, BLOCK))
     else:

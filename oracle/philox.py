@@ -35,9 +35,10 @@ PHILOX_W0 = 0x9E3779B9
 PHILOX_W1 = 0xBB67AE85
 ROUNDS = 10
 
-# tag roles (bits 8..11 of the 32-bit tag word)
-ROLE_RESID_AX0 = 0
-ROLE_RESID_AX1 = 1
+# tag roles (bits 8..11 of the 32-bit tag word); both quantised orientations
+# of an operand (its residual, or the operand itself) draw from ROLE_RESID,
+# role 1 is unused
+ROLE_RESID = 0
 ROLE_U = 2
 ROLE_V = 3
 ROLE_OMEGA = 4

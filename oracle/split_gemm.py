@@ -65,12 +65,12 @@ def quantize_operand(m, u, s, v, rounding, seed, tag, step, axes=(0, 1), m_r=Non
                                 philox.with_role(tag, philox.ROLE_U), step)
         op.v_q = nvfp4.quantize(np.asarray(v, np.float32), 0, rounding, seed,
                                 philox.with_role(tag, philox.ROLE_V), step)
+    # both orientations of the residual round each element with one draw
+    resid_tag = philox.with_role(tag, philox.ROLE_RESID)
     if 0 in axes:
-        op.r_ax0 = nvfp4.quantize(m_r, 0, rounding, seed,
-                                  philox.with_role(tag, philox.ROLE_RESID_AX0), step)
+        op.r_ax0 = nvfp4.quantize(m_r, 0, rounding, seed, resid_tag, step, draws="matrix")
     if 1 in axes:
-        op.r_ax1 = nvfp4.quantize(m_r, 1, rounding, seed,
-                                  philox.with_role(tag, philox.ROLE_RESID_AX1), step)
+        op.r_ax1 = nvfp4.quantize(m_r, 1, rounding, seed, resid_tag, step, draws="matrix")
     return op
 
 

@@ -27,8 +27,7 @@ constexpr uint32_t kPhiloxW1 = 0xBB67AE85u;
 
 // Draw roles, bits 8..11 of the tag.
 enum : uint32_t {
-  kRoleResidAx0 = 0,
-  kRoleResidAx1 = 1,
+  kRoleResid = 0,  // both orientations of an operand (role 1 unused)
   kRoleU = 2,
   kRoleV = 3,
   kRoleOmega = 4,

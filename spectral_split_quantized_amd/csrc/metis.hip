@@ -824,8 +824,10 @@ QuantParams resid_params(const void* M, int32_t dtype, int64_t rows, int64_t col
   qp.axes = axes;
   qp.sr = cfg->rounding == METIS_SR;
   qp.seed = cfg->seed;
-  qp.tag0 = tag_with_role(tag, kRoleResidAx0);
-  qp.tag1 = tag_with_role(tag, kRoleResidAx1);
+  // both orientations round each element with its draw at its row-major
+  // position in M
+  qp.tag0 = qp.tag1 = tag_with_role(tag, kRoleResid);
+  qp.shared_draws = 1;
   qp.step = (uint32_t)step;
   qp.resid = residual_out;
   if (axes & METIS_AXIS0) {

@@ -132,6 +132,10 @@ struct QuantParams {
   float* resid;  // optional rows x cols export
   int axes;      // bit 0: axis 0, bit 1: axis 1
   int sr;
+  // SR draws: 1 = by the element's row-major position in M (tag1), shared by
+  // both orientations; 0 = by its position in each orientation's own layout
+  // (tag0 along axis 0, tag1 along axis 1)
+  int shared_draws;
   uint64_t seed;
   uint32_t tag0, tag1, step;
   int tiles_per_wg;  // column tiles walked by one workgroup
@@ -170,6 +174,16 @@ __device__ inline QuantBlockOut quant_block16(const float (&x)[16], const uint32
       o.hi |= code << (4 * (i - 8));
   }
   return o;
+}
+
+// Complemented 16-bit draws of n <= 16 consecutive indices e0 .. e0+n-1 at
+// any alignment (one Philox block per element; the ragged edge only).
+__device__ inline void draws16_any(uint64_t e0, int n, uint32_t tag, uint32_t step, uint64_t seed,
+                                   uint32_t (&hc)[16]) {
+  for (int i = 0; i < 16; ++i) {
+    const uint64_t e = e0 + (uint64_t)i;
+    hc[i] = i < n ? 0xFFFFu - philox_half_of(philox_block(e >> 3, tag, step, seed), (uint32_t)(e & 7)) : 0u;
+  }
 }
 
 // Complemented 16-bit draws (0xFFFF - h) of 16 consecutive indices
@@ -414,6 +428,9 @@ __device__ __forceinline__ void quant_body(const QuantParams& p, int64_t bx, int
   constexpr int BFU = HAS_F ? NKK * 2 * 64 : 1;  // uint4 per tile
   __shared__ float R[kQT_R][kQT_C + 4];
   __shared__ uint4 Bf[BFU];
+  // complemented draws of the tile in M's layout, read back by axis 0 when
+  // the two orientations share them (row pitch 72: 16-byte aligned rows)
+  __shared__ __attribute__((aligned(16))) uint16_t H[SR ? kQT_R : 1][SR ? kQT_C + 8 : 1];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5;
@@ -452,6 +469,9 @@ __device__ __forceinline__ void quant_body(const QuantParams& p, int64_t bx, int
   }
   const bool ax0 = (p.axes & 1) != 0;
   const bool ax1 = (p.axes & 2) != 0;
+  const bool shared = SR && p.shared_draws != 0;
+  // row-major draws aligned to Philox blocks (the fast path's condition)
+  const bool draws_aligned = (p.cols & 7) == 0;
 
   // tile ct's vcat fragments -> Bf (LDS-DMA) and, on the fast path, its two
   // 16-column blocks of this lane's row -> raw
@@ -501,9 +521,24 @@ __device__ __forceinline__ void quant_body(const QuantParams& p, int64_t bx, int
         float* dst = p.resid + row * p.cols + gc;
         for (int i = 0; i < n; ++i) dst[i] = x[b][i];
       }
+      uint32_t hc[16];
+      if (SR && (ax1 || (ax0 && shared))) {
+        const uint64_t e0 = (uint64_t)row * (uint64_t)p.cols + (uint64_t)gc;
+        const int n = (int)min((int64_t)16, p.cols - gc);
+        if (n == 16 && draws_aligned)
+          draws16(e0, p.tag1, p.step, p.seed, hc);
+        else
+          draws16_any(e0, n, p.tag1, p.step, p.seed, hc);
+        if (ax0 && shared) {
+          const int lr = wave * 32 + (lane & 31), lc = 32 * b + 16 * hh;
+          uint32_t w[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) w[i] = hc[2 * i] | (hc[2 * i + 1] << 16);
+          *(uint4*)&H[lr][lc] = make_uint4(w[0], w[1], w[2], w[3]);
+          *(uint4*)&H[lr][lc + 8] = make_uint4(w[4], w[5], w[6], w[7]);
+        }
+      }
       if (ax1) {
-        uint32_t hc[16];
-        if (SR) draws16((uint64_t)row * (uint64_t)p.cols + (uint64_t)gc, p.tag1, p.step, p.seed, hc);
         const QuantBlockOut o = quant_block16(x[b], hc, s_g, d, SR);
         *(uint2*)(p.codes1 + row * (p.cols >> 1) + (gc >> 1)) = make_uint2(o.lo, o.hi);
         p.scales1[row * (p.cols >> 4) + (gc >> 4)] = (uint8_t)o.scale;
@@ -537,7 +572,12 @@ __device__ __forceinline__ void quant_body(const QuantParams& p, int64_t bx, int
         uint32_t hc[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) xc[i] = R[lr0 + i][lane];
-        if (SR) draws16((uint64_t)gcol * (uint64_t)p.rows + (uint64_t)(grow0 + 16 * b), p.tag0, p.step, p.seed, hc);
+        if (shared) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) hc[i] = H[lr0 + i][lane];
+        } else if (SR) {
+          draws16((uint64_t)gcol * (uint64_t)p.rows + (uint64_t)(grow0 + 16 * b), p.tag0, p.step, p.seed, hc);
+        }
         const QuantBlockOut o = quant_block16(xc, hc, s_g, d, SR);
         packed[2 * b] = o.lo;
         packed[2 * b + 1] = o.hi;

@@ -100,11 +100,12 @@ def test_ffn_residual_quant_sampled_panels():
     g0c, g0s = q.R_ax0.codes.cpu().numpy(), q.R_ax0.scales.cpu().numpy()
     for r0 in (0, 16 * 311, 16 * 777, T - 16):
         mr = (m_host[r0:r0 + 16].astype(np.float64) - us[r0:r0 + 16] @ v.astype(np.float64).T).astype(np.float32)
-        o1 = nvfp4.quantize(mr, 1, "sr", 0, philox.with_role(tag, 1), 5, amax=amax, origin=(r0, 0, F))
+        rt = philox.with_role(tag, philox.ROLE_RESID)
+        o1 = nvfp4.quantize(mr, 1, "sr", 0, rt, 5, amax=amax, origin=(r0, 0, F), draws="matrix")
         assert np.float32(q.R_ax1.tensor_scale.item()) == o1.s_g
         assert np.array_equal(g1s[r0:r0 + 16], o1.scales), "axis-1 scales, rows %d.." % r0
         assert np.array_equal(g1c[r0:r0 + 16], o1.codes), "axis-1 codes, rows %d.." % r0
-        o0 = nvfp4.quantize(mr, 0, "sr", 0, philox.with_role(tag, 0), 5, amax=amax, origin=(0, r0, T))
+        o0 = nvfp4.quantize(mr, 0, "sr", 0, rt, 5, amax=amax, origin=(r0, 0, F), draws="matrix")
         assert np.array_equal(g0s[:, r0 // 16:r0 // 16 + 1], o0.scales), "axis-0 scales, rows %d.." % r0
         assert np.array_equal(g0c[:, r0 // 2:r0 // 2 + 8], o0.codes), "axis-0 codes, rows %d.." % r0
     # the factors are small: compare them whole
@@ -177,10 +178,11 @@ def test_million_row_direct_quant_sampled_panels(big_activation):
         amax = max(amax, np.float32(np.max(np.abs(M[r0:r0 + (1 << 16)].float().cpu().numpy()))))
     for r0 in (0, 16 * 40000, (1 << 20) - 16 * 3, 16 * 65535):
         x = M[r0:r0 + 16].float().cpu().numpy()
-        o1 = nvfp4.quantize(x, 1, "sr", 0, philox.with_role(tag, 1), 0, amax=amax, origin=(r0, 0, H))
+        rt = philox.with_role(tag, philox.ROLE_RESID)
+        o1 = nvfp4.quantize(x, 1, "sr", 0, rt, 0, amax=amax, origin=(r0, 0, H), draws="matrix")
         assert np.array_equal(q.R_ax1.codes[r0:r0 + 16].cpu().numpy(), o1.codes), "axis 1 rows %d" % r0
         assert np.array_equal(q.R_ax1.scales[r0:r0 + 16].cpu().numpy(), o1.scales)
-        o0 = nvfp4.quantize(x, 0, "sr", 0, philox.with_role(tag, 0), 0, amax=amax, origin=(0, r0, rows))
+        o0 = nvfp4.quantize(x, 0, "sr", 0, rt, 0, amax=amax, origin=(r0, 0, H), draws="matrix")
         assert np.array_equal(q.R_ax0.codes[:, r0 // 2:r0 // 2 + 8].cpu().numpy(), o0.codes), "axis 0 rows %d" % r0
         assert np.array_equal(q.R_ax0.scales[:, r0 // 16:r0 // 16 + 1].cpu().numpy(), o0.scales)
 

@@ -61,8 +61,25 @@ def test_direct_quant_bit_exact(shape, dtype, rounding):
     metis.status_sync()
     x = to_np(M).astype(np.float32)
     for axis, gq in ((0, q.R_ax0), (1, q.R_ax1)):
-        oq = nvfp4.quantize(x, axis, rounding, 123, philox.with_role(tag, axis), 5)
+        oq = nvfp4.quantize(x, axis, rounding, 123, philox.with_role(tag, philox.ROLE_RESID), 5, draws="matrix")
         assert_qtensor_equal(gq, oq, "axis %d" % axis)
+
+
+@pytest.mark.parametrize("shape", [(96, 37), (48, 200)])
+def test_direct_quant_axis0_only_ragged_cols(shape):
+    """Axis 0 alone allows any column count; the shared SR draws then start at
+    row-major positions that are not multiples of 8 (cols = 37) or end in a
+    partial group of 16 columns (cols = 200)."""
+    say("direct quant axis 0 only %s" % (shape,))
+    rows, cols = shape
+    M = _rand(rows, cols, torch.float32, seed=rows + cols)
+    cfg = metis.make_config(k=1, rounding=metis.SR, seed=9)
+    tag = metis.make_tag(1, metis.OPERAND_W)
+    q = metis.quantize(M, cfg, tag, 2, metis.AXIS0)
+    metis.status_sync()
+    oq = nvfp4.quantize(to_np(M).astype(np.float32), 0, "sr", 9, philox.with_role(tag, philox.ROLE_RESID), 2,
+                        draws="matrix")
+    assert_qtensor_equal(q.R_ax0, oq, "axis 0")
 
 
 def test_nan_input_sets_numeric_status():

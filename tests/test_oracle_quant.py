@@ -170,3 +170,43 @@ def test_part_quantisation_matches_whole(rounding):
                            origin=(16, 48, 96))
     assert np.array_equal(part0.codes, full0.codes[16:32, 24:48])
     assert np.array_equal(part0.scales, full0.scales[16:32, 3:6])
+
+
+@pytest.mark.parametrize("rounding", ["rne", "sr"])
+def test_part_quantisation_matches_whole_matrix_draws(rounding):
+    # the same with draws laid out by the tensor's own row-major positions:
+    # a panel's origin is its (row, column) in the whole tensor
+    x = (np.random.default_rng(22).standard_normal((96, 80)) * 3).astype(np.float32)
+    amax = np.float32(np.max(np.abs(x)))
+    kw = dict(seed=3, tag=77, step=2, draws="matrix")
+    full1 = nvfp4.quantize(x, 1, rounding, **kw)
+    part1 = nvfp4.quantize(x[32:64, 16:48], 1, rounding, amax=amax, origin=(32, 16, 80), **kw)
+    assert np.array_equal(part1.codes, full1.codes[32:64, 8:24])
+    assert np.array_equal(part1.scales, full1.scales[32:64, 1:3])
+    full0 = nvfp4.quantize(x, 0, rounding, **kw)
+    part0 = nvfp4.quantize(x[48:96, 16:32], 0, rounding, amax=amax, origin=(48, 16, 80), **kw)
+    assert np.array_equal(part0.codes, full0.codes[16:32, 24:48])
+    assert np.array_equal(part0.scales, full0.scales[16:32, 3:6])
+
+
+def test_matrix_draws_shared_between_orientations():
+    # Every 16-block of x, along rows and along columns, holds one entry 6 and
+    # smaller magnitudes elsewhere (6 at (i, i % 16) and (i, 16 + i % 16)), so
+    # all block scales are equal in both orientations and each element gets
+    # the same y in both.  With one draw per element (draws="matrix") the two
+    # orientations then round every element alike; with a draw per position
+    # in each orientation's own layout they disagree on many elements.
+    rng = np.random.default_rng(23)
+    x = rng.uniform(-5.0, 5.0, (32, 32)).astype(np.float32)
+    i = np.arange(32)
+    x[i, i % 16] = 6.0
+    x[i, 16 + i % 16] = 6.0
+    kw = dict(seed=8, tag=5, step=1)
+    q1 = nvfp4.quantize(x, 1, "sr", draws="matrix", **kw)
+    q0 = nvfp4.quantize(x, 0, "sr", draws="matrix", **kw)
+    assert np.all(q1.scales == q1.scales[0, 0]) and np.all(q0.scales == q1.scales[0, 0])
+    assert np.array_equal(nvfp4.unpack_codes(q1), nvfp4.unpack_codes(q0).T)
+    o1 = nvfp4.quantize(x, 1, "sr", draws="own", **kw)
+    o0 = nvfp4.quantize(x, 0, "sr", draws="own", **kw)
+    assert np.array_equal(nvfp4.unpack_codes(o1), nvfp4.unpack_codes(q1))  # same index along axis 1
+    assert (nvfp4.unpack_codes(o1) != nvfp4.unpack_codes(o0).T).mean() > 0.1

@@ -174,7 +174,7 @@ def test_k0_split_equals_direct_codes():
     b = split_gemm.quantize_operand(m, z, np.zeros(0, np.float32), np.zeros((48, 0), np.float32),
                                     "sr", 3, philox.make_tag(1, 2, 0), 2)
     assert np.array_equal(a.r_ax0.codes, b.r_ax0.codes) and np.array_equal(a.r_ax1.codes, b.r_ax1.codes)
-    q = nvfp4.quantize(m, 1, "sr", 3, philox.make_tag(1, 2, philox.ROLE_RESID_AX1), 2)
+    q = nvfp4.quantize(m, 1, "sr", 3, philox.make_tag(1, 2, philox.ROLE_RESID), 2, draws="matrix")
     assert np.array_equal(a.r_ax1.codes, q.codes) and np.array_equal(a.r_ax1.scales, q.scales)
 
 
