@@ -123,43 +123,52 @@ void gemm_fp4_reg_kernel(GemmParams p) {
 
   // fragment reads: row R = g * 32 + (lane & 31), chunk c = 2 j + h
   const int hh = lane >> 5, li = lane & 31, lr8 = li & 7;
-  uint4 ac[TM], bc[TN];      // 16 code bytes per fragment
-  uint32_t as[TM], bs[TN];   // fp16 scales of this lane's two blocks
-  auto read_frags = [&](auto s, int j) {
+  // two register sets of raw fragments: a sub-block's codes and scales are
+  // read into one set while the previous sub-block expands from the other
+  uint4 ac[2][TM], bc[2][TN];      // 16 code bytes per fragment
+  uint32_t as[2][TM], bs[2][TN];   // fp16 scales of this lane's two blocks
+  using F0 = std::integral_constant<int, 0>;
+  using F1 = std::integral_constant<int, 1>;
+  auto read_frags = [&](auto s, int j, auto f) {
+    constexpr int F = decltype(f)::value;
     const int sw = ((2 * j + hh) ^ lr8) * 16 + lr8 * 128;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int R = (wm * TM + i) * 32 + li;
-      ac[i] = *(const uint4*)(code_a(s) + (R >> 3) * 1024 + sw);
-      as[i] = *(const uint32_t*)(sc_a(s) + R * 16 + 4 * j);
+      ac[F][i] = *(const uint4*)(code_a(s) + (R >> 3) * 1024 + sw);
+      as[F][i] = *(const uint32_t*)(sc_a(s) + R * 16 + 4 * j);
     }
 #pragma unroll
     for (int jn = 0; jn < TN; ++jn) {
       const int R = (wn * TN + jn) * 32 + li;
-      bc[jn] = *(const uint4*)(code_b(s) + (R >> 3) * 1024 + sw);
-      bs[jn] = *(const uint32_t*)(sc_b(s) + R * 16 + 4 * j);
+      bc[F][jn] = *(const uint4*)(code_b(s) + (R >> 3) * 1024 + sw);
+      bs[F][jn] = *(const uint32_t*)(sc_b(s) + R * 16 + 4 * j);
     }
   };
   // blocks 4 j + 2 h and 4 j + 2 h + 1 -> {s, s'} in fp16 (exact)
-  auto cvt_scales = [&]() {
+  auto cvt_scales = [&](auto f) {
+    constexpr int F = decltype(f)::value;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
-      as[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(as[i] >> (16 * hh), 1.0f, false));
+      as[F][i] = __builtin_bit_cast(uint32_t,
+                                    __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(as[F][i] >> (16 * hh), 1.0f, false));
 #pragma unroll
     for (int jn = 0; jn < TN; ++jn)
-      bs[jn] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bs[jn] >> (16 * hh), 1.0f, false));
+      bs[F][jn] = __builtin_bit_cast(uint32_t,
+                                     __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bs[F][jn] >> (16 * hh), 1.0f, false));
   };
   auto pair = [](uint32_t s2, int kk) {
     const uint32_t h = (kk < 2) ? (s2 & 0xFFFFu) : (s2 >> 16);
     return __builtin_bit_cast(half2_t, h | (h << 16));
   };
-  auto expand = [&](int kk, half8_t* af, half8_t* bf) {
+  auto expand = [&](int kk, half8_t* af, half8_t* bf, auto f) {
+    constexpr int F = decltype(f)::value;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
-      af[i] = __builtin_bit_cast(half8_t, dequant8(u4_get(ac[i], kk), pair(as[i], kk)));
+      af[i] = __builtin_bit_cast(half8_t, dequant8(u4_get(ac[F][i], kk), pair(as[F][i], kk)));
 #pragma unroll
     for (int jn = 0; jn < TN; ++jn)
-      bf[jn] = __builtin_bit_cast(half8_t, dequant8(u4_get(bc[jn], kk), pair(bs[jn], kk)));
+      bf[jn] = __builtin_bit_cast(half8_t, dequant8(u4_get(bc[F][jn], kk), pair(bs[F][jn], kk)));
   };
   auto mfmas = [&](const half8_t* af, const half8_t* bf) {
 #pragma unroll
@@ -177,69 +186,76 @@ void gemm_fp4_reg_kernel(GemmParams p) {
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
     }
   };
-  // after new fragment reads: four MFMAs cover their latency, then one MFMA
-  // per seven VALU (scale conversion and expansion of the next sub-step 0)
+  // the sub-block's last sub-step: its raw fragments were read a sub-block
+  // earlier, so the scale conversion and the expansion of the next sub-step
+  // 0 spread evenly over the MFMAs (six VALU each)
   auto interleave_tail = [&]() {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-#pragma unroll
-    for (int t = 4; t < TM * TN; ++t) {
-      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+    for (int t = 0; t < TM * TN; ++t) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
     }
   };
 
   half8_t a0[TM], b0[TN], a1[TM], b1[TN];
-  // sub-steps 0..2 of the current 64-wide sub-block (sub-step 0 expanded)
-  auto sub_head = [&]() {
+  // sub-steps 0..2 of the current 64-wide sub-block (sub-step 0 expanded;
+  // its raw fragments in set f)
+  auto sub_head = [&](auto f) {
     mfmas(a0, b0);
-    expand(1, a1, b1);
+    expand(1, a1, b1, f);
     interleave();
     __builtin_amdgcn_sched_barrier(0);
     mfmas(a1, b1);
-    expand(2, a0, b0);
+    expand(2, a0, b0, f);
     interleave();
     __builtin_amdgcn_sched_barrier(0);
     mfmas(a0, b0);
-    expand(3, a1, b1);
+    expand(3, a1, b1, f);
     interleave();
     __builtin_amdgcn_sched_barrier(0);
   };
-  // Stage kt sits in ring slot S with its sub-block 0 fragments in
-  // registers.  It first issues the DMA of stage kt + 1 into the other slot
-  // (every wave finished reading it before the previous barrier).  Sub-blocks
-  // 1..3 are read from slot S while the previous sub-block's sub-step 3
-  // multiplies; after sub-block 3 every wave waits for its DMA, the barrier
-  // publishes the other slot and its sub-block 0 is read.  A DMA past the
-  // last stage repeats it into a slot that is never read again.
+  // sub-step 3 of the current sub-block, with the scale conversion and the
+  // sub-step 0 expansion of the next sub-block (raw fragments in set g)
+  auto sub_tail = [&](auto g) {
+    mfmas(a1, b1);
+    cvt_scales(g);
+    expand(0, a0, b0, g);
+    interleave_tail();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Stage kt sits in ring slot S with its sub-block 0 fragments in register
+  // set 0 (sub-step 0 expanded).  It first issues the DMA of stage kt + 1
+  // into the other slot (every wave finished reading it before the previous
+  // barrier).  The raw fragments of sub-block j + 1 are read into the other
+  // register set when sub-block j starts, a whole sub-block ahead of their
+  // use.  Sub-block 3's fragments were read (and consumed) before sub-block
+  // 3 starts, so there every wave waits for its DMA and the barrier
+  // publishes the other slot, whose sub-block 0 is then read.  A DMA past
+  // the last stage repeats it into a slot that is never read again.
   auto stage_step = [&](int64_t kt, auto sc) {
     using SN = std::integral_constant<int, 1 - decltype(sc)::value>;
     issue(kt + 1 < nk ? kt + 1 : kt, SN{});
-    for (int j = 1; j < 4; ++j) {
-      sub_head();
-      read_frags(sc, j);
-      mfmas(a1, b1);
-      cvt_scales();
-      expand(0, a0, b0);
-      interleave_tail();
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    sub_head();
+    read_frags(sc, 1, F1{});
+    sub_head(F0{});
+    sub_tail(F1{});
+    read_frags(sc, 2, F0{});
+    sub_head(F1{});
+    sub_tail(F0{});
+    read_frags(sc, 3, F1{});
+    sub_head(F0{});
+    sub_tail(F1{});
     ring_barrier();
-    read_frags(SN{}, 0);
-    mfmas(a1, b1);
-    cvt_scales();
-    expand(0, a0, b0);
-    interleave_tail();
-    __builtin_amdgcn_sched_barrier(0);
+    read_frags(SN{}, 0, F0{});
+    sub_head(F1{});
+    sub_tail(F0{});
   };
 
   if (nk > 0) {
     issue((int64_t)0, S0{});
     ring_barrier();
-    read_frags(S0{}, 0);
-    cvt_scales();
-    expand(0, a0, b0);
+    read_frags(S0{}, 0, F0{});
+    cvt_scales(F0{});
+    expand(0, a0, b0, F0{});
     __builtin_amdgcn_sched_barrier(0);
     for (int64_t kt = 0; kt < nk; kt += 2) {
       stage_step(kt, S0{});
