@@ -78,7 +78,9 @@ void gemm_fp4_reg_kernel(GemmParams p) {
   using S1 = std::integral_constant<int, 1>;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  // the wave index is uniform: keep it (and every LDS destination derived
+  // from it) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wm = wave / WN, wn = wave % WN;
   const int64_t tiles_m = ceil_div<int64_t>(p.M, BM);
   const int64_t tiles_n = ceil_div<int64_t>(p.N, BN);
@@ -197,6 +199,30 @@ void gemm_fp4_reg_kernel(GemmParams p) {
     }
   };
 
+  // K-extension stages (bf16, kext % 64 == 0) travel through the same LDS
+  // ring after the FP4 stages: stage e holds sub-steps 4 e .. 4 e + 3 of the
+  // tile's 32-row groups, each (group, sub-step) fragment the 1 KB block the
+  // extension layout stores contiguously, at ((group * 4 + sub-step) * 1 KB)
+  // for A and EA KB further for B.  Groups past the matrix are clamped to
+  // its last group (padded rows are zeros; their results are never stored).
+  constexpr int EA = (BM / 32) * 4, EB = (BN / 32) * 4;  // 1 KB blocks per stage
+  static_assert(EA % NW == 0 && EB % NW == 0 && (EA + EB) * 1024 <= Cfg::STAGE, "extension stage");
+  const int64_t ne = p.kext >> 6, kx16 = p.kext >> 4;
+  const int64_t gla = (p.M - 1) >> 5, glb = (p.N - 1) >> 5;
+  auto issue_ext = [&](int64_t e, auto s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int d = 0; d < EA / NW; ++d) {
+      const int idx = wave + d * NW;
+      const int64_t g = min((m0 >> 5) + (idx >> 2), gla);
+      dma16(p.a_ext + ((g * kx16 + 4 * e + (idx & 3)) * 64 + lane) * 8, stage_base(s) + idx * 1024);
+    }
+#pragma unroll
+    for (int d = 0; d < EB / NW; ++d) {
+      const int idx = wave + d * NW;
+      const int64_t g = min((n0 >> 5) + (idx >> 2), glb);
+      dma16(p.b_ext + ((g * kx16 + 4 * e + (idx & 3)) * 64 + lane) * 8, stage_base(s) + (EA + idx) * 1024);
+    }
+  };
   half8_t a0[TM], b0[TN], a1[TM], b1[TN];
   // sub-steps 0..2 of the current 64-wide sub-block (sub-step 0 expanded;
   // its raw fragments in set f)
@@ -271,43 +297,49 @@ void gemm_fp4_reg_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] *= alpha;
 
-  // ---- K-extension (bf16, kext % 64 == 0): fragments straight from global
-  // memory, four 16-wide sub-steps in flight ahead of the one multiplying
-  if (p.kext > 0) {
-    const uint16_t* ap[TM];
-    const uint16_t* bp[TN];
-    // 32-row groups past the matrix are clamped to its last group (padded
-    // rows are zeros; their results are never stored)
-    const int64_t gla = (p.M - 1) >> 5, glb = (p.N - 1) >> 5;
+  // ---- K-extension: stage e sits in ring slot (nk - 1 + e) % 2; every wave
+  // reads its fragments of a sub-step straight from the stage (lane L at
+  // block offset 16 L) while the next stage's DMA is in flight
+  auto ext_step = [&](int64_t e, auto sc) __attribute__((always_inline)) {
+    using SN = std::integral_constant<int, 1 - decltype(sc)::value>;
+    if (e + 1 < ne) issue_ext(e + 1, SN{});
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-      ap[i] = p.a_ext + ext_off(min((m0 >> 5) + wm * TM + i, gla) * 32 + (lane & 31), 8 * (lane >> 5), p.kext);
+    for (int u = 0; u < 4; ++u) {
+      bf16x8_t ea[TM], eb[TN];
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-      bp[j] = p.b_ext + ext_off(min((n0 >> 5) + wn * TN + j, glb) * 32 + (lane & 31), 8 * (lane >> 5), p.kext);
-    bf16x8_t ea[4][TM], eb[4][TN];
-    // sub-step kk of a fragment is 512 elements past sub-step kk - 1
-    auto eload = [&](int u, int64_t k0) {
+      for (int i = 0; i < TM; ++i)
+        ea[i] = *(const bf16x8_t*)(stage_base(sc) + ((wm * TM + i) * 4 + u) * 1024 + lane * 16);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) ea[u][i] = *(const bf16x8_t*)(ap[i] + (k0 >> 4) * 512);
+      for (int j = 0; j < TN; ++j)
+        eb[j] = *(const bf16x8_t*)(stage_base(sc) + (EA + (wn * TN + j) * 4 + u) * 1024 + lane * 16);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) eb[u][j] = *(const bf16x8_t*)(bp[j] + (k0 >> 4) * 512);
-    };
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) eload(u, 16 * u);
-    for (int64_t k0 = 0; k0 < p.kext; k0 += 64) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ea[u][i], eb[u][j], acc[i][j], 0, 0, 0);
-        // the last four refills repeat the final sub-step (never used)
-        const int64_t kn = k0 + 64 + 16 * u;
-        eload(u, kn < p.kext ? kn : p.kext - 16);
-      }
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ea[i], eb[j], acc[i][j], 0, 0, 0);
     }
+    ring_barrier();
+  };
+  auto ext_loop = [&](auto first) __attribute__((always_inline)) {
+    using SB = std::integral_constant<int, 1 - decltype(first)::value>;
+    for (int64_t e = 0; e < ne; e += 2) {
+      ext_step(e, first);
+      if (e + 1 < ne) ext_step(e + 1, SB{});
+    }
+  };
+  if (ne > 0) {
+    // the first stage goes into the last FP4 stage's slot, which every wave
+    // finished reading before the main loop's final barrier
+    const bool s0 = nk == 0 || ((nk - 1) & 1) == 0;
+    if (s0)
+      issue_ext(0, S0{});
+    else
+      issue_ext(0, S1{});
+    ring_barrier();
+    if (s0)
+      ext_loop(S0{});
+    else
+      ext_loop(S1{});
   }
 
   // ---- epilogue: lane holds column lane%32 and rows 8(v/4) + 4(lane/32) + v%4
