@@ -159,9 +159,11 @@ void gemm_fp4_reg_kernel(GemmParams p) {
       bs[F][jn] = __builtin_bit_cast(uint32_t,
                                      __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bs[F][jn] >> (16 * hh), 1.0f, false));
   };
+  // {s, s} or {s', s'}: a broadcast the packed multiply takes by operand
+  // selection, with no instruction of its own
   auto pair = [](uint32_t s2, int kk) {
-    const uint32_t h = (kk < 2) ? (s2 & 0xFFFFu) : (s2 >> 16);
-    return __builtin_bit_cast(half2_t, h | (h << 16));
+    const half2_t h = __builtin_bit_cast(half2_t, s2);
+    return (kk < 2) ? __builtin_shufflevector(h, h, 0, 0) : __builtin_shufflevector(h, h, 1, 1);
   };
   auto expand = [&](int kk, half8_t* af, half8_t* bf, auto f) {
     constexpr int F = decltype(f)::value;
