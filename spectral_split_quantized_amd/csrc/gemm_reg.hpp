@@ -355,7 +355,7 @@ void gemm_fp4_reg_kernel(GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int64_t row = m0 + (wm * TM + i) * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (row < p.M) C[row * p.ldc + col] = acc[i][j][v];
+        if (row < p.M) __builtin_nontemporal_store(acc[i][j][v], &C[row * p.ldc + col]);
       }
     }
   }
