@@ -42,13 +42,13 @@ K_RANK, OVERSAMPLE, L_K, REFRESH = 61, 8, 164, 8
 
 
 # HBM traffic of the main split-GEMM kernel, bytes per launch averaged over
-# the 18 launches of one step (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE,
-# on ``bench.py --steps 1 --warmup 1 --no-cpu-baseline``; each counter scaled
+# the 18 launches of two steps (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE,
+# on ``bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-extras``; each counter scaled
 # by what it reads for a plain 256 MiB copy, ``bench.py --copy-calibration``).
 # The figure belongs to the kernel source it was taken on: if any file below
 # changes, the stored figure no longer applies and ``traffic`` is reported null.
-GEMM_TRAFFIC_BYTES = 1835941043
-GEMM_TRAFFIC_SHA = "121102e81c9dc36e"
+GEMM_TRAFFIC_BYTES = 1673542347
+GEMM_TRAFFIC_SHA = "6e3a1ca3823e765e"
 GEMM_SOURCES = ("common.hpp", "gemm_common.hpp", "gemm_reg.hpp", "gemm_launch.hpp", "gemm_big.hip")
 
 
@@ -669,7 +669,7 @@ def main():
     traffic = GEMM_TRAFFIC_BYTES if GEMM_TRAFFIC_SHA is not None and gemm_source_sha() == GEMM_TRAFFIC_SHA else None
     roofline = {"bound": "mfma", "achieved": round(g_tflops, 1), "peak": PEAK_F16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(g_tflops / PEAK_F16_TFLOPS, 4), "traffic": traffic,
-                "kernel": "gemm_fp4_kernel (main split GEMM)", "launches": len(g),
+                "kernel": "gemm_fp4_reg_kernel (main split GEMM)", "launches": len(g),
                 "avg_ms": round(g_ms / max(len(g), 1), 4)}
     # streaming: both quantiser sweeps (amax + quantise-on-store) of the
     # largest operand, X_down's residual in both orientations with SR, timed
