@@ -595,7 +595,7 @@ def main():
     ap.add_argument("--steps", type=int, default=16)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=512)
+    ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--cpu-cols", type=int, default=4096)
     ap.add_argument("--streams", type=int, default=3,
                     help="HIP streams per step (1: every call in order on one stream)")
