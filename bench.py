@@ -587,6 +587,126 @@ def cpu_baseline(inputs_cpu, tokens, ncols):
                       "(decompose + quantise + fwd + bwd), float64 numpy oracle" % (tokens, ncols)}
 
 
+def _top_right_subspace(m, k):
+    """Orthonormal basis (cols x k) of the top-k right singular subspace of m,
+    from the eigenvectors of the smaller Gram matrix in float64."""
+    import torch
+    md = m.double()
+    if md.shape[0] >= md.shape[1]:
+        _, vec = torch.linalg.eigh(md.T @ md)
+        return vec[:, -k:]
+    lam, vec = torch.linalg.eigh(md @ md.T)
+    v = md.T @ vec[:, -k:]
+    return torch.linalg.qr(v)[0]
+
+
+def _captured(m, basis, best):
+    """Share of m's best rank-k energy that the right subspace span(basis)
+    captures: ||m Q||_F^2 / ||m Q_best||_F^2 (1 for the top-k subspace)."""
+    import torch
+    md = m.double()
+    q = torch.linalg.qr(basis.double())[0]
+    return float((md @ q).pow(2).sum() / (md @ best).pow(2).sum())
+
+
+def measure_training_loop(dev, steps=48, periods=(1, 8, 32), tokens=8192, lr=2e-5):
+    """A GPT-2-130M-shaped MLP block (768 -> 3072 -> GELU -> 768, no bias),
+    both linears through the Metis autograd layer, trained with Adam on a
+    synthetic teacher-student regression, once per factor refresh period.
+    Each step draws new inputs whose dominant right subspace turns by 0.01 rad
+    per step.  Reports the relative loss, how well each cached right factor
+    still spans its operand's current top-k right singular subspace
+    (staleness), how much that subspace moves between adjacent steps, and the
+    time per training step.  A float32 run of the same model and data is the
+    reference loss."""
+    import torch
+    import torch.nn.functional as Fn
+    from spectral_split_quantized_amd import synth
+    from spectral_split_quantized_amd.layer import MetisLinear, set_step
+    H, F_, k = 768, 3072, 12
+
+    def weight(r, c, seed):
+        w, _ = synth.anisotropic_fast(r, c, synth.FRAC_W, seed, out_dtype=torch.float32, device=dev)
+        return w / torch.linalg.matrix_norm(w, ord=2)
+
+    t1, t2 = weight(H, F_, 901), weight(F_, H, 902)
+    s1, s2 = weight(H, F_, 903), weight(F_, H, 904)
+    _, basis = synth.anisotropic_fast(tokens, H, synth.FRAC_X, 905, device=dev)
+
+    def batch(t):
+        x, _ = synth.anisotropic_fast(tokens, H, synth.FRAC_X, 1000 + t, device=dev, basis=basis, theta=0.01 * t)
+        with torch.no_grad():
+            y = Fn.gelu(x.float() @ t1) @ t2
+        return x, y
+
+    def run(period):
+        if period is None:
+            w1 = torch.nn.Parameter(s1.clone())
+            w2 = torch.nn.Parameter(s2.clone())
+            params = [w1, w2]
+            fwd = lambda x: Fn.gelu(x.float() @ w1) @ w2
+        else:
+            l1 = MetisLinear(H, F_, k, l_k=82, refresh=period, weight=s1.clone(), layer=0, device=dev)
+            l2 = MetisLinear(F_, H, k, l_k=82, refresh=period, weight=s2.clone(), layer=1, device=dev)
+            params = [l1.weight, l2.weight]
+            fwd = lambda x: l2(Fn.gelu(l1(x.float())))
+        opt = torch.optim.Adam(params, lr=lr)
+        rec = {"loss": [], "ms": [], "align_w": [], "align_x": [], "drift_w": [], "drift_x": []}
+        prev = None
+        for t in range(steps):
+            x, y = batch(t)
+            # the operands' current top-k right subspaces (the weight before this step's update)
+            w_now = params[0].detach().clone()
+            cur = (_top_right_subspace(w_now, k), _top_right_subspace(x, k))
+            if prev is not None:
+                rec["drift_w"].append(_captured(w_now, prev[0], cur[0]))
+                rec["drift_x"].append(_captured(x, prev[1], cur[1]))
+            prev = cur
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            if period is not None:
+                set_step(l1, t)
+                set_step(l2, t)
+            out = fwd(x)
+            loss = (out - y).pow(2).mean() / y.pow(2).mean()
+            opt.zero_grad(set_to_none=True)
+            loss.backward()
+            opt.step()
+            torch.cuda.synchronize()
+            rec["ms"].append(1e3 * (time.perf_counter() - t0))
+            rec["loss"].append(float(loss.detach()))
+            if period is not None:
+                # the right factors this step used: sketched at its last refresh, rotated since
+                rec["align_w"].append(_captured(w_now, l1.factors["W"].V, cur[0]))
+                rec["align_x"].append(_captured(x, l1.factors["X"].V, cur[1]))
+            del out, loss
+        return rec
+
+    def mean(v):
+        return round(sum(v) / len(v), 5) if v else None
+
+    out = {"model": "GPT-2-130M MLP block 768 -> 3072 -> GELU -> 768, no bias; teacher-student regression",
+           "tokens": tokens, "steps": steps, "k": k, "l_k": 82, "optimizer": "Adam lr %g" % lr,
+           "input_drift": "dominant right subspace of X turned 0.01 rad per step",
+           "loss": "||Y - Y*||^2 / ||Y*||^2 of the step's batch"}
+    ref = run(None)
+    out["float32"] = {"loss_first": round(ref["loss"][0], 5), "loss_last8": mean(ref["loss"][-8:]),
+                      "ms_per_step": mean(ref["ms"][2:])}
+    out["previous_step_subspace_energy"] = {"W1": mean(ref["drift_w"]), "X": mean(ref["drift_x"]),
+                                      "W1_min": round(min(ref["drift_w"]), 5), "X_min": round(min(ref["drift_x"]), 5)}
+    for period in periods:
+        r = run(period)
+        out["refresh_%d" % period] = {
+            "loss_first": round(r["loss"][0], 5), "loss_last8": mean(r["loss"][-8:]),
+            "ms_per_step": mean(r["ms"][2:]),
+            "cached_factor_energy": {"W1": mean(r["align_w"]), "X": mean(r["align_x"]),
+                                        "W1_min": round(min(r["align_w"]), 5), "X_min": round(min(r["align_x"]), 5)}}
+    out["energy_note"] = ("share of the operand's best rank-k energy ||M Q||^2 / ||M V_k||^2 that a k-dim right subspace "
+                          "captures (1 = as good as the exact top-k): cached_factor_energy for the factor each step used, "
+                          "previous_step_subspace_energy for the previous step's exact top-k subspace (the float32 run)")
+    return out
+
+
 # -------------------------------------------------------------------- main --
 
 def main():
@@ -721,6 +841,8 @@ def main():
         extras["direct_nvfp4"] = measure_direct(mlp, inputs, args.warmup + args.steps - 1, ms_per_step)
         log("1M x 4096 activation")
         extras["c4_activation"] = measure_c4(dev, extras["ceilings"]["copy_GBps"])
+        log("training loop through the autograd layer (refresh periods 1, 8, 32)")
+        extras["training_loop"] = measure_training_loop(dev)
         ceil_tf = extras["ceilings"]["hipblaslt_bf16_TFLOPs"]
         roofline["frac_vs_hipblaslt_bf16"] = round(g_tflops / ceil_tf, 4) if ceil_tf else None
         streaming["frac_vs_copy"] = round(streaming["achieved"] / extras["ceilings"]["copy_GBps"], 4)
