@@ -510,6 +510,56 @@ def measure_direct(mlp, inputs, t_last, mlp_ms=None, steps=4, warmup=2, sample_r
                             "below 1/8 of their 16-block's largest magnitude that dequantise to 0"}
 
 
+def measure_mxfp4(mlp, inputs, t_last, nvfp4_gemm_ms, reps=10, sample_rows=256):
+    """The scaled-FP4 matrix-instruction variant: MXFP4 (block 32, E8M0
+    power-of-two scales) operands of the gate projection, quantised by the
+    library and multiplied on v_mfma_scale_f32_32x32x64_f8f6f4 with no
+    expansion.  Times the GEMM at the gate shape (kind-3 HIP events on the
+    launch stream, median of ``reps``) against the NVFP4 split GEMM's average
+    from the timed steps, and reports the forward error against the exact
+    product on the same sampled rows and inputs as ``direct_nvfp4``."""
+    import torch
+    m = mlp.metis
+    X = inputs["X_gu"][t_last % len(inputs["X_gu"])]
+    W = inputs["W_gate"][t_last % len(inputs["W_gate"])]
+    T, H = X.shape
+    F = W.shape[1]
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    qx = m.mxfp4_quantize(X, 1)
+    qw = m.mxfp4_quantize(W, 0)
+    b.record()
+    C = m.mxfp4_gemm(qx, qw)
+    m.status_sync()
+    q_ms = a.elapsed_time(b)
+    m.timing_kinds(1 << 3)
+    m.timing_enable(reps)
+    for _ in range(reps):
+        m.mxfp4_gemm(qx, qw, C)
+    recs = [r for r in m.timing_read() if r[0] == 3]
+    m.timing_enable(0)
+    m.timing_kinds(-1)
+    ts = sorted(r[1] for r in recs)
+    g_ms = ts[len(ts) // 2]
+    flop = 2.0 * T * F * H
+    tflops = flop / (g_ms * 1e-3) / 1e12
+    idx = torch.arange(0, T, T // sample_rows, device=X.device)
+    exact = X[idx].float() @ W.float()
+    err = float(torch.linalg.norm(C[idx] - exact) / torch.linalg.norm(exact))
+    return {"shape_MNK": [T, F, H], "gemm_ms": round(g_ms, 4), "gemm_tflops": round(tflops, 1),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": 10100.0, "unit": "TFLOP/s",
+                         "frac": round(tflops / 10100.0, 4), "dtype": "fp4 e2m1 x fp4 e2m1, e8m0 block scales"},
+            "nvfp4_split_gemm_ms": round(nvfp4_gemm_ms, 4),
+            "speedup_vs_nvfp4_split_gemm": round(nvfp4_gemm_ms / g_ms, 3),
+            "quantize_both_operands_ms": round(q_ms, 3),
+            "y_rel_fro_err_vs_exact": round(err, 6),
+            "y_sample": "gate projection forward on %d evenly spaced token rows of the step-%d inputs (the rows "
+                        "and inputs of direct_nvfp4)" % (sample_rows, t_last),
+            "note": "a different format from the pages' NVFP4 (block 32 instead of 16, power-of-two scales, "
+                    "no tensor scale, no spectral split, round to nearest)"}
+
+
 def measure_c4(dev, copy_gbps):
     """The 1M x 4096 activation (4.3e9 elements, l_k = 10486): decompose at a
     refresh and at a cached step, and the residual quantisation in both
@@ -839,6 +889,8 @@ def main():
         extras["ceilings"] = measure_ceilings(dev)
         log("plain NVFP4 (k = 0) on the same workload")
         extras["direct_nvfp4"] = measure_direct(mlp, inputs, args.warmup + args.steps - 1, ms_per_step)
+        log("MXFP4 variant on the scaled FP4 matrix instruction")
+        extras["mxfp4_variant"] = measure_mxfp4(mlp, inputs, args.warmup + args.steps - 1, roofline["avg_ms"])
         log("1M x 4096 activation")
         extras["c4_activation"] = measure_c4(dev, extras["ceilings"]["copy_GBps"])
         log("training loop through the autograd layer (refresh periods 1, 8, 32)")

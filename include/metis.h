@@ -224,12 +224,47 @@ metis_status metis_gemm_bwd_prepared(const metis_qoperand *D, const metis_qopera
  * failure flag (METIS_OK or METIS_E_NUMERIC). */
 metis_status metis_status_sync(void *stream);
 
+/* ------------------------------------------------------------------ MXFP4
+ * A separate FP4 format, for comparison with NVFP4 on the same hardware: the
+ * pages name MXFP4 only as a format their NVFP4 recipes are not claimed for
+ * ("Full-Stack FP4: Stable LLM Pretraining with Quantized Projections,
+ * Optimizers, and Attention", 局限性).  Its definition is the OCP Microscaling
+ * (MX) one: 32 consecutive elements along K share a power-of-two scale
+ * X = 2^(floor(log2 amax) - 2), stored as an E8M0 byte (exponent + 127,
+ * clamped to [-127, 127]; an all-zero block stores 0); each element is x / X
+ * rounded to the nearest E2M1 value, ties to even mantissa, saturating at 6.
+ * No spectral split and no stochastic rounding on this path.
+ *
+ * metis_mxfp4_quantize: M is rows x cols, row-major with leading dimension
+ * ld, bf16 or fp32 (dtype), finite (a non-finite block sets the numeric flag
+ * of metis_status_sync; its codes are then unspecified).  axis names the K
+ * axis: 1 along a row, 0 down a column (the output is then the quantised
+ * transpose).  With outer = the other dimension and K its length: codes is
+ * outer x K/2 bytes (element 2i in the low nibble of byte i), 16-byte
+ * aligned; scales is outer x K/32 E8M0 bytes.  K % 32 == 0.  Both buffers are
+ * caller-owned device memory, written on stream.
+ *
+ * metis_mxfp4_gemm: C = A B^T in fp32 (row-major, leading dimension ldc >= N)
+ * of two MXFP4 operands in that layout, A with M rows and B with N rows of
+ * K elements: codes M x K/2 and N x K/2, scales M x K/32 and N x K/32, all four
+ * arrays 16-byte aligned, K % 1024 == 0, M % 8 == 0 and N % 8 == 0
+ * (METIS_E_UNSUPPORTED otherwise).
+ * Products are exact and accumulate in fp32 on the block-scaled FP4 matrix
+ * instruction of gfx950.  M or N == 0 returns METIS_OK with nothing enqueued.
+ * Argument errors return synchronously; nothing is allocated. */
+metis_status metis_mxfp4_quantize(const void *M, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                                  int32_t axis, uint8_t *codes, uint8_t *scales, void *stream);
+metis_status metis_mxfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *b_codes,
+                              const uint8_t *b_scales, int64_t M, int64_t N, int64_t K, float *C,
+                              int64_t ldc, void *stream);
+
 /* Kernel timing for benchmarks.  metis_timing_enable(capacity) creates
  * capacity pairs of HIP events (0 disables timing and releases them); while
  * enabled, each main split-GEMM kernel (kind 0; d = M, N, K, K-extension) and
  * each quantiser sweep (kind 1: amax pass, kind 2: quantise pass; d = rows,
- * cols, axes, K of the rank-k product) is bracketed by events recorded on the
- * launching stream, until the capacity is used up.  metis_timing_read waits
+ * cols, axes, K of the rank-k product) and each MXFP4 GEMM kernel (kind 3;
+ * d = M, N, K, 0) is bracketed by events recorded on the launching stream,
+ * until the capacity is used up.  metis_timing_read waits
  * for the recorded events, writes up to max_records durations (ms) and
  * 5-tuples (kind, d0, d1, d2, d3), resets the record list and returns the
  * number written. */

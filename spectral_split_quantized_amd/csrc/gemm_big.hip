@@ -4,6 +4,7 @@
 
 #include "gemm_launch.hpp"
 #include "gemm_reg.hpp"
+#include "mxfp4_gemm.hpp"
 
 namespace metis {
 
@@ -14,6 +15,13 @@ hipError_t launch_gemm_big(const GemmParams& gp, int splits, hipStream_t st) {
   // LDS is static (one array per pipeline stage)
   hipLaunchKernelGGL((gemm_fp4_reg_kernel<2, 2, 4, 4>), dim3((unsigned)tiles, (unsigned)splits), dim3(Cfg::NT),
                      0, st, gp);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_gemm(const MxGemmParams& g, hipStream_t st) {
+  const int64_t tiles = ceil_div<int64_t>(g.M, 256) * ceil_div<int64_t>(g.N, 256);
+  if (tiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL((mx_gemm_kernel<2, 2, 4, 4>), dim3((unsigned)tiles), dim3(256), 0, st, g);
   return hipGetLastError();
 }
 

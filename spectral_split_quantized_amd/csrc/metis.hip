@@ -21,6 +21,8 @@
 #include "gemm_launch.hpp"
 #include "quant.hpp"
 #include "rsvd.hpp"
+#include "mxfp4.hpp"
+#include "mxfp4_gemm.hpp"
 
 using namespace metis;
 
@@ -53,8 +55,8 @@ metis_status fail(metis_status st, const char* fmt, ...) {
 // ---------------------------------------------- benchmark instrumentation
 
 // When enabled, a pair of HIP events is recorded on the launching stream
-// around each main split-GEMM kernel (kind 0) and each quantiser sweep (kind
-// 1: amax pass, kind 2: quantise pass).  Events are created once, when timing
+// around each main split-GEMM kernel (kind 0), each quantiser sweep (kind
+// 1: amax pass, kind 2: quantise pass) and each MXFP4 GEMM kernel (kind 3).  Events are created once, when timing
 // is enabled; recording them allocates nothing.
 struct TimingRec {
   hipEvent_t a, b;
@@ -1244,6 +1246,52 @@ metis_status metis_status_sync(void* stream) {
     HIP_TRY(hipMemcpyToSymbol(HIP_SYMBOL(g_metis_status), &zero, sizeof(int)));
     return fail(METIS_E_NUMERIC, "device numeric status 0x%x (1: non-finite input, 2: Cholesky, 4: sampler)", v);
   }
+  return METIS_OK;
+}
+
+// ------------------------------------------------------------- MXFP4 --
+
+metis_status metis_mxfp4_quantize(const void* M, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                                  int32_t axis, uint8_t* codes, uint8_t* scales, void* stream) {
+  if (!M || !codes || !scales) return fail(METIS_E_INVALID, "mxfp4_quantize: null pointer");
+  if (dtype != METIS_BF16 && dtype != METIS_F32) return fail(METIS_E_INVALID, "mxfp4_quantize: dtype %d", dtype);
+  if (rows <= 0 || cols <= 0 || ld < cols) return fail(METIS_E_INVALID, "mxfp4_quantize: shape %lld x %lld, ld %lld",
+                                                     (long long)rows, (long long)cols, (long long)ld);
+  if (axis != 0 && axis != 1) return fail(METIS_E_INVALID, "mxfp4_quantize: axis %d", axis);
+  const int64_t k_len = axis ? cols : rows;
+  if (k_len % 32) return fail(METIS_E_INVALID, "mxfp4_quantize: K = %lld is not a multiple of 32", (long long)k_len);
+  if ((uintptr_t)codes & 15) return fail(METIS_E_INVALID, "mxfp4_quantize: codes not 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  MxQuantParams q{M, dtype, rows, cols, ld, codes, scales};
+  if (axis == 1) {
+    hipLaunchKernelGGL(mx_quant_rows_kernel, dim3(grid1(rows * (cols >> 5), 256)), dim3(256), 0, st, q);
+  } else {
+    if ((rows >> 5) > 65535) return fail(METIS_E_UNSUPPORTED, "mxfp4_quantize: %lld rows", (long long)rows);
+    hipLaunchKernelGGL(mx_quant_cols_kernel, dim3(grid1(cols, 256), (unsigned)(rows >> 5)), dim3(256), 0, st, q);
+  }
+  LAUNCH_CHECK();
+  return METIS_OK;
+}
+
+metis_status metis_mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                              const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, float* C, int64_t ldc,
+                              void* stream) {
+  if (M < 0 || N < 0 || K <= 0) return fail(METIS_E_INVALID, "mxfp4_gemm: shape %lld x %lld x %lld",
+                                            (long long)M, (long long)N, (long long)K);
+  if (M == 0 || N == 0) return METIS_OK;
+  if (!a_codes || !a_scales || !b_codes || !b_scales || !C) return fail(METIS_E_INVALID, "mxfp4_gemm: null pointer");
+  if (K % 1024) return fail(METIS_E_UNSUPPORTED, "mxfp4_gemm: K = %lld is not a multiple of 1024", (long long)K);
+  if (M % 8 || N % 8) return fail(METIS_E_UNSUPPORTED, "mxfp4_gemm: M and N must be multiples of 8");
+  if (K / 2 * 8 > INT32_MAX) return fail(METIS_E_UNSUPPORTED, "mxfp4_gemm: K = %lld too large", (long long)K);
+  if (ldc < N) return fail(METIS_E_INVALID, "mxfp4_gemm: ldc %lld < N %lld", (long long)ldc, (long long)N);
+  if (((uintptr_t)a_codes | (uintptr_t)a_scales | (uintptr_t)b_codes | (uintptr_t)b_scales) & 15)
+    return fail(METIS_E_INVALID, "mxfp4_gemm: code and scale arrays must be 16-byte aligned");
+  MxGemmParams g{M, N, K, a_codes, a_scales, b_codes, b_scales, C, ldc};
+  hipStream_t st = (hipStream_t)stream;
+  TimingRec* tr = timing_begin(st, 3, M, N, K, 0);
+  const hipError_t e = launch_mx_gemm(g, st);
+  if (e != hipSuccess) return fail(METIS_E_HIP, "mxfp4_gemm launch: %s", hipGetErrorString(e));
+  timing_end(tr, st);
   return METIS_OK;
 }
 

@@ -73,6 +73,10 @@ def load():
     lib.metis_gemm_fwd_workspace.restype = sz
     lib.metis_gemm_bwd_workspace.argtypes = [ctypes.POINTER(_QOperand)] * 3
     lib.metis_gemm_bwd_workspace.restype = sz
+    lib.metis_mxfp4_quantize.argtypes = [P, i32, i64, i64, i64, i32, P, P, P]
+    lib.metis_mxfp4_quantize.restype = i32
+    lib.metis_mxfp4_gemm.argtypes = [P, P, P, P, i64, i64, i64, P, i64, P]
+    lib.metis_mxfp4_gemm.restype = i32
     lib.metis_decompose.argtypes = [P, i32, i64, i64, i64, ctypes.POINTER(Config), i32, u32, i64,
                                     ctypes.POINTER(_Factors), P, sz, P]
     lib.metis_decompose.restype = i32
@@ -371,7 +375,7 @@ def timing_enable(capacity):
 
 def timing_kinds(mask):
     """Record only the kernel kinds whose bits are set (bit 0: main GEMM,
-    1: amax sweep, 2: quantise sweep)."""
+    1: amax sweep, 2: quantise sweep, 3: MXFP4 GEMM)."""
     _check(load().metis_timing_kinds(int(mask)))
 
 
@@ -387,3 +391,38 @@ def timing_read(max_records=1 << 16):
         k, d0, d1, d2, d3 = (int(v) for v in shape[5 * i:5 * i + 5])
         out.append((k, float(ms[i]), d0, d1, d2, d3))
     return out
+
+
+# ----------------------------------------------------------------- MXFP4 --
+
+class MX4:
+    """One MXFP4 operand (metis_mxfp4_quantize): codes [outer, K/2], E8M0
+    scales [outer, K/32]."""
+
+    def __init__(self, outer, k_len, device="cuda"):
+        self.codes = torch.empty(outer, k_len // 2, dtype=torch.uint8, device=device)
+        self.scales = torch.empty(outer, k_len // 32, dtype=torch.uint8, device=device)
+        self.outer, self.k_len = outer, k_len
+
+
+def mxfp4_quantize(M, axis, out=None):
+    """MXFP4 codes and scales of M along K axis ``axis`` (1: along rows, 0:
+    down columns, giving the quantised transpose)."""
+    lib = load()
+    rows, cols = M.shape
+    outer, k_len = (rows, cols) if axis == 1 else (cols, rows)
+    if out is None:
+        out = MX4(outer, k_len, M.device)
+    _check(lib.metis_mxfp4_quantize(_ptr(M), _dtype_code(M), rows, cols, M.stride(0), axis,
+                                    _ptr(out.codes), _ptr(out.scales), _stream()))
+    return out
+
+
+def mxfp4_gemm(a, b, C=None):
+    """C = A-hat B-hat^T of two MXFP4 operands (metis_mxfp4_gemm), binary32."""
+    lib = load()
+    if C is None:
+        C = torch.empty(a.outer, b.outer, dtype=torch.float32, device=a.codes.device)
+    _check(lib.metis_mxfp4_gemm(_ptr(a.codes), _ptr(a.scales), _ptr(b.codes), _ptr(b.scales), a.outer,
+                                b.outer, a.k_len, _ptr(C), C.stride(0), _stream()))
+    return C
