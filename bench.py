@@ -47,8 +47,8 @@ K_RANK, OVERSAMPLE, L_K, REFRESH = 61, 8, 164, 8
 # by what it reads for a plain 256 MiB copy, ``bench.py --copy-calibration``).
 # The figure belongs to the kernel source it was taken on: if any file below
 # changes, the stored figure no longer applies and ``traffic`` is reported null.
-GEMM_TRAFFIC_BYTES = 1673542347
-GEMM_TRAFFIC_SHA = "6e3a1ca3823e765e"
+GEMM_TRAFFIC_BYTES = 1673719604
+GEMM_TRAFFIC_SHA = "d75c2af57ffcd2ca"
 GEMM_SOURCES = ("common.hpp", "gemm_common.hpp", "gemm_reg.hpp", "gemm_launch.hpp", "gemm_big.hip")
 
 
@@ -60,6 +60,19 @@ def gemm_source_sha():
         with open(os.path.join(d, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def mxfp4_only():
+    """The MXFP4 variant alone on seeded gate-projection operands (16384 x
+    4096 activations, 4096 x 14336 weight): one JSON line."""
+    import torch
+    from spectral_split_quantized_amd import metis, synth
+    torch.cuda.set_device(0)
+    metis.load()
+    X, _ = synth.anisotropic_fast(TOKENS, HIDDEN, synth.FRAC_X, 1, device="cuda")
+    W, _ = synth.anisotropic_fast(HIDDEN, FFN, synth.FRAC_W, 2, device="cuda")
+    print(json.dumps(measure_mxfp4(metis, X, W, 0, None)), flush=True)
+    return 0
 
 
 def copy_calibration():
@@ -510,7 +523,7 @@ def measure_direct(mlp, inputs, t_last, mlp_ms=None, steps=4, warmup=2, sample_r
                             "below 1/8 of their 16-block's largest magnitude that dequantise to 0"}
 
 
-def measure_mxfp4(mlp, inputs, t_last, nvfp4_gemm_ms, reps=10, sample_rows=256):
+def measure_mxfp4(m, X, W, t_last, nvfp4_gemm_ms, reps=10, sample_rows=256):
     """The scaled-FP4 matrix-instruction variant: MXFP4 (block 32, E8M0
     power-of-two scales) operands of the gate projection, quantised by the
     library and multiplied on v_mfma_scale_f32_32x32x64_f8f6f4 with no
@@ -519,9 +532,6 @@ def measure_mxfp4(mlp, inputs, t_last, nvfp4_gemm_ms, reps=10, sample_rows=256):
     from the timed steps, and reports the forward error against the exact
     product on the same sampled rows and inputs as ``direct_nvfp4``."""
     import torch
-    m = mlp.metis
-    X = inputs["X_gu"][t_last % len(inputs["X_gu"])]
-    W = inputs["W_gate"][t_last % len(inputs["W_gate"])]
     T, H = X.shape
     F = W.shape[1]
     torch.cuda.synchronize()
@@ -550,8 +560,8 @@ def measure_mxfp4(mlp, inputs, t_last, nvfp4_gemm_ms, reps=10, sample_rows=256):
     return {"shape_MNK": [T, F, H], "gemm_ms": round(g_ms, 4), "gemm_tflops": round(tflops, 1),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": 10100.0, "unit": "TFLOP/s",
                          "frac": round(tflops / 10100.0, 4), "dtype": "fp4 e2m1 x fp4 e2m1, e8m0 block scales"},
-            "nvfp4_split_gemm_ms": round(nvfp4_gemm_ms, 4),
-            "speedup_vs_nvfp4_split_gemm": round(nvfp4_gemm_ms / g_ms, 3),
+            "nvfp4_split_gemm_ms": round(nvfp4_gemm_ms, 4) if nvfp4_gemm_ms else None,
+            "speedup_vs_nvfp4_split_gemm": round(nvfp4_gemm_ms / g_ms, 3) if nvfp4_gemm_ms else None,
             "quantize_both_operands_ms": round(q_ms, 3),
             "y_rel_fro_err_vs_exact": round(err, 6),
             "y_sample": "gate projection forward on %d evenly spaced token rows of the step-%d inputs (the rows "
@@ -773,10 +783,14 @@ def main():
                     help="skip the ceilings, the plain-NVFP4 comparison and the 1M x 4096 activation")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy three times (PMC byte-counter scale)")
+    ap.add_argument("--mxfp4-only", action="store_true",
+                    help="only the MXFP4 variant at the gate projection's shape (for kernel profiles)")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
         return 0
+    if args.mxfp4_only:
+        return mxfp4_only()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -890,7 +904,10 @@ def main():
         log("plain NVFP4 (k = 0) on the same workload")
         extras["direct_nvfp4"] = measure_direct(mlp, inputs, args.warmup + args.steps - 1, ms_per_step)
         log("MXFP4 variant on the scaled FP4 matrix instruction")
-        extras["mxfp4_variant"] = measure_mxfp4(mlp, inputs, args.warmup + args.steps - 1, roofline["avg_ms"])
+        t_last = args.warmup + args.steps - 1
+        extras["mxfp4_variant"] = measure_mxfp4(mlp.metis, inputs["X_gu"][t_last % len(inputs["X_gu"])],
+                                                inputs["W_gate"][t_last % len(inputs["W_gate"])], t_last,
+                                                roofline["avg_ms"])
         log("1M x 4096 activation")
         extras["c4_activation"] = measure_c4(dev, extras["ceilings"]["copy_GBps"])
         log("training loop through the autograd layer (refresh periods 1, 8, 32)")
