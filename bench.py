@@ -556,7 +556,15 @@ def measure_mxfp4(m, X, W, t_last, nvfp4_gemm_ms, reps=10, sample_rows=256):
     tflops = flop / (g_ms * 1e-3) / 1e12
     idx = torch.arange(0, T, T // sample_rows, device=X.device)
     exact = X[idx].float() @ W.float()
-    err = float(torch.linalg.norm(C[idx] - exact) / torch.linalg.norm(exact))
+
+    def rel(Y):
+        return float(torch.linalg.norm(Y[idx] - exact) / torch.linalg.norm(exact))
+    err = rel(C)
+    # plain NVFP4 with the same rounding (nearest), for a like-for-like error
+    cfg = m.make_config(k=0, rounding=m.RNE)
+    qxn = m.quantize(X, cfg, m.make_tag(0, m.OPERAND_X), 0, m.AXIS1)
+    qwn = m.quantize(W, cfg, m.make_tag(0, m.OPERAND_W), 0, m.AXIS0)
+    err_nv = rel(m.gemm_fwd(qxn, qwn))
     return {"shape_MNK": [T, F, H], "gemm_ms": round(g_ms, 4), "gemm_tflops": round(tflops, 1),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": 10100.0, "unit": "TFLOP/s",
                          "frac": round(tflops / 10100.0, 4), "dtype": "fp4 e2m1 x fp4 e2m1, e8m0 block scales"},
@@ -564,6 +572,7 @@ def measure_mxfp4(m, X, W, t_last, nvfp4_gemm_ms, reps=10, sample_rows=256):
             "speedup_vs_nvfp4_split_gemm": round(nvfp4_gemm_ms / g_ms, 3) if nvfp4_gemm_ms else None,
             "quantize_both_operands_ms": round(q_ms, 3),
             "y_rel_fro_err_vs_exact": round(err, 6),
+            "nvfp4_rne_y_rel_fro_err_vs_exact": round(err_nv, 6),
             "y_sample": "gate projection forward on %d evenly spaced token rows of the step-%d inputs (the rows "
                         "and inputs of direct_nvfp4)" % (sample_rows, t_last),
             "note": "a different format from the pages' NVFP4 (block 32 instead of 16, power-of-two scales, "
@@ -775,7 +784,7 @@ def main():
     ap.add_argument("--steps", type=int, default=16)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--cpu-cols", type=int, default=4096)
     ap.add_argument("--streams", type=int, default=3,
                     help="HIP streams per step (1: every call in order on one stream)")
