@@ -124,3 +124,19 @@ def test_mxfp4_argument_errors_are_synchronous():
     _expect(lib.metis_mxfp4_gemm(d, d, d, d, 64, 64, 1024, None, 64, None), metis.E_INVALID)
     # an empty product is a no-op
     assert lib.metis_mxfp4_gemm(d, d, d, d, 0, 64, 1024, d, 64, None) == metis.OK
+
+
+def test_header_is_plain_c99(tmp_path):
+    """include/metis.h compiles as strict C99 with no warnings (no C++ or
+    torch types in the boundary)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "h.c"
+    src.write_text('#include "metis.h"\nint main(void) { return metis_abi_version() == 1 ? 0 : 1; }\n')
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I",
+                        os.path.join(ROOT, "include"), "-c", str(src), "-o", str(tmp_path / "h.o")],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
