@@ -100,3 +100,25 @@ def test_layer_refresh_period():
         seen.append(lin.factors["W"].refreshed_at)
     metis.status_sync()
     assert seen == [0, 0, 0, 3, 3, 3, 6]
+
+
+def test_layer_batched_input_shape():
+    """A (batch, sequence, features) input: the layer flattens the leading
+    dimensions for the library and restores them on the output and gradient."""
+    c, X, W, D, lin = _layer(1)
+    x = X.float().reshape(4, X.shape[0] // 4, X.shape[1]).clone().requires_grad_(True)
+    y = lin(x)
+    assert tuple(y.shape) == (4, X.shape[0] // 4, W.shape[1])
+    y.backward(D.float().reshape(4, -1, W.shape[1]))
+    metis.status_sync()
+    assert tuple(x.grad.shape) == tuple(x.shape) and tuple(lin.weight.grad.shape) == tuple(W.shape)
+    # the same numbers as the flat call on the same step
+    lin2 = MetisLinear(W.shape[0], W.shape[1], c["k"], s=c["s"], l_k=c["l_k"], rounding=c["rounding"],
+                       weight=W.float())
+    x2 = X.float().clone().requires_grad_(True)
+    y2 = lin2(x2)
+    y2.backward(D.float())
+    metis.status_sync()
+    assert torch.equal(y.reshape(y2.shape), y2)
+    assert torch.equal(x.grad.reshape(x2.grad.shape), x2.grad)
+    assert torch.equal(lin.weight.grad, lin2.weight.grad)

@@ -126,3 +126,15 @@ def test_full_size_gate_projection_sampled():
     assert np.array_equal(qw.codes[cols].cpu().numpy(), b[0]) and np.array_equal(qw.scales[cols].cpu().numpy(), b[1])
     got = C[rows][:, cols].cpu().double().numpy()
     assert np.all(np.abs(got - mxfp4.gemm(a, b)) <= _bound(a, b, H))
+
+
+@pytest.mark.parametrize("axis", [1, 0])
+def test_quantize_strided_input(axis):
+    """A view into a wider row-major buffer (leading dimension > columns)."""
+    wide = _inputs(96, 224, 17, torch.float32, axis)
+    x = wide[:, :160] if axis == 1 else wide[:64, :200]
+    say("mxfp4 quantize strided view %s (ld %d) axis %d" % (tuple(x.shape), x.stride(0), axis))
+    q = metis.mxfp4_quantize(wide.cuda()[:x.shape[0], :x.shape[1]], axis)
+    metis.status_sync()
+    oc, osc = mxfp4.quantize(x.double().numpy(), axis)
+    assert np.array_equal(q.scales.cpu().numpy(), osc) and np.array_equal(q.codes.cpu().numpy(), oc)
