@@ -409,10 +409,14 @@ def mxfp4_quantize(M, axis, out=None):
     """MXFP4 codes and scales of M along K axis ``axis`` (1: along rows, 0:
     down columns, giving the quantised transpose)."""
     lib = load()
+    if M.dim() != 2 or M.stride(1) != 1:
+        raise ValueError("M must be a row-major matrix (unit column stride)")
     rows, cols = M.shape
     outer, k_len = (rows, cols) if axis == 1 else (cols, rows)
     if out is None:
         out = MX4(outer, k_len, M.device)
+    elif (out.outer, out.k_len) != (outer, k_len):
+        raise ValueError("out holds a %d x %d operand, not %d x %d" % (out.outer, out.k_len, outer, k_len))
     _check(lib.metis_mxfp4_quantize(_ptr(M), _dtype_code(M), rows, cols, M.stride(0), axis,
                                     _ptr(out.codes), _ptr(out.scales), _stream()))
     return out
@@ -421,8 +425,12 @@ def mxfp4_quantize(M, axis, out=None):
 def mxfp4_gemm(a, b, C=None):
     """C = A-hat B-hat^T of two MXFP4 operands (metis_mxfp4_gemm), binary32."""
     lib = load()
+    if a.k_len != b.k_len:
+        raise ValueError("inner dimensions differ: %d and %d" % (a.k_len, b.k_len))
     if C is None:
         C = torch.empty(a.outer, b.outer, dtype=torch.float32, device=a.codes.device)
+    elif C.dtype != torch.float32 or tuple(C.shape) != (a.outer, b.outer) or C.stride(1) != 1:
+        raise ValueError("C must be a float32 %d x %d row-major matrix" % (a.outer, b.outer))
     _check(lib.metis_mxfp4_gemm(_ptr(a.codes), _ptr(a.scales), _ptr(b.codes), _ptr(b.scales), a.outer,
                                 b.outer, a.k_len, _ptr(C), C.stride(0), _stream()))
     return C

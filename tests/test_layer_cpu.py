@@ -27,3 +27,14 @@ def test_set_step_reaches_every_layer():
                                 MetisLinear(32, 16, 2, layer=1, device="cpu"))
     set_step(model, 9)
     assert [m.step for m in model if isinstance(m, MetisLinear)] == [9, 9]
+
+
+def test_mxfp4_binding_rejects_mismatched_operands():
+    a = metis.MX4(32, 1024, device="cpu")
+    b = metis.MX4(32, 2048, device="cpu")
+    with pytest.raises(ValueError):
+        metis.mxfp4_gemm(a, b)
+    with pytest.raises(ValueError):
+        metis.mxfp4_quantize(torch.zeros(64, 64)[:, ::2], 1)
+    with pytest.raises(ValueError):
+        metis.mxfp4_quantize(torch.zeros(64, 64), 1, out=metis.MX4(32, 64, device="cpu"))
