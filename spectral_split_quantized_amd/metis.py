@@ -199,6 +199,14 @@ class QOperand:
                          self.R_ax1._c() if self.R_ax1 else z)
 
 
+
+def _out_check(T, rows, cols, name):
+    """A caller-provided output must be a float32 rows x cols row-major view:
+    the library writes rows x cols values at its leading dimension."""
+    if T.dtype != torch.float32 or tuple(T.shape) != (rows, cols) or T.stride(1) != 1:
+        raise ValueError("%s must be a float32 %d x %d row-major matrix" % (name, rows, cols))
+    return T
+
 def _workspace(nbytes, device):
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
@@ -261,6 +269,7 @@ def gemm_fwd(xq, wq, Y=None, workspace=None):
     lib = load()
     if Y is None:
         Y = torch.empty(xq.rows, wq.cols, dtype=torch.float32, device=xq.R_ax1.codes.device)
+    _out_check(Y, xq.rows, wq.cols, "Y")
     xc, wc = xq._c(), wq._c()
     need = lib.metis_gemm_fwd_workspace(ctypes.byref(xc), ctypes.byref(wc))
     ws = workspace if workspace is not None and workspace.numel() >= need else _workspace(need, Y.device)
@@ -277,6 +286,10 @@ def gemm_bwd(dq, wq, xq, dX=None, dW=None, want_dx=True, want_dw=True, workspace
         dX = torch.empty(dq.rows, wq.rows, dtype=torch.float32, device=dev)
     if want_dw and dW is None:
         dW = torch.empty(xq.cols, dq.cols, dtype=torch.float32, device=dev)
+    if want_dx:
+        _out_check(dX, dq.rows, wq.rows, "dX")
+    if want_dw:
+        _out_check(dW, xq.cols, dq.cols, "dW")
     dc, wc, xc = dq._c(), wq._c(), xq._c()
     need = lib.metis_gemm_bwd_workspace(ctypes.byref(dc), ctypes.byref(wc), ctypes.byref(xc))
     ws = workspace if workspace is not None and workspace.numel() >= need else _workspace(need, dev)
@@ -311,6 +324,7 @@ def gemm_fwd_prepared(xq, wq, workspace, Y=None):
     lib = load()
     if Y is None:
         Y = torch.empty(xq.rows, wq.cols, dtype=torch.float32, device=xq.R_ax1.codes.device)
+    _out_check(Y, xq.rows, wq.cols, "Y")
     xc, wc = xq._c(), wq._c()
     ws = _gemm_ws(lib.metis_gemm_fwd_workspace(ctypes.byref(xc), ctypes.byref(wc)), workspace)
     _check(lib.metis_gemm_fwd_prepared(ctypes.byref(xc), ctypes.byref(wc), _ptr(Y), Y.stride(0), _ptr(ws),
@@ -337,6 +351,10 @@ def gemm_bwd_prepared(dq, wq, xq, workspace, dX=None, dW=None, want_dx=True, wan
         dX = torch.empty(dq.rows, wq.rows, dtype=torch.float32, device=dev)
     if want_dw and dW is None:
         dW = torch.empty(xq.cols, dq.cols, dtype=torch.float32, device=dev)
+    if want_dx:
+        _out_check(dX, dq.rows, wq.rows, "dX")
+    if want_dw:
+        _out_check(dW, xq.cols, dq.cols, "dW")
     dc, wc, xc = dq._c(), wq._c(), xq._c()
     ws = _gemm_ws(lib.metis_gemm_bwd_workspace(ctypes.byref(dc), ctypes.byref(wc), ctypes.byref(xc)), workspace)
     _check(lib.metis_gemm_bwd_prepared(ctypes.byref(dc), ctypes.byref(wc), ctypes.byref(xc),
@@ -429,8 +447,7 @@ def mxfp4_gemm(a, b, C=None):
         raise ValueError("inner dimensions differ: %d and %d" % (a.k_len, b.k_len))
     if C is None:
         C = torch.empty(a.outer, b.outer, dtype=torch.float32, device=a.codes.device)
-    elif C.dtype != torch.float32 or tuple(C.shape) != (a.outer, b.outer) or C.stride(1) != 1:
-        raise ValueError("C must be a float32 %d x %d row-major matrix" % (a.outer, b.outer))
+    _out_check(C, a.outer, b.outer, "C")
     _check(lib.metis_mxfp4_gemm(_ptr(a.codes), _ptr(a.scales), _ptr(b.codes), _ptr(b.scales), a.outer,
                                 b.outer, a.k_len, _ptr(C), C.stride(0), _stream()))
     return C

@@ -38,3 +38,12 @@ def test_mxfp4_binding_rejects_mismatched_operands():
         metis.mxfp4_quantize(torch.zeros(64, 64)[:, ::2], 1)
     with pytest.raises(ValueError):
         metis.mxfp4_quantize(torch.zeros(64, 64), 1, out=metis.MX4(32, 64, device="cpu"))
+
+
+def test_gemm_bindings_reject_mis_shaped_outputs():
+    x = metis.QOperand(64, 32, 0, metis.AXIS1, device="cpu")
+    w = metis.QOperand(32, 48, 0, metis.AXIS0, device="cpu")
+    with pytest.raises(ValueError):
+        metis.gemm_fwd(x, w, Y=torch.empty(64, 40))
+    with pytest.raises(ValueError):
+        metis.gemm_fwd(x, w, Y=torch.empty(64, 48, dtype=torch.float64))
