@@ -560,6 +560,10 @@ def measure_mxfp4(m, X, W, t_last, nvfp4_gemm_ms, reps=10, sample_rows=256):
     def rel(Y):
         return float(torch.linalg.norm(Y[idx] - exact) / torch.linalg.norm(exact))
     err = rel(C)
+    # stochastic rounding, as the pages' default and the bench's NVFP4 path
+    qxs = m.mxfp4_quantize(X, 1, rounding=m.SR, seed=0, tag=m.make_tag(0, m.OPERAND_X), step=t_last)
+    qws = m.mxfp4_quantize(W, 0, rounding=m.SR, seed=0, tag=m.make_tag(0, m.OPERAND_W), step=t_last)
+    err_sr = rel(m.mxfp4_gemm(qxs, qws))
     # plain NVFP4 with the same rounding (nearest), for a like-for-like error
     cfg = m.make_config(k=0, rounding=m.RNE)
     qxn = m.quantize(X, cfg, m.make_tag(0, m.OPERAND_X), 0, m.AXIS1)
@@ -572,11 +576,12 @@ def measure_mxfp4(m, X, W, t_last, nvfp4_gemm_ms, reps=10, sample_rows=256):
             "speedup_vs_nvfp4_split_gemm": round(nvfp4_gemm_ms / g_ms, 3) if nvfp4_gemm_ms else None,
             "quantize_both_operands_ms": round(q_ms, 3),
             "y_rel_fro_err_vs_exact": round(err, 6),
+            "y_rel_fro_err_vs_exact_sr": round(err_sr, 6),
             "nvfp4_rne_y_rel_fro_err_vs_exact": round(err_nv, 6),
             "y_sample": "gate projection forward on %d evenly spaced token rows of the step-%d inputs (the rows "
                         "and inputs of direct_nvfp4)" % (sample_rows, t_last),
             "note": "a different format from the pages' NVFP4 (block 32 instead of 16, power-of-two scales, "
-                    "no tensor scale, no spectral split, round to nearest)"}
+                    "no tensor scale, no spectral split; y_rel_fro_err_vs_exact rounds to nearest, _sr stochastically)"}
 
 
 def measure_c4(dev, copy_gbps):

@@ -232,8 +232,10 @@ metis_status metis_status_sync(void *stream);
  * (MX) one: 32 consecutive elements along K share a power-of-two scale
  * X = 2^(floor(log2 amax) - 2), stored as an E8M0 byte (exponent + 127,
  * clamped to [-127, 127]; an all-zero block stores 0); each element is x / X
- * rounded to the nearest E2M1 value, ties to even mantissa, saturating at 6.
- * No spectral split and no stochastic rounding on this path.
+ * rounded to the nearest E2M1 value, ties to even mantissa, saturating at 6
+ * (rounding METIS_RNE), or stochastically (METIS_SR) with the Philox draws of
+ * seed, tag and step indexed by the element's position outer * K + k in the
+ * output layout.  No spectral split on this path.
  *
  * metis_mxfp4_quantize: M is rows x cols, row-major with leading dimension
  * ld, bf16 or fp32 (dtype), finite (a non-finite block sets the numeric flag
@@ -253,7 +255,8 @@ metis_status metis_status_sync(void *stream);
  * instruction of gfx950.  M or N == 0 returns METIS_OK with nothing enqueued.
  * Argument errors return synchronously; nothing is allocated. */
 metis_status metis_mxfp4_quantize(const void *M, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
-                                  int32_t axis, uint8_t *codes, uint8_t *scales, void *stream);
+                                  int32_t axis, int32_t rounding, uint64_t seed, uint32_t tag, int64_t step,
+                                  uint8_t *codes, uint8_t *scales, void *stream);
 metis_status metis_mxfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *b_codes,
                               const uint8_t *b_scales, int64_t M, int64_t N, int64_t K, float *C,
                               int64_t ldc, void *stream);

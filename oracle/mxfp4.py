@@ -15,7 +15,12 @@ plainest reading:
     mantissa), saturating at +-6: a block's amax maps into [4, 8), so values
     of 7 and above land on 6;
   * an all-zero block takes the smallest scale (byte 0).
-Rounding is to nearest only (no stochastic variant).
+Rounding is to nearest, or stochastic with the generator of the NVFP4 path
+(Philox4x32-10, 16-bit draws; oracle/philox.py): an element's draw is indexed
+by its position in the quantised output's own row-major layout (outer x K),
+and it rounds up to the next E2M1 value iff draw * 2**-16 is below the
+element's fractional position between its two neighbours (values from 6 up
+saturate to 6).
 
 Every step is exact in float64 (and in binary32): the exponent is read off
 amax, X is a power of two and x / X only shifts exponents, so the codes are
@@ -29,7 +34,8 @@ the quantised transpose).
 
 import numpy as np
 
-from .formats import E2M1_GRID, e2m1_rne
+from . import philox
+from .formats import E2M1_GRID, e2m1_rne, e2m1_sr
 
 BLOCK = 32
 EMAX_ELEM = 2
@@ -47,8 +53,9 @@ def block_exponent(amax):
     return e
 
 
-def quantize(x, axis=1):
-    """MXFP4 codes and E8M0 scales of matrix x along K axis ``axis``.
+def quantize(x, axis=1, rounding="rne", seed=0, tag=0, step=0):
+    """MXFP4 codes and E8M0 scales of matrix x along K axis ``axis``, rounded
+    to nearest ("rne") or stochastically ("sr", draws from seed, tag, step).
     Returns (codes [outer, K/2] uint8, scales [outer, K/32] uint8)."""
     x = np.asarray(x, np.float64)
     if axis == 0:
@@ -59,7 +66,14 @@ def quantize(x, axis=1):
     blocks = x.reshape(outer, k // BLOCK, BLOCK)
     e = block_exponent(np.abs(blocks).max(axis=2))
     y = blocks * np.ldexp(1.0, -e)[:, :, None]
-    mag = e2m1_rne(np.abs(y))
+    if rounding == "rne":
+        mag = e2m1_rne(np.abs(y))
+    elif rounding == "sr":
+        idx = (np.arange(outer, dtype=np.uint64)[:, None] * np.uint64(k) + np.arange(k, dtype=np.uint64)[None, :])
+        u = philox.uniform_from_halves(philox.halves(idx.ravel(), seed, tag, step))
+        mag = e2m1_sr(np.abs(y), u.reshape(outer, k // BLOCK, BLOCK))
+    else:
+        raise ValueError("rounding must be 'rne' or 'sr'")
     code = (mag | np.where(y < 0, 8, 0)).astype(np.uint8).reshape(outer, k)
     packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
     return packed, (e + 127).astype(np.uint8)

@@ -1252,17 +1252,20 @@ metis_status metis_status_sync(void* stream) {
 // ------------------------------------------------------------- MXFP4 --
 
 metis_status metis_mxfp4_quantize(const void* M, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
-                                  int32_t axis, uint8_t* codes, uint8_t* scales, void* stream) {
+                                  int32_t axis, int32_t rounding, uint64_t seed, uint32_t tag, int64_t step,
+                                  uint8_t* codes, uint8_t* scales, void* stream) {
   if (!M || !codes || !scales) return fail(METIS_E_INVALID, "mxfp4_quantize: null pointer");
   if (dtype != METIS_BF16 && dtype != METIS_F32) return fail(METIS_E_INVALID, "mxfp4_quantize: dtype %d", dtype);
   if (rows <= 0 || cols <= 0 || ld < cols) return fail(METIS_E_INVALID, "mxfp4_quantize: shape %lld x %lld, ld %lld",
                                                      (long long)rows, (long long)cols, (long long)ld);
   if (axis != 0 && axis != 1) return fail(METIS_E_INVALID, "mxfp4_quantize: axis %d", axis);
+  if (rounding != METIS_RNE && rounding != METIS_SR) return fail(METIS_E_INVALID, "mxfp4_quantize: rounding %d", rounding);
+  if (step < 0) return fail(METIS_E_INVALID, "mxfp4_quantize: step %lld", (long long)step);
   const int64_t k_len = axis ? cols : rows;
   if (k_len % 32) return fail(METIS_E_INVALID, "mxfp4_quantize: K = %lld is not a multiple of 32", (long long)k_len);
   if ((uintptr_t)codes & 15) return fail(METIS_E_INVALID, "mxfp4_quantize: codes not 16-byte aligned");
   hipStream_t st = (hipStream_t)stream;
-  MxQuantParams q{M, dtype, rows, cols, ld, codes, scales};
+  MxQuantParams q{M, dtype, rows, cols, ld, codes, scales, rounding == METIS_SR, seed, tag, (uint32_t)step};
   if (axis == 1) {
     hipLaunchKernelGGL(mx_quant_rows_kernel, dim3(grid1(rows * (cols >> 5), 256)), dim3(256), 0, st, q);
   } else {

@@ -8,7 +8,8 @@
 // power-of-two scale X = 2^(floor(log2 amax) - 2), stored as an E8M0 byte
 // (e + 127, clamped to [-127, 127]; an all-zero block takes byte 0); each
 // element is x / X rounded to the nearest E2M1 value (ties to even mantissa,
-// saturating at 6).  Every step is exact in binary32.
+// saturating at 6), or stochastically with the path's Philox draws indexed
+// by the output position outer * K + k.  Every step is exact in binary32.
 #pragma once
 
 #include "gemm_common.hpp"
@@ -21,6 +22,9 @@ struct MxQuantParams {
   int64_t rows, cols, ld;
   uint8_t* codes;   // [outer][K / 2]
   uint8_t* scales;  // [outer][K / 32]
+  int sr;           // stochastic rounding (else nearest)
+  uint64_t seed;
+  uint32_t tag, step;
 };
 
 // shared exponent of a block with largest magnitude amax
@@ -31,8 +35,9 @@ __device__ inline int mx_exponent(float amax) {
   return max(-127, min(127, ex - 1 - 2));
 }
 
-// 32 values -> 16 code bytes (as 4 words) and the scale byte
-__device__ inline uint8_t mx_encode32(const float* v, uint32_t* w) {
+// 32 values -> 16 code bytes (as 4 words) and the scale byte; with draws
+// (complemented 16-bit draws, one per element) the rounding is stochastic
+__device__ inline uint8_t mx_encode32(const float* v, uint32_t* w, const uint32_t* hc) {
   float amax = 0.0f;
 #pragma unroll
   for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
@@ -44,12 +49,26 @@ __device__ inline uint8_t mx_encode32(const float* v, uint32_t* w) {
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const float y = ldexpf(v[8 * q + t], -e);  // exact: a power-of-two scaling
-      const uint32_t c = e2m1_rne(fabsf(y)) | (y < 0.0f ? 8u : 0u);
+      const uint32_t m = hc ? e2m1_sr_c(fabsf(y), hc[8 * q + t]) : e2m1_rne(fabsf(y));
+      const uint32_t c = m | (y < 0.0f ? 8u : 0u);
       word |= c << (4 * t);
     }
     w[q] = word;
   }
   return (uint8_t)(e + 127);
+}
+
+// complemented draws of 32 consecutive positions e0 .. e0 + 31 of the
+// output layout (e0 % 32 == 0)
+__device__ inline void mx_draws32(uint64_t e0, const MxQuantParams& p, uint32_t (&hc)[32]) {
+  uint32_t a[16], b[16];
+  draws16(e0, p.tag, p.step, p.seed, a);
+  draws16(e0 + 16, p.tag, p.step, p.seed, b);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    hc[j] = a[j];
+    hc[16 + j] = b[j];
+  }
 }
 
 // K along a row: one thread per 32-element block
@@ -61,8 +80,9 @@ __global__ void mx_quant_rows_kernel(MxQuantParams p) {
   float v[32];
 #pragma unroll
   for (int j = 0; j < 32; ++j) v[j] = load_as_float(p.src, p.dtype, r * p.ld + b * 32 + j);
-  uint32_t w[4];
-  p.scales[r * nb + b] = mx_encode32(v, w);
+  uint32_t w[4], hc[32];
+  if (p.sr) mx_draws32((uint64_t)r * p.cols + b * 32, p, hc);
+  p.scales[r * nb + b] = mx_encode32(v, w, p.sr ? hc : nullptr);
   *(uint4*)(p.codes + r * (p.cols >> 1) + b * 16) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
@@ -75,8 +95,9 @@ __global__ void mx_quant_cols_kernel(MxQuantParams p) {
   float v[32];
 #pragma unroll
   for (int j = 0; j < 32; ++j) v[j] = load_as_float(p.src, p.dtype, (b * 32 + j) * p.ld + c);
-  uint32_t w[4];
-  p.scales[c * (p.rows >> 5) + b] = mx_encode32(v, w);
+  uint32_t w[4], hc[32];
+  if (p.sr) mx_draws32((uint64_t)c * p.rows + b * 32, p, hc);
+  p.scales[c * (p.rows >> 5) + b] = mx_encode32(v, w, p.sr ? hc : nullptr);
   *(uint4*)(p.codes + c * (p.rows >> 1) + b * 16) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 

@@ -73,7 +73,7 @@ def load():
     lib.metis_gemm_fwd_workspace.restype = sz
     lib.metis_gemm_bwd_workspace.argtypes = [ctypes.POINTER(_QOperand)] * 3
     lib.metis_gemm_bwd_workspace.restype = sz
-    lib.metis_mxfp4_quantize.argtypes = [P, i32, i64, i64, i64, i32, P, P, P]
+    lib.metis_mxfp4_quantize.argtypes = [P, i32, i64, i64, i64, i32, i32, ctypes.c_uint64, u32, i64, P, P, P]
     lib.metis_mxfp4_quantize.restype = i32
     lib.metis_mxfp4_gemm.argtypes = [P, P, P, P, i64, i64, i64, P, i64, P]
     lib.metis_mxfp4_gemm.restype = i32
@@ -423,9 +423,10 @@ class MX4:
         self.outer, self.k_len = outer, k_len
 
 
-def mxfp4_quantize(M, axis, out=None):
+def mxfp4_quantize(M, axis, out=None, rounding=RNE, seed=0, tag=0, step=0):
     """MXFP4 codes and scales of M along K axis ``axis`` (1: along rows, 0:
-    down columns, giving the quantised transpose)."""
+    down columns, giving the quantised transpose), rounded to nearest (RNE)
+    or stochastically (SR, draws from seed, tag and step)."""
     lib = load()
     if M.dim() != 2 or M.stride(1) != 1:
         raise ValueError("M must be a row-major matrix (unit column stride)")
@@ -435,8 +436,8 @@ def mxfp4_quantize(M, axis, out=None):
         out = MX4(outer, k_len, M.device)
     elif (out.outer, out.k_len) != (outer, k_len):
         raise ValueError("out holds a %d x %d operand, not %d x %d" % (out.outer, out.k_len, outer, k_len))
-    _check(lib.metis_mxfp4_quantize(_ptr(M), _dtype_code(M), rows, cols, M.stride(0), axis,
-                                    _ptr(out.codes), _ptr(out.scales), _stream()))
+    _check(lib.metis_mxfp4_quantize(_ptr(M), _dtype_code(M), rows, cols, M.stride(0), axis, rounding, seed,
+                                    tag, step, _ptr(out.codes), _ptr(out.scales), _stream()))
     return out
 
 

@@ -110,12 +110,13 @@ def test_mxfp4_argument_errors_are_synchronous():
     lib = metis.load()
     d = ctypes.c_void_p(4096)  # 16-byte aligned stand-in, never dereferenced
     # quantiser: null input, K not a multiple of 32, bad axis, misaligned codes
-    _expect(lib.metis_mxfp4_quantize(None, 0, 64, 64, 64, 1, d, d, None), metis.E_INVALID)
-    _expect(lib.metis_mxfp4_quantize(d, 0, 64, 48, 48, 1, d, d, None), metis.E_INVALID)
-    _expect(lib.metis_mxfp4_quantize(d, 0, 48, 64, 64, 0, d, d, None), metis.E_INVALID)
-    _expect(lib.metis_mxfp4_quantize(d, 0, 64, 64, 64, 2, d, d, None), metis.E_INVALID)
-    _expect(lib.metis_mxfp4_quantize(d, 0, 64, 64, 64, 1, ctypes.c_void_p(4100), d, None), metis.E_INVALID)
-    _expect(lib.metis_mxfp4_quantize(d, 0, 64, 64, 32, 1, d, d, None), metis.E_INVALID)
+    _expect(lib.metis_mxfp4_quantize(None, 0, 64, 64, 64, 1, 0, 0, 0, 0, d, d, None), metis.E_INVALID)
+    _expect(lib.metis_mxfp4_quantize(d, 0, 64, 48, 48, 1, 0, 0, 0, 0, d, d, None), metis.E_INVALID)
+    _expect(lib.metis_mxfp4_quantize(d, 0, 48, 64, 64, 0, 0, 0, 0, 0, d, d, None), metis.E_INVALID)
+    _expect(lib.metis_mxfp4_quantize(d, 0, 64, 64, 64, 2, 0, 0, 0, 0, d, d, None), metis.E_INVALID)
+    _expect(lib.metis_mxfp4_quantize(d, 0, 64, 64, 64, 1, 0, 0, 0, 0, ctypes.c_void_p(4100), d, None), metis.E_INVALID)
+    _expect(lib.metis_mxfp4_quantize(d, 0, 64, 64, 32, 1, 0, 0, 0, 0, d, d, None), metis.E_INVALID)
+    _expect(lib.metis_mxfp4_quantize(d, 0, 64, 64, 64, 1, 7, 0, 0, 0, d, d, None), metis.E_INVALID)
     # GEMM: K not a multiple of 1024, M or N not a multiple of 8, ldc < N, misaligned scales, null C
     _expect(lib.metis_mxfp4_gemm(d, d, d, d, 64, 64, 512, d, 64, None), metis.E_UNSUPPORTED)
     _expect(lib.metis_mxfp4_gemm(d, d, d, d, 60, 64, 1024, d, 64, None), metis.E_UNSUPPORTED)

@@ -3,7 +3,8 @@ against oracle/mxfp4.py.
 
 The quantiser's codes and E8M0 scales are exact in binary32 and must match
 the oracle bit for bit, on both K axes and both input dtypes, including an
-all-zero block, negative zeros, saturating blocks and tiny magnitudes.  The
+all-zero block, negative zeros, saturating blocks and tiny magnitudes, with
+nearest and stochastic rounding.  The
 GEMM's products are exact and only the fp32 accumulation rounds: every output
 is held to the recursive-summation bound K * 2**-24 * (|A| |B|^T), on ragged
 multi-tile shapes from oracle-made codes, end to end, and at the gate
@@ -57,14 +58,16 @@ def _bound(a, b, k):
     return k * 2.0 ** -24 * (np.abs(mxfp4.dequantize(*a)) @ np.abs(mxfp4.dequantize(*b)).T) + 1e-300
 
 
+@pytest.mark.parametrize("rounding", ["rne", "sr"])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("axis,shape", [(1, (96, 160)), (0, (160, 96)), (1, (40, 1024)), (0, (1024, 72))])
-def test_quantize_bit_exact(dtype, axis, shape):
+def test_quantize_bit_exact(dtype, axis, shape, rounding):
     x = _inputs(*shape, 11 + shape[0], dtype, axis)
-    say("mxfp4 quantize %s axis %d %s" % (tuple(shape), axis, dtype))
-    q = metis.mxfp4_quantize(x.cuda(), axis)
+    say("mxfp4 quantize %s axis %d %s %s" % (tuple(shape), axis, dtype, rounding))
+    r = metis.SR if rounding == "sr" else metis.RNE
+    q = metis.mxfp4_quantize(x.cuda(), axis, rounding=r, seed=0x1234567890AB, tag=0x5A3C, step=7)
     metis.status_sync()
-    oc, osc = mxfp4.quantize(x.double().numpy(), axis)
+    oc, osc = mxfp4.quantize(x.double().numpy(), axis, rounding, seed=0x1234567890AB, tag=0x5A3C, step=7)
     assert np.array_equal(q.scales.cpu().numpy(), osc)
     assert np.array_equal(q.codes.cpu().numpy(), oc)
 

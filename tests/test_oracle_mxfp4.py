@@ -115,3 +115,34 @@ def test_gemm_against_loops():
     da, db = mxfp4.dequantize(*a), mxfp4.dequantize(*b)
     want = [[sum(da[i, t] * db[j, t] for t in range(64)) for j in range(2)] for i in range(3)]
     assert np.allclose(mxfp4.gemm(a, b), want, rtol=1e-15, atol=0)
+
+
+def test_stochastic_rounding_picks_a_neighbour_and_is_unbiased():
+    """SR codes are the two E2M1 neighbours of x / X (6 when saturated), the
+    draws are deterministic in (seed, tag, step), and the mean over many tags
+    approaches x within the binomial bound."""
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((4, 64)) * 3.0
+    a = mxfp4.quantize(x, rounding="sr", seed=1, tag=5, step=2)
+    b = mxfp4.quantize(x, rounding="sr", seed=1, tag=5, step=2)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert not np.array_equal(a[0], mxfp4.quantize(x, rounding="sr", seed=1, tag=6, step=2)[0])
+    scale = np.repeat(np.ldexp(1.0, a[1].astype(np.int64) - 127), 32, axis=1)
+    y = np.abs(x) / scale
+    got = np.abs(mxfp4.dequantize(*a)) / scale
+    grid = np.array(GRID)
+    lo = grid[np.searchsorted(grid, np.minimum(y, 6.0), side="right") - 1]
+    hi = grid[np.minimum(np.searchsorted(grid, np.minimum(y, 6.0), side="right"), 7)]
+    assert np.all((got == lo) | (got == hi) | ((y >= 6) & (got == 6)))
+    # unbiasedness on one row over 400 tags
+    v = np.array([[0.3, -1.1, 2.6, 4.9, 0.0, 5.5] + [1.0] * 26])
+    acc = np.zeros(32)
+    n = 400
+    for t in range(n):
+        acc += mxfp4.dequantize(*mxfp4.quantize(v, rounding="sr", seed=3, tag=t))[0]
+    mean = acc / n
+    s = 2.0 ** (mxfp4.block_exponent(np.abs(v).max())) * 1.0
+    # per element: |mean - v| <= 4 sigma of a Bernoulli mixture with gap <= 2 s
+    assert np.all(np.abs(mean - v[0]) <= 4 * (2 * s) * 0.5 / np.sqrt(n) + 1e-12)
+    with pytest.raises(ValueError):
+        mxfp4.quantize(v, rounding="up")
