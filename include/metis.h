@@ -243,8 +243,10 @@ metis_status metis_status_sync(void *stream);
  * axis: 1 along a row, 0 down a column (the output is then the quantised
  * transpose).  With outer = the other dimension and K its length: codes is
  * outer x K/2 bytes (element 2i in the low nibble of byte i), 16-byte
- * aligned; scales is outer x K/32 E8M0 bytes.  K % 32 == 0.  Both buffers are
- * caller-owned device memory, written on stream.
+ * aligned; scales is outer x K/32 E8M0 bytes.  K % 32 == 0, rounding is
+ * METIS_RNE or METIS_SR and step >= 0 (METIS_E_INVALID otherwise); with
+ * axis 0, rows / 32 <= 65535 (METIS_E_UNSUPPORTED otherwise).  Both buffers
+ * are caller-owned device memory, written on stream.
  *
  * metis_mxfp4_gemm: C = A B^T in fp32 (row-major, leading dimension ldc >= N)
  * of two MXFP4 operands in that layout, A with M rows and B with N rows of
