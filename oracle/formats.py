@@ -44,12 +44,25 @@ def e2m1_floor(y):
     return (np.searchsorted(E2M1_GRID, y, side="right") - 1).astype(np.uint8)
 
 
+SR_FRACTION_BITS = 22
+
+
 def e2m1_sr(y, u):
     """Stochastic rounding of y >= 0 onto the E2M1 grid with uniforms u.
 
     y >= 6 saturates to 6.  Otherwise lo = floor-grid(y), hi = the next grid
     value, p = (y - lo) / (hi - lo) (exact: hi - lo is a power of two and
-    y - lo is exact by Sterbenz), and the result is hi iff u < p.
+    y - lo is exact by Sterbenz), and the result is hi iff u < p22, where p22
+    is p truncated to SR_FRACTION_BITS = 22 binary fraction digits,
+    floor(p * 2**22) / 2**22.
+
+    The truncation is a reading (the pages give stochastic rounding without
+    a precision): a binary32 value in [1, 6) carries exactly 22 bits below
+    the E2M1 spacing, so p22 = p there; only values below 1 (E2M1's
+    subnormal range), whose binary32 form has further bits, lose
+    probability mass below 2**-22.  With 16-bit uniforms the decision
+    u < p22 is that of adding a random integer to those 22 bits and
+    truncating, the classic way stochastic rounding is built.
     """
     y = np.asarray(y, np.float64)
     u = np.asarray(u, np.float64)
@@ -60,7 +73,8 @@ def e2m1_sr(y, u):
     glo = E2M1_GRID[lo]
     ghi = E2M1_GRID[hi]
     p = (ys - glo) / (ghi - glo)
-    m = np.where(u < p, hi, lo).astype(np.uint8)
+    p22 = np.floor(p * 2.0 ** SR_FRACTION_BITS) / 2.0 ** SR_FRACTION_BITS
+    m = np.where(u < p22, hi, lo).astype(np.uint8)
     return np.where(sat, np.uint8(7), m)
 
 

@@ -19,8 +19,8 @@ Rounding is to nearest, or stochastic with the generator of the NVFP4 path
 (Philox4x32-10, 16-bit draws; oracle/philox.py): an element's draw is indexed
 by its position in the quantised output's own row-major layout (outer x K),
 and it rounds up to the next E2M1 value iff draw * 2**-16 is below the
-element's fractional position between its two neighbours (values from 6 up
-saturate to 6).
+element's fractional position between its two neighbours, truncated to 22
+binary digits (formats.e2m1_sr; values from 6 up saturate to 6).
 
 Every step is exact in float64 (and in binary32): the exponent is read off
 amax, X is a power of two and x / X only shifts exponents, so the codes are

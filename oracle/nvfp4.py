@@ -13,7 +13,8 @@ The pages leave the scale rules open; the readings taken are:
   Q6  s_eff = RN32(s_b * s_g); inv = RN32(1 / s_eff)
   Q7  y = RN32(|x| * inv); an input of +-0 always gives magnitude 0
   Q8  RNE: nearest grid value, ties to even mantissa, saturate at 6.
-      SR: y >= 6 -> 6; otherwise hi iff u < (y - lo) / (hi - lo), with u the
+      SR: y >= 6 -> 6; otherwise hi iff u < p22, p22 = (y - lo) / (hi - lo)
+      truncated to 22 binary fraction digits (formats.e2m1_sr), with u the
       element's 16-bit Philox uniform (oracle.philox, 16-bit draws)
   Q9  code = sign(x) << 3 | m  (the sign bit of x is kept, also for zeros)
 

@@ -92,3 +92,39 @@ def test_signed_zero_codes():
     q = nvfp4.quantize(x, 1, "rne")
     codes = nvfp4.unpack_codes(q)[0]
     assert codes[1] == 0x8 and codes[2] == 0x8 and codes[3] == 0x0
+
+
+def test_e2m1_sr_golden():
+    rows = []
+    with open(os.path.join(GOLDEN, "e2m1_sr.txt")) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                a, h, c = line.split()
+                rows.append((np.float32(float(a)), int(h), int(c)))
+    y = np.array([r[0] for r in rows], dtype=np.float64)
+    u = np.array([r[1] for r in rows], dtype=np.float64) * 2.0 ** -16
+    want = [r[2] for r in rows]
+    assert list(formats.e2m1_sr(y, u)) == want
+
+
+def test_e2m1_sr_truncation_only_below_one():
+    # a binary32 y in [1, 6) has exactly 22 bits below its E2M1 spacing, so
+    # there the rule is the plain "hi iff u < p"; below 1 it differs only
+    # where p has bits past the 22nd and u sits within 2**-22 under p
+    rng = np.random.default_rng(7)
+    y = rng.uniform(1.0, 6.0, 200000).astype(np.float32).astype(np.float64)
+    h = rng.integers(0, 65536, y.size)
+    lo = formats.e2m1_floor(y)
+    glo, ghi = formats.E2M1_GRID[lo], formats.E2M1_GRID[np.minimum(lo + 1, 7)]
+    p = (y - glo) / (ghi - glo)
+    plain = np.where(h * 2.0 ** -16 < p, lo + 1, lo)
+    assert np.array_equal(formats.e2m1_sr(y, h * 2.0 ** -16), plain)
+    ys = rng.uniform(0.0, 1.0, 200000).astype(np.float32).astype(np.float64)
+    lo = formats.e2m1_floor(ys)
+    p = (ys - formats.E2M1_GRID[lo]) / 0.5
+    u = np.floor(p * 2 ** 16) * 2.0 ** -16          # the largest draw below p
+    m = formats.e2m1_sr(ys, u)
+    p22 = np.floor(p * 2 ** 22) / 2 ** 22
+    assert np.array_equal(m == lo + 1, u < p22)
+    assert np.any(u < p) and np.all((u < p22) <= (u < p))
