@@ -102,11 +102,17 @@ typedef struct {
  * n_outer = k, k_len = rows), S (binary32, not quantised), Q(V) (n_outer = k,
  * k_len = cols), and the residual along K = rows (R_ax0: n_outer = cols,
  * k_len = rows) and/or K = cols (R_ax1: n_outer = rows, k_len = cols).
- * k == 0 is direct NVFP4 (U, V, S unused). */
+ * k == 0 is direct NVFP4 (U, V, S unused).
+ * S: k binary32 values in device memory.  metis_quantize and
+ * metis_prepare_operand copy the factors' S into it when it is non-NULL on
+ * entry, so the operand keeps the singular values its codes were made with
+ * while later calls update the same factors; when it is NULL they set it to
+ * f->S, the live factor buffer, which the next decomposition of those factors
+ * overwrites. */
 typedef struct {
   int64_t rows, cols;
   int32_t k;
-  const float *S;
+  float *S;
   metis_q4 U, V, R_ax0, R_ax1;
 } metis_qoperand;
 
@@ -135,7 +141,9 @@ size_t metis_prepare_operand_workspace(int64_t rows, int64_t cols, const metis_c
  * f->refreshed_at is then set to step (host side, before the call returns).
  * Every call then projects P = M V, rediagonalises P^T P by Jacobi and writes
  * U = P R Lambda^-1/2, S = Lambda^1/2, V <- V R, so U S V^T = M V_old V_old^T.
- * Requires 1 <= k, k + s <= 96 and k + s <= min(l_k (or rows), cols).
+ * Requires 1 <= k, k + s <= 96 and k + s <= min(l_k (or rows), cols); with
+ * sample_rows != 0, rows <= 2^27 (METIS_E_UNSUPPORTED otherwise: the row
+ * sampler resolves the boundary of its key histogram among at most 4096 rows).
  * tag: layer << 16 | operand << 12 (Omega and the row sample take roles 4, 5). */
 metis_status metis_decompose(const void *M, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
                              const metis_config *cfg, int32_t sample_rows, uint32_t tag,
@@ -152,7 +160,8 @@ metis_status metis_decompose(const void *M, int32_t dtype, int64_t rows, int64_t
  * rounding (16-bit uniform per element).  out->S is set to f->S.
  * residual_out: optional rows x cols binary32 (ld = cols) copy of the exact
  * binary32 residual the quantiser consumed (for verification; NULL normally).
- * Requires K (rows for AXIS0, cols for AXIS1) to be a multiple of 16. */
+ * Requires K (rows for AXIS0, cols for AXIS1) to be a multiple of 16.
+ * out->S: see metis_qoperand (snapshot copy when non-NULL). */
 metis_status metis_quantize(const void *M, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
                             const metis_factors *f, const metis_config *cfg, uint32_t tag,
                             int64_t step, int32_t axes, metis_qoperand *out, float *residual_out,

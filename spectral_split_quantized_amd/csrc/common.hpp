@@ -139,18 +139,98 @@ __host__ __device__ inline uint32_t e2m1_rne(float y) {
 
 // Stochastic rounding with a 16-bit draw h (u = h 2^-16), given as its
 // complement hc = 0xFFFF - h: with position n + p (n its integer part, p in
-// [0, 1)) the code is n + 1 iff u < p, i.e. iff h < ceil(p 2^16).
-// z = y 2^(17-j) is exact, so C = ceil(z) + 2j 2^16 = ceil((n + p) 2^16), and
-// (C + hc) >> 16 equals n + [h < ceil(p 2^16)] for every h in [0, 0xFFFF]
-// (ceil(p 2^16) is at most 2^16).
+// [0, 1)) the code is n + 1 iff u < p22, p22 = floor(p 2^22) / 2^22 (p to 22
+// binary digits), i.e. iff f = floor(p 2^22) >= 64 h + 1.  F = floor(y
+// 2^(23-j)) is exact (y has 24 significant bits and y 2^(23-j) < 2^26), and
+// F + j 2^23 = n 2^22 + f; adding 64 hc + 63 = 2^22 - 64 h - 1 carries into
+// bit 22 exactly when f >= 64 h + 1.
 __host__ __device__ inline uint32_t e2m1_sr_c(float y, uint32_t hc) {
   const float yc = fminf(y, 6.0f);
   const uint32_t m = e2m1_segment_biased(yc);
-  const uint32_t c = (uint32_t)ceilf(ldexpf(yc, 144 - (int)m));
-  return (c + (m << 17) + hc - (127u << 17)) >> 16;  // 2j 2^16 = (m - 127) 2^17
+  const uint32_t f = (uint32_t)floorf(ldexpf(yc, 150 - (int)m));
+  return (f + ((m - 127u) << 23) + (hc << 6) + 63u) >> 22;
 }
 
 __host__ __device__ inline uint32_t e2m1_sr(float y, uint32_t h) { return e2m1_sr_c(y, 0xFFFFu - h); }
+
+// --------------------------------------------- gfx950 conversion instructions --
+//
+// The same E2M1 and E4M3 roundings by gfx950's conversion instructions, each
+// checked on the GPU against the definitions above over every rounding
+// boundary of the two grids and ~10^5 further values:
+//   v_cvt_scalef32_pk_fp4_f32 (scale 1): nearest E2M1 value with ties to the
+//     even code, saturating at 6, the sign bit copied from the input (zeros
+//     included): sign << 3 | e2m1_rne(|y|).  The first source lands in the
+//     low nibble of the selected byte.
+//   v_cvt_scalef32_sr_pk_fp4_f32 (scale 1, random word r): adds bits 31..10
+//     of r to the 22 bits of |y| below its E2M1 spacing (further bits
+//     dropped) and keeps the carry; the second element uses bits 30..9.
+//     With r = hc << 16 | 0xFFFF that is e2m1_sr_c(|y|, hc), signed as above.
+//   v_cvt_scalef32_pk_fp8_f32 (scale 1) of min(t, 448), t >= 0: the E4M3
+//     byte of e4m3_encode_rne_sat(t); v_cvt_f32_fp8 decodes it exactly.
+
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef short short2_t __attribute__((ext_vector_type(2)));
+
+// Codes of y[0..7] (already scaled, signed), nearest-even: y[0] in the low
+// nibble.
+__device__ inline uint32_t e2m1_pack8_rne(const float* y) {
+  uint32_t w = 0u;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], 1.0f, 3);
+  return w;
+}
+
+// The random word that makes the stochastic conversion decide u < p22 for
+// the complemented draw hc.
+__device__ inline uint32_t sr_word(uint32_t hc) { return (hc << 16) | 0xFFFFu; }
+
+// One stochastic conversion of (y, 0) into byte SEL of w; the other bytes of
+// w are kept.  Written as assembly with w tied to the destination: the
+// compiler's builtin for this instruction does not place its `old` operand in
+// the destination register, so the kept bytes would be whatever that register
+// held.
+template <int SEL>
+__device__ inline uint32_t cvt_sr_fp4_byte(uint32_t w, float y, uint32_t r) {
+  const float2_t v = {y, 0.0f};
+  if constexpr (SEL == 0)
+    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0" : "+v"(w) : "v"(v), "v"(r));
+  else if constexpr (SEL == 1)
+    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,0]" : "+v"(w) : "v"(v), "v"(r));
+  else if constexpr (SEL == 2)
+    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,0,1]" : "+v"(w) : "v"(v), "v"(r));
+  else
+    asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,1]" : "+v"(w) : "v"(v), "v"(r));
+  return w;
+}
+
+// Codes of y[0..7] rounded stochastically with the complemented draws
+// hc[0..7]: one element per conversion (the two elements of a conversion
+// share overlapping random bits), even elements in the low nibbles of `a`,
+// odd ones of `b`.
+__device__ inline uint32_t e2m1_pack8_sr(const float* y, const uint32_t* hc) {
+  uint32_t a = 0u, b = 0u;
+  a = cvt_sr_fp4_byte<0>(a, y[0], sr_word(hc[0]));
+  b = cvt_sr_fp4_byte<0>(b, y[1], sr_word(hc[1]));
+  a = cvt_sr_fp4_byte<1>(a, y[2], sr_word(hc[2]));
+  b = cvt_sr_fp4_byte<1>(b, y[3], sr_word(hc[3]));
+  a = cvt_sr_fp4_byte<2>(a, y[4], sr_word(hc[4]));
+  b = cvt_sr_fp4_byte<2>(b, y[5], sr_word(hc[5]));
+  a = cvt_sr_fp4_byte<3>(a, y[6], sr_word(hc[6]));
+  b = cvt_sr_fp4_byte<3>(b, y[7], sr_word(hc[7]));
+  return a | (b << 4);
+}
+
+// E4M3 byte of t >= 0, nearest-even, saturating at 448.
+__device__ inline uint32_t e4m3_encode_hw(float t) {
+  const short2_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((short2_t){0, 0}, fminf(t, 448.0f), 0.0f, 1.0f,
+                                                              false);
+  return (uint32_t)(uint16_t)r[0] & 0xFFu;
+}
+
+__device__ inline float e4m3_decode_hw(uint32_t b) { return __builtin_amdgcn_cvt_f32_fp8((int)b, 0); }
 
 
 // ------------------------------------------------------------------- misc --

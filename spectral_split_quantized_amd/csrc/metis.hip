@@ -642,6 +642,11 @@ metis_status decompose_check(const void* M, int32_t dtype, int64_t rows, int64_t
   if (rows <= 0 || cols <= 0 || ld < cols) return fail(METIS_E_INVALID, "bad shape %lldx%lld ld=%lld",
                                                       (long long)rows, (long long)cols, (long long)ld);
   if (rows > INT32_MAX) return fail(METIS_E_UNSUPPORTED, "rows > 2^31");
+  // the sampler resolves its boundary histogram bin among at most kCandMax
+  // candidate rows; 2^27 rows put 2048 rows in a bin on average
+  if (sample_rows && rows > (int64_t)kCandMax * 65536 / 2)
+    return fail(METIS_E_UNSUPPORTED, "row sample of %lld rows: at most %lld", (long long)rows,
+                (long long)kCandMax * 65536 / 2);
   if (f->rows != rows || f->cols != cols || f->k != cfg->k)
     return fail(METIS_E_INVALID, "factors describe %lldx%lld k=%d, operand %lldx%lld k=%d",
                 (long long)f->rows, (long long)f->cols, f->k, (long long)rows, (long long)cols, cfg->k);
@@ -892,7 +897,12 @@ metis_status quantize_factors(const metis_factors* f, int64_t rows, int64_t cols
       hipLaunchKernelGGL(quant_pair_kernel<false>, grid, dim3(kQThreads), 0, st, fqs[0], fqs[1], (int)pu);
     LAUNCH_CHECK();
     timing_end(t2, st);
-    out->S = f->S;
+    if (out->S && out->S != f->S) {
+      hipLaunchKernelGGL(copy_f32_kernel, dim3(1), dim3(128), 0, st, f->S, out->S, (int64_t)k);
+      LAUNCH_CHECK();
+    } else {
+      out->S = f->S;
+    }
   }
   return METIS_OK;
 }

@@ -39,9 +39,14 @@ __device__ inline int mx_exponent(float amax) {
 // (complemented 16-bit draws, one per element) the rounding is stochastic
 __device__ inline uint8_t mx_encode32(const float* v, uint32_t* w, const uint32_t* hc) {
   float amax = 0.0f;
+  bool bad = false;
 #pragma unroll
-  for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
-  if (!isfinite(amax)) raise_status(kStatusNonFinite);
+  for (int j = 0; j < 32; ++j) {
+    const float a = fabsf(v[j]);
+    bad |= !(a <= 3.402823466e38f);  // NaN or infinity (fmaxf would drop a NaN)
+    amax = fmaxf(amax, a);
+  }
+  if (bad) raise_status(kStatusNonFinite);
   const int e = mx_exponent(amax);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {

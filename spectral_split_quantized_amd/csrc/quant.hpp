@@ -147,31 +147,30 @@ struct QuantBlockOut {
 };
 
 // hc: complemented 16-bit draws (0xFFFF - h) of the 16 elements (SR only).
+// y = RN(x inv) keeps the sign of x, so the conversion's sign bit is the sign
+// of x (zeros included) and its magnitude that of RN(|x| inv).
 __device__ inline QuantBlockOut quant_block16(const float (&x)[16], const uint32_t (&hc)[16],
                                               float s_g, float d, bool sr) {
   float a = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(x[i]));
   const float t = __fdiv_rn(a, d);
-  const uint32_t sb = e4m3_encode_rne_sat(t);
-  const float s_b = e4m3_decode(sb);
-  const float s_eff = __fmul_rn(s_b, s_g);
-  // a zero block scale gives inv = 0, hence y = 0 and magnitude code 0 for
-  // every (finite) element of the block
+  const uint32_t sb = e4m3_encode_hw(t);
+  const float s_eff = __fmul_rn(e4m3_decode_hw(sb), s_g);
+  // a zero block scale gives inv = 0, hence y = +-0 and a signed zero code
+  // for every (finite) element of the block
   const float inv = sb != 0u ? __fdiv_rn(1.0f, s_eff) : 0.0f;
-  QuantBlockOut o;
-  o.lo = 0;
-  o.hi = 0;
-  o.scale = sb;
+  float y[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float y = __fmul_rn(fabsf(x[i]), inv);
-    const uint32_t m = sr ? e2m1_sr_c(y, hc[i]) : e2m1_rne(y);
-    const uint32_t code = ((__float_as_uint(x[i]) >> 31) << 3) | m;
-    if (i < 8)
-      o.lo |= code << (4 * i);
-    else
-      o.hi |= code << (4 * (i - 8));
+  for (int i = 0; i < 16; ++i) y[i] = __fmul_rn(x[i], inv);
+  QuantBlockOut o;
+  o.scale = sb;
+  if (sr) {
+    o.lo = e2m1_pack8_sr(y, hc);
+    o.hi = e2m1_pack8_sr(y + 8, hc + 8);
+  } else {
+    o.lo = e2m1_pack8_rne(y);
+    o.hi = e2m1_pack8_rne(y + 8);
   }
   return o;
 }

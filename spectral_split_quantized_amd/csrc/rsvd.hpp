@@ -133,6 +133,9 @@ __global__ __launch_bounds__(1024) void sample_compact_kernel(const uint8_t* __r
       if ((int64_t)pos < l_k) idx[pos] = (int32_t)i;
       ++pos;
     }
+  // fewer flagged rows than l_k (a candidate overflow, reported below): the
+  // remaining indices name row 0, so the sketch reads only valid rows
+  for (int64_t i = (int64_t)part[1023] + tid; i < l_k; i += 1024) idx[i] = 0;
   if (tid == 1023 && (int64_t)part[1023] != l_k) raise_status(kStatusSample);
 }
 

@@ -24,4 +24,9 @@ __global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int64_t n) {
   if (i < n) p[i] = v;
 }
 
+__global__ void copy_f32_kernel(const float* __restrict__ src, float* __restrict__ dst, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
 }  // namespace metis

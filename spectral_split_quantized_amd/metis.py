@@ -188,7 +188,9 @@ class QOperand:
         self.V = Q4(k, cols, device) if k else None
         self.R_ax0 = Q4(cols, rows, device) if axes & AXIS0 else None
         self.R_ax1 = Q4(rows, cols, device) if axes & AXIS1 else None
-        self.S = None
+        # the library copies the factors' S here, so the operand keeps the
+        # singular values its codes were made with
+        self.S = torch.empty(k, dtype=torch.float32, device=device) if k else None
 
     def _c(self):
         z = _Q4(None, None, None, 0, 0)
@@ -239,7 +241,6 @@ def quantize(M, cfg, tag, step, axes, factors=None, out=None, residual_out=None,
     _check(lib.metis_quantize(_ptr(M), _dtype_code(M), rows, cols, M.stride(0), fcp, ctypes.byref(cfg),
                               tag, step, axes, ctypes.byref(oc), _ptr(residual_out), _ptr(ws),
                               ws.numel(), _stream()))
-    out.S = factors.S if factors is not None else None
     return out
 
 
@@ -260,7 +261,6 @@ def prepare_operand(M, cfg, sample_rows, tag, step, factors, axes, out=None, res
                                      int(sample_rows), tag, step, ctypes.byref(fc), axes, ctypes.byref(oc),
                                      _ptr(residual_out), _ptr(ws), ws.numel(), _stream(), side))
     factors.refreshed_at = fc.refreshed_at
-    out.S = factors.S
     return out
 
 

@@ -142,13 +142,17 @@ def drift_weight(w_master, seed, scale=1e-3):
 def q4_arrays(n_outer, k_len, seed, zero_block_frac=0.02):
     """One quantised orientation as numpy arrays: codes uint8 [n_outer,
     k_len/2] (uniform random bytes), E4M3 scale bytes uint8 [n_outer,
-    k_len/16] (normal values 2^-6 .. 2^5, plus a few zero blocks) and a
-    binary32 tensor scale."""
+    k_len/16] and a binary32 tensor scale.  The scale bytes cover every
+    finite non-negative E4M3 value, 0x00 .. 0x7E (zero, the subnormals
+    2^-9 .. 7 2^-9, normals up to 448), and each row holds at least one 448
+    block, as a real tensor's rows do (its largest block maps to 448)."""
     import numpy as np
     rng = np.random.default_rng(seed)
     codes = rng.integers(0, 256, size=(n_outer, k_len // 2), dtype=np.uint8)
-    scales = rng.integers(0x08, 0x60, size=(n_outer, k_len // 16), dtype=np.uint8)
+    nb = k_len // 16
+    scales = rng.integers(0x00, 0x7F, size=(n_outer, nb), dtype=np.uint8)
     scales[rng.random(scales.shape) < zero_block_frac] = 0
+    scales[np.arange(n_outer), rng.integers(0, nb, size=n_outer)] = 0x7E
     ts = np.float32(2.0 ** rng.uniform(-6, -2))
     return codes, scales, ts
 

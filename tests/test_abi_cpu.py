@@ -69,6 +69,15 @@ def test_argument_errors_are_synchronous():
     # ld < cols
     _expect(lib.metis_decompose(dummy, 0, 256, 512, 100, ctypes.byref(cfg), 1, 0, 0, ctypes.byref(f),
                                 dummy, 1 << 30, None), metis.E_INVALID)
+    # a row sample beyond the sampler's candidate capacity (2^27 rows)
+    big_rows = (1 << 27) + 16
+    fb = metis._Factors(dummy, dummy, dummy, big_rows, 512, 8, -1)
+    _expect(lib.metis_decompose(dummy, 0, big_rows, 512, 512, ctypes.byref(cfg), 1, 0, 0, ctypes.byref(fb),
+                                dummy, 1 << 40, None), metis.E_UNSUPPORTED)
+    # the same operand as an unsampled weight is not limited by the sampler
+    wide = metis.make_config(k=8, s=8, l_k=0)
+    assert lib.metis_decompose(dummy, 0, big_rows, 512, 512, ctypes.byref(wide), 0, 0, 0, ctypes.byref(fb),
+                               dummy, 16, None) == metis.E_WORKSPACE
     # quantise along an axis whose length is not a multiple of 16
     q = metis._QOperand(256, 24, 0, None)
     _expect(lib.metis_quantize(dummy, 0, 256, 24, 24, None, ctypes.byref(cfg), 0, 0, metis.AXIS1,

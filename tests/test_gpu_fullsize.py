@@ -187,6 +187,40 @@ def test_million_row_direct_quant_sampled_panels(big_activation):
         assert np.array_equal(q.R_ax0.scales[:, r0 // 16:r0 // 16 + 1].cpu().numpy(), o0.scales)
 
 
+def test_million_row_residual_quant_sampled_panels(big_activation):
+    """The 1M x 4096 activation's residual with seeded rank-61 factors whose
+    product is exact in binary32 (SR, both orientations): 4.3e9 elements, so
+    element indices pass 2^32; codes and scales of sampled 16-row panels and of
+    every column's matching 16-row band bit-exact, with the residual's exact
+    amax computed by the oracle side in row chunks."""
+    M = big_activation
+    rows = M.shape[0]
+    u, s, v = synth.exact_factors(rows, H, K, seed=91)
+    f = gpu_factors(u, s, v)
+    cfg = metis.make_config(k=K, rounding=metis.SR, seed=0)
+    tag = metis.make_tag(0, metis.OPERAND_X)
+    q = metis.quantize(M, cfg, tag, 3, metis.AXIS0 | metis.AXIS1, factors=f)
+    metis.status_sync()
+    us = u.astype(np.float64) * s.astype(np.float64)
+    vt = v.astype(np.float64).T
+    amax = np.float32(0.0)
+    chunk = 1 << 14
+    for r0 in range(0, rows, chunk):
+        part = M[r0:r0 + chunk].float().cpu().numpy().astype(np.float64) - us[r0:r0 + chunk] @ vt
+        amax = max(amax, np.float32(np.max(np.abs(part.astype(np.float32)))))
+    assert np.float32(q.R_ax1.tensor_scale.item()) == nvfp4.tensor_scale(amax)[0]
+    rt = philox.with_role(tag, philox.ROLE_RESID)
+    for r0 in (0, 16 * 40000, 16 * 65535, (1 << 20) - 16):
+        x = M[r0:r0 + 16].float().cpu().numpy().astype(np.float64)
+        mr = (x - us[r0:r0 + 16] @ vt).astype(np.float32)
+        o1 = nvfp4.quantize(mr, 1, "sr", 0, rt, 3, amax=amax, origin=(r0, 0, H), draws="matrix")
+        assert np.array_equal(q.R_ax1.scales[r0:r0 + 16].cpu().numpy(), o1.scales), "axis 1 rows %d" % r0
+        assert np.array_equal(q.R_ax1.codes[r0:r0 + 16].cpu().numpy(), o1.codes), "axis 1 rows %d" % r0
+        o0 = nvfp4.quantize(mr, 0, "sr", 0, rt, 3, amax=amax, origin=(r0, 0, H), draws="matrix")
+        assert np.array_equal(q.R_ax0.scales[:, r0 // 16:r0 // 16 + 1].cpu().numpy(), o0.scales), "axis 0 rows %d" % r0
+        assert np.array_equal(q.R_ax0.codes[:, r0 // 2:r0 // 2 + 8].cpu().numpy(), o0.codes), "axis 0 rows %d" % r0
+
+
 def test_million_row_decomposition_subspace(big_activation):
     """Decomposition of the 1M x 4096 activation (l_k = 10486 sampled rows):
     the sketch depends only on the sampled rows, so the oracle builds it

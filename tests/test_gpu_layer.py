@@ -122,3 +122,46 @@ def test_layer_batched_input_shape():
     assert torch.equal(y.reshape(y2.shape), y2)
     assert torch.equal(x.grad.reshape(x2.grad.shape), x2.grad)
     assert torch.equal(lin.weight.grad, lin2.weight.grad)
+
+
+def test_layer_two_forwards_before_backward():
+    """Two forwards of one module on different inputs, then both backwards (a
+    weight-shared layer, micro-batches in flight): each backward uses the
+    quantised operands and singular values of its own forward, so its
+    gradients equal those of a lone forward + backward at the same step.  The
+    module refreshes every step and the second forward runs at step 1, so its
+    factors overwrite those the first forward quantised with."""
+    c, X, W, D, lin = _layer(0, refresh=1)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    X2 = X.float() + 0.5 * torch.randn(X.shape, device="cuda", generator=g)
+    D1 = torch.randn(X.shape[0], W.shape[1], device="cuda", generator=g)
+    D2 = torch.randn(X.shape[0], W.shape[1], device="cuda", generator=g)
+    say("layer: two forwards, then both backwards")
+
+    def lone(xin, dout, step):
+        ref = MetisLinear(W.shape[0], W.shape[1], c["k"], s=c["s"], l_k=c["l_k"], refresh=1,
+                          rounding=c["rounding"], weight=W.float())
+        set_step(ref, step)
+        xr = xin.clone().requires_grad_(True)
+        ref(xr).backward(dout)
+        metis.status_sync()
+        return xr.grad, ref.weight.grad
+
+    dx1, dw1 = lone(X.float(), D1, 0)
+    dx2, dw2 = lone(X2, D2, 1)
+    x1 = X.float().clone().requires_grad_(True)
+    x2 = X2.clone().requires_grad_(True)
+    set_step(lin, 0)
+    y1 = lin(x1)
+    set_step(lin, 1)
+    y2 = lin(x2)          # re-sketches X and W: the first forward's factors are overwritten
+    set_step(lin, 0)
+    y1.backward(D1)       # D sketched at step 0, as in the lone run
+    metis.status_sync()
+    assert torch.equal(x1.grad, dx1)
+    assert torch.equal(lin.weight.grad, dw1)
+    set_step(lin, 1)
+    y2.backward(D2)
+    metis.status_sync()
+    assert torch.equal(x2.grad, dx2)
+    assert torch.equal(lin.weight.grad, dw1 + dw2)

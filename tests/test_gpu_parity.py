@@ -137,6 +137,7 @@ def test_reconstruction_and_orthonormality(layer):
 
 def test_decomposition_matches_oracle(layer):
     L = layer
+    not_unique = []
     for n, M in L.mats().items():
         if M is None:
             continue
@@ -154,11 +155,13 @@ def test_decomposition_matches_oracle(layer):
         srel = np.abs(sg - s).max() / s[0]
         say("%s: sketch gap %.2e sin(V) %.2e sin(U) %.2e |dS|/S0 %.2e" % (n, gap, sin_v, sin_u, srel))
         if gap < 1e-3:
-            say("%s: gap below 1e-3, the top-k subspace is not unique; not asserted" % n)
+            not_unique.append("%s (relative gap %.2e)" % (n, gap))
             continue
         assert sin_v <= SUBSPACE_TOL
         assert sin_u <= SUBSPACE_TOL
         assert srel <= S_TOL
+    if not_unique:
+        pytest.skip("top-k subspace not unique, not compared: " + ", ".join(not_unique))
 
 
 def test_end_to_end_matches_oracle(layer):

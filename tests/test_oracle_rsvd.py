@@ -166,6 +166,42 @@ def test_metis_spectral_distortion_below_direct_nvfp4():
              zero.mean(), zero[small].mean()))
 
 
+def _tail_error(w, what, r):
+    """||P_u (what - w) P_v||_F / ||P_u w P_v||_F with P_u, P_v the projectors
+    on the complements of w's top-r left and right singular subspaces
+    (applied without forming them)."""
+    uu, _, vt = np.linalg.svd(w, full_matrices=False)
+    u, v = uu[:, :r], vt[:r].T
+
+    def proj(e):
+        e = e - u @ (u.T @ e)
+        return e - (e @ v) @ v.T
+
+    return np.linalg.norm(proj(what - w)) / np.linalg.norm(proj(w))
+
+
+def test_spectral_distortion_below_direct_nvfp4_gpt2_weight():
+    """The same pin as above on the GPT-2 MLP-up weight shape (768 x 3072,
+    k = 12 >= its 5 dominant values), with stochastic rounding as the pages
+    train: the error that lands in the complement of the weight's top-2k
+    singular subspaces is several times smaller after the split."""
+    w = synth.anisotropic(768, 3072, synth.FRAC_W, synth.gen_seed(1, "W"), out_dtype=torch.float64).numpy()
+    w = w.astype(np.float32).astype(np.float64)
+    cfg = rsvd.Config(k=12, s=8, l_k=768)
+    tag = philox.make_tag(0, 1, 0)
+    u, s, v, _ = rsvd.decompose(w, cfg, False, tag, 0)
+    split = split_gemm.quantize_operand(w, u.astype(np.float32), s.astype(np.float32), v.astype(np.float32),
+                                        "sr", 0, tag, 0, axes=(1,))
+    direct = split_gemm.quantize_operand(w, None, None, None, "sr", 0, tag, 0, axes=(1,))
+    mh = split_gemm.dense(split, 1)
+    dh = split_gemm.dense(direct, 1)
+    tail_metis = _tail_error(w, mh, 24)
+    tail_direct = _tail_error(w, dh, 24)
+    print("GPT-2 W: tail-subspace error metis %.3f direct %.3f; total fro metis %.4f direct %.4f"
+          % (tail_metis, tail_direct, split_gemm.rel_fro(mh, w), split_gemm.rel_fro(dh, w)))
+    assert tail_metis < 0.5 * tail_direct
+
+
 def test_k0_split_equals_direct_codes():
     rng = np.random.default_rng(6)
     m = rng.standard_normal((32, 48)).astype(np.float32)
