@@ -167,6 +167,25 @@ metis_status metis_quantize(const void *M, int32_t dtype, int64_t rows, int64_t 
                             int64_t step, int32_t axes, metis_qoperand *out, float *residual_out,
                             void *ws, size_t ws_bytes, void *stream);
 
+/* metis_quantize_static -- metis_quantize without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Arguments, outputs
+ * and errors are those of metis_quantize.  The call allocates nothing: its
+ * scratch (the tensor amax words and the fp16 operands of the rank-k
+ * product) lives in one static device array of the library per GPU,
+ * metis_quantize_static_capacity() bytes (16 MiB), held until the process
+ * ends.  An operand whose scratch exceeds it (with factors about
+ * (rows + cols) * 6 * round_up(k, 16) bytes) returns METIS_E_UNSUPPORTED with
+ * nothing enqueued.  Every call on one GPU uses that GPU's array: calls that
+ * overlap in time on one GPU (other streams or threads) race, so the caller
+ * orders them; the array keeps the last call's contents and each call clears
+ * what it needs zeroed. */
+size_t metis_quantize_static_capacity(void);
+metis_status metis_quantize_static(const void *M, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                                   const metis_factors *f, const metis_config *cfg, uint32_t tag,
+                                   int64_t step, int32_t axes, metis_qoperand *out, float *residual_out,
+                                   void *stream);
+
 /* metis_prepare_operand -- metis_decompose followed by metis_quantize with
  * the new factors (关键设计 1-3), as one call.  After the projection
  * P = M V_old the residual M_R = M - P V_old^T is quantised on `stream` while

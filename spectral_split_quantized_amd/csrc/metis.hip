@@ -26,6 +26,14 @@
 
 using namespace metis;
 
+// Scratch of the allocation-free quantiser entry point (metis_quantize_static):
+// one array per GPU, held until the process ends.  Host code never names it
+// directly: the device address of each GPU's copy comes from
+// hipGetSymbolAddress at set-up (g_scratch_ptr below), and only that address
+// is passed to kernels.
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -129,20 +137,36 @@ const uint16_t* host_omega_table() {
   return table;
 }
 
+std::mutex g_dev_mu;
+bool g_dev_ready[64] = {false};
+void* g_scratch_ptr[64] = {nullptr};
+
+// Once per device, with that device current: the Gaussian quantile table, the
+// numeric status word and the address of the static scratch array.
 metis_status ensure_device_tables() {
-  static std::mutex mu;
-  static bool done[64] = {false};
   int dev = 0;
   HIP_TRY(hipGetDevice(&dev));
   if (dev < 0 || dev >= 64) return fail(METIS_E_UNSUPPORTED, "device index %d", dev);
-  std::lock_guard<std::mutex> lk(mu);
-  if (!done[dev]) {
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (!g_dev_ready[dev]) {
     HIP_TRY(hipMemcpyToSymbol(HIP_SYMBOL(g_omega_table), host_omega_table(), 65536 * 2));
     const int zero = 0;
     HIP_TRY(hipMemcpyToSymbol(HIP_SYMBOL(g_metis_status), &zero, sizeof(int)));
-    done[dev] = true;
+    void* p = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(METIS_E_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+    g_dev_ready[dev] = true;
   }
   return METIS_OK;
+}
+
+// This device's static scratch (after ensure_device_tables).
+void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  return g_scratch_ptr[dev];
 }
 
 // ------------------------------------------------------------- workspace --
@@ -1057,18 +1081,17 @@ metis_status metis_decompose(const void* M, int32_t dtype, int64_t rows, int64_t
   return METIS_OK;
 }
 
-metis_status metis_quantize(const void* M, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
-                            const metis_factors* f, const metis_config* cfg, uint32_t tag,
-                            int64_t step, int32_t axes, metis_qoperand* out, float* residual_out,
-                            void* ws, size_t ws_bytes, void* stream) {
-  metis_status s = quantize_check(M, dtype, rows, cols, ld, f, cfg, step, axes, out);
-  if (s != METIS_OK) return s;
+}  // extern "C"
+
+namespace {
+
+// metis_quantize after its checks, with the workspace carved.
+metis_status quantize_body(const void* M, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                           const metis_factors* f, const metis_config* cfg, uint32_t tag, int64_t step,
+                           int32_t axes, metis_qoperand* out, float* residual_out, const QuantWs& w,
+                           hipStream_t st) {
+  metis_status s;
   const int k = f ? f->k : 0;
-  Carver cv(ws, ws_bytes);
-  QuantWs w = carve_quantize(cv, rows, cols, k);
-  if (!ws || cv.used() > ws_bytes) return fail(METIS_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, cv.used());
-  if ((s = ensure_device_tables()) != METIS_OK) return s;
-  hipStream_t st = (hipStream_t)stream;
   hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, st, w.amax, 0u, (int64_t)4);
   LAUNCH_CHECK();
   QuantParams qp = resid_params(M, dtype, rows, cols, ld, cfg, tag, step, axes, out, residual_out, w);
@@ -1088,6 +1111,49 @@ metis_status metis_quantize(const void* M, int32_t dtype, int64_t rows, int64_t 
   if ((s = run_quant(qp, f != nullptr, rows, cols, st)) != METIS_OK) return s;
   if (f) return quantize_factors(f, rows, cols, cfg, tag, step, out, w, st);
   return METIS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+metis_status metis_quantize(const void* M, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                            const metis_factors* f, const metis_config* cfg, uint32_t tag,
+                            int64_t step, int32_t axes, metis_qoperand* out, float* residual_out,
+                            void* ws, size_t ws_bytes, void* stream) {
+  metis_status s = quantize_check(M, dtype, rows, cols, ld, f, cfg, step, axes, out);
+  if (s != METIS_OK) return s;
+  const int k = f ? f->k : 0;
+  Carver cv(ws, ws_bytes);
+  QuantWs w = carve_quantize(cv, rows, cols, k);
+  if (!ws || cv.used() > ws_bytes) return fail(METIS_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, cv.used());
+  if ((s = ensure_device_tables()) != METIS_OK) return s;
+  return quantize_body(M, dtype, rows, cols, ld, f, cfg, tag, step, axes, out, residual_out, w,
+                       (hipStream_t)stream);
+}
+
+size_t metis_quantize_static_capacity(void) { return kStaticScratchBytes; }
+
+metis_status metis_quantize_static(const void* M, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                                   const metis_factors* f, const metis_config* cfg, uint32_t tag, int64_t step,
+                                   int32_t axes, metis_qoperand* out, float* residual_out, void* stream) {
+  metis_status s = quantize_check(M, dtype, rows, cols, ld, f, cfg, step, axes, out);
+  if (s != METIS_OK) return s;
+  const int k = f ? f->k : 0;
+  Carver probe(nullptr, 0);
+  carve_quantize(probe, rows, cols, k);
+  if (probe.used() > kStaticScratchBytes)
+    return fail(METIS_E_UNSUPPORTED,
+                "quantize_static: this operand (%lld x %lld, k = %d) needs %zu bytes of scratch; the static "
+                "scratch holds %zu (use metis_quantize with a workspace)",
+                (long long)rows, (long long)cols, k, probe.used(), kStaticScratchBytes);
+  if ((s = ensure_device_tables()) != METIS_OK) return s;
+  void* base = device_scratch();
+  if (!base) return fail(METIS_E_HIP, "quantize_static: no scratch address for the current device");
+  Carver cv(base, kStaticScratchBytes);
+  QuantWs w = carve_quantize(cv, rows, cols, k);
+  return quantize_body(M, dtype, rows, cols, ld, f, cfg, tag, step, axes, out, residual_out, w,
+                       (hipStream_t)stream);
 }
 
 size_t metis_prepare_operand_workspace(int64_t rows, int64_t cols, const metis_config* cfg,

@@ -84,6 +84,11 @@ def load():
                                    ctypes.POINTER(Config), u32, i64, i32,
                                    ctypes.POINTER(_QOperand), P, P, sz, P]
     lib.metis_quantize.restype = i32
+    lib.metis_quantize_static.argtypes = [P, i32, i64, i64, i64, ctypes.POINTER(_Factors),
+                                          ctypes.POINTER(Config), u32, i64, i32,
+                                          ctypes.POINTER(_QOperand), P, P]
+    lib.metis_quantize_static.restype = i32
+    lib.metis_quantize_static_capacity.restype = sz
     lib.metis_prepare_operand_workspace.argtypes = [i64, i64, ctypes.POINTER(Config), i32]
     lib.metis_prepare_operand_workspace.restype = sz
     lib.metis_prepare_operand.argtypes = [P, i32, i64, i64, i64, ctypes.POINTER(Config), i32, u32, i64,
@@ -242,6 +247,27 @@ def quantize(M, cfg, tag, step, axes, factors=None, out=None, residual_out=None,
                               tag, step, axes, ctypes.byref(oc), _ptr(residual_out), _ptr(ws),
                               ws.numel(), _stream()))
     return out
+
+
+def quantize_static(M, cfg, tag, step, axes, factors=None, out=None, residual_out=None):
+    """metis_quantize without a workspace: the library's static per-GPU scratch
+    (metis_quantize_static) serves as workspace, so the call allocates no
+    device memory (``out`` given: none at all)."""
+    lib = load()
+    rows, cols = M.shape
+    k = factors.k if factors is not None else 0
+    if out is None:
+        out = QOperand(rows, cols, k, axes, M.device)
+    oc = out._c()
+    fcp = ctypes.byref(factors._c()) if factors is not None else None
+    _check(lib.metis_quantize_static(_ptr(M), _dtype_code(M), rows, cols, M.stride(0), fcp, ctypes.byref(cfg),
+                                     tag, step, axes, ctypes.byref(oc), _ptr(residual_out), _stream()))
+    return out
+
+
+def quantize_static_capacity():
+    """Bytes of the static scratch behind quantize_static."""
+    return int(load().metis_quantize_static_capacity())
 
 
 def prepare_operand(M, cfg, sample_rows, tag, step, factors, axes, out=None, residual_out=None,
