@@ -65,14 +65,37 @@ __host__ __device__ inline Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
   return out;
 }
 
-__host__ __device__ inline Philox4 philox_block(uint64_t q, uint32_t tag, uint32_t step,
-                                                uint64_t seed) {
-  return philox4x32_10((uint32_t)q, (uint32_t)(q >> 32), tag, step, (uint32_t)seed,
-                       (uint32_t)(seed >> 32));
+// The same ten rounds on the GPU: each round's two three-way XORs as one
+// v_bitop3_b32 each (truth table 0x96 = a ^ b ^ c).
+__device__ inline Philox4 philox4x32_10_dev(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                            uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)kPhiloxM0 * c0;
+    const uint64_t p1 = (uint64_t)kPhiloxM1 * c2;
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += kPhiloxW0;
+    k1 += kPhiloxW1;
+  }
+  Philox4 out;
+  out.v[0] = c0;
+  out.v[1] = c1;
+  out.v[2] = c2;
+  out.v[3] = c3;
+  return out;
+}
+
+__device__ inline Philox4 philox_block(uint64_t q, uint32_t tag, uint32_t step, uint64_t seed) {
+  return philox4x32_10_dev((uint32_t)q, (uint32_t)(q >> 32), tag, step, (uint32_t)seed, (uint32_t)(seed >> 32));
 }
 
 // 32-bit draw of element e.
-__host__ __device__ inline uint32_t philox_word(uint64_t e, uint32_t tag, uint32_t step,
+__device__ inline uint32_t philox_word(uint64_t e, uint32_t tag, uint32_t step,
                                                 uint64_t seed) {
   const Philox4 b = philox_block(e >> 2, tag, step, seed);
   return b.v[e & 3];
@@ -187,14 +210,13 @@ __device__ inline uint32_t e2m1_pack8_rne(const float* y) {
 // the complemented draw hc.
 __device__ inline uint32_t sr_word(uint32_t hc) { return (hc << 16) | 0xFFFFu; }
 
-// One stochastic conversion of (y, 0) into byte SEL of w; the other bytes of
-// w are kept.  Written as assembly with w tied to the destination: the
-// compiler's builtin for this instruction does not place its `old` operand in
-// the destination register, so the kept bytes would be whatever that register
-// held.
+// One stochastic conversion of the pair v = (y0, y1) into byte SEL of w; the
+// other bytes of w are kept.  Written as assembly with w tied to the
+// destination: the compiler's builtin for this instruction does not place
+// its `old` operand in the destination register, so the kept bytes would be
+// whatever that register held.
 template <int SEL>
-__device__ inline uint32_t cvt_sr_fp4_byte(uint32_t w, float y, uint32_t r) {
-  const float2_t v = {y, 0.0f};
+__device__ __forceinline__ uint32_t cvt_sr_fp4_byte(uint32_t w, float2_t v, uint32_t r) {
   if constexpr (SEL == 0)
     asm volatile("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0" : "+v"(w) : "v"(v), "v"(r));
   else if constexpr (SEL == 1)
@@ -206,21 +228,38 @@ __device__ inline uint32_t cvt_sr_fp4_byte(uint32_t w, float y, uint32_t r) {
   return w;
 }
 
+// The random word that makes the conversion's second element decide u < p22
+// for the complemented draw hc: that element adds bits 30..9 of the word.
+__device__ inline uint32_t sr_word_hi(uint32_t hc) { return (hc << 15) | 0x7FFFu; }
+
 // Codes of y[0..7] rounded stochastically with the complemented draws
-// hc[0..7]: one element per conversion (the two elements of a conversion
-// share overlapping random bits), even elements in the low nibbles of `a`,
-// odd ones of `b`.
+// hc[0..7].  Each conversion takes a pair (y[2i], y[2i+1]) but its two
+// elements draw from overlapping bits of one random word, so every pair is
+// converted twice: once with the word of the even element (whose low nibble
+// is kept, in `a`) and once with the word of the odd one (high nibble, `b`).
 __device__ inline uint32_t e2m1_pack8_sr(const float* y, const uint32_t* hc) {
   uint32_t a = 0u, b = 0u;
-  a = cvt_sr_fp4_byte<0>(a, y[0], sr_word(hc[0]));
-  b = cvt_sr_fp4_byte<0>(b, y[1], sr_word(hc[1]));
-  a = cvt_sr_fp4_byte<1>(a, y[2], sr_word(hc[2]));
-  b = cvt_sr_fp4_byte<1>(b, y[3], sr_word(hc[3]));
-  a = cvt_sr_fp4_byte<2>(a, y[4], sr_word(hc[4]));
-  b = cvt_sr_fp4_byte<2>(b, y[5], sr_word(hc[5]));
-  a = cvt_sr_fp4_byte<3>(a, y[6], sr_word(hc[6]));
-  b = cvt_sr_fp4_byte<3>(b, y[7], sr_word(hc[7]));
-  return a | (b << 4);
+  const float2_t v0 = {y[0], y[1]}, v1 = {y[2], y[3]}, v2 = {y[4], y[5]}, v3 = {y[6], y[7]};
+  a = cvt_sr_fp4_byte<0>(a, v0, sr_word(hc[0]));
+  b = cvt_sr_fp4_byte<0>(b, v0, sr_word_hi(hc[1]));
+  a = cvt_sr_fp4_byte<1>(a, v1, sr_word(hc[2]));
+  b = cvt_sr_fp4_byte<1>(b, v1, sr_word_hi(hc[3]));
+  a = cvt_sr_fp4_byte<2>(a, v2, sr_word(hc[4]));
+  b = cvt_sr_fp4_byte<2>(b, v2, sr_word_hi(hc[5]));
+  a = cvt_sr_fp4_byte<3>(a, v3, sr_word(hc[6]));
+  b = cvt_sr_fp4_byte<3>(b, v3, sr_word_hi(hc[7]));
+  return __builtin_amdgcn_bitop3_b32(a, b, 0x0F0F0F0Fu, 0xE4);  // (a & m) | (b & ~m)
+}
+
+// Largest |x| of 16 values, as the binary32 bits of a non-negative value
+// (which order like unsigned integers): integer maxima need no NaN
+// canonicalisation of their operands.
+__device__ inline uint32_t abs_max16_bits(const float* x) {
+  uint32_t m = 0u;
+#pragma unroll
+  for (int i = 0; i < 16; i += 2)
+    m = max(m, max(__float_as_uint(x[i]) & 0x7FFFFFFFu, __float_as_uint(x[i + 1]) & 0x7FFFFFFFu));
+  return m;
 }
 
 // E4M3 byte of t >= 0, nearest-even, saturating at 448.

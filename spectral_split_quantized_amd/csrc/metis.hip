@@ -20,6 +20,7 @@
 #include "gemm.hpp"
 #include "gemm_launch.hpp"
 #include "quant.hpp"
+#include "quant_fast.hpp"
 #include "rsvd.hpp"
 #include "mxfp4.hpp"
 #include "mxfp4_gemm.hpp"
@@ -334,8 +335,10 @@ metis_status validate_config(const metis_config* cfg) {
 
 // ------------------------------------------------------------ quantiser --
 
+constexpr int64_t kAmaxWords = (int64_t)kAmaxSlotStride * (1 + kAmaxSlots);
+
 struct QuantWs {
-  uint32_t* amax;  // 3 words: residual, U, V
+  uint32_t* amax;  // words 0..2: residual, U, V; from word kAmaxSlotStride: the residual's slots
   float* pre;
   float* pscale;
   float* ones;     // kMaxN ones (S of a residual formed from the projection)
@@ -345,7 +348,7 @@ struct QuantWs {
 
 QuantWs carve_quantize(Carver& cv, int64_t rows, int64_t cols, int k) {
   QuantWs w{};
-  w.amax = cv.take<uint32_t>(4);
+  w.amax = cv.take<uint32_t>(kAmaxWords);
   w.pre = cv.take<float>(1);
   w.pscale = cv.take<float>(1);
   w.ones = cv.take<float>(kMaxN);
@@ -375,9 +378,72 @@ metis_status launch_quant_pair(const QuantParams& qp, dim3 grid, int64_t rows, i
   return METIS_OK;
 }
 
+template <int NKK, int TPW>
+metis_status launch_quant_fast(const QuantParams& qp, unsigned nwg, int64_t rows, int64_t cols, hipStream_t st) {
+  const int64_t kc = NKK * 16;
+  const dim3 g(nwg), b(kQThreads);
+  TimingRec* t1 = timing_begin(st, 1, rows, cols, qp.axes, kc);
+  hipLaunchKernelGGL((qf_amax_kernel<NKK, TPW>), g, b, 0, st, qp);
+  LAUNCH_CHECK();
+  timing_end(t1, st);
+  TimingRec* t2 = timing_begin(st, 2, rows, cols, qp.axes, kc);
+#define QF_LAUNCH(SR_, AX_) hipLaunchKernelGGL((qf_quant_kernel<NKK, SR_, AX_, TPW>), g, b, 0, st, qp)
+  switch (qp.axes | (qp.sr ? 4 : 0)) {
+    case 1: QF_LAUNCH(false, 1); break;
+    case 2: QF_LAUNCH(false, 2); break;
+    case 3: QF_LAUNCH(false, 3); break;
+    case 5: QF_LAUNCH(true, 1); break;
+    case 6: QF_LAUNCH(true, 2); break;
+    default: QF_LAUNCH(true, 3); break;
+  }
+#undef QF_LAUNCH
+  LAUNCH_CHECK();
+  timing_end(t2, st);
+  return METIS_OK;
+}
+
+// The whole-tile sweeps (quant_fast.hpp) take bf16 operands of whole 128 x 64
+// tiles with 16-byte aligned rows and outputs, both orientations, and no
+// residual export.
+bool quant_fast_ok(const QuantParams& qp) {
+  auto al = [](const void* p, uintptr_t a) { return p == nullptr || ((uintptr_t)p % a) == 0; };
+  return qp.amax_slots && qp.dtype == METIS_BF16 && qp.rows % kQT_R == 0 && qp.cols % kQT_C == 0 && qp.ld % 8 == 0 &&
+         al(qp.M, 16) && qp.resid == nullptr && qp.shared_draws && qp.axes >= 1 && qp.axes <= 3 && al(qp.codes0, 16) &&
+         al(qp.codes1, 16) && al(qp.scales0, 2) && al(qp.scales1, 2) && qp.rows / kQT_R <= INT32_MAX &&
+         qp.cols / kQT_C <= INT32_MAX / 2;
+}
+
+template <int TPW>
+metis_status launch_quant_fast_w(const QuantParams& qp, bool has_f, int64_t rows, int64_t cols, hipStream_t st,
+                                 bool* done) {
+  const int64_t P = rows / kQT_R, ntc = cols / kQT_C;
+  const int64_t W = P * ceil_div<int64_t>(ntc, TPW);
+  const int64_t nwg = 8 * ceil_div<int64_t>(W, 8);
+  *done = false;
+  if (nwg > INT32_MAX) return METIS_OK;
+  *done = true;
+  if (!has_f) return launch_quant_fast<0, TPW>(qp, (unsigned)nwg, rows, cols, st);
+  switch (qp.kc / 16) {
+    case 3: return launch_quant_fast<3, TPW>(qp, (unsigned)nwg, rows, cols, st);
+    case 6: return launch_quant_fast<6, TPW>(qp, (unsigned)nwg, rows, cols, st);
+    case 9: return launch_quant_fast<9, TPW>(qp, (unsigned)nwg, rows, cols, st);
+    case 12: return launch_quant_fast<12, TPW>(qp, (unsigned)nwg, rows, cols, st);
+    default: *done = false; return METIS_OK;
+  }
+}
+
 metis_status run_quant(const QuantParams& qp0, bool has_f, int64_t rows, int64_t cols,
                        hipStream_t st) {
   QuantParams qp = qp0;
+  if (quant_fast_ok(qp)) {
+    // four tiles (256 columns: whole 128-byte lines of axis-1 codes) per
+    // workgroup when that still gives ~2 workgroups per CU, else one
+    const int64_t tiles = (rows / kQT_R) * (cols / kQT_C);
+    bool done = false;
+    metis_status s = tiles >= 4 * 512 && cols >= 4 * kQT_C ? launch_quant_fast_w<4>(qp, has_f, rows, cols, st, &done)
+                                                            : launch_quant_fast_w<1>(qp, has_f, rows, cols, st, &done);
+    if (done || s != METIS_OK) return s;
+  }
   const int64_t panels = ceil_div<int64_t>(rows, kQT_R);
   const int64_t ntc = ceil_div<int64_t>(cols, kQT_C);
   int64_t tpw = panels * ntc / 2048;
@@ -852,6 +918,7 @@ QuantParams resid_params(const void* M, int32_t dtype, int64_t rows, int64_t col
   qp.cols = cols;
   qp.ld = ld;
   qp.amax = w.amax;
+  qp.amax_slots = w.amax + kAmaxSlotStride;
   qp.axes = axes;
   qp.sr = cfg->rounding == METIS_SR;
   qp.seed = cfg->seed;
@@ -1092,7 +1159,7 @@ metis_status quantize_body(const void* M, int32_t dtype, int64_t rows, int64_t c
                            hipStream_t st) {
   metis_status s;
   const int k = f ? f->k : 0;
-  hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, st, w.amax, 0u, (int64_t)4);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(grid1(kAmaxWords, 256)), dim3(256), 0, st, w.amax, 0u, kAmaxWords);
   LAUNCH_CHECK();
   QuantParams qp = resid_params(M, dtype, rows, cols, ld, cfg, tag, step, axes, out, residual_out, w);
   if (f) {
@@ -1189,7 +1256,7 @@ metis_status metis_prepare_operand(const void* M, int32_t dtype, int64_t rows, i
   // P = M V_old and G = P^T P (the sketch first on refresh steps)
   if ((s = decompose_project(c, st)) != METIS_OK) return s;
   // the residual's rank-k product from P and V_old, before V is rotated
-  hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, st, qw.amax, 0u, (int64_t)4);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(grid1(kAmaxWords, 256)), dim3(256), 0, st, qw.amax, 0u, kAmaxWords);
   LAUNCH_CHECK();
   hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(128), 0, st, (uint32_t*)qw.ones, 0x3F800000u,
                      (int64_t)kMaxN);

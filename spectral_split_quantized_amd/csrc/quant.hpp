@@ -114,6 +114,9 @@ __global__ void resid_prep_kernel(const float* __restrict__ U, const float* __re
 
 // ------------------------------------------------------------- quantiser --
 
+constexpr int kAmaxSlots = 16;
+constexpr int kAmaxSlotStride = 32;
+
 struct QuantParams {
   const void* M;
   int dtype;  // 0 bf16, 1 f32
@@ -123,6 +126,10 @@ struct QuantParams {
   int kc;
   const float* pscale;
   uint32_t* amax;
+  // streaming sweeps only: kAmaxSlots partial maxima, kAmaxSlotStride words
+  // apart (one cache line each), so the workgroups' atomics spread over many
+  // addresses instead of queueing on one
+  uint32_t* amax_slots;
   uint8_t* codes0;  // axis 0 (K = rows): [cols][rows/2]
   uint8_t* scales0;
   float* sg0;
@@ -151,9 +158,7 @@ struct QuantBlockOut {
 // of x (zeros included) and its magnitude that of RN(|x| inv).
 __device__ inline QuantBlockOut quant_block16(const float (&x)[16], const uint32_t (&hc)[16],
                                               float s_g, float d, bool sr) {
-  float a = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(x[i]));
+  const float a = __uint_as_float(abs_max16_bits(x));
   const float t = __fdiv_rn(a, d);
   const uint32_t sb = e4m3_encode_hw(t);
   const float s_eff = __fmul_rn(e4m3_decode_hw(sb), s_g);
@@ -274,27 +279,43 @@ __device__ inline void unpack_bf16x16(const uint4& q0, const uint4& q1, float (&
   }
 }
 
-// x -= (V (U S)^T)^T of this wave's 32 rows x the tile's 64 columns; Bf holds
-// the tile's vcat fragments, uf this wave's ucat fragments.
+// The rank-k product (V (U S)^T) of this wave's 32 rows x the tile's 64
+// columns on MFMA: Bf holds the tile's vcat fragments, uf this wave's ucat
+// fragments; a0 covers columns 0..31, a1 columns 32..63.
 template <int NKK>
-__device__ inline void subtract_lowrank(const uint4* Bf, const half8_t (&uf)[NKK], float ps, int lane,
-                                        float (&x)[2][16]) {
-  f32x16_t acc0 = {}, acc1 = {};
+__device__ __forceinline__ void lowrank_mfma(const uint4* Bf, const half8_t (&uf)[NKK], int lane, f32x16_t& a0,
+                                             f32x16_t& a1) {
+  a0 = f32x16_t{};
+  a1 = f32x16_t{};
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
     const half8_t v0 = __builtin_bit_cast(half8_t, Bf[kk * 64 + lane]);
     const half8_t v1 = __builtin_bit_cast(half8_t, Bf[(NKK + kk) * 64 + lane]);
-    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(v0, uf[kk], acc0, 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(v1, uf[kk], acc1, 0, 0, 0);
+    a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(v0, uf[kk], a0, 0, 0, 0);
+    a1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(v1, uf[kk], a1, 0, 0, 0);
   }
+}
+
+// x -= pscale * product, one rounding per element: x - p ps with p ps exact
+// (ps is a power of two), evaluated as one fused multiply-add.
+__device__ __forceinline__ void lowrank_subtract(const f32x16_t& a0, const f32x16_t& a1, float ps,
+                                                 float (&x)[2][16]) {
   float p0[16], p1[16];
-  gather_cols16(acc0, p0);
-  gather_cols16(acc1, p1);
+  gather_cols16(a0, p0);
+  gather_cols16(a1, p1);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    x[0][i] = __fsub_rn(x[0][i], __fmul_rn(p0[i], ps));
-    x[1][i] = __fsub_rn(x[1][i], __fmul_rn(p1[i], ps));
+    x[0][i] = __fmaf_rn(-p0[i], ps, x[0][i]);
+    x[1][i] = __fmaf_rn(-p1[i], ps, x[1][i]);
   }
+}
+
+template <int NKK>
+__device__ inline void subtract_lowrank(const uint4* Bf, const half8_t (&uf)[NKK], float ps, int lane,
+                                        float (&x)[2][16]) {
+  f32x16_t a0, a1;
+  lowrank_mfma<NKK>(Bf, uf, lane, a0, a1);
+  lowrank_subtract(a0, a1, ps, x);
 }
 
 // Pass 1: tensor |max| of the residual (or of M when NKK == 0).  A workgroup
