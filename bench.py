@@ -7,7 +7,8 @@ Workload (the 8-step LLaMA-3-8B MLP case): 16384 tokens, hidden 4096, FFN
 (164 rows), stochastic rounding, factors sketched every 8 steps and reused in
 between.  Weights drift each step (W += 1e-3 ||W||_F / sqrt(numel) N(0,1));
 activations and gradients are redrawn each step with their dominant right
-subspace rotated by 0.01 rad per step.  A "step" is one pass of the whole
+subspace rotated by 0.01 rad per step; every step (warmup and timed) has
+its own inputs, so both continue over the run.  A "step" is one pass of the whole
 path over all three projections: decompose (sketch on refresh steps,
 projection + rediag always), quantise (residual and factors, both K
 orientations), split GEMM forward, split GEMM backward (dX and dW).
@@ -19,7 +20,9 @@ HIP events on its stream) and the CPU oracle timed on a bounded sample.
 Outside the timed region it also measures (unless --no-extras): the copy and
 vendor bf16 GEMM ceilings of the GPU, plain NVFP4 (k = 0) through the same
 kernels on the same workload (step time and quantisation error against
-Metis), and the 1M x 4096 activation (decompose and quantise).
+Metis), the GPT-2 130M MLP-up and LLaMA-3 8B q_proj projections on their
+own (ms per step, TFLOP/s, rSVD ms of X, W and D), and the 1M x 4096
+activation (decompose and quantise).
 """
 
 import argparse
@@ -39,6 +42,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
 TOKENS, HIDDEN, FFN = 16384, 4096, 14336
 K_RANK, OVERSAMPLE, L_K, REFRESH = 61, 8, 164, 8
+MAX_INPUT_STEPS = 64          # ~2 GB of bf16 inputs per step
 
 
 # HBM traffic of the main split-GEMM kernel, bytes per launch averaged over
@@ -437,7 +441,28 @@ def dequant_q4(q4):
     return vals * sc.repeat_interleave(16, dim=1) * q4.tensor_scale.float()
 
 
-def operand_errors(M, qm, qd, V):
+def tail_projector(M, r):
+    """Projection onto the complements of M's top-r left and right singular
+    subspaces, E -> (I - U U^T) E (I - V V^T).  U from the top-r eigenvectors
+    of M M^T (M has no more rows than columns) by host LAPACK in float64,
+    V = M^T U normalised.  Measurement only."""
+    import scipy.linalg
+    import torch
+    Mf = M.float()
+    G = (Mf @ Mf.T).double().cpu().numpy()
+    n = G.shape[0]
+    _, U = scipy.linalg.eigh(G, subset_by_index=[n - r, n - 1])
+    U = torch.from_numpy(U).float().to(M.device)
+    V = Mf.T @ U
+    V = V / torch.linalg.norm(V, dim=0)
+
+    def proj(E):
+        E = E - U @ (U.T @ E)
+        return E - (E @ V) @ V.T
+    return proj
+
+
+def operand_errors(M, qm, qd, V, tail_r=None):
     """Quantisation error of one operand for Metis (qm: factors + residual)
     and for plain NVFP4 (qd), in the K-along-columns orientation: over the
     whole matrix, and inside the residual subspace (the orthogonal
@@ -457,11 +482,14 @@ def operand_errors(M, qm, qd, V):
     a = Mf.abs()
     small = a < a.reshape(a.shape[0], -1, 16).amax(dim=2).repeat_interleave(16, dim=1) / 8
     out = {}
+    tail = tail_projector(M, tail_r) if tail_r else None
     for name, hat in (("metis", metis_hat), ("nvfp4", plain_hat)):
         E = hat - Mf
         out[name] = {"all": round(float(torch.linalg.norm(E) / ref_all), 6),
                      "residual_subspace": round(float(torch.linalg.norm(perp(E)) / ref_perp), 6),
                      "small_values_to_zero": round(float(((hat == 0) & small & (Mf != 0)).sum() / small.sum()), 6)}
+        if tail is not None:
+            out[name]["tail_two_sided"] = round(float(torch.linalg.norm(tail(E)) / torch.linalg.norm(tail(Mf))), 6)
     return out
 
 
@@ -512,7 +540,8 @@ def measure_direct(mlp, inputs, t_last, mlp_ms=None, steps=4, warmup=2, sample_r
     ops = {}
     for name in ("X_gu", "W_gate", "D_gate"):
         M = inputs[name][t_last % len(inputs[name])]
-        ops[name] = operand_errors(M, mlp.q[name], q[name], mlp.factors[name].V)
+        ops[name] = operand_errors(M, mlp.q[name], q[name], mlp.factors[name].V,
+                                   tail_r=2 * K_RANK if name == "W_gate" else None)
     return {"ms_per_step": round(ms, 3), "streams": 1, "metis_over_nvfp4_time": round(mlp_ms / ms, 4) if mlp_ms else None,
             "y_rel_fro_err_vs_exact": err,
             "y_sample": "forward Y of each projection on %d evenly spaced token rows of the step-%d inputs"
@@ -520,7 +549,9 @@ def measure_direct(mlp, inputs, t_last, mlp_ms=None, steps=4, warmup=2, sample_r
             "operand_rel_err": ops,
             "operand_note": "||M-hat - M|| / ||M|| over the matrix; the same ratio inside the orthogonal "
                             "complement of the cached right factor V (residual subspace); the fraction of values "
-                            "below 1/8 of their 16-block's largest magnitude that dequantise to 0"}
+                            "below 1/8 of their 16-block's largest magnitude that dequantise to 0; for W_gate "
+                            "also the two-sided tail metric ||P_u (M-hat - M) P_v|| / ||P_u M P_v|| with P_u, P_v "
+                            "the projectors on the complements of W's top-2k singular subspaces"}
 
 
 def measure_mxfp4(m, X, W, t_last, nvfp4_gemm_ms, reps=10, sample_rows=256):
@@ -683,6 +714,119 @@ def _captured(m, basis, best):
     return float((md @ q).pow(2).sum() / (md @ best).pow(2).sum())
 
 
+LAYER_CONFIGS = {
+    # GPT-2 130M MLP up-projection: X 8192 x 768, W 768 x 3072, k = 12
+    "c1_gpt2_130m_mlp_up": dict(tokens=8192, n_in=768, n_out=3072, k=12, s=8, l_k=82),
+    # LLaMA-3 8B q_proj: X 16384 x 4096, W 4096 x 4096, k = 61
+    "c2_llama3_8b_q_proj": dict(tokens=16384, n_in=4096, n_out=4096, k=61, s=8, l_k=164),
+}
+
+
+def measure_layer(dev, name, steps=16, warmup=8):
+    """One split projection on its own (one stream, calls in data order):
+    decompose + quantise X, W and D (both K orientations), the split GEMM
+    forward and backward (dX, dW), the factors refreshed every 8 steps.
+    Every step has its own inputs: W drifts, X and D turn their dominant
+    subspace 0.01 rad per step.  Reports ms per step, algorithmic TFLOP/s,
+    the main GEMM's share, and the decomposition times of X, W and D at a
+    refresh step and at a cached step."""
+    import torch
+    from spectral_split_quantized_amd import metis, synth
+    c = LAYER_CONFIGS[name]
+    l, m, n, k = c["tokens"], c["n_in"], c["n_out"], c["k"]
+    cfg = metis.make_config(k=k, s=c["s"], l_k=c["l_k"], refresh=REFRESH, rounding=metis.SR, seed=0)
+    shapes = {"X": (l, m, synth.FRAC_X, True, metis.OPERAND_X), "W": (m, n, synth.FRAC_W, False, metis.OPERAND_W),
+              "D": (l, n, synth.FRAC_D, True, metis.OPERAND_D)}
+    nst = warmup + steps
+    seqs = {}
+    for op, (r, cc, frac, _, _) in shapes.items():
+        seed = 5000 + 10 * synth.OPERAND_ID[op]
+        if op == "W":
+            master, _ = synth.anisotropic_fast(r, cc, frac, seed, out_dtype=torch.float32, device=dev)
+            seq = []
+            for t in range(nst):
+                seq.append(master.to(torch.bfloat16))
+                master = synth.drift_weight(master, seed + 7919 * (t + 1))
+        else:
+            seq, basis = [], None
+            for t in range(nst):
+                mt, basis = synth.anisotropic_fast(r, cc, frac, seed + t, device=dev, basis=basis, theta=0.01 * t)
+                seq.append(mt)
+        seqs[op] = seq
+    f = {op: metis.Factors(r, cc, k, dev) for op, (r, cc, _, _, _) in shapes.items()}
+    q = {op: metis.QOperand(r, cc, k, metis.AXIS0 | metis.AXIS1, dev) for op, (r, cc, _, _, _) in shapes.items()}
+    lib = metis.load()
+    import ctypes
+    need = max(lib.metis_prepare_operand_workspace(r, cc, ctypes.byref(cfg), int(smp))
+               for r, cc, _, smp, _ in shapes.values())
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    Y = torch.empty(l, n, dtype=torch.float32, device=dev)
+    dX = torch.empty(l, m, dtype=torch.float32, device=dev)
+    dW = torch.empty(m, n, dtype=torch.float32, device=dev)
+    xc, wc, dc = q["X"]._c(), q["W"]._c(), q["D"]._c()
+    gwf = torch.empty(lib.metis_gemm_fwd_workspace(ctypes.byref(xc), ctypes.byref(wc)), dtype=torch.uint8, device=dev)
+    gwb = torch.empty(lib.metis_gemm_bwd_workspace(ctypes.byref(dc), ctypes.byref(wc), ctypes.byref(xc)),
+                      dtype=torch.uint8, device=dev)
+
+    def step(t):
+        for op, (_, _, _, smp, kind) in shapes.items():
+            metis.prepare_operand(seqs[op][t], cfg, smp, metis.make_tag(9, kind), t, f[op],
+                                  metis.AXIS0 | metis.AXIS1, out=q[op], workspace=ws)
+            if op == "W":
+                metis.gemm_fwd(q["X"], q["W"], Y=Y, workspace=gwf)
+        metis.gemm_bwd(q["D"], q["W"], q["X"], dX=dX, dW=dW, workspace=gwb)
+
+    for t in range(warmup):
+        step(t)
+    torch.cuda.synchronize()
+    metis.status_sync()
+    metis.timing_enable(1024)
+    metis.timing_kinds(1)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for t in range(warmup, nst):
+        step(t)
+    b.record()
+    torch.cuda.synchronize()
+    total = a.elapsed_time(b)
+    recs = metis.timing_read(1024)
+    metis.timing_enable(0)
+    metis.timing_kinds(-1)
+    metis.status_sync()
+    flops = 0
+    for t in range(warmup, nst):
+        refresh = (t % REFRESH) == 0
+        for op, (r, cc, _, smp, _) in shapes.items():
+            flops += decompose_flops(r, cc, k, c["s"], c["l_k"] if smp else r, refresh) + residual_flops(r, cc, k)
+        flops += split_gemm_flops(l, n, m, k, k) + split_gemm_flops(l, m, n, k, k) + split_gemm_flops(m, n, l, k, k)
+    g = [r for r in recs if r[0] == 0]
+    g_ms = sum(r[1] for r in g) / steps
+    g_flops = sum(2 * r[2] * r[3] * r[4] + 2 * r[2] * r[3] * 2 * k for r in g) / steps
+    g_tf = g_flops / (g_ms * 1e-3) / 1e12 if g_ms > 0 else 0.0
+    # decomposition alone, at a refresh step and at the cached step after it
+    rsvd = {}
+    for op, (r, cc, _, smp, kind) in shapes.items():
+        fo = metis.Factors(r, cc, k, dev)
+        t0 = (nst // REFRESH) * REFRESH
+        for label, t in (("refresh", t0), ("cached", t0 + 1)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            metis.decompose(seqs[op][t % nst], cfg, smp, metis.make_tag(9, kind), t, fo, workspace=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            rsvd["%s_%s" % (op, label)] = round(e0.elapsed_time(e1), 3)
+    metis.status_sync()
+    del seqs
+    torch.cuda.empty_cache()
+    return {"workload": name, "shapes": {"X": [l, m], "W": [m, n], "D": [l, n]}, "k": k, "s": c["s"],
+            "l_k": c["l_k"], "refresh": REFRESH, "rounding": "sr", "steps": steps, "warmup": warmup,
+            "ms_per_step": round(total / steps, 4), "tflops": round(flops / (total * 1e-3) / 1e12, 2),
+            "main_gemm": {"ms_per_step": round(g_ms, 4), "launches_per_step": len(g) / steps,
+                          "roofline": {"bound": "mfma", "achieved": round(g_tf, 1), "peak": PEAK_F16_TFLOPS,
+                                       "unit": "TFLOP/s", "frac": round(g_tf / PEAK_F16_TFLOPS, 4)}},
+            "rsvd_ms": rsvd, "streams": 1}
+
+
 def measure_training_loop(dev, steps=48, periods=(1, 8, 32), tokens=8192, lr=2e-5):
     """A GPT-2-130M-shaped MLP block (768 -> 3072 -> GELU -> 768, no bias),
     both linears through the Metis autograd layer, trained with Adam on a
@@ -821,9 +965,12 @@ def main():
     dev = torch.device("cuda", 0)
     metis.load()
 
-    log("building inputs (8 steps, LLaMA-3-8B MLP shapes)")
+    # one input set per step, so the weight drift and the activation rotation
+    # continue over the whole run (cycled only past MAX_INPUT_STEPS)
+    n_in = min(args.warmup + args.steps, MAX_INPUT_STEPS)
+    log("building inputs (%d steps, LLaMA-3-8B MLP shapes)" % n_in)
     t_build = time.time()
-    inputs = build_inputs(REFRESH, dev)
+    inputs = build_inputs(n_in, dev)
     log("inputs built in %.1f s" % (time.time() - t_build))
     mlp = MetisMLP(dev, streams=args.streams)
 
@@ -922,6 +1069,9 @@ def main():
         extras["mxfp4_variant"] = measure_mxfp4(mlp.metis, inputs["X_gu"][t_last % len(inputs["X_gu"])],
                                                 inputs["W_gate"][t_last % len(inputs["W_gate"])], t_last,
                                                 roofline["avg_ms"])
+        for name in LAYER_CONFIGS:
+            log("single projection %s" % name)
+            extras.setdefault("layers", {})[name] = measure_layer(dev, name)
         log("1M x 4096 activation")
         extras["c4_activation"] = measure_c4(dev, extras["ceilings"]["copy_GBps"])
         log("training loop through the autograd layer (refresh periods 1, 8, 32)")
@@ -947,7 +1097,7 @@ def main():
            "config": {"workload": "llama3_8b_mlp_gate_up_down_16k_tokens_8step_factor_cache",
                       "streams": mlp.nstreams + (1 if mlp.side is not None else 0),
                       "tokens": TOKENS, "hidden": HIDDEN, "ffn": FFN, "k": K_RANK, "s": OVERSAMPLE,
-                      "l_k": L_K, "refresh": REFRESH, "rounding": "sr"},
+                      "l_k": L_K, "refresh": REFRESH, "rounding": "sr", "input_steps": n_in},
            "dense_equiv_tflops": round(dense_equiv_flops() * args.steps / (total_ms * 1e-3) / 1e12, 2),
            "algorithmic_flop_per_step": round(flops / args.steps),
            "roofline": roofline, "streaming_roofline": streaming, "rsvd_ms": rsvd_ms,

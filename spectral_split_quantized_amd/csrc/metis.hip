@@ -299,6 +299,16 @@ DecompWs carve_decompose(Carver& cv, int64_t rows, int64_t cols, int k, int n, i
   return w;
 }
 
+// The Jacobi eigensolver with LDS sized to n (callers check the launch).
+void launch_jacobi(const double* g, int n, double* w, double* z, hipStream_t st) {
+  if (n <= 32)
+    hipLaunchKernelGGL(jacobi_kernel<32>, dim3(1), dim3(1024), 0, st, g, n, w, z);
+  else if (n <= 72)
+    hipLaunchKernelGGL(jacobi_kernel<72>, dim3(1), dim3(1024), 0, st, g, n, w, z);
+  else
+    hipLaunchKernelGGL(jacobi_kernel<kMaxN>, dim3(1), dim3(1024), 0, st, g, n, w, z);
+}
+
 metis_status launch_gram(const float* X, int64_t nr, int n, int64_t rs, int64_t cs, int maxblocks,
                          double* part, double* G, hipStream_t st) {
   int64_t per = (nr + maxblocks - 1) / maxblocks;
@@ -828,7 +838,7 @@ metis_status decompose_project(DecompCall& c, hipStream_t st) {
                        w.bpart, w.slices, (int64_t)n * cols, scale, w.b);
     LAUNCH_CHECK();
     if ((s = launch_gram(w.b, cols, n, 1, cols, w.gblocks, w.gpart, w.g, st)) != METIS_OK) return s;
-    hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(1024), 0, st, w.g, n, w.theta, w.z);
+    launch_jacobi(w.g, n, w.theta, w.z, st);
     LAUNCH_CHECK();
     hipLaunchKernelGGL(sketch_v_kernel, dim3(grid1(cols * k, 256)), dim3(256), 0, st, w.b, cols, n, k,
                        w.z, w.theta, f->V);
@@ -857,7 +867,7 @@ metis_status decompose_rediag(DecompCall& c, hipStream_t st) {
   const int k = c.k;
   metis_factors* f = c.f;
   DecompWs& w = c.w;
-  hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(1024), 0, st, w.ptp, k, w.lam, w.rot);
+  launch_jacobi(w.ptp, k, w.lam, w.rot, st);
   LAUNCH_CHECK();
   hipLaunchKernelGGL(apply_rot_kernel<true>, dim3((unsigned)ceil_div<int64_t>(cols, 64)), dim3(256), 0, st,
                      f->V, cols, k, w.rot, nullptr, nullptr, w.vn);

@@ -451,44 +451,72 @@ __device__ __forceinline__ int jacobi_pair(int kp, int r, int np) {
   return min(a, b) | (max(a, b) << 8);
 }
 
+// 1 / x and 1 / sqrt(x) (x > 0, normal) from the hardware estimates with one
+// Newton step each: a few units in the last place, enough for rotations
+// (the rotation below stays orthogonal to that accuracy) and far shorter
+// than the correctly rounded division, square root and hypot, which made
+// the rotation the latency of every Jacobi round.
+__device__ __forceinline__ double rcp_nr(double x) {
+  const double r = __builtin_amdgcn_rcp(x);
+  return fma(r, fma(-x, r, 1.0), r);
+}
+__device__ __forceinline__ double rsq_nr(double x) {
+  const double y = __builtin_amdgcn_rsq(x);
+  const double e = fma(-x * y, y, 1.0);  // 1 - x y^2
+  return fma(0.5 * y, e, y);
+}
+
 // Symmetric 2x2 Schur rotation (Golub & Van Loan, section 8.5) that zeroes
-// a_pq: [c s; -s c]^T [app apq; apq aqq] [c s; -s c] is diagonal.
+// a_pq: [c s; -s c]^T [app apq; apq aqq] [c s; -s c] is diagonal, with
+// tau = (aqq - app) / (2 apq), t = sign(tau) / (|tau| + sqrt(1 + tau^2)),
+// c = 1 / sqrt(1 + t^2), s = t c.
 __device__ __forceinline__ void jacobi_rot(double app, double aqq, double apq, double& c, double& s) {
   c = 1.0;
   s = 0.0;
   if (apq == 0.0) return;
-  const double diff = aqq - app;
+  const double tau = (aqq - app) * rcp_nr(2.0 * apq);
+  const double at = fabs(tau);
   double t;
-  if (fabs(diff) > 1e300 * fabs(apq)) {
-    t = apq / diff;  // tau would overflow: t = 1 / (2 tau)
+  if (at > 1e150) {
+    t = 0.5 * rcp_nr(tau);  // tau^2 would overflow: t -> 1 / (2 tau)
   } else {
-    const double tau = diff / (2.0 * apq);
-    const double h = hypot(1.0, tau);
-    t = tau >= 0.0 ? 1.0 / (tau + h) : -1.0 / (-tau + h);
+    const double q = fma(tau, tau, 1.0);
+    const double h = q * rsq_nr(q);  // sqrt(1 + tau^2)
+    t = copysign(rcp_nr(at + h), tau);
   }
-  c = 1.0 / sqrt(1.0 + t * t);
+  c = rsq_nr(fma(t, t, 1.0));
   s = t * c;
 }
 
 // Cyclic Jacobi with the symmetric Schur rotation in the parallel circle
-// order; stops when off(A) <= 1e-15 ||A||_F (or 30 sweeps).  Output:
+// order; stops when off(A) <= 1e-12 ||A||_F (or 30 sweeps).  By Weyl's
+// bound the diagonal is then within 1e-12 ||A||_F of the eigenvalues, which
+// for the Gram matrices here (||A||_F <= 1e5 lambda_min / 1e-7 or so) keeps
+// the singular values to ~1e-6 relative; the last, quadratically converging
+// sweep to 1e-15 would only refine rounding.  Output:
 // eigenvalues descending (ties by index) and eigenvectors (column-major in
 // Z: Z[a * n + i] = component a of vector i) signed so the largest-magnitude
 // component is positive (lowest index on ties).
 //
-// One round applies its np/2 disjoint rotations as J^T A J on 2x2 blocks
-// (block (P, Q) of pairs P <= Q, mirrored below the diagonal), then wave 0
-// forms the next round's rotations while the other waves apply this round's
-// to V: two barriers per round.
+// One round applies its np/2 disjoint rotations as J^T A J on 2x2 blocks:
+// block (P, Q), P <= Q, of pairs P and Q is owned by one thread for the
+// whole run.  A is kept as its upper triangle (entry (r, c) at
+// A[min][max]); the eigenvector matrix is kept transposed (VT[p][i] =
+// V[i][p]) so the column updates read consecutive addresses.  After the
+// blocks, wave 0 forms the next round's rotations while the other waves
+// apply this round's to V: two barriers per round.
+template <int NM>
 __global__ __launch_bounds__(1024) void jacobi_kernel(const double* __restrict__ Ain, int n,
                                                       double* __restrict__ w_out,
                                                       double* __restrict__ Z) {
-  constexpr int kHalf = kMaxN / 2;
-  __shared__ double A[kMaxN][kMaxN + 1];
-  __shared__ double V[kMaxN][kMaxN + 1];
-  __shared__ double cs[2][kHalf], sn[2][kHalf];
-  __shared__ int pq[2][kHalf];
-  __shared__ uint16_t blk[kHalf * (kHalf + 1) / 2];
+  static_assert(NM % 2 == 0 && NM <= kMaxN, "even, at most kMaxN");
+  constexpr int kHalf = NM / 2;
+  constexpr int kBlk = kHalf * (kHalf + 1) / 2;
+  constexpr int kPer = (kBlk + 1023) / 1024;  // blocks per thread
+  __shared__ double A[NM][NM + 1];
+  __shared__ double VT[NM][NM + 1];
+  __shared__ double2 rot[2][kHalf];  // (c, s) of pair P
+  __shared__ int2 rpq[2][kHalf];     // (p, q), p < q
   __shared__ double red[16];
   __shared__ int go;
   const int tid = threadIdx.x;
@@ -497,43 +525,60 @@ __global__ __launch_bounds__(1024) void jacobi_kernel(const double* __restrict__
   const int nblk = half * (half + 1) / 2;
   for (int e = tid; e < np * np; e += 1024) {
     const int a = e / np, b = e % np;
-    A[a][b] = (a < n && b < n) ? 0.5 * (Ain[a * n + b] + Ain[b * n + a]) : 0.0;
-    V[a][b] = (a == b) ? 1.0 : 0.0;
+    if (a <= b) A[a][b] = (a < n && b < n) ? 0.5 * (Ain[a * n + b] + Ain[b * n + a]) : 0.0;
+    VT[a][b] = (a == b) ? 1.0 : 0.0;
   }
-  if (tid < half) {
-    const int base = tid * half - tid * (tid - 1) / 2;
-    for (int q = tid; q < half; ++q) blk[base + q - tid] = (uint16_t)(tid | (q << 8));
+  // this thread's blocks (P, Q): the e-th pair with P <= Q in row order
+  int bP[kPer], bQ[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    int rem = tid + 1024 * u, P = 0;
+    while (P < half && rem >= half - P) {
+      rem -= half - P;
+      ++P;
+    }
+    bP[u] = P;
+    bQ[u] = P + rem;
   }
   __syncthreads();
   double loc = 0.0;
   for (int e = tid; e < np * np; e += 1024) {
-    const double v = A[e / np][e % np];
-    loc += v * v;
+    const int a = e / np, b = e % np;
+    if (a <= b) {
+      const double v = A[a][b];
+      loc += (a == b ? 1.0 : 2.0) * v * v;
+    }
   }
   loc = wave_sum_d(loc);
   if ((tid & 63) == 0) red[tid >> 6] = loc;
   if (tid < half) {
     const int pr = jacobi_pair(tid, 0, np);
     const int p = pr & 255, q = pr >> 8;
-    pq[0][tid] = pr;
-    jacobi_rot(A[p][p], A[q][q], A[p][q], cs[0][tid], sn[0][tid]);
+    double c, sn;
+    jacobi_rot(A[p][p], A[q][q], A[p][q], c, sn);
+    rpq[0][tid] = make_int2(p, q);
+    rot[0][tid] = make_double2(c, sn);
   }
   __syncthreads();
   double norm2 = 0.0;
   for (int i = 0; i < 16; ++i) norm2 += red[i];
-  const double tol2 = 1e-30 * norm2;
-  // V update: thread t of waves 1..15 owns pair t % half and rows t / half + g * G
-  const int vt = tid - 64;
-  const int G = 960 / half;
-  const bool vact = vt >= 0 && vt < G * half;
-  const int vk = vact ? vt % half : 0;
-  const int vi0 = vact ? vt / half : 0;
+  const double tol2 = 1e-24 * norm2;
+  // V update by waves 1..15: slot e = tid - 64 + 960 j is (pair e / np, row
+  // e % np), lanes over consecutive rows
+  constexpr int kVPer = (kHalf * NM + 959) / 960;
+  int vk[kVPer], vi[kVPer];
+#pragma unroll
+  for (int j = 0; j < kVPer; ++j) {
+    const int e = tid - 64 + 960 * j;
+    vk[j] = e >= 0 && e < half * np ? e / np : -1;
+    vi[j] = e >= 0 && e < half * np ? e - (e / np) * np : 0;
+  }
   int par = 0;
   for (int sweep = 0; sweep < 30; ++sweep) {
     double o = 0.0;
     for (int e = tid; e < np * np; e += 1024) {
       const int a = e / np, b = e % np;
-      if (a != b) o += A[a][b] * A[a][b];
+      if (a < b) o += 2.0 * A[a][b] * A[a][b];
     }
     o = wave_sum_d(o);
     __syncthreads();
@@ -547,28 +592,30 @@ __global__ __launch_bounds__(1024) void jacobi_kernel(const double* __restrict__
     __syncthreads();
     if (!go) break;
     for (int round = 0; round < np - 1; ++round) {
-      for (int e = tid; e < nblk; e += 1024) {
-        const int bq = blk[e];
-        const int P = bq & 255, Q = bq >> 8;
-        const int r1 = pq[par][P], r2 = pq[par][Q];
-        const int p1 = r1 & 255, q1 = r1 >> 8, p2 = r2 & 255, q2 = r2 >> 8;
-        const double c1 = cs[par][P], s1 = sn[par][P], c2 = cs[par][Q], s2 = sn[par][Q];
-        const double a = A[p1][p2], b = A[p1][q2], c = A[q1][p2], d = A[q1][q2];
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        if (tid + 1024 * u >= nblk) break;
+        const int P = bP[u], Q = bQ[u];
+        const int2 r1 = rpq[par][P], r2 = rpq[par][Q];
+        const double2 g1 = rot[par][P], g2 = rot[par][Q];
+        const int p1 = r1.x, q1 = r1.y, p2 = r2.x, q2 = r2.y;
+        const double c1 = g1.x, s1 = g1.y, c2 = g2.x, s2 = g2.y;
+        // rows {p1, q1} x columns {p2, q2}, each at its upper-triangle place
+        // (in a diagonal block, P == Q, entry (q, p) is entry (p, q): it is
+        // read twice and written twice, the later value being the same
+        // quantity up to rounding, and near zero)
+        double* const ea = p1 < p2 ? &A[p1][p2] : &A[p2][p1];
+        double* const eb = p1 < q2 ? &A[p1][q2] : &A[q2][p1];
+        double* const ec = q1 < p2 ? &A[q1][p2] : &A[p2][q1];
+        double* const ed = q1 < q2 ? &A[q1][q2] : &A[q2][q1];
+        const double a = *ea, b = *eb, c = *ec, d = *ed;
         // rows (J^T from the left), then columns (J from the right)
         const double ra = c1 * a - s1 * c, rc = s1 * a + c1 * c;
         const double rb = c1 * b - s1 * d, rd = s1 * b + c1 * d;
-        const double na = c2 * ra - s2 * rb, nb = s2 * ra + c2 * rb;
-        const double nc = c2 * rc - s2 * rd, nd = s2 * rc + c2 * rd;
-        A[p1][p2] = na;
-        A[p1][q2] = nb;
-        A[q1][p2] = nc;
-        A[q1][q2] = nd;
-        if (P != Q) {
-          A[p2][p1] = na;
-          A[q2][p1] = nb;
-          A[p2][q1] = nc;
-          A[q2][q1] = nd;
-        }
+        *ea = c2 * ra - s2 * rb;
+        *eb = s2 * ra + c2 * rb;
+        *ec = c2 * rc - s2 * rd;
+        *ed = s2 * rc + c2 * rd;
       }
       __syncthreads();
       if (tid < 64) {
@@ -576,17 +623,21 @@ __global__ __launch_bounds__(1024) void jacobi_kernel(const double* __restrict__
           const int nr = round + 1 < np - 1 ? round + 1 : 0;
           const int pr = jacobi_pair(tid, nr, np);
           const int p = pr & 255, q = pr >> 8;
-          pq[par ^ 1][tid] = pr;
-          jacobi_rot(A[p][p], A[q][q], A[p][q], cs[par ^ 1][tid], sn[par ^ 1][tid]);
+          double c, sn;
+          jacobi_rot(A[p][p], A[q][q], A[p][q], c, sn);
+          rpq[par ^ 1][tid] = make_int2(p, q);
+          rot[par ^ 1][tid] = make_double2(c, sn);
         }
-      } else if (vact) {
-        const int r = pq[par][vk];
-        const int p = r & 255, q = r >> 8;
-        const double c = cs[par][vk], sv = sn[par][vk];
-        for (int i = vi0; i < np; i += G) {
-          const double vp = V[i][p], vq = V[i][q];
-          V[i][p] = c * vp - sv * vq;
-          V[i][q] = sv * vp + c * vq;
+      } else {
+#pragma unroll
+        for (int j = 0; j < kVPer; ++j) {
+          if (vk[j] < 0) break;
+          const int2 r = rpq[par][vk[j]];
+          const double2 g = rot[par][vk[j]];
+          const int i = vi[j];
+          const double vp = VT[r.x][i], vq = VT[r.y][i];
+          VT[r.x][i] = g.x * vp - g.y * vq;
+          VT[r.y][i] = g.y * vp + g.x * vq;
         }
       }
       __syncthreads();
@@ -605,15 +656,15 @@ __global__ __launch_bounds__(1024) void jacobi_kernel(const double* __restrict__
     int am = 0;
     double best = -1.0;
     for (int a = 0; a < n; ++a) {
-      const double v = fabs(V[a][i]);
+      const double v = fabs(VT[i][a]);
       if (v > best) {
         best = v;
         am = a;
       }
     }
-    const double sg = V[am][i] < 0.0 ? -1.0 : 1.0;
+    const double sg = VT[i][am] < 0.0 ? -1.0 : 1.0;
     w_out[rank] = wi;
-    for (int a = 0; a < n; ++a) Z[a * n + rank] = sg * V[a][i];
+    for (int a = 0; a < n; ++a) Z[a * n + rank] = sg * VT[i][a];
   }
 }
 
