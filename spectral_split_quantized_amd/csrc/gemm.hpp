@@ -10,8 +10,8 @@
 // lies in [2^-10, 2688], so it is exact in fp16; products of two fp16 values
 // are exact in fp32, and the MFMA accumulates them in fp32.  The per-tensor
 // scales are applied once in the epilogue (alpha).  The K-extension holds
-// the low-rank terms of the split as bf16 hi/lo pairs; it is accumulated
-// after alpha has been applied to the main sum.
+// the low-rank terms of the split as bf16 hi/lo pairs, divided by alpha
+// (epi_scale), and is accumulated into the same unscaled sum.
 //
 // Tiling: BM x BN output tile per workgroup of WM x WN waves, each wave
 // (BM/WM) x (BN/WN) as 32 x 32 MFMA tiles; K step 64; FP4 codes are loaded to
@@ -139,7 +139,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp4_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16_t{};
 
-  const int64_t nk = kend > kbeg ? ceil_div<int64_t>(kend - kbeg, BK) : 0;
+  const EpiScale es = epi_scale(p.sa, p.sb);
+  const int64_t nk = kend > kbeg && !es.skip_main ? ceil_div<int64_t>(kend - kbeg, BK) : 0;
   RawChunk ra[Cfg::NCA], rb[Cfg::NCB];
 
   auto load_tile = [&](int64_t kt) {
@@ -201,14 +202,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp4_kernel(GemmParams p) {
     }
   }
 
-  float alpha = 1.0f;
-  if (p.sa) alpha *= p.sa[0];
-  if (p.sb) alpha *= p.sb[0];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] *= alpha;
-
   // ---- K-extension: bf16 operands copied into the same fragment layout
   if (p.kext > 0) {
     const int64_t ne = p.kext / BK;
@@ -259,7 +252,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp4_kernel(GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int64_t row = m0 + (wm * TM + i) * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (row < p.M) C[row * p.ldc + col] = acc[i][j][v];
+        if (row < p.M) {
+          float y = acc[i][j][v] * es.post;
+          if (es.post2 != 1.0f) y *= es.post2;
+          C[row * p.ldc + col] = y;
+        }
       }
     }
   }
@@ -546,7 +543,8 @@ struct ExtParams {
   uint16_t* b_ext;    // cols x kext
 };
 
-// A_ext[i] = [hi(P'' s_J) | lo(..) | H_bar | H_bar | 0 ...]: one thread per
+// A_ext[i] = [hi(P'' s_J) | lo(..) | H_bar | H_bar | 0 ...] (P'' times the
+// epilogue's ext_mul, as G below): one thread per
 // row and 8-column chunk (rows past e.rows up to the next multiple of 32 are
 // written as zeros).
 __global__ void ext_prep_a_kernel(ExtParams e) {
@@ -561,13 +559,14 @@ __global__ void ext_prep_a_kernel(ExtParams e) {
     const int p0 = col0 % e.ksR;
     const bool lo_half = col0 >= e.ksR;
     const float sc = (e.s_LR[0] * e.s_E[0]);
+    const float emul = epi_scale(e.s_LR, e.s_RR).ext_mul;
     float acc[8];
     sum_parts8(e.praw + i * 64 + p0, e.rows * 64, e.sa, acc);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int p = p0 + t;
       if (p < e.kR) {
-        const float x = acc[t] * sc * e.S_R[p] * e.J.ts[0];
+        const float x = acc[t] * sc * e.S_R[p] * e.J.ts[0] * emul;
         const float hi = bf16_bits_to_float(bf16_rn_bits(x));
         v[t] = lo_half ? x - hi : hi;
       }
@@ -599,6 +598,7 @@ __global__ __launch_bounds__(256) void ext_prep_b_kernel(ExtParams e) {
   const float sFE = e.s_F[0] * e.s_E[0];
   const float sFR = e.s_F[0] * e.s_RR[0];
   const float sH = e.H.ts[0];
+  const float emul = epi_scale(e.s_LR, e.s_RR).ext_mul;
   for (int idx = tid; idx < 64 * e.kR; idx += 256) {
     const int c = idx & 63, pp = idx >> 6;
     jv[c][pp] = (j0 + c < e.cols) ? factor_val(e.J, pp, j0 + c) : 0.0f;
@@ -638,7 +638,7 @@ __global__ __launch_bounds__(256) void ext_prep_b_kernel(ExtParams e) {
         if (q < e.kL) {
           float acc = sFR * t1[t];
           for (int pp = 0; pp < e.kR; ++pp) acc += t2f[q][pp] * jv[c][pp];
-          const float g = sH * e.S_L[q] * acc;
+          const float g = sH * e.S_L[q] * acc * emul;
           hi[t] = bf16_bits_to_float(bf16_rn_bits(g));
           lo[t] = g - hi[t];
         }

@@ -40,6 +40,42 @@ __device__ inline uint4 dequant8(uint32_t w, half2_t s) {
   return o;
 }
 
+// Scaling of a split product's output.  C = alpha (sum + ext / alpha) with
+// alpha = s_a s_b, the residual operands' tensor scales: the K-extension is
+// prepared already divided by alpha (times ext_mul), so the GEMM applies
+// alpha once, in the epilogue, after the extension (the accumulators never
+// leave the matrix registers to be scaled in the middle).  A product below
+// 2^-64 works with alpha 2^64 and the epilogue applies the extra 2^-64, so
+// ext_mul stays below 2^86; alpha == 0 (a residual that is all zeros)
+// drops the residual sum and leaves the extension unscaled.  The extension's
+// preparation and every GEMM that reads it evaluate this from the same two
+// scales.
+struct EpiScale {
+  float ext_mul;  // factor of the K-extension values
+  float post;     // epilogue factor
+  float post2;    // second epilogue factor (a power of two, 1 if unused)
+  bool skip_main; // alpha == 0: the residual sum is not accumulated
+};
+
+__device__ inline EpiScale epi_scale(const float* sa, const float* sb) {
+  float alpha = 1.0f;
+  if (sa) alpha *= sa[0];
+  if (sb) alpha *= sb[0];
+  EpiScale e{1.0f, 1.0f, 1.0f, false};
+  if (!(alpha > 0.0f)) {
+    e.skip_main = true;
+  } else if (alpha < 0x1p-64f) {
+    const float a2 = alpha * 0x1p64f;  // exact
+    e.ext_mul = __fdiv_rn(1.0f, a2);
+    e.post = a2;
+    e.post2 = 0x1p-64f;
+  } else {
+    e.ext_mul = __fdiv_rn(1.0f, alpha);
+    e.post = alpha;
+  }
+  return e;
+}
+
 __device__ inline int64_t remap_tile(int64_t bid, int64_t tiles_m, int64_t tiles_n) {
   const int64_t total = tiles_m * tiles_n;
   int64_t pid = bid;

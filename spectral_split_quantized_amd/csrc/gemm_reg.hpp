@@ -1,8 +1,8 @@
 // gemm_reg.hpp -- register-dequant NVFP4 GEMM for the large split products
 // ("Metis: Training LLMs with FP4 Quantization", 关键设计 1: the split
 // forward GEMM; 整体框架: the same split in every forward and backward GEMM).
-// Same contract as gemm_fp4_kernel in gemm.hpp (C = alpha A B^T + the bf16
-// K-extension), restricted to K % 256 == 0 with 16-byte aligned code and
+// Same contract as gemm_fp4_kernel in gemm.hpp (C = alpha (A B^T + the bf16
+// K-extension prepared divided by alpha)), restricted to K % 256 == 0 with 16-byte aligned code and
 // scale rows.  It lives in its own translation unit so that it can be
 // scheduled for instruction-level parallelism without changing the other
 // kernels.
@@ -91,7 +91,8 @@ void gemm_fp4_reg_kernel(GemmParams p) {
   const int64_t kper = ceil_div<int64_t>(p.K / BK, nsplit) * BK;
   const int64_t kbeg = (int64_t)blockIdx.y * kper;
   const int64_t kend = min(p.K, kbeg + kper);
-  const int64_t nk = kend > kbeg ? (kend - kbeg) / BK : 0;
+  const EpiScale es = epi_scale(p.sa, p.sb);
+  const int64_t nk = kend > kbeg && !es.skip_main ? (kend - kbeg) / BK : 0;
 
   f32x16_t acc[TM][TN];
 #pragma unroll
@@ -291,14 +292,6 @@ void gemm_fp4_reg_kernel(GemmParams p) {
     }
   }
 
-  float alpha = 1.0f;
-  if (p.sa) alpha *= p.sa[0];
-  if (p.sb) alpha *= p.sb[0];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] *= alpha;
-
   // ---- K-extension: stage e sits in ring slot (nk - 1 + e) % 2; every wave
   // reads its fragments of a sub-step straight from the stage (lane L at
   // block offset 16 L) while the next stage's DMA is in flight
@@ -330,18 +323,14 @@ void gemm_fp4_reg_kernel(GemmParams p) {
     }
   };
   if (ne > 0) {
-    // the first stage goes into the last FP4 stage's slot, which every wave
-    // finished reading before the main loop's final barrier
-    const bool s0 = nk == 0 || ((nk - 1) & 1) == 0;
-    if (s0)
-      issue_ext(0, S0{});
-    else
-      issue_ext(0, S1{});
+    // both slots are free once every wave is past this barrier (the main
+    // loop's last DMA, into either slot, has landed and its last reads are
+    // done), so the extension always starts in slot 0: one loop instance,
+    // whose accumulators stay where the main loop left them
+    if (nk > 0) ring_barrier();
+    issue_ext(0, S0{});
     ring_barrier();
-    if (s0)
-      ext_loop(S0{});
-    else
-      ext_loop(S1{});
+    ext_loop(S0{});
   }
 
   // ---- epilogue: lane holds column lane%32 and rows 8(v/4) + 4(lane/32) + v%4
@@ -355,7 +344,11 @@ void gemm_fp4_reg_kernel(GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int64_t row = m0 + (wm * TM + i) * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (row < p.M) __builtin_nontemporal_store(acc[i][j][v], &C[row * p.ldc + col]);
+        if (row < p.M) {
+          float y = acc[i][j][v] * es.post;
+          if (es.post2 != 1.0f) y *= es.post2;
+          __builtin_nontemporal_store(y, &C[row * p.ldc + col]);
+        }
       }
     }
   }
