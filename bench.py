@@ -51,19 +51,29 @@ MAX_INPUT_STEPS = 64          # ~2 GB of bf16 inputs per step
 # by what it reads for a plain 256 MiB copy, ``bench.py --copy-calibration``).
 # The figure belongs to the kernel source it was taken on: if any file below
 # changes, the stored figure no longer applies and ``traffic`` is reported null.
-GEMM_TRAFFIC_BYTES = 1673719604
-GEMM_TRAFFIC_SHA = "d75c2af57ffcd2ca"
+GEMM_TRAFFIC_BYTES = 1397967663
+GEMM_TRAFFIC_SHA = "5ec41f2fe4a66bc1"
 GEMM_SOURCES = ("common.hpp", "gemm_common.hpp", "gemm_reg.hpp", "gemm_launch.hpp", "gemm_big.hip")
+# the same for both quantiser sweeps of one 16384 x 14336 residual (k = 61,
+# SR, both orientations): FETCH_SIZE + WRITE_SIZE of the amax and quantise
+# dispatches, scaled alike, per call
+QUANT_TRAFFIC_BYTES = 1372665947
+QUANT_TRAFFIC_SHA = "144a23112c3f5422"
+QUANT_SOURCES = ("common.hpp", "quant.hpp", "quant_fast.hpp", "metis.hip")
 
 
-def gemm_source_sha():
+def source_sha(names):
     import hashlib
     h = hashlib.sha256()
     d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "spectral_split_quantized_amd", "csrc")
-    for name in GEMM_SOURCES:
+    for name in names:
         with open(os.path.join(d, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def gemm_source_sha():
+    return source_sha(GEMM_SOURCES)
 
 
 def mxfp4_only():
@@ -1039,7 +1049,9 @@ def main():
     q_bytes = xd.rows * xd.cols * (2 * 2 + 2 * (0.5 + 1 / 16)) + 2 * (xd.rows + xd.cols) * K_RANK * 4
     q_gbs = q_bytes / (q_ms * 1e-3) / 1e9 if q_ms > 0 else 0.0
     streaming = {"bound": "hbm", "achieved": round(q_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                 "frac": round(q_gbs / PEAK_HBM_GBS, 4), "kernel": "quant_amax_kernel + quant_kernel",
+                 "frac": round(q_gbs / PEAK_HBM_GBS, 4),
+                 "traffic": QUANT_TRAFFIC_BYTES if source_sha(QUANT_SOURCES) == QUANT_TRAFFIC_SHA else None,
+                 "kernel": "qf_amax_kernel + qf_quant_kernel (both quantiser sweeps)",
                  "operand": "X_down residual %d x %d, both orientations, SR" % (xd.rows, xd.cols),
                  "ms": round(q_ms, 4)}
 
