@@ -54,6 +54,38 @@ def build(verbose=False):
     return OUT
 
 
+# Host code under AddressSanitizer and UndefinedBehaviorSanitizer (the device
+# code is built as usual): each sanitizer option applies to the host pass only.
+HOST_SANITIZE = [
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=all",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+]
+SAN_OUT = os.path.join(OBJ, "libmetis_san.so")
+
+
+def build_host_sanitized(verbose=False):
+    """_build/libmetis_san.so: the C-ABI translation unit (metis.hip, all of
+    the host-side argument checking, workspace carving and scheduling) with
+    host ASan + UBSan, linked with the regular GEMM unit.  Load it with
+    METIS_LIBRARY set to its path and the ASan runtime preloaded; only calls
+    that need no GPU can run where there is none."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    os.makedirs(OBJ, exist_ok=True)
+    gemm_obj = os.path.join(OBJ, "gemm_big.o")
+    if not os.path.exists(gemm_obj):
+        build(verbose)
+    obj = os.path.join(OBJ, "metis_san.o")
+    flags = [f for f in FLAGS if f != "-O3"] + ["-O1", "-g"] + HOST_SANITIZE
+    _run([hipcc] + flags + ["-c", os.path.join(CSRC, "metis.hip"), "-o", obj], verbose)
+    tmp = SAN_OUT + ".tmp"
+    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC"] + HOST_SANITIZE[:4] + [obj, gemm_obj, "-o", tmp],
+         verbose)
+    os.replace(tmp, SAN_OUT)
+    return SAN_OUT
+
+
 if __name__ == "__main__":
     build(verbose=True)
     print("built", OUT)

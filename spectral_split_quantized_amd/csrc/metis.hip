@@ -212,6 +212,10 @@ struct DecompWs {
 // Split-K plan of an MFMA product with nr output rows over nkb 64-wide K
 // blocks: about 1024 workgroups of 128 rows; returns the split count.
 int64_t split_plan(int64_t nr, int64_t nkb, int64_t* kbps) {
+  if (nkb <= 0 || nr <= 0) {  // no K blocks (cols < 64): the MFMA product is not used
+    *kbps = 0;
+    return 0;
+  }
   const int64_t row_blocks = (nr + 127) / 128;
   int64_t splits = (1024 + row_blocks - 1) / row_blocks;
   if (splits > nkb) splits = nkb;

@@ -11,7 +11,9 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmetis.so")
+# METIS_LIBRARY names another build of the same library (the CPU tests use it
+# for a host-sanitized build); by default the in-tree libmetis.so
+LIB_PATH = os.environ.get("METIS_LIBRARY") or os.path.join(HERE, "libmetis.so")
 
 OK, E_INVALID, E_UNSUPPORTED, E_HIP, E_NUMERIC, E_WORKSPACE = 0, -1, -2, -3, -4, -5
 BF16, F32 = 0, 1
