@@ -58,8 +58,8 @@ GEMM_SOURCES = ("common.hpp", "gemm_common.hpp", "gemm_reg.hpp", "gemm_launch.hp
 # SR, both orientations): FETCH_SIZE + WRITE_SIZE of the amax and quantise
 # dispatches, scaled alike, per call
 QUANT_TRAFFIC_BYTES = 1372665947
-QUANT_TRAFFIC_SHA = "144a23112c3f5422"
-QUANT_SOURCES = ("common.hpp", "quant.hpp", "quant_fast.hpp", "metis.hip")
+QUANT_TRAFFIC_SHA = "ea76dad5668b2bf6"
+QUANT_SOURCES = ("common.hpp", "quant.hpp", "quant_fast.hpp")
 
 
 def source_sha(names):
