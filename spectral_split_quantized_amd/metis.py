@@ -139,6 +139,13 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+def _rows_check(M):
+    """The boundary takes row-major matrices with a leading dimension: the
+    elements of a row must be contiguous."""
+    if M.dim() != 2 or (M.shape[1] > 1 and M.stride(1) != 1):
+        raise ValueError("M must be a 2-D row-major view (stride(1) == 1), got strides %s" % (M.stride(),))
+
+
 def _dtype_code(t):
     if t.dtype == torch.bfloat16:
         return BF16
@@ -222,6 +229,7 @@ def _workspace(nbytes, device):
 
 def decompose(M, cfg, sample_rows, tag, step, factors, workspace=None):
     """Spectral split of M (metis_decompose); updates ``factors`` in place."""
+    _rows_check(M)
     lib = load()
     rows, cols = M.shape
     need = lib.metis_decompose_workspace(rows, cols, ctypes.byref(cfg), int(sample_rows))
@@ -236,6 +244,7 @@ def decompose(M, cfg, sample_rows, tag, step, factors, workspace=None):
 
 def quantize(M, cfg, tag, step, axes, factors=None, out=None, residual_out=None, workspace=None):
     """NVFP4 quantisation of M or of its residual (metis_quantize)."""
+    _rows_check(M)
     lib = load()
     rows, cols = M.shape
     k = factors.k if factors is not None else 0
@@ -255,6 +264,7 @@ def quantize_static(M, cfg, tag, step, axes, factors=None, out=None, residual_ou
     """metis_quantize without a workspace: the library's static per-GPU scratch
     (metis_quantize_static) serves as workspace, so the call allocates no
     device memory (``out`` given: none at all)."""
+    _rows_check(M)
     lib = load()
     rows, cols = M.shape
     k = factors.k if factors is not None else 0
@@ -277,6 +287,7 @@ def prepare_operand(M, cfg, sample_rows, tag, step, factors, axes, out=None, res
     """Decompose and quantise M in one call (metis_prepare_operand): the
     residual sweeps run on the current stream while the rediagonalisation runs
     on ``side_stream`` (a torch.cuda.Stream; None: the current stream)."""
+    _rows_check(M)
     lib = load()
     rows, cols = M.shape
     if out is None:

@@ -74,3 +74,26 @@ def test_streaming_sweeps_single_axis(axes):
     general = metis.quantize(M, cfg, 0, 0, axes, factors=f, residual_out=export)
     metis.status_sync()
     _equal(fast, general, "axes %d" % axes)
+
+
+@pytest.mark.parametrize("k", [0, 61])
+def test_streaming_sweeps_strided_rows(k):
+    """M as a column slice of a wider matrix (leading dimension cols + 64):
+    the streaming sweeps read rows at the leading dimension."""
+    rows, cols = 1024, 16384
+    wide, _ = synth.anisotropic_fast(rows, cols + 64, synth.FRAC_X, 23, device="cuda")
+    M = wide[:, :cols]
+    assert M.stride(0) == cols + 64
+    cfg = metis.make_config(k=max(k, 1), rounding=metis.SR, seed=2)
+    f = None
+    if k:
+        u, s, v = synth.exact_factors(rows, cols, k, seed=9)
+        f = gpu_factors(u, s, v)
+    both = metis.AXIS0 | metis.AXIS1
+    fast = metis.quantize(M, cfg, 0, 3, both, factors=f)
+    dense = metis.quantize(M.contiguous(), cfg, 0, 3, both, factors=f)
+    export = torch.empty(rows, cols, dtype=torch.float32, device="cuda")
+    general = metis.quantize(M, cfg, 0, 3, both, factors=f, residual_out=export)
+    metis.status_sync()
+    _equal(fast, dense, "strided vs contiguous")
+    _equal(fast, general, "strided streaming vs general")
