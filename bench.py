@@ -237,7 +237,7 @@ class MetisMLP:
         # the critical path runs there while their residual is quantised
         self.side = torch.cuda.Stream(device=device) if self.nstreams > 1 else None
         self.ws = [torch.empty(need, dtype=torch.uint8, device=device) for _ in self.streams]
-        self.free_gate = self.free_up = None
+        self.free_gate = self.free_up = self.free_down = None
         log("  workspace %.1f MB x %d streams, %.1f MB for the split products"
             % (need / 1e6, self.nstreams, sum(a.numel() + b.numel() for a, b in self.gws.values()) / 1e6))
 
@@ -317,6 +317,7 @@ class MetisMLP:
         if self.free_gate is not None:
             self.streams[sw].wait_event(self.free_gate)
             self.streams[sw2].wait_event(self.free_up)
+
         ev = {}
         # the weights keep their rediagonalisation on their own stream (W_up
         # on the second side stream, so that at a refresh step its sketch
@@ -334,6 +335,10 @@ class MetisMLP:
         e_up = self._ahead("up", "fwd", [x_ready, ev["W_up"]])
         main.wait_event(e_up)
         self._gemm("up", "fwd")
+        # the previous step's down-projection dW (on a side stream) may still
+        # read X_down, D_down and its K-extension, which are rewritten now
+        if self.free_down is not None:
+            main.wait_event(self.free_down)
         self._prep("X_down", t, inputs, 0)
         main.wait_event(ev["W_down"])
         self._ext("down", "fwd", main)
@@ -341,17 +346,26 @@ class MetisMLP:
         self._prep("D_down", t, inputs, 0)
         d_ready = self._event(0)
         # backward: dX of the down projection first (D_gate and D_up are
-        # computed from it in a real layer); D_gate is prepared on the main
-        # stream and D_up beside it on the side stream (both are chains of
-        # small kernels that leave room for each other, whereas a chain
-        # running beside a GEMM waits for its tiles); every K-extension that
-        # can be built ahead is built on the companion stream beside an
-        # earlier GEMM; the down projection's dW, needed by nothing in the
-        # step, runs last
+        # computed from it in a real layer); its dW, needed by nothing in the
+        # step, then runs on the second side stream beside D_gate's
+        # preparation on the main stream and D_up's on the first side stream
+        # (with fewer streams it runs last on the main stream); every
+        # K-extension that can be built ahead is built on the companion
+        # stream beside an earlier GEMM
         self._ext("down", "dx", main)
         e_down_dw = self._ahead("down", "dw", [d_ready])
         self._gemm("down", "dx")
         dx_ready = self._event(0)
+        if self.nstreams > 2:
+            # the down projection's dW, needed by nothing in the step, runs on
+            # the second side stream beside the D_gate and D_up preparations,
+            # whose chains of small kernels leave most of the chip idle
+            st2 = self.streams[sw2]
+            st2.wait_event(dx_ready)
+            st2.wait_event(e_down_dw)
+            with self.torch.cuda.stream(st2):
+                self._gemm("down", "dw")
+            self.free_down = self._event(sw2)
         self.streams[sw].wait_event(dx_ready)
         self._prep("D_up", t, inputs, sw, companion=False)
         self._prep("D_gate", t, inputs, 0)
@@ -370,8 +384,9 @@ class MetisMLP:
         main.wait_event(e_up_dw)
         self._gemm("up", "dw")
         self.free_up = self._event(0)
-        main.wait_event(e_down_dw)
-        self._gemm("down", "dw")
+        if self.nstreams <= 2:
+            main.wait_event(e_down_dw)
+            self._gemm("down", "dw")
 
     def step_flops(self, t):
         refresh = (t % REFRESH) == 0
@@ -1004,6 +1019,8 @@ def main():
     ev0.record(stream)
     for t in range(args.warmup, args.warmup + args.steps):
         mlp.step(t, inputs)
+    if mlp.free_down is not None:
+        stream.wait_event(mlp.free_down)  # the last step's side-stream GEMM
     ev1.record(stream)
     torch.cuda.synchronize()
     total_ms = ev0.elapsed_time(ev1)
