@@ -201,7 +201,8 @@ struct DecompWs {
   uint2* cand;
   uint8_t* flags;
   int32_t* idx;
-  float *om, *y, *q, *bpart, *b, *p, *vn, *sign, *ppart, *spart;
+  float *om, *y, *q, *bpart, *b, *p, *vn, *ppart, *spart;
+  unsigned long long* key;  // per-column sign keys of the rediagonalisation
   uint16_t *vfrag, *ofrag;
   int64_t proj_nkb, proj_kbps, proj_splits, sk_kbps, sk_splits;
   double *gpart, *g, *rinv, *z, *theta, *ptp, *rot, *lam;
@@ -290,7 +291,7 @@ DecompWs carve_decompose(Carver& cv, int64_t rows, int64_t cols, int k, int n, i
   w.rot = cv.take<double>(kMaxN * kMaxN);
   w.lam = cv.take<double>(kMaxN);
   w.vn = cv.take<float>(cols * k);
-  w.sign = cv.take<float>(kMaxN);
+  w.key = cv.take<unsigned long long>(kMaxN);
   // MFMA products (bf16 operands, cols % 64 == 0): split-K plans for the
   // projection P = M V (rows x k) and the sketch Y = M_s Omega (lr x n)
   w.proj_nkb = cols / 64;
@@ -303,14 +304,27 @@ DecompWs carve_decompose(Carver& cv, int64_t rows, int64_t cols, int k, int n, i
   return w;
 }
 
-// The Jacobi eigensolver with LDS sized to n (callers check the launch).
-void launch_jacobi(const double* g, int n, double* w, double* z, hipStream_t st) {
+// The Jacobi eigensolver with LDS sized to n (callers check the launch);
+// clear (n words, may be null) is zeroed on the way.
+void launch_jacobi(const double* g, int n, double* w, double* z, unsigned long long* clear, hipStream_t st) {
   if (n <= 32)
-    hipLaunchKernelGGL(jacobi_kernel<32>, dim3(1), dim3(1024), 0, st, g, n, w, z);
+    hipLaunchKernelGGL(jacobi_kernel<32>, dim3(1), dim3(1024), 0, st, g, n, w, z, clear);
   else if (n <= 72)
-    hipLaunchKernelGGL(jacobi_kernel<72>, dim3(1), dim3(1024), 0, st, g, n, w, z);
+    hipLaunchKernelGGL(jacobi_kernel<72>, dim3(1), dim3(1024), 0, st, g, n, w, z, clear);
   else
-    hipLaunchKernelGGL(jacobi_kernel<kMaxN>, dim3(1), dim3(1024), 0, st, g, n, w, z);
+    hipLaunchKernelGGL(jacobi_kernel<kMaxN>, dim3(1), dim3(1024), 0, st, g, n, w, z, clear);
+}
+
+// The rediagonalisation's two tail kernels with LDS sized to k.
+template <int NM>
+void launch_rot(DecompWs& w, const metis_factors* f, int64_t rows, int64_t cols, int k, uint32_t* amax_u,
+                uint32_t* amax_v, hipStream_t st) {
+  hipLaunchKernelGGL(rot_v_kernel<NM>, dim3((unsigned)ceil_div<int64_t>(cols, 64)), dim3(256), 0, st, f->V, cols,
+                     k, w.rot, w.vn, w.key, amax_v);
+  const int nbu = (int)ceil_div<int64_t>(rows, 64);
+  const int nbv = (int)ceil_div<int64_t>(cols, 64);
+  hipLaunchKernelGGL(rot_u_kernel<NM>, dim3((unsigned)(nbu + nbv)), dim3(256), 0, st, w.p, rows, k, w.rot, w.lam,
+                     w.key, w.vn, cols, f->U, f->V, f->S, amax_u, nbu);
 }
 
 metis_status launch_gram(const float* X, int64_t nr, int n, int64_t rs, int64_t cs, int maxblocks,
@@ -745,7 +759,11 @@ metis_status decompose_check(const void* M, int32_t dtype, int64_t rows, int64_t
   if (!dtype_ok(dtype)) return fail(METIS_E_INVALID, "dtype=%d", dtype);
   if (rows <= 0 || cols <= 0 || ld < cols) return fail(METIS_E_INVALID, "bad shape %lldx%lld ld=%lld",
                                                       (long long)rows, (long long)cols, (long long)ld);
-  if (rows > INT32_MAX) return fail(METIS_E_UNSUPPORTED, "rows > 2^31");
+  // rows and cols below 2^30: the rediagonalisation's sign keys hold a row
+  // index in 31 bits and its tail launches one workgroup per 64 rows of U
+  // and of V
+  if (rows > (1LL << 30) || cols > (1LL << 30))
+    return fail(METIS_E_UNSUPPORTED, "rows or cols above 2^30");
   // the sampler resolves its boundary histogram bin among at most kCandMax
   // candidate rows; 2^27 rows put 2048 rows in a bin on average
   if (sample_rows && rows > (int64_t)kCandMax * 65536 / 2)
@@ -842,7 +860,7 @@ metis_status decompose_project(DecompCall& c, hipStream_t st) {
                        w.bpart, w.slices, (int64_t)n * cols, scale, w.b);
     LAUNCH_CHECK();
     if ((s = launch_gram(w.b, cols, n, 1, cols, w.gblocks, w.gpart, w.g, st)) != METIS_OK) return s;
-    launch_jacobi(w.g, n, w.theta, w.z, st);
+    launch_jacobi(w.g, n, w.theta, w.z, nullptr, st);
     LAUNCH_CHECK();
     hipLaunchKernelGGL(sketch_v_kernel, dim3(grid1(cols * k, 256)), dim3(256), 0, st, w.b, cols, n, k,
                        w.z, w.theta, f->V);
@@ -864,29 +882,25 @@ metis_status decompose_project(DecompCall& c, hipStream_t st) {
 }
 
 // Rediagonalisation: eig(G) = R Lambda R^T, V <- V R, U = P R Lambda^-1/2,
-// S = Lambda^1/2 (columns signed, descending).
-metis_status decompose_rediag(DecompCall& c, hipStream_t st) {
-  metis_status s = METIS_OK;
+// S = Lambda^1/2, columns signed so that the largest-magnitude entry of each
+// V column (lowest row on ties) is positive, in descending order.  With
+// amax_u / amax_v given (zeroed words), the tensor amax of the new U and V
+// lands there, so quantising the factors needs no amax sweep of its own.
+metis_status decompose_rediag(DecompCall& c, hipStream_t st, uint32_t* amax_u = nullptr,
+                              uint32_t* amax_v = nullptr) {
   const int64_t rows = c.rows, cols = c.cols;
   const int k = c.k;
   metis_factors* f = c.f;
   DecompWs& w = c.w;
-  launch_jacobi(w.ptp, k, w.lam, w.rot, st);
+  launch_jacobi(w.ptp, k, w.lam, w.rot, w.key, st);
   LAUNCH_CHECK();
-  hipLaunchKernelGGL(apply_rot_kernel<true>, dim3((unsigned)ceil_div<int64_t>(cols, 64)), dim3(256), 0, st,
-                     f->V, cols, k, w.rot, nullptr, nullptr, w.vn);
+  if (k <= 32)
+    launch_rot<32>(w, f, rows, cols, k, amax_u, amax_v, st);
+  else if (k <= 72)
+    launch_rot<72>(w, f, rows, cols, k, amax_u, amax_v, st);
+  else
+    launch_rot<kMaxN>(w, f, rows, cols, k, amax_u, amax_v, st);
   LAUNCH_CHECK();
-  hipLaunchKernelGGL(column_sign_kernel, dim3(k), dim3(256), 0, st, w.vn, cols, k, w.sign);
-  LAUNCH_CHECK();
-  hipLaunchKernelGGL(finalize_v_kernel, dim3(grid1(cols * k, 256)), dim3(256), 0, st, w.vn, cols, k,
-                     w.sign, f->V);
-  LAUNCH_CHECK();
-  hipLaunchKernelGGL(finalize_s_kernel, dim3(1), dim3(128), 0, st, w.lam, k, f->S);
-  LAUNCH_CHECK();
-  hipLaunchKernelGGL(apply_rot_kernel<false>, dim3((unsigned)ceil_div<int64_t>(rows, 64)), dim3(256), 0, st,
-                     w.p, rows, k, w.rot, w.lam, w.sign, f->U);
-  LAUNCH_CHECK();
-  (void)s;
   return METIS_OK;
 }
 
@@ -959,7 +973,7 @@ QuantParams resid_params(const void* M, int32_t dtype, int64_t rows, int64_t col
 // their rows; out->S = f->S.
 metis_status quantize_factors(const metis_factors* f, int64_t rows, int64_t cols, const metis_config* cfg,
                               uint32_t tag, int64_t step, metis_qoperand* out, const QuantWs& w,
-                              hipStream_t st) {
+                              hipStream_t st, bool amax_ready = false) {
   const int k = f->k;
   QuantParams qp{};
   qp.sr = cfg->rounding == METIS_SR;
@@ -991,10 +1005,12 @@ metis_status quantize_factors(const metis_factors* f, int64_t rows, int64_t cols
     const int64_t pu = ceil_div<int64_t>(rows, kQT_R), pv = ceil_div<int64_t>(cols, kQT_R);
     const dim3 grid((unsigned)(pu + pv), (unsigned)ceil_div<int64_t>(k, kQT_C));
     if (pu + pv > INT32_MAX) return fail(METIS_E_UNSUPPORTED, "operand too large");
-    TimingRec* t1 = timing_begin(st, 1, rows + cols, k, METIS_AXIS0, 0);
-    hipLaunchKernelGGL(quant_amax_pair_kernel, grid, dim3(kQThreads), 0, st, fqs[0], fqs[1], (int)pu);
-    LAUNCH_CHECK();
-    timing_end(t1, st);
+    if (!amax_ready) {  // else the rediagonalisation left the amax of U and V in w.amax[1], [2]
+      TimingRec* t1 = timing_begin(st, 1, rows + cols, k, METIS_AXIS0, 0);
+      hipLaunchKernelGGL(quant_amax_pair_kernel, grid, dim3(kQThreads), 0, st, fqs[0], fqs[1], (int)pu);
+      LAUNCH_CHECK();
+      timing_end(t1, st);
+    }
     TimingRec* t2 = timing_begin(st, 2, rows + cols, k, METIS_AXIS0, 0);
     if (qp.sr)
       hipLaunchKernelGGL(quant_pair_kernel<true>, grid, dim3(kQThreads), 0, st, fqs[0], fqs[1], (int)pu);
@@ -1301,8 +1317,9 @@ metis_status metis_prepare_operand(const void* M, int32_t dtype, int64_t rows, i
       return s;
     }
   }
-  // rediagonalisation on the side stream, residual sweeps on the main stream
-  s = decompose_rediag(c, st2);
+  // rediagonalisation on the side stream (with the factors' amax into the
+  // words zeroed above), residual sweeps on the main stream
+  s = decompose_rediag(c, st2, qw.amax + 1, qw.amax + 2);
   if (s == METIS_OK) s = run_quant(qp, true, rows, cols, st);
   if (fork) {
     const metis_status sj = stream_after(st, st2, e_join);
@@ -1311,7 +1328,7 @@ metis_status metis_prepare_operand(const void* M, int32_t dtype, int64_t rows, i
     give_event(e_join);
   }
   if (s != METIS_OK) return s;
-  if ((s = quantize_factors(f, rows, cols, cfg, tag, step, out, qw, st)) != METIS_OK) return s;
+  if ((s = quantize_factors(f, rows, cols, cfg, tag, step, out, qw, st, true)) != METIS_OK) return s;
   if (c.refresh) f->refreshed_at = step;
   return METIS_OK;
 }

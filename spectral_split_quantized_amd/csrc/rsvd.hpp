@@ -504,11 +504,13 @@ __device__ __forceinline__ void jacobi_rot(double app, double aqq, double apq, d
 // A[min][max]); the eigenvector matrix is kept transposed (VT[p][i] =
 // V[i][p]) so the column updates read consecutive addresses.  After the
 // blocks, wave 0 forms the next round's rotations while the other waves
-// apply this round's to V: two barriers per round.
+// apply this round's to V: two barriers per round.  clear (n words, may be
+// null) is zeroed for the caller's next kernel.
 template <int NM>
 __global__ __launch_bounds__(1024) void jacobi_kernel(const double* __restrict__ Ain, int n,
                                                       double* __restrict__ w_out,
-                                                      double* __restrict__ Z) {
+                                                      double* __restrict__ Z,
+                                                      unsigned long long* __restrict__ clear) {
   static_assert(NM % 2 == 0 && NM <= kMaxN, "even, at most kMaxN");
   constexpr int kHalf = NM / 2;
   constexpr int kBlk = kHalf * (kHalf + 1) / 2;
@@ -523,6 +525,7 @@ __global__ __launch_bounds__(1024) void jacobi_kernel(const double* __restrict__
   const int np = (n + 1) & ~1;  // even, padded with a zero row/column
   const int half = np / 2;
   const int nblk = half * (half + 1) / 2;
+  if (clear && tid < n) clear[tid] = 0ull;
   for (int e = tid; e < np * np; e += 1024) {
     const int a = e / np, b = e % np;
     if (a <= b) A[a][b] = (a < n && b < n) ? 0.5 * (Ain[a * n + b] + Ain[b * n + a]) : 0.0;
@@ -860,34 +863,35 @@ __global__ void project_reduce_kernel(const float* __restrict__ part, int64_t sp
   out[id] = acc * scale;
 }
 
-// Out (n x k) = In R D for In binary32 (n x k), R binary64 (k x k) and a
-// column scaling D: D = I (ROT: V <- V R) or D = diag(sign_j lambda_j^-1/2,
-// 0 below the eigenvalue threshold) (U = P R Lambda^-1/2 with the column
-// signs).  binary64 accumulation.  A workgroup stages 64 rows of In and the
-// scaled R in LDS; thread item (row, 4-column group) keeps four sums.
-template <bool ROT>
-__global__ __launch_bounds__(256) void apply_rot_kernel(const float* __restrict__ In, int64_t n, int k,
-                                                        const double* __restrict__ R,
-                                                        const double* __restrict__ lam,
-                                                        const float* __restrict__ sign,
-                                                        float* __restrict__ Out) {
-  constexpr int kRs = kMaxN + 4;  // row pitch: 4-column groups stay 16-byte aligned
-  __shared__ __align__(16) double rs[kMaxN][kRs];
-  __shared__ float ins[64][kMaxN + 1];
+// Sign key of a factor entry v in row r (r < 2^31): the bits of |v| on top,
+// then the row complemented (a lower row ranks higher) and whether v < 0.
+// The largest key of a column is its largest-magnitude entry (lowest row on
+// ties), and its low bit is that entry's sign.
+__device__ __forceinline__ unsigned long long sign_key(float v, int64_t r) {
+  return ((unsigned long long)(__float_as_uint(v) & 0x7FFFFFFFu) << 32) |
+         ((unsigned long long)(0x7FFFFFFFu - (uint32_t)r) << 1) | (v < 0.0f ? 1ull : 0ull);
+}
+
+// rs[p][j] = R[p][j] for j < k (D = I) or R[p][j] sign_j / sqrt(lambda_j)
+// (0 below the eigenvalue threshold), zero from k to the end of the last
+// 4-column group; ins[rl][p] = In[r0 + rl][p] (0 past row n).
+template <int NM, bool SCALE>
+__device__ __forceinline__ void rot_stage(double (*rs)[NM + 4], float (*ins)[NM + 1], const float* __restrict__ In,
+                                          int64_t n, int64_t r0, int k, const double* __restrict__ R,
+                                          const double* __restrict__ lam, const float* sg) {
   const int tid = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.x * 64;
-  const double l0 = ROT ? 0.0 : lam[0];
+  const double l0 = SCALE ? lam[0] : 0.0;
   for (int e = tid; e < k * k; e += blockDim.x) {
     const int p = e / k, j = e - p * k;
     double v = R[e];
-    if (!ROT) {
+    if (SCALE) {
       const double lj = lam[j];
-      v = (l0 > 0.0 && lj > kEigZero * l0) ? v * (double)sign[j] / sqrt(lj) : 0.0;
+      v = (l0 > 0.0 && lj > kEigZero * l0) ? v * (double)sg[j] / sqrt(lj) : 0.0;
     }
     rs[p][j] = v;
   }
   const int kg = (k + 3) >> 2;
-  for (int e = tid; e < k * kg * 4; e += blockDim.x) {  // zero the tail of the last group
+  for (int e = tid; e < k * kg * 4; e += blockDim.x) {
     const int p = e / (kg * 4), j = e - p * kg * 4;
     if (j >= k) rs[p][j] = 0.0;
   }
@@ -896,78 +900,152 @@ __global__ __launch_bounds__(256) void apply_rot_kernel(const float* __restrict_
     const int64_t r = r0 + rl;
     ins[rl][p] = r < n ? In[r * k + p] : 0.0f;
   }
-  __syncthreads();
-  for (int item = tid; item < 64 * kg; item += blockDim.x) {
-    const int rl = item / kg, jg = item - rl * kg;
-    const int64_t r = r0 + rl;
-    if (r >= n) continue;
-    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-    for (int p = 0; p < k; ++p) {
-      const double x = (double)ins[rl][p];
-      const double2 q0 = *(const double2*)&rs[p][4 * jg];
-      const double2 q1 = *(const double2*)&rs[p][4 * jg + 2];
-      a0 += x * q0.x;
-      a1 += x * q0.y;
-      a2 += x * q1.x;
-      a3 += x * q1.y;
-    }
-    const int j = 4 * jg;
-    float* o = Out + r * k + j;
-    o[0] = (float)a0;
-    if (j + 1 < k) o[1] = (float)a1;
-    if (j + 2 < k) o[2] = (float)a2;
-    if (j + 3 < k) o[3] = (float)a3;
-  }
 }
 
-// sign[j] = -1 if the largest-magnitude entry of column j of Vn (lowest row
-// on ties) is negative, else +1.  One block per column.
-__global__ __launch_bounds__(256) void column_sign_kernel(const float* __restrict__ Vn,
-                                                          int64_t cols, int k,
-                                                          float* __restrict__ sign) {
-  __shared__ float bv[256];
-  __shared__ int64_t bi[256];
-  const int j = blockIdx.x, tid = threadIdx.x;
-  float best = -1.0f;
-  int64_t bidx = 0;
-  for (int64_t c = tid; c < cols; c += 256) {
-    const float v = fabsf(Vn[c * k + j]);
-    if (v > best) {
-      best = v;
-      bidx = c;
-    }
+// Four consecutive columns 4 jg .. 4 jg + 3 of row rl of ins . rs, binary64.
+template <int NM>
+__device__ __forceinline__ void rot_row(const double (*rs)[NM + 4], const float (*ins)[NM + 1], int rl, int jg,
+                                        int k, float (&o)[4]) {
+  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+  for (int p = 0; p < k; ++p) {
+    const double x = (double)ins[rl][p];
+    const double2 q0 = *(const double2*)&rs[p][4 * jg];
+    const double2 q1 = *(const double2*)&rs[p][4 * jg + 2];
+    a0 += x * q0.x;
+    a1 += x * q0.y;
+    a2 += x * q1.x;
+    a3 += x * q1.y;
   }
-  bv[tid] = best;
-  bi[tid] = bidx;
+  o[0] = (float)a0;
+  o[1] = (float)a1;
+  o[2] = (float)a2;
+  o[3] = (float)a3;
+}
+
+// First half of the rediagonalisation's tail: Vn = V_old R (n = cols rows of
+// binary32, R binary64 k x k, binary64 accumulation), 64 rows per workgroup.
+// Thread t keeps the column group jg = t % kg of the rows t / kg + i (256 /
+// kg), so it max-reduces one sign key per column; the workgroup's keys go to
+// key[j] (zeroed beforehand) by one atomic each.  With amax given, the
+// largest |Vn| goes there too (the factor's tensor amax: |V| = |Vn|) and a
+// non-finite entry raises the status word.
+template <int NM>
+__global__ __launch_bounds__(256) void rot_v_kernel(const float* __restrict__ Vold, int64_t n, int k,
+                                                    const double* __restrict__ R, float* __restrict__ Vn,
+                                                    unsigned long long* __restrict__ key,
+                                                    uint32_t* __restrict__ amax) {
+  __shared__ __align__(16) double rs[NM][NM + 4];
+  __shared__ float ins[64][NM + 1];
+  __shared__ unsigned long long ks[NM];
+  __shared__ uint32_t am;
+  const int tid = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  rot_stage<NM, false>(rs, ins, Vold, n, r0, k, R, nullptr, nullptr);
+  if (tid < k) ks[tid] = 0ull;
+  if (tid == 0) am = 0u;
   __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) {
-      const float v2 = bv[tid + o];
-      const int64_t i2 = bi[tid + o];
-      if (v2 > bv[tid] || (v2 == bv[tid] && i2 < bi[tid])) {
-        bv[tid] = v2;
-        bi[tid] = i2;
+  const int kg = (k + 3) >> 2;
+  const int tr = 256 / kg;
+  const int jg = tid % kg, rl0 = tid / kg;
+  unsigned long long best[4] = {0ull, 0ull, 0ull, 0ull};
+  float mx = 0.0f;
+  bool bad = false;
+  if (rl0 < tr) {
+    for (int rl = rl0; rl < 64; rl += tr) {
+      const int64_t r = r0 + rl;
+      if (r >= n) break;
+      float o[4];
+      rot_row<NM>(rs, ins, rl, jg, k, o);
+      float* out = Vn + r * k + 4 * jg;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (4 * jg + c >= k) break;
+        out[c] = o[c];
+        const unsigned long long kk = sign_key(o[c], r);
+        best[c] = kk > best[c] ? kk : best[c];
+        const float a = fabsf(o[c]);
+        bad |= !(a <= 3.402823466e38f);
+        mx = fmaxf(mx, a);
       }
     }
-    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (4 * jg + c < k) atomicMax(&ks[4 * jg + c], best[c]);
   }
-  if (tid == 0) sign[j] = Vn[bi[0] * k + j] < 0.0f ? -1.0f : 1.0f;
+  if (amax) {
+    mx = wave_max(mx);
+    if ((tid & 63) == 0) atomicMax(&am, __float_as_uint(mx));
+    if (bad) raise_status(kStatusNonFinite);
+  }
+  __syncthreads();
+  if (tid < k) atomicMax(&key[tid], ks[tid]);
+  if (amax && tid == 0) atomicMax(amax, am);
 }
 
-// V = sign * Vn; S = sqrt(lambda) (0 below the threshold); U = P (R sign) lambda^-1/2.
-__global__ void finalize_v_kernel(const float* __restrict__ Vn, int64_t cols, int k,
-                                  const float* __restrict__ sign, float* __restrict__ V) {
-  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (id >= cols * k) return;
-  V[id] = Vn[id] * sign[id % k];
+// Second half: workgroups [0, nbu) form U = P R diag(sign_j lambda_j^-1/2)
+// (64 rows each, binary64 accumulation; 0 below the eigenvalue threshold),
+// the others V = Vn diag(sign) (64 rows each); workgroup 0 also writes
+// S = sqrt(lambda) (0 below the threshold).  sign_j is the low bit of key[j].
+// With amax given, the largest |U| goes there and a non-finite U entry
+// raises the status word.
+template <int NM>
+__global__ __launch_bounds__(256) void rot_u_kernel(const float* __restrict__ P, int64_t rows, int k,
+                                                    const double* __restrict__ R, const double* __restrict__ lam,
+                                                    const unsigned long long* __restrict__ key,
+                                                    const float* __restrict__ Vn, int64_t cols,
+                                                    float* __restrict__ U, float* __restrict__ V,
+                                                    float* __restrict__ S, uint32_t* __restrict__ amax, int nbu) {
+  __shared__ __align__(16) double rs[NM][NM + 4];
+  __shared__ float ins[64][NM + 1];
+  __shared__ float sg[NM];
+  __shared__ uint32_t am;
+  const int tid = threadIdx.x;
+  if (tid < k) sg[tid] = (key[tid] & 1ull) ? -1.0f : 1.0f;
+  if (tid == 0) am = 0u;
+  if ((int)blockIdx.x >= nbu) {
+    __syncthreads();
+    const int64_t r0 = (int64_t)((int)blockIdx.x - nbu) * 64;
+    const int64_t r1 = r0 + 64 < cols ? r0 + 64 : cols;
+    const int nloc = (int)(r1 - r0) * k;
+    const float* src = Vn + r0 * k;
+    float* dst = V + r0 * k;
+    for (int e = tid; e < nloc; e += 256) dst[e] = src[e] * sg[e % k];
+    return;
+  }
+  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  if (blockIdx.x == 0 && tid < k) {
+    const double l0 = lam[0], lj = lam[tid];
+    S[tid] = (l0 > 0.0 && lj > kEigZero * l0) ? (float)sqrt(lj) : 0.0f;
+  }
+  __syncthreads();
+  rot_stage<NM, true>(rs, ins, P, rows, r0, k, R, lam, sg);
+  __syncthreads();
+  const int kg = (k + 3) >> 2;
+  float mx = 0.0f;
+  bool bad = false;
+  for (int item = tid; item < 64 * kg; item += 256) {
+    const int rl = item / kg, jg = item - rl * kg;
+    const int64_t r = r0 + rl;
+    if (r >= rows) continue;
+    float o[4];
+    rot_row<NM>(rs, ins, rl, jg, k, o);
+    float* out = U + r * k + 4 * jg;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (4 * jg + c >= k) break;
+      out[c] = o[c];
+      const float a = fabsf(o[c]);
+      bad |= !(a <= 3.402823466e38f);
+      mx = fmaxf(mx, a);
+    }
+  }
+  if (amax) {
+    mx = wave_max(mx);
+    if ((tid & 63) == 0) atomicMax(&am, __float_as_uint(mx));
+    if (bad) raise_status(kStatusNonFinite);
+    __syncthreads();
+    if (tid == 0) atomicMax(amax, am);
+  }
 }
-
-__global__ void finalize_s_kernel(const double* __restrict__ lam, int k, float* __restrict__ S) {
-  const int j = threadIdx.x;
-  if (j >= k) return;
-  const double l0 = lam[0], lj = lam[j];
-  S[j] = (l0 > 0.0 && lj > kEigZero * l0) ? (float)sqrt(lj) : 0.0f;
-}
-
 
 }  // namespace metis
