@@ -311,9 +311,11 @@ class MetisMLP:
         # a side stream overwrites a weight's quantised operand once the
         # previous step's last GEMM reading it is done: the gate projection's
         # dW for W_gate (and the down projection's dX before it for W_down),
-        # the up projection's dW for W_up.  The weights of a step are thus
-        # prepared beside the previous step's last GEMMs, as an optimizer
-        # updates each weight as soon as its gradient is ready.
+        # the up projection's dW for W_up.  A weight is also prepared only
+        # after the previous step's gradient of that weight (W_down: the down
+        # projection's dW, on the second side stream), as an optimizer
+        # updates each weight as soon as its gradient is ready; the weights of
+        # a step are thus prepared beside the previous step's last GEMMs.
         if self.free_gate is not None:
             self.streams[sw].wait_event(self.free_gate)
             self.streams[sw2].wait_event(self.free_up)
@@ -323,6 +325,8 @@ class MetisMLP:
         # on the second side stream, so that at a refresh step its sketch
         # runs beside W_gate's instead of after it)
         for w, si in (("W_gate", sw), ("W_up", sw2), ("W_down", sw)):
+            if w == "W_down" and self.free_down is not None:
+                self.streams[si].wait_event(self.free_down)
             self._prep(w, t, inputs, si, companion=False)
             ev[w] = self._event(si)
         self._prep("X_gu", t, inputs, 0)

@@ -288,12 +288,25 @@ constexpr int kThinRows = 128;  // rows per workgroup: 4 waves x 32
 
 // fragment id = ((kb * 4 + kk) * 2 + nt) * 64 + lane holds the 8 values
 // B[nt * 32 + lane % 32][kb * 64 + 32 (lane / 32) + 8 kk + i], i < 8 (zero
-// outside B)
-__global__ void thin_bfrag_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-                                  int nb, int64_t K, uint4* __restrict__ bfrag) {
-  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// outside B).  Up to two B operands over the same K per launch: the first
+// nks * 512 threads form the first, the next nks * 512 the second.
+struct ThinB {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  int nb;
+  uint4* bfrag;
+};
+
+__global__ void thin_bfrag_kernel(ThinB b0, ThinB b1, int64_t K) {
+  int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t nks = (K + 63) >> 6;
-  if (id >= nks * 512) return;
+  const bool second = id >= nks * 512;
+  if (second) id -= nks * 512;
+  if (id >= nks * 512 || (second && !b1.bfrag)) return;
+  const uint8_t* __restrict__ codes = second ? b1.codes : b0.codes;
+  const uint8_t* __restrict__ scales = second ? b1.scales : b0.scales;
+  const int nb = second ? b1.nb : b0.nb;
+  uint4* __restrict__ bfrag = second ? b1.bfrag : b0.bfrag;
   const int lane = (int)(id & 63);
   const int nt = (int)((id >> 6) & 1);
   const int kk = (int)((id >> 7) & 3);
@@ -336,20 +349,34 @@ __device__ inline void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Up to three thin products (same K) in one launch: product i owns the
+// workgroups [first[i], first[i + 1]) of a 1-D grid, as a (row block, split)
+// grid of gx[i] row blocks.
+struct ThinBatch {
+  ThinParams p[3];
+  int64_t gx[3];
+  int64_t first[4];
+};
+
 template <bool A16>
-__global__ __launch_bounds__(256) void gemm_thin_kernel(ThinParams p) {
+__global__ __launch_bounds__(256) void gemm_thin_kernel(ThinBatch tb) {
   __shared__ uint4 B0[512];
   __shared__ uint4 B1[512];
   __shared__ uint4 B2[512];
   __shared__ uint4 B3[512];
+  const int64_t blk = blockIdx.x;
+  const int which = blk < tb.first[1] ? 0 : (blk < tb.first[2] ? 1 : 2);
+  const ThinParams& p = tb.p[which];
+  const int64_t lb = blk - tb.first[which];
+  const int64_t bx = lb % tb.gx[which], by = lb / tb.gx[which];
   constexpr int OPS = ThinOps<A16>::kStep;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5;
-  const int64_t row = (int64_t)blockIdx.x * kThinRows + wave * 32 + (lane & 31);
+  const int64_t row = bx * kThinRows + wave * 32 + (lane & 31);
   const bool row_ok = row < p.M;
   const int64_t nks = (p.K + 63) >> 6;
-  const int64_t s0 = (int64_t)blockIdx.y * p.steps;
+  const int64_t s0 = by * p.steps;
   const int64_t s1 = min(nks, s0 + p.steps);
   const int64_t lrow = row_ok ? row : p.M - 1;
   const uint8_t* arow = p.a_codes + lrow * (p.K >> 1);
@@ -429,8 +456,8 @@ __global__ __launch_bounds__(256) void gemm_thin_kernel(ThinParams p) {
     compute(B3, r3);
   }
   // lane holds column lane % 32 of each n-tile and rows 8(v/4) + 4(lane/32) + v%4
-  float* out = p.part + (int64_t)blockIdx.y * p.M * 64;
-  const int64_t rbase = (int64_t)blockIdx.x * kThinRows + wave * 32 + 4 * hh;
+  float* out = p.part + by * p.M * 64;
+  const int64_t rbase = bx * kThinRows + wave * 32 + 4 * hh;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int64_t r = rbase + 8 * (v >> 2) + (v & 3);
@@ -546,9 +573,9 @@ struct ExtParams {
 // A_ext[i] = [hi(P'' s_J) | lo(..) | H_bar | H_bar | 0 ...] (P'' times the
 // epilogue's ext_mul, as G below): one thread per
 // row and 8-column chunk (rows past e.rows up to the next multiple of 32 are
-// written as zeros).
-__global__ void ext_prep_a_kernel(ExtParams e) {
-  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// written as zeros).  Workgroup bx of 256 threads.
+__device__ void ext_prep_a(const ExtParams& e, int64_t bx) {
+  const int64_t id = bx * 256 + threadIdx.x;
   const int64_t chunks = e.kext >> 3;
   const int64_t i = id / chunks;
   const int col0 = (int)(id % chunks) * 8;
@@ -589,11 +616,10 @@ __global__ void ext_prep_a_kernel(ExtParams e) {
 // 8-wide chunk groups part, part + 4, ...: J_bar chunks (written twice), G
 // chunks (hi and lo from one evaluation) and the zero tail.
 constexpr int kExtMaxK = 64;
-__global__ __launch_bounds__(256) void ext_prep_b_kernel(ExtParams e) {
-  __shared__ float jv[64][kExtMaxK + 1];         // J_bar[j0 + c][p]
-  __shared__ float t2f[kExtMaxK][kExtMaxK + 1];  // s_F s_E T2[q][p] S_R[p] s_J
+__device__ void ext_prep_b(const ExtParams& e, int64_t bx, float (*jv)[kExtMaxK + 1],
+                           float (*t2f)[kExtMaxK + 1]) {
   const int tid = threadIdx.x;
-  const int64_t j0 = (int64_t)blockIdx.x * 64;
+  const int64_t j0 = bx * 64;
   const float sJ = e.J.ts[0];
   const float sFE = e.s_F[0] * e.s_E[0];
   const float sFR = e.s_F[0] * e.s_RR[0];
@@ -649,6 +675,18 @@ __global__ __launch_bounds__(256) void ext_prep_b_kernel(ExtParams e) {
   }
   for (int64_t c0 = 2 * e.ksR + 2 * e.ksL + 8 * part; c0 < e.kext; c0 += 32)
     *(uint4*)(out + ext_off(j, c0, e.kext)) = zero;
+}
+
+// Both operands of the K-extension in one launch: workgroups [0, nba) form
+// A_ext (256 rows-and-chunks each), the rest B_ext (64 columns each).
+__global__ __launch_bounds__(256) void ext_prep_kernel(ExtParams e, int64_t nba) {
+  __shared__ float jv[64][kExtMaxK + 1];         // J_bar[j0 + c][p]
+  __shared__ float t2f[kExtMaxK][kExtMaxK + 1];  // s_F s_E T2[q][p] S_R[p] s_J
+  const int64_t blk = blockIdx.x;
+  if (blk < nba)
+    ext_prep_a(e, blk);
+  else
+    ext_prep_b(e, blk - nba, jv, t2f);
 }
 
 }  // namespace metis

@@ -367,9 +367,7 @@ constexpr int64_t kAmaxWords = (int64_t)kAmaxSlotStride * (1 + kAmaxSlots);
 
 struct QuantWs {
   uint32_t* amax;  // words 0..2: residual, U, V; from word kAmaxSlotStride: the residual's slots
-  float* pre;
   float* pscale;
-  float* ones;     // kMaxN ones (S of a residual formed from the projection)
   _Float16* ucat;
   _Float16* vcat;
 };
@@ -377,9 +375,7 @@ struct QuantWs {
 QuantWs carve_quantize(Carver& cv, int64_t rows, int64_t cols, int k) {
   QuantWs w{};
   w.amax = cv.take<uint32_t>(kAmaxWords);
-  w.pre = cv.take<float>(1);
   w.pscale = cv.take<float>(1);
-  w.ones = cv.take<float>(kMaxN);
   if (k > 0) {
     const int kc = 3 * round_up(k, 16);
     w.ucat = cv.take<_Float16>((size_t)((rows + 31) & ~(int64_t)31) * kc);
@@ -607,83 +603,82 @@ SplitWs carve_split(Carver& cv, int64_t M, int64_t N, int64_t K, int kL, int kR)
   return w;
 }
 
-// Thin product part[s][m][64] = A (m x K) B^T, B = the nb <= 64 rows in bfrag.
-metis_status thin_product(const metis_q4& A, int64_t m, int64_t K, const uint4* bfrag, int splits,
-                          float* part, hipStream_t st) {
-  ThinParams tp{A.codes, A.scales, bfrag, m, K, 0, part};
-  const int64_t nks = ceil_div<int64_t>(K, 64);
-  tp.steps = ceil_div<int64_t>(nks, splits);
-  const dim3 grid((unsigned)ceil_div<int64_t>(m, kThinRows), (unsigned)splits);
-  if (K % 32 == 0) hipLaunchKernelGGL(gemm_thin_kernel<true>, grid, dim3(256), 0, st, tp);
-  else hipLaunchKernelGGL(gemm_thin_kernel<false>, grid, dim3(256), 0, st, tp);
-  LAUNCH_CHECK();
-  return METIS_OK;
-}
-
-metis_status thin_operand(const metis_q4& B, int nb, int64_t K, uint4* bfrag, hipStream_t st) {
-  const int64_t n = ceil_div<int64_t>(K, 64) * 512;
-  hipLaunchKernelGGL(thin_bfrag_kernel, dim3(grid1(n, 256)), dim3(256), 0, st, B.codes, B.scales, nb, K, bfrag);
-  LAUNCH_CHECK();
-  return METIS_OK;
-}
-
 // The K-extension of a split product: P_raw = L_R E, T1^T = R_R F^T and
-// T2 = F E on the thin-product kernel, then the bf16 hi/lo operands
-// a_ext / b_ext of the extra K columns (with S, Lambda and the tensor scales
-// folded in).
+// T2 = F E on the thin-product kernel (the three in one launch, after one
+// launch that dequantises E and F into MFMA fragments), then the bf16 hi/lo
+// operands a_ext / b_ext of the extra K columns (with S, Lambda and the
+// tensor scales folded in), both in one launch.
 metis_status split_ext(const SideQ& L, const SideQ& R, int64_t M, int64_t N, int64_t K, const SplitWs& w,
                        hipStream_t st) {
-  hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, st, (uint32_t*)w.ones, 0x3F800000u,
-                     (int64_t)4);
-  LAUNCH_CHECK();
-  metis_status s;
-  if (R.k > 0) {  // P_raw = L_R . E   (M x kR)
-    if ((s = thin_operand(*R.kf, R.k, K, w.bf_E, st)) != METIS_OK) return s;
-    if ((s = thin_product(*L.res, M, K, w.bf_E, w.sa, w.pa, st)) != METIS_OK) return s;
+  if (L.k == 0 && R.k == 0) return METIS_OK;
+  if (L.k == 0 || R.k == 0) {  // the ones stand in for the scales of the side without factors
+    hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(64), 0, st, (uint32_t*)w.ones, 0x3F800000u,
+                       (int64_t)4);
+    LAUNCH_CHECK();
   }
-  if (L.k > 0) {  // T1^T = R_R . F^T   (N x kL)
-    if ((s = thin_operand(*L.kf, L.k, K, w.bf_F, st)) != METIS_OK) return s;
-    if ((s = thin_product(*R.res, N, K, w.bf_F, w.s1, w.p1, st)) != METIS_OK) return s;
+  const int64_t nks = ceil_div<int64_t>(K, 64);
+  {  // fragments of E (R's factor) and F (L's factor)
+    ThinB b[2] = {};
+    int nbf = 0;
+    if (R.k > 0) b[nbf++] = ThinB{R.kf->codes, R.kf->scales, R.k, w.bf_E};
+    if (L.k > 0) b[nbf++] = ThinB{L.kf->codes, L.kf->scales, L.k, w.bf_F};
+    hipLaunchKernelGGL(thin_bfrag_kernel, dim3(grid1(nks * 512 * nbf, 256)), dim3(256), 0, st, b[0], b[1], K);
+    LAUNCH_CHECK();
   }
-  if (L.k > 0 && R.k > 0) {  // T2 = F . E   (kL x kR)
-    if ((s = thin_product(*L.kf, L.k, K, w.bf_E, w.s2, w.p2, st)) != METIS_OK) return s;
+  {  // P_raw = L_R E (M x kR), T1^T = R_R F^T (N x kL), T2 = F E (kL x kR)
+    ThinBatch tb{};
+    int n = 0;
+    auto add = [&](const metis_q4& A, int64_t m, const uint4* bfrag, int splits, float* part) {
+      tb.p[n] = ThinParams{A.codes, A.scales, bfrag, m, K, ceil_div<int64_t>(nks, splits), part};
+      tb.gx[n] = ceil_div<int64_t>(m, kThinRows);
+      tb.first[n + 1] = tb.first[n] + tb.gx[n] * splits;
+      ++n;
+    };
+    if (R.k > 0) add(*L.res, M, w.bf_E, w.sa, w.pa);
+    if (L.k > 0) add(*R.res, N, w.bf_F, w.s1, w.p1);
+    if (L.k > 0 && R.k > 0) add(*L.kf, L.k, w.bf_E, w.s2, w.p2);
+    for (int i = n; i < 3; ++i) tb.first[i + 1] = tb.first[i];
+    if (tb.first[3] > INT32_MAX) return fail(METIS_E_UNSUPPORTED, "thin products too large");
+    if (K % 32 == 0) hipLaunchKernelGGL(gemm_thin_kernel<true>, dim3((unsigned)tb.first[3]), dim3(256), 0, st, tb);
+    else hipLaunchKernelGGL(gemm_thin_kernel<false>, dim3((unsigned)tb.first[3]), dim3(256), 0, st, tb);
+    LAUNCH_CHECK();
+  }
+  if (L.k > 0 && R.k > 0) {  // T2 summed over its splits
     const int64_t n2 = (int64_t)L.k * 64;
     hipLaunchKernelGGL(sum_parts_kernel, dim3(grid1(n2 / 8, 256)), dim3(256), 0, st, w.p2, w.s2, n2, w.t2);
     LAUNCH_CHECK();
   }
-  if (L.k > 0 || R.k > 0) {
-    const int64_t kext = w.kext;
-    ExtParams e{};
-    e.rows = M;
-    e.cols = N;
-    e.kR = R.k;
-    e.kL = L.k;
-    e.ksR = w.ksR;
-    e.ksL = w.ksL;
-    e.kext = kext;
-    e.praw = w.pa;
-    e.t1 = w.p1;
-    e.t2 = w.t2;
-    e.sa = w.sa;
-    e.s1 = w.s1;
-    e.S_R = R.k > 0 ? R.S : w.ones;
-    e.S_L = L.k > 0 ? L.S : w.ones;
-    e.s_LR = L.res->tensor_scale;
-    e.s_RR = R.res->tensor_scale;
-    e.s_E = R.k > 0 ? R.kf->tensor_scale : w.ones;
-    e.s_F = L.k > 0 ? L.kf->tensor_scale : w.ones;
-    e.H = SplitSide{L.k > 0 ? L.out->codes : nullptr, L.k > 0 ? L.out->scales : nullptr,
-                    L.k > 0 ? L.out->tensor_scale : w.ones, L.k, M};
-    e.J = SplitSide{R.k > 0 ? R.out->codes : nullptr, R.k > 0 ? R.out->scales : nullptr,
-                    R.k > 0 ? R.out->tensor_scale : w.ones, R.k, N};
-    e.a_ext = w.a_ext;
-    e.b_ext = w.b_ext;
-    hipLaunchKernelGGL(ext_prep_a_kernel, dim3(grid1(round_up64(M, 32) * (kext / 8), 256)), dim3(256), 0, st, e);
-    LAUNCH_CHECK();
-    hipLaunchKernelGGL(ext_prep_b_kernel, dim3((unsigned)ceil_div<int64_t>(round_up64(N, 32), 64)), dim3(256), 0,
-                       st, e);
-    LAUNCH_CHECK();
-  }
+  const int64_t kext = w.kext;
+  ExtParams e{};
+  e.rows = M;
+  e.cols = N;
+  e.kR = R.k;
+  e.kL = L.k;
+  e.ksR = w.ksR;
+  e.ksL = w.ksL;
+  e.kext = kext;
+  e.praw = w.pa;
+  e.t1 = w.p1;
+  e.t2 = w.t2;
+  e.sa = w.sa;
+  e.s1 = w.s1;
+  e.S_R = R.k > 0 ? R.S : w.ones;
+  e.S_L = L.k > 0 ? L.S : w.ones;
+  e.s_LR = L.res->tensor_scale;
+  e.s_RR = R.res->tensor_scale;
+  e.s_E = R.k > 0 ? R.kf->tensor_scale : w.ones;
+  e.s_F = L.k > 0 ? L.kf->tensor_scale : w.ones;
+  e.H = SplitSide{L.k > 0 ? L.out->codes : nullptr, L.k > 0 ? L.out->scales : nullptr,
+                  L.k > 0 ? L.out->tensor_scale : w.ones, L.k, M};
+  e.J = SplitSide{R.k > 0 ? R.out->codes : nullptr, R.k > 0 ? R.out->scales : nullptr,
+                  R.k > 0 ? R.out->tensor_scale : w.ones, R.k, N};
+  e.a_ext = w.a_ext;
+  e.b_ext = w.b_ext;
+  const int64_t nba = grid1(round_up64(M, 32) * (kext / 8), 256);
+  const int64_t nbb = ceil_div<int64_t>(round_up64(N, 32), 64);
+  if (nba + nbb > INT32_MAX) return fail(METIS_E_UNSUPPORTED, "K-extension too large");
+  hipLaunchKernelGGL(ext_prep_kernel, dim3((unsigned)(nba + nbb)), dim3(256), 0, st, e, nba);
+  LAUNCH_CHECK();
   return METIS_OK;
 }
 
@@ -1189,16 +1184,17 @@ metis_status quantize_body(const void* M, int32_t dtype, int64_t rows, int64_t c
                            hipStream_t st) {
   metis_status s;
   const int k = f ? f->k : 0;
-  hipLaunchKernelGGL(fill_u32_kernel, dim3(grid1(kAmaxWords, 256)), dim3(256), 0, st, w.amax, 0u, kAmaxWords);
-  LAUNCH_CHECK();
   QuantParams qp = resid_params(M, dtype, rows, cols, ld, cfg, tag, step, axes, out, residual_out, w);
-  if (f) {
-    const int kp = round_up(k, 16);
-    hipLaunchKernelGGL(resid_scale_kernel, dim3(1), dim3(64), 0, st, f->S, k, w.pre, w.pscale);
+  if (!f) {
+    hipLaunchKernelGGL(fill_u32_kernel, dim3(grid1(kAmaxWords, 256)), dim3(256), 0, st, w.amax, 0u, kAmaxWords);
     LAUNCH_CHECK();
-    const int64_t rc_pad = ((rows + 31) & ~(int64_t)31) + ((cols + 63) & ~(int64_t)63);
-    hipLaunchKernelGGL(resid_prep_kernel, dim3(grid1(rc_pad * kp, 256)), dim3(256), 0, st, f->U,
-                       f->S, f->V, rows, cols, k, kp, w.pre, w.ucat, w.vcat);
+  } else {
+    // fragments of U S and V, pre-scale from S[0], amax words cleared
+    const int kp = round_up(k, 16);
+    const ResidPrep rp{f->U, f->S, f->V, nullptr, rows, cols, k, kp, w.pscale, w.ucat, w.vcat, w.amax,
+                       (int)kAmaxWords};
+    hipLaunchKernelGGL(resid_prep_kernel, dim3(grid1(resid_prep_threads(rows, cols, kp), 256)), dim3(256), 0, st,
+                       rp);
     LAUNCH_CHECK();
     qp.ucat = w.ucat;
     qp.vcat = w.vcat;
@@ -1286,17 +1282,12 @@ metis_status metis_prepare_operand(const void* M, int32_t dtype, int64_t rows, i
   // P = M V_old and G = P^T P (the sketch first on refresh steps)
   if ((s = decompose_project(c, st)) != METIS_OK) return s;
   // the residual's rank-k product from P and V_old, before V is rotated
-  hipLaunchKernelGGL(fill_u32_kernel, dim3(grid1(kAmaxWords, 256)), dim3(256), 0, st, qw.amax, 0u, kAmaxWords);
-  LAUNCH_CHECK();
-  hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(128), 0, st, (uint32_t*)qw.ones, 0x3F800000u,
-                     (int64_t)kMaxN);
-  LAUNCH_CHECK();
-  hipLaunchKernelGGL(resid_scale_gram_kernel, dim3(1), dim3(64), 0, st, c.w.ptp, k, qw.pre, qw.pscale);
-  LAUNCH_CHECK();
+  // (pre-scale from the Gram diagonal), with the amax words cleared
   const int kp = round_up(k, 16);
-  const int64_t rc_pad = ((rows + 31) & ~(int64_t)31) + ((cols + 63) & ~(int64_t)63);
-  hipLaunchKernelGGL(resid_prep_kernel, dim3(grid1(rc_pad * kp, 256)), dim3(256), 0, st, c.w.p, qw.ones,
-                     f->V, rows, cols, k, kp, qw.pre, qw.ucat, qw.vcat);
+  const ResidPrep rp{c.w.p, nullptr, f->V, c.w.ptp, rows, cols, k, kp, qw.pscale, qw.ucat, qw.vcat, qw.amax,
+                     (int)kAmaxWords};
+  hipLaunchKernelGGL(resid_prep_kernel, dim3(grid1(resid_prep_threads(rows, cols, kp), 256)), dim3(256), 0, st,
+                     rp);
   LAUNCH_CHECK();
   QuantParams qp = resid_params(M, dtype, rows, cols, ld, cfg, tag, step, axes, out, residual_out, qw);
   qp.ucat = qw.ucat;

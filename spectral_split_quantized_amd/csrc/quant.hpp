@@ -48,67 +48,100 @@ constexpr int kQMaxKK = 12;  // K of the rank-k product / 16 (k <= 64)
 // so one wave's fragment load is 1 KB of contiguous memory.
 constexpr float kVPre = 256.0f;
 
-__global__ void resid_scale_kernel(const float* __restrict__ S, int k, float* __restrict__ pre_out,
-                                   float* __restrict__ pscale_out) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  const float s0 = k > 0 ? S[0] : 0.0f;
-  int ex = 0;
-  if (s0 > 0.0f) frexpf(s0, &ex);  // s0 < 2^ex
-  const float pre = ldexpf(1.0f, 14 - ex);
-  pre_out[0] = pre;
-  pscale_out[0] = ldexpf(1.0f, ex - 14 - 8);  // 1 / (pre * kVPre)
-}
-
-// pre / pscale when the rank-k product is formed as P V^T from the
-// projection P = M V (equal to U S V^T after the rediagonalisation, whose
-// rotation is orthogonal): every |P_ij| <= sqrt(G_jj) with G = P^T P, so the
-// largest Gram diagonal entry bounds P as S[0] bounds U S.
-__global__ void resid_scale_gram_kernel(const double* __restrict__ G, int k, float* __restrict__ pre_out,
-                                        float* __restrict__ pscale_out) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  double g = 0.0;
-  for (int j = 0; j < k; ++j) g = fmax(g, G[j * k + j]);
-  const float s0 = (float)sqrt(g);
-  int ex = 0;
-  if (s0 > 0.0f) frexpf(s0, &ex);  // s0 < 2^ex
-  pre_out[0] = ldexpf(1.0f, 14 - ex);
-  pscale_out[0] = ldexpf(1.0f, ex - 14 - 8);  // 1 / (pre * kVPre)
-}
+// Everything the residual sweeps read besides M, in one launch:
+//  - pre and pscale: pre is the power of two that puts the largest entry of
+//    the row operand U S below 2^14.  Its bound is S[0] for given factors, or
+//    sqrt of the largest Gram diagonal entry when the row operand is the
+//    projection P = M V (equal to U S up to the rediagonalisation's
+//    orthogonal rotation, and |P_ij| <= sqrt(G_jj)).  pscale = 1 / (pre kVPre)
+//    goes to memory for the sweeps; every workgroup forms pre itself.
+//  - the ucat and vcat fragments: one thread per padded row and 8-wide group
+//    of the k index writes whole 16-byte fragment pieces, 32 threads (32
+//    consecutive rows) one contiguous 512-byte run;
+//  - nzero words at zero cleared (the sweeps' amax words), by workgroup 0.
+struct ResidPrep {
+  const float* U;   // rows x k
+  const float* S;   // k (null: S = 1, the row operand is P)
+  const float* V;   // cols x k
+  const double* G;  // k x k Gram matrix of P (null: bound from S[0])
+  int64_t rows, cols;
+  int k, kp;
+  float* pscale;
+  _Float16* ucat;
+  _Float16* vcat;
+  uint32_t* zero;
+  int nzero;
+};
 
 __device__ inline int64_t frag_off(int64_t row, int kidx, int kc) {
   const int lane = ((kidx & 15) >> 3) * 32 + (int)(row & 31);
   return (((row >> 5) * (kc >> 4) + (kidx >> 4)) * 64 + lane) * 8 + (kidx & 7);
 }
 
-// one thread per (padded row, j < kp) of ucat and of vcat
-__global__ void resid_prep_kernel(const float* __restrict__ U, const float* __restrict__ S,
-                                  const float* __restrict__ V, int64_t rows, int64_t cols, int k,
-                                  int kp, const float* __restrict__ pre_p, _Float16* __restrict__ ucat,
-                                  _Float16* __restrict__ vcat) {
-  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t rows_p = (rows + 31) & ~(int64_t)31, cols_p = (cols + 63) & ~(int64_t)63;
-  const int64_t total = (rows_p + cols_p) * kp;
-  if (id >= total) return;
-  const int64_t r = id / kp;
-  const int j = (int)(id % kp);
-  const int kc = 3 * kp;
-  if (r < rows_p) {
-    float x = 0.0f;
-    if (j < k && r < rows) x = __fmul_rn(__fmul_rn(U[r * k + j], S[j]), pre_p[0]);
-    const _Float16 h = (_Float16)x;
-    const _Float16 l = (_Float16)__fsub_rn(x, (float)h);
-    ucat[frag_off(r, j, kc)] = h;
-    ucat[frag_off(r, kp + j, kc)] = h;
-    ucat[frag_off(r, 2 * kp + j, kc)] = l;
+inline int64_t resid_prep_threads(int64_t rows, int64_t cols, int kp) {
+  return (((rows + 31) & ~(int64_t)31) + ((cols + 63) & ~(int64_t)63)) * (kp / 8);
+}
+
+__global__ __launch_bounds__(256) void resid_prep_kernel(ResidPrep p) {
+  __shared__ float pre_s;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    // max_j (float) sqrt(G_jj) = (float) sqrt(max_j G_jj): both are monotone
+    float s0 = 0.0f;
+    if (p.G) {
+      for (int j = tid; j < p.k; j += 64) s0 = fmaxf(s0, (float)sqrt(p.G[(int64_t)j * p.k + j]));
+      s0 = wave_max(s0);
+    } else {
+      s0 = p.k > 0 ? p.S[0] : 0.0f;
+    }
+    if (tid == 0) {
+      int ex = 0;
+      if (s0 > 0.0f) frexpf(s0, &ex);  // s0 < 2^ex
+      pre_s = ldexpf(1.0f, 14 - ex);
+      if (blockIdx.x == 0) p.pscale[0] = ldexpf(1.0f, ex - 14 - 8);  // 1 / (pre * kVPre)
+    }
+  }
+  if (blockIdx.x == 0)
+    for (int i = tid; i < p.nzero; i += 256) p.zero[i] = 0u;
+  __syncthreads();
+  const int ng = p.kp >> 3, kc = 3 * p.kp;
+  const int64_t per_rb = 32 * (int64_t)ng;  // threads per 32 padded rows
+  const int64_t nu = ((p.rows + 31) >> 5) * per_rb;
+  const int64_t nv = ((p.cols + 63) >> 6) * 2 * per_rb;
+  const int64_t id = (int64_t)blockIdx.x * 256 + tid;
+  if (id >= nu + nv) return;
+  const bool is_u = id < nu;
+  const int64_t lid = is_u ? id : id - nu;
+  const int64_t rb = lid / per_rb;
+  const int rem = (int)(lid - rb * per_rb);
+  const int j0 = 8 * (rem >> 5);
+  const int64_t r = rb * 32 + (rem & 31);
+  half8_t h, l;
+  if (is_u) {
+    const float pre = pre_s;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int j = j0 + t;
+      float x = 0.0f;
+      if (j < p.k && r < p.rows) x = __fmul_rn(__fmul_rn(p.U[r * p.k + j], p.S ? p.S[j] : 1.0f), pre);
+      h[t] = (_Float16)x;
+      l[t] = (_Float16)__fsub_rn(x, (float)h[t]);
+    }
+    *(half8_t*)(p.ucat + frag_off(r, j0, kc)) = h;
+    *(half8_t*)(p.ucat + frag_off(r, p.kp + j0, kc)) = h;
+    *(half8_t*)(p.ucat + frag_off(r, 2 * p.kp + j0, kc)) = l;
   } else {
-    const int64_t c = r - rows_p;
-    float v = 0.0f;
-    if (j < k && c < cols) v = __fmul_rn(V[c * k + j], kVPre);
-    const _Float16 h = (_Float16)v;
-    const _Float16 l = (_Float16)__fsub_rn(v, (float)h);
-    vcat[frag_off(c, j, kc)] = h;
-    vcat[frag_off(c, kp + j, kc)] = l;
-    vcat[frag_off(c, 2 * kp + j, kc)] = h;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int j = j0 + t;
+      float v = 0.0f;
+      if (j < p.k && r < p.cols) v = __fmul_rn(p.V[r * p.k + j], kVPre);
+      h[t] = (_Float16)v;
+      l[t] = (_Float16)__fsub_rn(v, (float)h[t]);
+    }
+    *(half8_t*)(p.vcat + frag_off(r, j0, kc)) = h;
+    *(half8_t*)(p.vcat + frag_off(r, p.kp + j0, kc)) = l;
+    *(half8_t*)(p.vcat + frag_off(r, 2 * p.kp + j0, kc)) = h;
   }
 }
 
