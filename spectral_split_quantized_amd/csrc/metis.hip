@@ -210,15 +210,23 @@ struct DecompWs {
   int64_t rows_per_gblock, rows_per_slice;
 };
 
+// Compute units of the target (MI355X: 8 XCDs of 32).  Launch plans that
+// size a grid to one round of resident workgroups use it; on another chip
+// they stay correct, only less even.
+constexpr int64_t kCUs = 256;
+
 // Split-K plan of an MFMA product with nr output rows over nkb 64-wide K
-// blocks: about 1024 workgroups of 128 rows; returns the split count.
-int64_t split_plan(int64_t nr, int64_t nkb, int64_t* kbps) {
+// blocks, for workgroups of 128 rows: with `wave` > 0, at most that many
+// workgroups when the rows alone do not fill them (one full round of
+// resident workgroups, so no second, mostly idle round); else about 1024.
+// Returns the split count.
+int64_t split_plan(int64_t nr, int64_t nkb, int64_t* kbps, int64_t wave = 0) {
   if (nkb <= 0 || nr <= 0) {  // no K blocks (cols < 64): the MFMA product is not used
     *kbps = 0;
     return 0;
   }
   const int64_t row_blocks = (nr + 127) / 128;
-  int64_t splits = (1024 + row_blocks - 1) / row_blocks;
+  int64_t splits = wave > 0 ? wave / row_blocks : (1024 + row_blocks - 1) / row_blocks;
   if (splits > nkb) splits = nkb;
   if (splits < 1) splits = 1;
   *kbps = (nkb + splits - 1) / splits;
@@ -295,7 +303,8 @@ DecompWs carve_decompose(Carver& cv, int64_t rows, int64_t cols, int k, int n, i
   // MFMA products (bf16 operands, cols % 64 == 0): split-K plans for the
   // projection P = M V (rows x k) and the sketch Y = M_s Omega (lr x n)
   w.proj_nkb = cols / 64;
-  w.proj_splits = split_plan(rows, w.proj_nkb, &w.proj_kbps);
+  // the projection kernel keeps 3 workgroups per CU (48 KB of LDS each)
+  w.proj_splits = split_plan(rows, w.proj_nkb, &w.proj_kbps, 3 * kCUs);
   w.sk_splits = split_plan(lr, w.proj_nkb, &w.sk_kbps);
   w.vfrag = cv.take<uint16_t>((size_t)w.proj_nkb * proj_frag_u4<3, 3>() * 8);
   w.ofrag = cv.take<uint16_t>((size_t)w.proj_nkb * proj_frag_u4<1, 3>() * 8);
