@@ -57,8 +57,8 @@ GEMM_SOURCES = ("common.hpp", "gemm_common.hpp", "gemm_reg.hpp", "gemm_launch.hp
 # the same for both quantiser sweeps of one 16384 x 14336 residual (k = 61,
 # SR, both orientations): FETCH_SIZE + WRITE_SIZE of the amax and quantise
 # dispatches, scaled alike, per call
-QUANT_TRAFFIC_BYTES = 1372665947
-QUANT_TRAFFIC_SHA = "ea76dad5668b2bf6"
+QUANT_TRAFFIC_BYTES = 1370589209
+QUANT_TRAFFIC_SHA = "15dba22dd793e833"
 QUANT_SOURCES = ("common.hpp", "quant.hpp", "quant_fast.hpp")
 
 
