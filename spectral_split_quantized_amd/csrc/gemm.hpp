@@ -573,13 +573,11 @@ struct ExtParams {
 // A_ext[i] = [hi(P'' s_J) | lo(..) | H_bar | H_bar | 0 ...] (P'' times the
 // epilogue's ext_mul, as G below): one thread per
 // row and 8-column chunk (rows past e.rows up to the next multiple of 32 are
-// written as zeros).  Workgroup bx of 256 threads.
-__device__ void ext_prep_a(const ExtParams& e, int64_t bx) {
-  const int64_t id = bx * 256 + threadIdx.x;
+// written as zeros).  Item id of the rows x chunks grid.
+__device__ void ext_prep_a_item(const ExtParams& e, int64_t id) {
   const int64_t chunks = e.kext >> 3;
   const int64_t i = id / chunks;
   const int col0 = (int)(id % chunks) * 8;
-  if (i >= ((e.rows + 31) & ~(int64_t)31)) return;
   float v[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
   uint4 out = make_uint4(0, 0, 0, 0);
   if (i < e.rows && col0 < 2 * e.ksR) {
@@ -607,6 +605,14 @@ __device__ void ext_prep_a(const ExtParams& e, int64_t bx) {
     out = pack8_bf16(v);
   }
   *(uint4*)(e.a_ext + ext_off(i, col0, e.kext)) = out;
+}
+
+// Workgroup bx of nba walks the items bx * 256 + tid, + 256 nba, ...: the
+// launch's static LDS (for the B side) limits how many workgroups a CU
+// holds, so A_ext is formed by a few workgroups that loop.
+__device__ void ext_prep_a(const ExtParams& e, int64_t bx, int64_t nba) {
+  const int64_t total = ((e.rows + 31) & ~(int64_t)31) * (e.kext >> 3);
+  for (int64_t id = bx * 256 + threadIdx.x; id < total; id += nba * 256) ext_prep_a_item(e, id);
 }
 
 // B_ext[j] = [J_bar | J_bar | hi(s_H G) | lo(..) | 0 ...]: one workgroup per
@@ -678,13 +684,13 @@ __device__ void ext_prep_b(const ExtParams& e, int64_t bx, float (*jv)[kExtMaxK 
 }
 
 // Both operands of the K-extension in one launch: workgroups [0, nba) form
-// A_ext (256 rows-and-chunks each), the rest B_ext (64 columns each).
+// A_ext, the rest B_ext (64 columns each).
 __global__ __launch_bounds__(256) void ext_prep_kernel(ExtParams e, int64_t nba) {
   __shared__ float jv[64][kExtMaxK + 1];         // J_bar[j0 + c][p]
   __shared__ float t2f[kExtMaxK][kExtMaxK + 1];  // s_F s_E T2[q][p] S_R[p] s_J
   const int64_t blk = blockIdx.x;
   if (blk < nba)
-    ext_prep_a(e, blk);
+    ext_prep_a(e, blk, nba);
   else
     ext_prep_b(e, blk - nba, jv, t2f);
 }

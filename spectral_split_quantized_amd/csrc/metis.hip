@@ -239,7 +239,7 @@ template <int NTERM, int NSUB>
 metis_status mfma_product_n(const uint16_t* A, int64_t ld, int64_t nr, const int32_t* idx,
                             const float* B, int64_t K, int width, int64_t ldb, int64_t nkb,
                             int64_t kbps, int64_t splits, float scale, uint16_t* frag, float* part,
-                            float* out, hipStream_t st) {
+                            float* out, hipStream_t st, bool reduce) {
   hipLaunchKernelGGL((proj_prep_kernel<NTERM, NSUB>), dim3(grid1(nkb * NSUB * 2048, 256)), dim3(256), 0,
                      st, B, K, width, ldb, nkb, frag);
   LAUNCH_CHECK();
@@ -247,24 +247,30 @@ metis_status mfma_product_n(const uint16_t* A, int64_t ld, int64_t nr, const int
                      dim3((unsigned)ceil_div<int64_t>(nr, 128), (unsigned)splits), dim3(256), 0, st, A, ld,
                      nr, idx, frag, nkb, kbps, part);
   LAUNCH_CHECK();
-  hipLaunchKernelGGL(project_reduce_kernel, dim3(grid1(nr * width, 256)), dim3(256), 0, st, part, splits,
-                     nr, NSUB * 32, width, scale, out);
-  LAUNCH_CHECK();
+  if (reduce) {
+    hipLaunchKernelGGL(project_reduce_kernel, dim3(grid1(nr * width, 256)), dim3(256), 0, st, part, splits,
+                       nr, NSUB * 32, width, scale, out);
+    LAUNCH_CHECK();
+  }
   return METIS_OK;
 }
+
+// Row pitch of the split partials of mfma_product for an output width.
+inline int mfma_part_pitch(int width) { return width <= 32 ? 32 : (width <= 64 ? 64 : 96); }
 
 template <int NTERM>
 metis_status mfma_product(const uint16_t* A, int64_t ld, int64_t nr, const int32_t* idx, const float* B,
                           int64_t K, int width, int64_t ldb, int64_t nkb, int64_t kbps, int64_t splits,
-                          float scale, uint16_t* frag, float* part, float* out, hipStream_t st) {
+                          float scale, uint16_t* frag, float* part, float* out, hipStream_t st,
+                          bool reduce = true) {
   if (width <= 32)
     return mfma_product_n<NTERM, 1>(A, ld, nr, idx, B, K, width, ldb, nkb, kbps, splits, scale, frag,
-                                    part, out, st);
+                                    part, out, st, reduce);
   if (width <= 64)
     return mfma_product_n<NTERM, 2>(A, ld, nr, idx, B, K, width, ldb, nkb, kbps, splits, scale, frag,
-                                    part, out, st);
+                                    part, out, st, reduce);
   return mfma_product_n<NTERM, 3>(A, ld, nr, idx, B, K, width, ldb, nkb, kbps, splits, scale, frag, part,
-                                  out, st);
+                                  out, st, reduce);
 }
 
 DecompWs carve_decompose(Carver& cv, int64_t rows, int64_t cols, int k, int n, int64_t lr,
@@ -283,7 +289,8 @@ DecompWs carve_decompose(Carver& cv, int64_t rows, int64_t cols, int k, int n, i
   w.q = cv.take<float>(lr * n);
   const int64_t gmax = rows > lr ? rows : lr;
   const int64_t gsrc = gmax > cols ? gmax : cols;
-  w.gblocks = (int)((gsrc + 255) / 256 < 512 ? (gsrc + 255) / 256 : 512);
+  // Gram partials: a workgroup per 64 rows, at most 512
+  w.gblocks = (int)((gsrc + 63) / 64 < 512 ? (gsrc + 63) / 64 : 512);
   if (w.gblocks < 1) w.gblocks = 1;
   w.gpart = cv.take<double>((size_t)w.gblocks * kMaxN * kMaxN);
   w.g = cv.take<double>(kMaxN * kMaxN);
@@ -352,8 +359,32 @@ metis_status launch_gram(const float* X, int64_t nr, int n, int64_t rs, int64_t 
     default: hipLaunchKernelGGL(gram_partial_kernel<6>, grid, dim3(256), 0, st, X, nr, n, rs, cs, per, part); break;
   }
   LAUNCH_CHECK();
-  hipLaunchKernelGGL(reduce_gram_kernel, dim3(grid1(n * n, 256)), dim3(256), 0, st, part,
+  hipLaunchKernelGGL(reduce_gram_kernel, dim3(grid1(n * n, 64)), dim3(256), 0, st, part,
                      blocks > 0 ? blocks : 1, n * n, G);
+  LAUNCH_CHECK();
+  return METIS_OK;
+}
+
+// P (nr x n) from the split partials of an MFMA product (pitch pw) and G =
+// P^T P, with the row blocks of launch_gram: the same bits as the split
+// reduction followed by launch_gram on P.
+metis_status launch_gram_from_parts(const float* part, int64_t splits, int pw, float scale, float* P, int64_t nr,
+                                    int n, int maxblocks, double* gpart, double* G, hipStream_t st) {
+  int64_t per = (nr + maxblocks - 1) / maxblocks;
+  per = (per + 31) / 32 * 32;
+  if (per < 64) per = 64;
+  const int blocks = (int)((nr + per - 1) / per);
+  const dim3 grid(blocks > 0 ? blocks : 1);
+  switch ((n + 15) / 16) {
+    case 1: hipLaunchKernelGGL(gram_rows_kernel<1>, grid, dim3(256), 0, st, part, splits, pw, scale, P, nr, n, per, gpart); break;
+    case 2: hipLaunchKernelGGL(gram_rows_kernel<2>, grid, dim3(256), 0, st, part, splits, pw, scale, P, nr, n, per, gpart); break;
+    case 3: hipLaunchKernelGGL(gram_rows_kernel<3>, grid, dim3(256), 0, st, part, splits, pw, scale, P, nr, n, per, gpart); break;
+    case 4: hipLaunchKernelGGL(gram_rows_kernel<4>, grid, dim3(256), 0, st, part, splits, pw, scale, P, nr, n, per, gpart); break;
+    case 5: hipLaunchKernelGGL(gram_rows_kernel<5>, grid, dim3(256), 0, st, part, splits, pw, scale, P, nr, n, per, gpart); break;
+    default: hipLaunchKernelGGL(gram_rows_kernel<6>, grid, dim3(256), 0, st, part, splits, pw, scale, P, nr, n, per, gpart); break;
+  }
+  LAUNCH_CHECK();
+  hipLaunchKernelGGL(reduce_gram_kernel, dim3(grid1(n * n, 64)), dim3(256), 0, st, gpart, (int)grid.x, n * n, G);
   LAUNCH_CHECK();
   return METIS_OK;
 }
@@ -683,7 +714,9 @@ metis_status split_ext(const SideQ& L, const SideQ& R, int64_t M, int64_t N, int
                   R.k > 0 ? R.out->tensor_scale : w.ones, R.k, N};
   e.a_ext = w.a_ext;
   e.b_ext = w.b_ext;
-  const int64_t nba = grid1(round_up64(M, 32) * (kext / 8), 256);
+  // A_ext: at most 512 looping workgroups (with B_ext's static LDS a CU
+  // holds four of the launch's workgroups)
+  const int64_t nba = std::min<int64_t>(grid1(round_up64(M, 32) * (kext / 8), 256), 512);
   const int64_t nbb = ceil_div<int64_t>(round_up64(N, 32), 64);
   if (nba + nbb > INT32_MAX) return fail(METIS_E_UNSUPPORTED, "K-extension too large");
   hipLaunchKernelGGL(ext_prep_kernel, dim3((unsigned)(nba + nbb)), dim3(256), 0, st, e, nba);
@@ -873,14 +906,16 @@ metis_status decompose_project(DecompCall& c, hipStream_t st) {
 
   // projection and rediagonalisation (every step); V as three bf16 terms
   if (mfma_ok) {
+    // the split reduction into P happens inside the Gram kernel
     if ((s = mfma_product<3>((const uint16_t*)M, ld, rows, nullptr, f->V, cols, k, k, w.proj_nkb, w.proj_kbps,
-                             w.proj_splits, 1.0f, w.vfrag, w.ppart, w.p, st)) != METIS_OK)
+                             w.proj_splits, 1.0f, w.vfrag, w.ppart, w.p, st, false)) != METIS_OK)
       return s;
-  } else {
-    hipLaunchKernelGGL(project_kernel, dim3(grid1(rows, 64)), dim3(256), 0, st, M, dtype, ld, rows, cols,
-                       f->V, k, w.p);
-    LAUNCH_CHECK();
+    return launch_gram_from_parts(w.ppart, w.proj_splits, mfma_part_pitch(k), 1.0f, w.p, rows, k, w.gblocks,
+                                  w.gpart, w.ptp, st);
   }
+  hipLaunchKernelGGL(project_kernel, dim3(grid1(rows, 64)), dim3(256), 0, st, M, dtype, ld, rows, cols, f->V, k,
+                     w.p);
+  LAUNCH_CHECK();
   if ((s = launch_gram(w.p, rows, k, k, 1, w.gblocks, w.gpart, w.ptp, st)) != METIS_OK) return s;
   return METIS_OK;
 }

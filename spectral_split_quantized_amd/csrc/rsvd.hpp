@@ -321,13 +321,107 @@ __global__ __launch_bounds__(256) void gram_partial_kernel(const float* __restri
     }
 }
 
-__global__ void reduce_gram_kernel(const double* __restrict__ part, int blocks, int nn,
-                                   double* __restrict__ G) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= nn) return;
+// The projection's split reduction fused with the Gram partials: rows
+// [rb, re) of P = scale * sum_s part[s][r][j] (j < n; the splits added in
+// order from zero, then scaled, as project_reduce_kernel does) are written
+// to P and, 32 rows at a time, accumulated as gram_partial_kernel does
+// (same thread ownership, same row order), so P and the partials are the
+// same bits as the two kernels in sequence.  The next 32 rows' split sums
+// are formed in registers while the current rows are accumulated.
+template <int T>
+__global__ __launch_bounds__(256) void gram_rows_kernel(const float* __restrict__ part, int64_t splits, int pw,
+                                                        float scale, float* __restrict__ P, int64_t nr, int n,
+                                                        int64_t rows_per_block, double* __restrict__ gpart) {
+  constexpr int W = 16 * T;
+  constexpr int PER = (32 * W + 255) / 256;  // row-chunk elements per thread
+  __shared__ float xs[2][32][W + 1];
+  const int tid = threadIdx.x;
+  const int ti = tid & 15, tj = tid >> 4;
+  const int64_t rb = (int64_t)blockIdx.x * rows_per_block;
+  const int64_t re = min(nr, rb + rows_per_block);
+  double acc[T][T];
+#pragma unroll
+  for (int u = 0; u < T; ++u)
+#pragma unroll
+    for (int v = 0; v < T; ++v) acc[u][v] = 0.0;
+  float val[PER];
+  auto fetch = [&](int64_t r0) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + 256 * u;
+      float a = 0.0f;
+      if (e < 32 * n) {
+        const int r = e / n, j = e - r * n;
+        if (r0 + r < re) {
+          const float* src = part + (r0 + r) * pw + j;
+#pragma unroll 4
+          for (int64_t sp = 0; sp < splits; ++sp) a += src[sp * nr * pw];
+          a = a * scale;
+          P[(r0 + r) * n + j] = a;
+        }
+      }
+      val[u] = a;
+    }
+  };
+  auto stash = [&](int b) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + 256 * u;
+      if (e < 32 * n) {
+        const int r = e / n, j = e - r * n;
+        xs[b][r][j] = val[u];
+      }
+    }
+  };
+  if (rb < re) {
+    fetch(rb);
+    stash(0);
+  }
+  __syncthreads();
+  int b = 0;
+  for (int64_t r0 = rb; r0 < re; r0 += 32) {
+    const bool more = r0 + 32 < re;
+    if (more) fetch(r0 + 32);
+#pragma unroll 4
+    for (int r = 0; r < 32; ++r) {
+      double xa[T], xb[T];
+#pragma unroll
+      for (int u = 0; u < T; ++u) xa[u] = (double)xs[b][r][ti + 16 * u];
+#pragma unroll
+      for (int v = 0; v < T; ++v) xb[v] = (double)xs[b][r][tj + 16 * v];
+#pragma unroll
+      for (int u = 0; u < T; ++u)
+#pragma unroll
+        for (int v = 0; v < T; ++v) acc[u][v] += xa[u] * xb[v];
+    }
+    if (more) stash(b ^ 1);
+    __syncthreads();
+    b ^= 1;
+  }
+  const int nn = n * n;
+#pragma unroll
+  for (int u = 0; u < T; ++u)
+#pragma unroll
+    for (int v = 0; v < T; ++v) {
+      const int a = ti + 16 * u, c = tj + 16 * v;
+      if (a < n && c < n) gpart[(int64_t)blockIdx.x * nn + a * n + c] = acc[u][v];
+    }
+}
+
+// G[e] = sum of the blocks' partials, in a fixed order: 64 entries per
+// workgroup, wave q adds the partials b = q, q + 4, ... in order, then the
+// four sums are added pairwise.
+__global__ __launch_bounds__(256) void reduce_gram_kernel(const double* __restrict__ part, int blocks, int nn,
+                                                          double* __restrict__ G) {
+  __shared__ double red[4][64];
+  const int el = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + el;
   double s = 0.0;
-  for (int b = 0; b < blocks; ++b) s += part[(int64_t)b * nn + e];
-  G[e] = s;
+  if (e < nn)
+    for (int b = q; b < blocks; b += 4) s += part[(int64_t)b * nn + e];
+  red[q][el] = s;
+  __syncthreads();
+  if (q == 0 && e < nn) G[e] = (red[0][el] + red[1][el]) + (red[2][el] + red[3][el]);
 }
 
 // ------------------------------------------------------ Cholesky (one WG) --
