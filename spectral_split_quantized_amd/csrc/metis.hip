@@ -321,10 +321,14 @@ DecompWs carve_decompose(Carver& cv, int64_t rows, int64_t cols, int k, int n, i
 }
 
 // The Jacobi eigensolver with LDS sized to n (callers check the launch);
-// clear (n words, may be null) is zeroed on the way.
+// clear (n words, may be null) is zeroed on the way.  With n <= 64 (the
+// rediagonalisation at k = 61) it takes 67 KB of LDS, which fits beside one
+// workgroup of the residual sweeps (78 KB).
 void launch_jacobi(const double* g, int n, double* w, double* z, unsigned long long* clear, hipStream_t st) {
   if (n <= 32)
     hipLaunchKernelGGL(jacobi_kernel<32>, dim3(1), dim3(1024), 0, st, g, n, w, z, clear);
+  else if (n <= 64)
+    hipLaunchKernelGGL(jacobi_kernel<64>, dim3(1), dim3(1024), 0, st, g, n, w, z, clear);
   else if (n <= 72)
     hipLaunchKernelGGL(jacobi_kernel<72>, dim3(1), dim3(1024), 0, st, g, n, w, z, clear);
   else
@@ -935,6 +939,8 @@ metis_status decompose_rediag(DecompCall& c, hipStream_t st, uint32_t* amax_u = 
   LAUNCH_CHECK();
   if (k <= 32)
     launch_rot<32>(w, f, rows, cols, k, amax_u, amax_v, st);
+  else if (k <= 64)
+    launch_rot<64>(w, f, rows, cols, k, amax_u, amax_v, st);
   else if (k <= 72)
     launch_rot<72>(w, f, rows, cols, k, amax_u, amax_v, st);
   else

@@ -141,3 +141,19 @@ def test_quantize_strided_input(axis):
     metis.status_sync()
     oc, osc = mxfp4.quantize(x.double().numpy(), axis)
     assert np.array_equal(q.scales.cpu().numpy(), osc) and np.array_equal(q.codes.cpu().numpy(), oc)
+
+
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")])
+@pytest.mark.parametrize("axis", [0, 1])
+def test_quantize_non_finite_sets_numeric_status(axis, bad):
+    """A NaN or an infinity anywhere in the operand is reported through the
+    status word (E_NUMERIC at the next status_sync), and the flag clears."""
+    say("MXFP4 non-finite input axis %d %s" % (axis, bad))
+    M = torch.randn(64, 128, dtype=torch.float32, device="cuda")
+    M[17, 45] = bad
+    metis.mxfp4_quantize(M, axis)
+    with pytest.raises(metis.MetisError) as ei:
+        metis.status_sync()
+    assert ei.value.status == metis.E_NUMERIC
+    metis.mxfp4_quantize(torch.randn(64, 128, dtype=torch.float32, device="cuda"), axis)
+    metis.status_sync()

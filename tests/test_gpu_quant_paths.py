@@ -97,3 +97,27 @@ def test_streaming_sweeps_strided_rows(k):
     metis.status_sync()
     _equal(fast, dense, "strided vs contiguous")
     _equal(fast, general, "strided streaming vs general")
+
+
+@pytest.mark.parametrize("k", [0, 61])
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")])
+def test_streaming_sweeps_non_finite_status(k, bad):
+    """The streaming sweeps (whole-tile bf16 operand) report a NaN or an
+    infinity in M through the status word, with and without factors, and
+    the flag clears afterwards."""
+    rows, cols = 1024, 16384
+    say("streaming sweeps non-finite input k=%d %s" % (k, bad))
+    M, _ = synth.anisotropic_fast(rows, cols, synth.FRAC_X, 31, device="cuda")
+    M[300, 9001] = bad
+    cfg = metis.make_config(k=max(k, 1), rounding=metis.SR, seed=4)
+    f = None
+    if k:
+        u, s, v = synth.exact_factors(rows, cols, k, seed=6)
+        f = gpu_factors(u, s, v)
+    metis.quantize(M, cfg, 0, 2, metis.AXIS0 | metis.AXIS1, factors=f)
+    with pytest.raises(metis.MetisError) as ei:
+        metis.status_sync()
+    assert ei.value.status == metis.E_NUMERIC
+    M[300, 9001] = 0.0
+    metis.quantize(M, cfg, 0, 2, metis.AXIS0 | metis.AXIS1, factors=f)
+    metis.status_sync()
