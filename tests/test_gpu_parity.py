@@ -334,3 +334,39 @@ def test_run_to_run_determinism():
                      L.factors["X"].V.cpu().clone(), Y.cpu().clone()))
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("k", [40, 70, 80])
+def test_decomposition_wide_ranks_match_oracle(k):
+    """Ranks whose Jacobi solves and rotations take the 64-, 72- and 96-wide
+    kernels (k + s up to 88 in the sketch, k up to 80 in the
+    rediagonalisation; ranks above 64 reach them through metis_decompose
+    only), at a refresh step and at a cached step on a changed matrix,
+    against the oracle's decomposition with its factor cache.  M is an exact
+    rank-k product plus noise 1e-4 times smaller, so its top-k subspace is
+    well separated."""
+    rows, cols, s = 768, 1024, 8
+    say("wide-rank decomposition k=%d" % k)
+    u0, s0, v0 = synth.exact_factors(rows, cols, k, seed=50 + k)
+    base = (u0 * s0) @ v0.T
+    rng = np.random.default_rng(k)
+    noise = rng.standard_normal((rows, cols)) * (1e-4 * np.abs(base).max())
+    cfg = metis.make_config(k=k, s=s, l_k=0, refresh=8, rounding=metis.SR, seed=3)
+    ocfg = rsvd.Config(k=k, s=s, l_k=0, refresh=8, rounding="sr", seed=3)
+    tag = metis.make_tag(2, metis.OPERAND_X)
+    f = metis.Factors(rows, cols, k)
+    cache = rsvd.FactorCache()
+    for step in (0, 1):
+        m = (base + noise * (1.0 + step)).astype(np.float32)
+        metis.decompose(torch.from_numpy(m).cuda(), cfg, 0, tag, step, f)
+        metis.status_sync()
+        u, sv, v, refreshed = rsvd.decompose(m.astype(np.float64), ocfg, False, tag, step, cache=cache)
+        assert refreshed == (step == 0) and f.refreshed_at == 0
+        ug, sg, vg = (t.cpu().double().numpy() for t in (f.U, f.S, f.V))
+        sin_v, sin_u = sin_max(vg, v), sin_max(ug, u)
+        srel = np.abs(sg - sv).max() / sv[0]
+        say("  step %d: sin(V) %.2e sin(U) %.2e |dS|/S0 %.2e" % (step, sin_v, sin_u, srel))
+        assert sin_v <= SUBSPACE_TOL and sin_u <= SUBSPACE_TOL
+        assert srel <= S_TOL
+        assert np.all(np.diff(sg) <= 0)
+        assert np.abs(vg.T @ vg - np.eye(k)).max() <= 1e-5
