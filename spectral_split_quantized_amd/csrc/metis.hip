@@ -884,10 +884,24 @@ metis_status decompose_project(DecompCall& c, hipStream_t st) {
     float* dst = w.q;
     for (int pass = 0; pass < 3; ++pass) {
       if ((s = launch_gram(src, lr, n, n, 1, w.gblocks, w.gpart, w.g, st)) != METIS_OK) return s;
-      hipLaunchKernelGGL(cholinv_kernel, dim3(1), dim3(256), 0, st, w.g, n, lr, pass, w.rinv);
+      if (n <= 32)
+        hipLaunchKernelGGL(cholinv_kernel<32>, dim3(1), dim3(256), 0, st, w.g, n, lr, pass, w.rinv);
+      else if (n <= 64)
+        hipLaunchKernelGGL(cholinv_kernel<64>, dim3(1), dim3(256), 0, st, w.g, n, lr, pass, w.rinv);
+      else if (n <= 72)
+        hipLaunchKernelGGL(cholinv_kernel<72>, dim3(1), dim3(256), 0, st, w.g, n, lr, pass, w.rinv);
+      else
+        hipLaunchKernelGGL(cholinv_kernel<kMaxN>, dim3(1), dim3(256), 0, st, w.g, n, lr, pass, w.rinv);
       LAUNCH_CHECK();
-      hipLaunchKernelGGL(apply_rinv_kernel, dim3(grid1(lr, 64)), dim3(256), 0, st, src, lr, n, w.rinv,
-                         dst);
+      if (n <= 32)
+        hipLaunchKernelGGL(apply_rinv_kernel<32>, dim3(grid1(lr, 64)), dim3(256), 0, st, src, lr, n, w.rinv, dst);
+      else if (n <= 64)
+        hipLaunchKernelGGL(apply_rinv_kernel<64>, dim3(grid1(lr, 64)), dim3(256), 0, st, src, lr, n, w.rinv, dst);
+      else if (n <= 72)
+        hipLaunchKernelGGL(apply_rinv_kernel<72>, dim3(grid1(lr, 64)), dim3(256), 0, st, src, lr, n, w.rinv, dst);
+      else
+        hipLaunchKernelGGL(apply_rinv_kernel<kMaxN>, dim3(grid1(lr, 64)), dim3(256), 0, st, src, lr, n, w.rinv,
+                           dst);
       LAUNCH_CHECK();
       float* t = src;  // next pass reads what was just written
       src = dst;

@@ -211,18 +211,27 @@ __global__ __launch_bounds__(256) void sketch_y_kernel(const void* __restrict__ 
     }
 }
 
-// Partial B[j][c] over a slice of sample rows: part[slice][j][c].
-// 64 columns per block; threads: column = tid % 64, j group = tid / 64.
+// Partial B[j][c] over a slice of sample rows: part[slice][j][c] = the sum,
+// in sample-row order, of Q[s][j] M[idx[s]][c] (binary32 FMA).  64 columns
+// per block, one per lane.  Wave w owns the jw consecutive rows j of B from
+// w jw (jw: n / 4 rounded up to a multiple of 4), read from the Q tile in
+// LDS four at a time (all lanes read the same address), and the M values of
+// eight sample rows are loaded before their FMAs.
 __global__ __launch_bounds__(256) void sketch_b_kernel(const void* __restrict__ M, int dtype,
                                                        int64_t ld, const int32_t* __restrict__ idx,
                                                        int64_t ns, int64_t cols,
                                                        const float* __restrict__ Q, int n,
                                                        int64_t rows_per_slice,
                                                        float* __restrict__ part) {
-  __shared__ float qs[64][kMaxN + 1];
-  const int tid = threadIdx.x;
-  const int64_t c = (int64_t)blockIdx.x * 64 + (tid & 63);
-  const int jg = tid >> 6;
+  constexpr int QP = kMaxN;  // Q tile pitch in floats (16-byte rows)
+  static_assert(QP % 4 == 0, "Q tile pitch");
+  __shared__ __attribute__((aligned(16))) float qs[64][QP];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int jw = ((n + 3) / 4 + 3) & ~3;
+  const int j0 = wave * jw;
+  const int64_t c = (int64_t)blockIdx.x * 64 + lane;
+  const int64_t cl = c < cols ? c : cols - 1;  // a valid column for the loads
   const int64_t sb = (int64_t)blockIdx.y * rows_per_slice;
   const int64_t se = min(ns, sb + rows_per_slice);
   float acc[kMaxN / 4];
@@ -230,26 +239,39 @@ __global__ __launch_bounds__(256) void sketch_b_kernel(const void* __restrict__ 
   for (int t = 0; t < kMaxN / 4; ++t) acc[t] = 0.0f;
   for (int64_t s0 = sb; s0 < se; s0 += 64) {
     __syncthreads();
-    for (int e = tid; e < 64 * n; e += 256) {
-      const int r = e / n, j = e % n;
-      qs[r][j] = (s0 + r < se) ? Q[(s0 + r) * n + j] : 0.0f;
+    for (int e = tid; e < 64 * QP; e += 256) {
+      const int r = e / QP, j = e - r * QP;
+      qs[r][j] = (j < n && s0 + r < se) ? Q[(s0 + r) * n + j] : 0.0f;
     }
     __syncthreads();
     const int lim = (int)min((int64_t)64, se - s0);
-    for (int r = 0; r < lim; ++r) {
-      const float mv = (c < cols) ? load_as_float(M, dtype, (int64_t)idx[s0 + r] * ld + c) : 0.0f;
+    for (int r0 = 0; r0 < lim; r0 += 8) {
+      float mv[8];
 #pragma unroll
-      for (int t = 0; t < kMaxN / 4; ++t) {
-        const int j = jg + 4 * t;
-        if (j < n) acc[t] = fmaf(qs[r][j], mv, acc[t]);
+      for (int u = 0; u < 8; ++u)
+        mv[u] = (r0 + u < lim) ? load_as_float(M, dtype, (int64_t)idx[s0 + r0 + u] * ld + cl) : 0.0f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (r0 + u >= lim) break;
+        const float4* q4 = (const float4*)&qs[r0 + u][j0];
+#pragma unroll
+        for (int t4 = 0; t4 < kMaxN / 16; ++t4) {
+          if (4 * t4 < jw) {
+            const float4 q = q4[t4];
+            acc[4 * t4 + 0] = fmaf(q.x, mv[u], acc[4 * t4 + 0]);
+            acc[4 * t4 + 1] = fmaf(q.y, mv[u], acc[4 * t4 + 1]);
+            acc[4 * t4 + 2] = fmaf(q.z, mv[u], acc[4 * t4 + 2]);
+            acc[4 * t4 + 3] = fmaf(q.w, mv[u], acc[4 * t4 + 3]);
+          }
+        }
       }
     }
   }
   if (c < cols)
 #pragma unroll
     for (int t = 0; t < kMaxN / 4; ++t) {
-      const int j = jg + 4 * t;
-      if (j < n) part[((int64_t)blockIdx.y * n + j) * cols + c] = acc[t];
+      const int j = j0 + t;
+      if (t < jw && j < n) part[((int64_t)blockIdx.y * n + j) * cols + c] = acc[t];
     }
 }
 
@@ -432,11 +454,13 @@ __global__ __launch_bounds__(256) void reduce_gram_kernel(const double* __restri
 // Right-looking Cholesky (column j: pivot square root, column scaling,
 // rank-1 update of the trailing lower triangle, all threads sharing each
 // phase), then X = L^-1 by right-looking forward elimination of L X = I.
+// LDS holds L and X at NM x (NM + 1) doubles (n <= NM).
+template <int NM>
 __global__ __launch_bounds__(256) void cholinv_kernel(const double* __restrict__ G, int n,
                                                       int64_t p, int pass,
                                                       double* __restrict__ Rinv) {
-  __shared__ double L[kMaxN][kMaxN + 1];
-  __shared__ double X[kMaxN][kMaxN + 1];
+  __shared__ double L[NM][NM + 1];
+  __shared__ double X[NM][NM + 1];
   __shared__ double red[4];
   __shared__ int fail;
   const int tid = threadIdx.x;
@@ -507,11 +531,12 @@ __global__ __launch_bounds__(256) void cholinv_kernel(const double* __restrict__
   }
 }
 
-// Qout[s] = Y[s] Rinv (fp64 accumulation), 64 rows per block.
+// Qout[s] = Y[s] Rinv (fp64 accumulation), 64 rows per block (n <= NM).
+template <int NM>
 __global__ __launch_bounds__(256) void apply_rinv_kernel(const float* __restrict__ Y, int64_t ns,
                                                          int n, const double* __restrict__ Rinv,
                                                          float* __restrict__ Qout) {
-  __shared__ double ri[kMaxN][kMaxN + 1];
+  __shared__ double ri[NM][NM + 1];
   const int tid = threadIdx.x;
   for (int e = tid; e < n * n; e += blockDim.x) ri[e / n][e % n] = Rinv[e];
   __syncthreads();
