@@ -826,6 +826,23 @@ metis_status decompose_check(const void* M, int32_t dtype, int64_t rows, int64_t
   return METIS_OK;
 }
 
+// One CholeskyQR pass after its Gram: Rinv from the Cholesky factor, then
+// dst = src Rinv, with LDS sized to the sketch width n.
+template <int NM>
+void cholqr_pass(const double* g, int n, int64_t lr, int pass, double* rinv, const float* src, float* dst,
+                 hipStream_t st) {
+  hipLaunchKernelGGL(cholinv_kernel<NM>, dim3(1), dim3(256), 0, st, g, n, lr, pass, rinv);
+  hipLaunchKernelGGL(apply_rinv_kernel<NM>, dim3(grid1(lr, kApplyRows)), dim3(256), 0, st, src, lr, n, rinv, dst);
+}
+
+void launch_cholqr_pass(const double* g, int n, int64_t lr, int pass, double* rinv, const float* src, float* dst,
+                        hipStream_t st) {
+  if (n <= 32) cholqr_pass<32>(g, n, lr, pass, rinv, src, dst, st);
+  else if (n <= 64) cholqr_pass<64>(g, n, lr, pass, rinv, src, dst, st);
+  else if (n <= 72) cholqr_pass<72>(g, n, lr, pass, rinv, src, dst, st);
+  else cholqr_pass<kMaxN>(g, n, lr, pass, rinv, src, dst, st);
+}
+
 // The sketch on refresh steps (V from the range of a row sample of M), then
 // the projection P = M V and its Gram matrix G = P^T P.
 metis_status decompose_project(DecompCall& c, hipStream_t st) {
@@ -884,24 +901,7 @@ metis_status decompose_project(DecompCall& c, hipStream_t st) {
     float* dst = w.q;
     for (int pass = 0; pass < 3; ++pass) {
       if ((s = launch_gram(src, lr, n, n, 1, w.gblocks, w.gpart, w.g, st)) != METIS_OK) return s;
-      if (n <= 32)
-        hipLaunchKernelGGL(cholinv_kernel<32>, dim3(1), dim3(256), 0, st, w.g, n, lr, pass, w.rinv);
-      else if (n <= 64)
-        hipLaunchKernelGGL(cholinv_kernel<64>, dim3(1), dim3(256), 0, st, w.g, n, lr, pass, w.rinv);
-      else if (n <= 72)
-        hipLaunchKernelGGL(cholinv_kernel<72>, dim3(1), dim3(256), 0, st, w.g, n, lr, pass, w.rinv);
-      else
-        hipLaunchKernelGGL(cholinv_kernel<kMaxN>, dim3(1), dim3(256), 0, st, w.g, n, lr, pass, w.rinv);
-      LAUNCH_CHECK();
-      if (n <= 32)
-        hipLaunchKernelGGL(apply_rinv_kernel<32>, dim3(grid1(lr, 64)), dim3(256), 0, st, src, lr, n, w.rinv, dst);
-      else if (n <= 64)
-        hipLaunchKernelGGL(apply_rinv_kernel<64>, dim3(grid1(lr, 64)), dim3(256), 0, st, src, lr, n, w.rinv, dst);
-      else if (n <= 72)
-        hipLaunchKernelGGL(apply_rinv_kernel<72>, dim3(grid1(lr, 64)), dim3(256), 0, st, src, lr, n, w.rinv, dst);
-      else
-        hipLaunchKernelGGL(apply_rinv_kernel<kMaxN>, dim3(grid1(lr, 64)), dim3(256), 0, st, src, lr, n, w.rinv,
-                           dst);
+      launch_cholqr_pass(w.g, n, lr, pass, w.rinv, src, dst, st);
       LAUNCH_CHECK();
       float* t = src;  // next pass reads what was just written
       src = dst;

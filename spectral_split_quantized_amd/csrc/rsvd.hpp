@@ -531,22 +531,30 @@ __global__ __launch_bounds__(256) void cholinv_kernel(const double* __restrict__
   }
 }
 
-// Qout[s] = Y[s] Rinv (fp64 accumulation), 64 rows per block (n <= NM).
+// Qout[s] = Y[s] Rinv (fp64 accumulation over a = 0 .. j in order),
+// kApplyRows rows per block (n <= NM); the block's rows of Y are staged in
+// LDS next to Rinv, so the inner products read only LDS.
+constexpr int kApplyRows = 16;
 template <int NM>
 __global__ __launch_bounds__(256) void apply_rinv_kernel(const float* __restrict__ Y, int64_t ns,
                                                          int n, const double* __restrict__ Rinv,
                                                          float* __restrict__ Qout) {
   __shared__ double ri[NM][NM + 1];
+  __shared__ float ys[kApplyRows][NM + 1];
   const int tid = threadIdx.x;
+  const int64_t s0 = (int64_t)blockIdx.x * kApplyRows;
   for (int e = tid; e < n * n; e += blockDim.x) ri[e / n][e % n] = Rinv[e];
+  for (int e = tid; e < kApplyRows * n; e += blockDim.x) {
+    const int r = e / n, a = e - r * n;
+    ys[r][a] = s0 + r < ns ? Y[(s0 + r) * n + a] : 0.0f;
+  }
   __syncthreads();
-  const int64_t s0 = (int64_t)blockIdx.x * 64;
-  for (int e = tid; e < 64 * n; e += blockDim.x) {
-    const int r = e / n, j = e % n;
+  for (int e = tid; e < kApplyRows * n; e += blockDim.x) {
+    const int r = e / n, j = e - r * n;
     const int64_t s = s0 + r;
     if (s >= ns) continue;
     double acc = 0.0;
-    for (int a = 0; a <= j; ++a) acc += (double)Y[s * n + a] * ri[a][j];
+    for (int a = 0; a <= j; ++a) acc += (double)ys[r][a] * ri[a][j];
     Qout[s * n + j] = (float)acc;
   }
 }
