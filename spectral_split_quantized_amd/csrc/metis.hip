@@ -295,7 +295,15 @@ DecompWs carve_decompose(Carver& cv, int64_t rows, int64_t cols, int k, int n, i
   w.gpart = cv.take<double>((size_t)w.gblocks * kMaxN * kMaxN);
   w.g = cv.take<double>(kMaxN * kMaxN);
   w.rinv = cv.take<double>(kMaxN * kMaxN);
-  w.slices = (int)(lr >= 4096 ? 16 : (lr >= 512 ? 4 : 1));
+  // sketch product B = Q^T M_s split over sample-row slices; a small sample
+  // takes enough slices of >= 16 rows for about 512 workgroups, since each
+  // workgroup walks its rows one dependent batch of loads after another
+  int64_t slices = lr >= 4096 ? 16 : (lr >= 512 ? 4 : 1);
+  const int64_t cblocks = (cols + 63) / 64, fill = (512 + cblocks - 1) / cblocks;
+  const int64_t cap = lr / 16 > 1 ? lr / 16 : 1;
+  if (slices < fill) slices = fill < cap ? fill : cap;
+  if (slices < 1) slices = 1;
+  w.slices = (int)slices;
   w.rows_per_slice = (lr + w.slices - 1) / w.slices;
   w.bpart = cv.take<float>((size_t)w.slices * n * cols);
   w.b = cv.take<float>((size_t)n * cols);
