@@ -684,6 +684,18 @@ def measure_c4(dev, copy_gbps):
 
 # ------------------------------------------------------------ CPU baseline --
 
+def host_cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return None
+
+
 def cpu_baseline(inputs_cpu, tokens, ncols):
     """Time the float64 oracle on a bounded sample of the gate projection:
     `tokens` rows of X and D and the first `ncols` output columns of W."""
@@ -709,14 +721,21 @@ def cpu_baseline(inputs_cpu, tokens, ncols):
         flops += decompose_flops(r, c, K_RANK, OVERSAMPLE, lk, True) + residual_flops(r, c, K_RANK)
     flops += split_gemm_flops(l, n, h, K_RANK, K_RANK) + split_gemm_flops(l, h, n, K_RANK, K_RANK)
     flops += split_gemm_flops(h, n, l, K_RANK, K_RANK)
-    threads = None
+    threads, blas = None, None
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 0) for i in threadpool_info()), default=None)
+        pools = threadpool_info()
+        threads = max((i.get("num_threads", 0) for i in pools), default=None)
+        libs = [i for i in pools if i.get("user_api") == "blas"]
+        if libs:
+            b = libs[0]
+            blas = "%s %s (%s kernels, %s threads)" % (b.get("internal_api"), b.get("version"),
+                                                       b.get("architecture"), b.get("num_threads"))
     except Exception:  # pragma: no cover
         pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads or os.cpu_count(),
-            "kind": "oracle", "seconds": round(dt, 2),
+            "kind": "oracle", "seconds": round(dt, 2), "cpu_model": host_cpu_model(),
+            "host_logical_cpus": os.cpu_count(), "blas": blas,
             "sample": "gate projection, first %d tokens x first %d output columns, refresh step "
                       "(decompose + quantise + fwd + bwd), float64 numpy oracle" % (tokens, ncols)}
 
