@@ -121,6 +121,17 @@ enum { METIS_AXIS0 = 1, METIS_AXIS1 = 2 }; /* bitmask for metis_quantize */
 int32_t metis_abi_version(void);
 const char *metis_last_error(void);
 
+/* metis_init_device -- set up the library on the current device: its copy of
+ * the Gaussian quantile table that Omega is drawn from, the numeric status
+ * word that metis_status_sync reads, and the address of the static scratch
+ * array of metis_quantize_static.  Every other call does this itself on its
+ * first use of a device; it copies to device symbols synchronously, so a
+ * caller that captures library calls into a HIP graph calls this first, on
+ * each device, outside the capture.  Repeated calls return METIS_OK at once.
+ * Errors: METIS_E_HIP (no device, or a failed copy), METIS_E_UNSUPPORTED
+ * (device index >= 64). */
+metis_status metis_init_device(void);
+
 /* Workspace sizes in bytes (0 never means "no workspace needed"; always
  * pass at least the returned size). */
 size_t metis_decompose_workspace(int64_t rows, int64_t cols, const metis_config *cfg,

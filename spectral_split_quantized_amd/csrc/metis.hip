@@ -1190,6 +1190,8 @@ int32_t metis_abi_version(void) { return METIS_ABI_VERSION; }
 
 const char* metis_last_error(void) { return g_last_error.c_str(); }
 
+metis_status metis_init_device(void) { return ensure_device_tables(); }
+
 void metis_omega_table(uint16_t* out65536) {
   if (out65536) memcpy(out65536, host_omega_table(), 65536 * sizeof(uint16_t));
 }

@@ -112,6 +112,8 @@ def load():
     lib.metis_gemm_bwd_prepared.restype = i32
     lib.metis_status_sync.argtypes = [P]
     lib.metis_status_sync.restype = i32
+    lib.metis_init_device.argtypes = []
+    lib.metis_init_device.restype = i32
     lib.metis_omega_table.argtypes = [P]
     lib.metis_omega_table.restype = None
     lib.metis_timing_enable.argtypes = [i32]
@@ -401,6 +403,12 @@ def gemm_bwd_prepared(dq, wq, xq, workspace, dX=None, dW=None, want_dx=True, wan
                                        _ptr(dW) if want_dw else None, dW.stride(0) if want_dw else 0,
                                        _ptr(ws), ws.numel(), _stream()))
     return dX, dW
+
+
+def init_device():
+    """Set up the library on the current device (metis_init_device); needed
+    only before capturing library calls into a graph."""
+    _check(load().metis_init_device())
 
 
 def status_sync():

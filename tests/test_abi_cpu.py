@@ -31,6 +31,20 @@ def test_library_exports_every_declared_symbol():
     assert lib.metis_abi_version() == 1
 
 
+def test_init_device_reports_a_missing_gpu():
+    """metis_init_device is the one call that sets up a device ahead of a
+    graph capture: with no GPU it returns METIS_E_HIP with a message, it does
+    not crash; with one it succeeds, and again at once."""
+    lib = metis.load()
+    from conftest import gpu_available
+    if gpu_available():
+        assert lib.metis_init_device() == metis.OK
+        assert lib.metis_init_device() == metis.OK
+    else:
+        assert lib.metis_init_device() == metis.E_HIP
+        assert lib.metis_last_error()
+
+
 def test_omega_table_matches_oracle():
     ours = metis.omega_table_bits().astype(np.uint32)
     lib_vals = (ours << 16).view(np.float32).astype(np.float64)

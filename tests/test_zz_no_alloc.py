@@ -23,6 +23,9 @@ def _gpu():
         pytest.fail("GPU tests need an MI355X; none is visible")
     metis.load()
     torch.cuda.set_device(0)
+    # the set-up a graph-capturing caller does before capture; idempotent
+    metis.init_device()
+    metis.init_device()
 
 
 def _factors(rows, cols, k, seed):
