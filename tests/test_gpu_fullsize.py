@@ -15,7 +15,8 @@ import torch
 from oracle import nvfp4, philox, rsvd, split_gemm
 from spectral_split_quantized_amd import metis, synth
 
-from gpu_helpers import gpu_factors, gpu_qop, oracle_qop, rel_fro, say, sin_max, to_np
+from gpu_helpers import (E2E_FACTOR_FLIPS, E2E_RESID_FLIPS, E2E_TOL, Layer, gpu_factors, gpu_qop, oracle_qop,
+                         rel_fro, say, sin_max, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -113,6 +114,101 @@ def test_ffn_residual_quant_sampled_panels():
     ov = nvfp4.quantize(v, 0, "sr", 0, philox.with_role(tag, philox.ROLE_V), 5)
     assert np.array_equal(q.U.codes.cpu().numpy(), ou.codes)
     assert np.array_equal(q.V.codes.cpu().numpy(), ov.codes)
+
+
+# ------------------------------------------------------------ end to end --
+
+def _oracle_operand(m, ocfg, sample, tag, seed):
+    """The oracle's decomposition of one operand (step 0, a refresh) and what
+    quantising it needs: float64 factors, the binary32 residual formed in
+    float64 (as split_gemm.quantize_operand forms it), its exact amax, and
+    the whole quantised factors (small)."""
+    u, s, v, _ = rsvd.decompose(m, ocfg, sample, tag, 0)
+    us = u * s
+    mr = np.empty(m.shape, np.float32)
+    for r0 in range(0, m.shape[0], 2048):
+        mr[r0:r0 + 2048] = (m[r0:r0 + 2048] - us[r0:r0 + 2048] @ v.T).astype(np.float32)
+    uq = nvfp4.quantize(u.astype(np.float32), 0, "sr", seed, philox.with_role(tag, philox.ROLE_U), 0)
+    vq = nvfp4.quantize(v.astype(np.float32), 0, "sr", seed, philox.with_role(tag, philox.ROLE_V), 0)
+    return {"s": s.astype(np.float32).astype(np.float64), "mr": mr, "amax": np.float32(np.max(np.abs(mr))),
+            "uh": nvfp4.dequantize(uq), "vh": nvfp4.dequantize(vq), "uq": uq, "vq": vq,
+            "rt": philox.with_role(tag, philox.ROLE_RESID)}
+
+
+def _flips(gpu_codes, oracle_codes):
+    return float((gpu_codes != oracle_codes).mean())
+
+
+def test_q_proj_end_to_end_sampled_outputs():
+    """LLaMA-3-8B q_proj (X 16384 x 4096, W 4096 x 4096, D 16384 x 4096, k = 61,
+    l_k = 164, SR) through the whole HIP path (decompose, quantise, split GEMM
+    forward and backward) and the whole oracle pipeline on the same seeded
+    inputs.  Checked: flip rates of the residual codes on sampled row panels
+    (K = cols) and column bands (K = rows) of X and D and on all of W, and of
+    every factor code; Y and dX on 64 sampled rows and a 64 x 64 block of dW
+    within the end-to-end bar (both sides decide each code in binary32 from
+    factors computed in binary32 and binary64, so a few codes on a rounding
+    boundary may differ)."""
+    say("q_proj end to end, 16384 x 4096 x 4096, k = 61, SR")
+    c = synth.CONFIGS[2]
+    X, _ = synth.anisotropic_fast(T, H, synth.FRAC_X, synth.gen_seed(2, "X"), device="cuda")
+    W, _ = synth.anisotropic_fast(H, H, synth.FRAC_W, synth.gen_seed(2, "W"), device="cuda")
+    D, _ = synth.anisotropic_fast(T, H, synth.FRAC_D, synth.gen_seed(2, "D"), device="cuda")
+    L = Layer(X, W, D, c["k"], c["s"], c["l_k"], "sr", seed=0)
+    L.decompose()
+    L.quantize(export=False)
+    Y = metis.gemm_fwd(L.q["X"], L.q["W"])
+    dX, dW = metis.gemm_bwd(L.q["D"], L.q["W"], L.q["X"])
+    metis.status_sync()
+    o = {n: _oracle_operand(to_np(M).astype(np.float64), L.ocfg, L.sample[n], L.tags[n], 0)
+         for n, M in L.mats().items()}
+    for n in ("X", "W", "D"):
+        fu = _flips(L.q[n].U.codes.cpu().numpy(), o[n]["uq"].codes)
+        fv = _flips(L.q[n].V.codes.cpu().numpy(), o[n]["vq"].codes)
+        say("  %s factor code flips U %.1e V %.1e" % (n, fu, fv))
+        assert fu <= E2E_FACTOR_FLIPS and fv <= E2E_FACTOR_FLIPS
+
+    def low_rank(n, rows=slice(None), cols=slice(None)):
+        return (o[n]["uh"][rows] * o[n]["s"]) @ o[n]["vh"][cols].T
+
+    def row_panels(n, r0s, ncols):
+        """M-hat rows (K = cols) of operand n on 16-row panels starting at r0s."""
+        out, flips = [], []
+        g = L.q[n].R_ax1.codes.cpu().numpy()
+        for r0 in r0s:
+            q1 = nvfp4.quantize(o[n]["mr"][r0:r0 + 16], 1, "sr", 0, o[n]["rt"], 0, amax=o[n]["amax"],
+                                origin=(r0, 0, ncols), draws="matrix")
+            flips.append(_flips(g[r0:r0 + 16], q1.codes))
+            out.append(nvfp4.dequantize(q1) + low_rank(n, slice(r0, r0 + 16)))
+        return np.concatenate(out), max(flips)
+
+    def col_band(n, c0, width, ncols):
+        """M-hat columns c0 .. c0 + width (K = rows) of operand n."""
+        q0 = nvfp4.quantize(o[n]["mr"][:, c0:c0 + width], 0, "sr", 0, o[n]["rt"], 0, amax=o[n]["amax"],
+                            origin=(0, c0, ncols), draws="matrix")
+        f = _flips(L.q[n].R_ax0.codes[c0:c0 + width].cpu().numpy(), q0.codes)
+        return nvfp4.dequantize(q0) + low_rank(n, cols=slice(c0, c0 + width)), f
+
+    def whole(n, axis):
+        q = nvfp4.quantize(o[n]["mr"], axis, "sr", 0, o[n]["rt"], 0, draws="matrix")
+        g = (L.q[n].R_ax0 if axis == 0 else L.q[n].R_ax1).codes.cpu().numpy()
+        return nvfp4.dequantize(q) + low_rank(n), _flips(g, q.codes)
+
+    r0s = (0, 16 * 311, 16 * 700, T - 16)
+    rows = np.concatenate([np.arange(r, r + 16) for r in r0s])
+    x1, fx1 = row_panels("X", r0s, H)
+    d1, fd1 = row_panels("D", r0s, H)
+    w0, fw0 = whole("W", 0)
+    w1, fw1 = whole("W", 1)
+    x0, fx0 = col_band("X", 16 * 37, 64, H)
+    d0, fd0 = col_band("D", 16 * 200, 64, H)
+    say("  residual code flips X %.1e/%.1e D %.1e/%.1e W %.1e/%.1e" % (fx1, fx0, fd1, fd0, fw1, fw0))
+    assert max(fx1, fx0, fd1, fd0, fw1, fw0) <= E2E_RESID_FLIPS
+    ey = rel_fro(Y[torch.from_numpy(rows).cuda()].cpu().double().numpy(), x1 @ w0)
+    edx = rel_fro(dX[torch.from_numpy(rows).cuda()].cpu().double().numpy(), d1 @ w1.T)
+    edw = rel_fro(dW[16 * 37:16 * 37 + 64, 16 * 200:16 * 200 + 64].cpu().double().numpy(), x0.T @ d0)
+    say("  sampled end-to-end rel Frobenius errors Y %.2e dX %.2e dW %.2e" % (ey, edx, edw))
+    assert max(ey, edx, edw) <= E2E_TOL
 
 
 # --------------------------------------------------------- decomposition --
