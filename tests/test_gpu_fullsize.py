@@ -139,74 +139,81 @@ def _flips(gpu_codes, oracle_codes):
     return float((gpu_codes != oracle_codes).mean())
 
 
-def test_q_proj_end_to_end_sampled_outputs():
-    """LLaMA-3-8B q_proj (X 16384 x 4096, W 4096 x 4096, D 16384 x 4096, k = 61,
-    l_k = 164, SR) through the whole HIP path (decompose, quantise, split GEMM
-    forward and backward) and the whole oracle pipeline on the same seeded
-    inputs.  Checked: flip rates of the residual codes on sampled row panels
-    (K = cols) and column bands (K = rows) of X and D and on all of W, and of
-    every factor code; Y and dX on 64 sampled rows and a 64 x 64 block of dW
-    within the end-to-end bar (both sides decide each code in binary32 from
-    factors computed in binary32 and binary64, so a few codes on a rounding
-    boundary may differ)."""
-    say("q_proj end to end, 16384 x 4096 x 4096, k = 61, SR")
+@pytest.mark.parametrize("name,config,l,m,n", [
+    ("LLaMA-3-8B q_proj", 2, T, H, H),
+    ("LLaMA-3-8B MLP gate projection", 3, T, H, F),
+])
+def test_projection_end_to_end_sampled_outputs(name, config, l, m, n):
+    """One linear layer (X l x m, W m x n, D l x n, k = 61, l_k = 164, SR) at
+    a refresh step, through the whole HIP path (decompose, quantise, split
+    GEMM forward and backward) and the whole oracle pipeline on the same
+    seeded inputs.  Checked: flip rates of every factor code and of the
+    residual codes on sampled row panels (K = cols) and column bands
+    (K = rows); a 64 x 64 block of each of Y, dX and dW within the
+    end-to-end bar (both sides decide each code in binary32 from factors
+    computed in binary32 and binary64, so a few codes on a rounding boundary
+    may differ)."""
+    say("%s end to end, l %d m %d n %d, k = 61, SR" % (name, l, m, n))
     c = synth.CONFIGS[2]
-    X, _ = synth.anisotropic_fast(T, H, synth.FRAC_X, synth.gen_seed(2, "X"), device="cuda")
-    W, _ = synth.anisotropic_fast(H, H, synth.FRAC_W, synth.gen_seed(2, "W"), device="cuda")
-    D, _ = synth.anisotropic_fast(T, H, synth.FRAC_D, synth.gen_seed(2, "D"), device="cuda")
+    X, _ = synth.anisotropic_fast(l, m, synth.FRAC_X, synth.gen_seed(config, "X"), device="cuda")
+    W, _ = synth.anisotropic_fast(m, n, synth.FRAC_W, synth.gen_seed(config, "W"), device="cuda")
+    D, _ = synth.anisotropic_fast(l, n, synth.FRAC_D, synth.gen_seed(config, "D"), device="cuda")
     L = Layer(X, W, D, c["k"], c["s"], c["l_k"], "sr", seed=0)
     L.decompose()
     L.quantize(export=False)
     Y = metis.gemm_fwd(L.q["X"], L.q["W"])
     dX, dW = metis.gemm_bwd(L.q["D"], L.q["W"], L.q["X"])
     metis.status_sync()
-    o = {n: _oracle_operand(to_np(M).astype(np.float64), L.ocfg, L.sample[n], L.tags[n], 0)
-         for n, M in L.mats().items()}
-    for n in ("X", "W", "D"):
-        fu = _flips(L.q[n].U.codes.cpu().numpy(), o[n]["uq"].codes)
-        fv = _flips(L.q[n].V.codes.cpu().numpy(), o[n]["vq"].codes)
-        say("  %s factor code flips U %.1e V %.1e" % (n, fu, fv))
+    r0s = (0, 16 * 311, 16 * 700, l - 16)
+    rows = torch.from_numpy(np.concatenate([np.arange(r, r + 16) for r in r0s])).cuda()
+    cm0, cn0 = 16 * 37, 16 * 200
+    Ys = Y[rows, cn0:cn0 + 64].cpu().double().numpy()
+    dXs = dX[rows, cm0:cm0 + 64].cpu().double().numpy()
+    dWs = dW[cm0:cm0 + 64, cn0:cn0 + 64].cpu().double().numpy()
+    del Y, dX, dW
+    o = {}
+    for nm, M in L.mats().items():
+        o[nm] = _oracle_operand(to_np(M).astype(np.float64), L.ocfg, L.sample[nm], L.tags[nm], 0)
+        fu = _flips(L.q[nm].U.codes.cpu().numpy(), o[nm]["uq"].codes)
+        fv = _flips(L.q[nm].V.codes.cpu().numpy(), o[nm]["vq"].codes)
+        say("  %s factor code flips U %.1e V %.1e" % (nm, fu, fv))
         assert fu <= E2E_FACTOR_FLIPS and fv <= E2E_FACTOR_FLIPS
 
-    def low_rank(n, rows=slice(None), cols=slice(None)):
-        return (o[n]["uh"][rows] * o[n]["s"]) @ o[n]["vh"][cols].T
+    def low_rank(nm, r=slice(None), cc=slice(None)):
+        return (o[nm]["uh"][r] * o[nm]["s"]) @ o[nm]["vh"][cc].T
 
-    def row_panels(n, r0s, ncols):
-        """M-hat rows (K = cols) of operand n on 16-row panels starting at r0s."""
-        out, flips = [], []
-        g = L.q[n].R_ax1.codes.cpu().numpy()
-        for r0 in r0s:
-            q1 = nvfp4.quantize(o[n]["mr"][r0:r0 + 16], 1, "sr", 0, o[n]["rt"], 0, amax=o[n]["amax"],
-                                origin=(r0, 0, ncols), draws="matrix")
-            flips.append(_flips(g[r0:r0 + 16], q1.codes))
-            out.append(nvfp4.dequantize(q1) + low_rank(n, slice(r0, r0 + 16)))
-        return np.concatenate(out), max(flips)
+    def row_block(nm, r0, nrows):
+        """M-hat rows r0 .. r0 + nrows of operand nm, quantised along its columns."""
+        cols = o[nm]["mr"].shape[1]
+        q1 = nvfp4.quantize(o[nm]["mr"][r0:r0 + nrows], 1, "sr", 0, o[nm]["rt"], 0, amax=o[nm]["amax"],
+                            origin=(r0, 0, cols), draws="matrix")
+        f = _flips(L.q[nm].R_ax1.codes[r0:r0 + nrows].cpu().numpy(), q1.codes)
+        return nvfp4.dequantize(q1) + low_rank(nm, slice(r0, r0 + nrows)), f
 
-    def col_band(n, c0, width, ncols):
-        """M-hat columns c0 .. c0 + width (K = rows) of operand n."""
-        q0 = nvfp4.quantize(o[n]["mr"][:, c0:c0 + width], 0, "sr", 0, o[n]["rt"], 0, amax=o[n]["amax"],
-                            origin=(0, c0, ncols), draws="matrix")
-        f = _flips(L.q[n].R_ax0.codes[c0:c0 + width].cpu().numpy(), q0.codes)
-        return nvfp4.dequantize(q0) + low_rank(n, cols=slice(c0, c0 + width)), f
+    def col_band(nm, c0, width):
+        """M-hat columns c0 .. c0 + width of operand nm, quantised along its rows."""
+        cols = o[nm]["mr"].shape[1]
+        q0 = nvfp4.quantize(o[nm]["mr"][:, c0:c0 + width], 0, "sr", 0, o[nm]["rt"], 0, amax=o[nm]["amax"],
+                            origin=(0, c0, cols), draws="matrix")
+        f = _flips(L.q[nm].R_ax0.codes[c0:c0 + width].cpu().numpy(), q0.codes)
+        return nvfp4.dequantize(q0) + low_rank(nm, cc=slice(c0, c0 + width)), f
 
-    def whole(n, axis):
-        q = nvfp4.quantize(o[n]["mr"], axis, "sr", 0, o[n]["rt"], 0, draws="matrix")
-        g = (L.q[n].R_ax0 if axis == 0 else L.q[n].R_ax1).codes.cpu().numpy()
-        return nvfp4.dequantize(q) + low_rank(n), _flips(g, q.codes)
+    def panels(nm):
+        parts = [row_block(nm, r0, 16) for r0 in r0s]
+        return np.concatenate([p for p, _ in parts]), max(f for _, f in parts)
 
-    r0s = (0, 16 * 311, 16 * 700, T - 16)
-    rows = np.concatenate([np.arange(r, r + 16) for r in r0s])
-    x1, fx1 = row_panels("X", r0s, H)
-    d1, fd1 = row_panels("D", r0s, H)
-    w0, fw0 = whole("W", 0)
-    w1, fw1 = whole("W", 1)
-    x0, fx0 = col_band("X", 16 * 37, 64, H)
-    d0, fd0 = col_band("D", 16 * 200, 64, H)
-    say("  residual code flips X %.1e/%.1e D %.1e/%.1e W %.1e/%.1e" % (fx1, fx0, fd1, fd0, fw1, fw0))
+    x1, fx1 = panels("X")
+    d1, fd1 = panels("D")
+    w1, fw1 = row_block("W", cm0, 64)
+    w0, fw0 = col_band("W", cn0, 64)
+    x0, fx0 = col_band("X", cm0, 64)
+    d0, fd0 = col_band("D", cn0, 64)
+    say("  residual code flips (K = cols / K = rows) X %.1e/%.1e W %.1e/%.1e D %.1e/%.1e"
+        % (fx1, fx0, fw1, fw0, fd1, fd0))
     assert max(fx1, fx0, fd1, fd0, fw1, fw0) <= E2E_RESID_FLIPS
-    ey = rel_fro(Y[torch.from_numpy(rows).cuda()].cpu().double().numpy(), x1 @ w0)
-    edx = rel_fro(dX[torch.from_numpy(rows).cuda()].cpu().double().numpy(), d1 @ w1.T)
-    edw = rel_fro(dW[16 * 37:16 * 37 + 64, 16 * 200:16 * 200 + 64].cpu().double().numpy(), x0.T @ d0)
+    ey = rel_fro(Ys, x1 @ w0)
+    edx = rel_fro(dXs, d1 @ w1.T)
+    edw = rel_fro(dWs, x0.T @ d0)
     say("  sampled end-to-end rel Frobenius errors Y %.2e dX %.2e dW %.2e" % (ey, edx, edw))
     assert max(ey, edx, edw) <= E2E_TOL
 
