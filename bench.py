@@ -763,21 +763,27 @@ def _captured(m, basis, best):
 
 
 # companion: run each operand's rediagonalisation on a second stream beside
-# its residual sweeps.  Measured: the q_proj step 3.61 -> 3.47 ms; the GPT-2
-# step, whose rank-12 Jacobi is short, 0.92 -> 0.95 ms (the fork and join
-# cost more than they hide), so it stays on one stream.
+# its residual sweeps.  weight_stream: prepare the weight on a stream of its
+# own beside X's preparation.  Measured (ms per step): q_proj 3.61 -> 3.47
+# with the companion, 3.28 / 3.51 against 3.47 / 3.48 with the weight stream
+# as well (no clear gain, not used); GPT-2 0.92 -> 0.95 with the companion
+# (its rank-12 Jacobi is short: the fork and join cost more than they hide),
+# 0.92 -> 0.85 with the weight stream.
 LAYER_CONFIGS = {
     # GPT-2 130M MLP up-projection: X 8192 x 768, W 768 x 3072, k = 12
-    "c1_gpt2_130m_mlp_up": dict(tokens=8192, n_in=768, n_out=3072, k=12, s=8, l_k=82, companion=False),
+    "c1_gpt2_130m_mlp_up": dict(tokens=8192, n_in=768, n_out=3072, k=12, s=8, l_k=82, companion=False,
+                                weight_stream=True),
     # LLaMA-3 8B q_proj: X 16384 x 4096, W 4096 x 4096, k = 61
-    "c2_llama3_8b_q_proj": dict(tokens=16384, n_in=4096, n_out=4096, k=61, s=8, l_k=164, companion=True),
+    "c2_llama3_8b_q_proj": dict(tokens=16384, n_in=4096, n_out=4096, k=61, s=8, l_k=164, companion=True,
+                                weight_stream=False),
 }
 
 
-def measure_layer(dev, name, steps=16, warmup=8, companion=None):
+def measure_layer(dev, name, steps=16, warmup=8, companion=None, weight_stream=None):
     """One split projection on its own (calls in data order on one stream;
     with ``companion`` each operand's rediagonalisation runs on a second
-    stream beside its residual sweeps, as metis_prepare_operand allows):
+    stream beside its residual sweeps, as metis_prepare_operand allows, and
+    with ``weight_stream`` the weight is prepared on a stream of its own):
     decompose + quantise X, W and D (both K orientations), the split GEMM
     forward and backward (dX, dW), the factors refreshed every 8 steps.
     Every step has its own inputs: W drifts, X and D turn their dominant
@@ -789,6 +795,8 @@ def measure_layer(dev, name, steps=16, warmup=8, companion=None):
     c = LAYER_CONFIGS[name]
     if companion is None:
         companion = c["companion"]
+    if weight_stream is None:
+        weight_stream = c.get("weight_stream", False)
     l, m, n, k = c["tokens"], c["n_in"], c["n_out"], c["k"]
     cfg = metis.make_config(k=k, s=c["s"], l_k=c["l_k"], refresh=REFRESH, rounding=metis.SR, seed=0)
     shapes = {"X": (l, m, synth.FRAC_X, True, metis.OPERAND_X), "W": (m, n, synth.FRAC_W, False, metis.OPERAND_W),
@@ -817,6 +825,9 @@ def measure_layer(dev, name, steps=16, warmup=8, companion=None):
                for r, cc, _, smp, _ in shapes.values())
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     side = torch.cuda.Stream(device=dev) if companion else None  # default priority
+    wst = torch.cuda.Stream(device=dev) if weight_stream else None
+    main = torch.cuda.current_stream(dev)
+    w_free = None
     Y = torch.empty(l, n, dtype=torch.float32, device=dev)
     dX = torch.empty(l, m, dtype=torch.float32, device=dev)
     dW = torch.empty(m, n, dtype=torch.float32, device=dev)
@@ -825,13 +836,33 @@ def measure_layer(dev, name, steps=16, warmup=8, companion=None):
     gwb = torch.empty(lib.metis_gemm_bwd_workspace(ctypes.byref(dc), ctypes.byref(wc), ctypes.byref(xc)),
                       dtype=torch.uint8, device=dev)
 
+    wws = torch.empty(need, dtype=torch.uint8, device=dev) if weight_stream else None
+
     def step(t):
+        nonlocal w_free
+        w_ready = None
+        if wst is not None:
+            # the weight is prepared on its own stream, beside X's preparation
+            # (after the previous step's last GEMM reading its codes)
+            if w_free is not None:
+                wst.wait_event(w_free)
+            with torch.cuda.stream(wst):
+                metis.prepare_operand(seqs["W"][t], cfg, False, metis.make_tag(9, metis.OPERAND_W), t, f["W"],
+                                      metis.AXIS0 | metis.AXIS1, out=q["W"], workspace=wws)
+                w_ready = torch.cuda.Event()
+                w_ready.record(wst)
         for op, (_, _, _, smp, kind) in shapes.items():
-            metis.prepare_operand(seqs[op][t], cfg, smp, metis.make_tag(9, kind), t, f[op],
-                                  metis.AXIS0 | metis.AXIS1, out=q[op], workspace=ws, side_stream=side)
+            if op == "W" and wst is not None:
+                main.wait_event(w_ready)
+            else:
+                metis.prepare_operand(seqs[op][t], cfg, smp, metis.make_tag(9, kind), t, f[op],
+                                      metis.AXIS0 | metis.AXIS1, out=q[op], workspace=ws, side_stream=side)
             if op == "W":
                 metis.gemm_fwd(q["X"], q["W"], Y=Y, workspace=gwf)
         metis.gemm_bwd(q["D"], q["W"], q["X"], dX=dX, dW=dW, workspace=gwb)
+        if wst is not None:
+            w_free = torch.cuda.Event()
+            w_free.record(main)
 
     for t in range(warmup):
         step(t)
@@ -881,7 +912,7 @@ def measure_layer(dev, name, steps=16, warmup=8, companion=None):
             "main_gemm": {"ms_per_step": round(g_ms, 4), "launches_per_step": len(g) / steps,
                           "roofline": {"bound": "mfma", "achieved": round(g_tf, 1), "peak": PEAK_F16_TFLOPS,
                                        "unit": "TFLOP/s", "frac": round(g_tf / PEAK_F16_TFLOPS, 4)}},
-            "rsvd_ms": rsvd, "streams": 2 if companion else 1}
+            "rsvd_ms": rsvd, "streams": 1 + int(bool(companion)) + int(bool(weight_stream))}
 
 
 def measure_training_loop(dev, steps=48, periods=(1, 8, 32), tokens=8192, lr=2e-5):
