@@ -644,6 +644,26 @@ def measure_mxfp4(m, X, W, t_last, nvfp4_gemm_ms, reps=10, sample_rows=256):
                     "no tensor scale, no spectral split; y_rel_fro_err_vs_exact rounds to nearest, _sr stochastically)"}
 
 
+def decompose_timed(M, cfg, sample, tag, t, f, workspace=None):
+    """metis_decompose on the current stream, timed with HIP events: (total
+    ms, sketch ms, projection + rediagonalisation ms), the last two from the
+    library's own event pairs (None where the call has no such part)."""
+    import torch
+    from spectral_split_quantized_amd import metis
+    metis.timing_enable(8)
+    metis.timing_kinds((1 << 4) | (1 << 5))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    metis.decompose(M, cfg, sample, tag, t, f, workspace=workspace)
+    b.record()
+    torch.cuda.synchronize()
+    parts = metis.timing_read(8)
+    metis.timing_enable(0)
+    metis.timing_kinds(-1)
+    pick = [[r[1] for r in parts if r[0] == kind] for kind in (4, 5)]
+    return (round(a.elapsed_time(b), 3),) + tuple(round(p[0], 3) if p else None for p in pick)
+
+
 def measure_c4(dev, copy_gbps):
     """The 1M x 4096 activation (4.3e9 elements, l_k = 10486): decompose at a
     refresh and at a cached step, and the residual quantisation in both
@@ -661,12 +681,9 @@ def measure_c4(dev, copy_gbps):
     q = metis.QOperand(rows, cols, k, metis.AXIS0 | metis.AXIS1, dev)
     res = {}
     for label, t in (("decompose_refresh_ms", 0), ("decompose_cached_ms", 1)):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        metis.decompose(M, cfg, True, tag, t, f)
-        b.record()
-        torch.cuda.synchronize()
-        res[label] = round(a.elapsed_time(b), 3)
+        res[label], sketch, proj = decompose_timed(M, cfg, True, tag, t, f)
+        if t == 0:
+            res["decompose_refresh_sketch_ms"], res["decompose_refresh_project_rediag_ms"] = sketch, proj
     t_q = _median_ms(lambda: metis.quantize(M, cfg, tag, 1, metis.AXIS0 | metis.AXIS1, factors=f, out=q), 5)
     metis.status_sync()
     # algorithmic bytes per element: M read twice (bf16), codes and scales of
@@ -897,12 +914,12 @@ def measure_layer(dev, name, steps=16, warmup=8, companion=None, weight_stream=N
         fo = metis.Factors(r, cc, k, dev)
         t0 = (nst // REFRESH) * REFRESH
         for label, t in (("refresh", t0), ("cached", t0 + 1)):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            metis.decompose(seqs[op][t % nst], cfg, smp, metis.make_tag(9, kind), t, fo, workspace=ws)
-            e1.record()
-            torch.cuda.synchronize()
-            rsvd["%s_%s" % (op, label)] = round(e0.elapsed_time(e1), 3)
+            total, sketch, proj = decompose_timed(seqs[op][t % nst], cfg, smp, metis.make_tag(9, kind), t, fo,
+                                                  workspace=ws)
+            rsvd["%s_%s" % (op, label)] = total
+            if label == "refresh":
+                rsvd["%s_refresh_sketch" % op] = sketch
+                rsvd["%s_refresh_project_rediag" % op] = proj
     metis.status_sync()
     del seqs
     torch.cuda.empty_cache()
@@ -1135,19 +1152,21 @@ def main():
                  "operand": "X_down residual %d x %d, both orientations, SR" % (xd.rows, xd.cols),
                  "ms": round(q_ms, 4)}
 
-    # rSVD timing at a refresh step and a cached step (outside the timed region)
+    # rSVD timing at a refresh step and at the cached step after it, on that
+    # step's own (drifted) input (outside the timed region); the refresh is
+    # also split into the sketch (row sample to V) and the projection with
+    # its rediagonalisation, from the library's own event pairs
     rsvd_ms = {}
     for name in ("W_gate", "X_gu", "D_gate"):
-        M = inputs[name][0]
         op = mlp.ops[name]
         f = metis.Factors(op.rows, op.cols, K_RANK, dev)
         for label, t in (("refresh", 64), ("cached", 65)):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            metis.decompose(M, mlp.cfg, op.sample, op.tag, t, f, workspace=mlp.ws[0])
-            b.record(stream)
-            torch.cuda.synchronize()
-            rsvd_ms["%s_%s" % (name, label)] = round(a.elapsed_time(b), 3)
+            M = inputs[name][(t - 64) % len(inputs[name])]
+            total, sketch, proj = decompose_timed(M, mlp.cfg, op.sample, op.tag, t, f, workspace=mlp.ws[0])
+            rsvd_ms["%s_%s" % (name, label)] = total
+            if label == "refresh":
+                rsvd_ms["%s_refresh_sketch" % name] = sketch
+                rsvd_ms["%s_refresh_project_rediag" % name] = proj
     metis.status_sync()
 
     extras = {}

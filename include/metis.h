@@ -306,8 +306,11 @@ metis_status metis_mxfp4_gemm(const uint8_t *a_codes, const uint8_t *a_scales, c
  * capacity pairs of HIP events (0 disables timing and releases them); while
  * enabled, each main split-GEMM kernel (kind 0; d = M, N, K, K-extension) and
  * each quantiser sweep (kind 1: amax pass, kind 2: quantise pass; d = rows,
- * cols, axes, K of the rank-k product) and each MXFP4 GEMM kernel (kind 3;
- * d = M, N, K, 0) is bracketed by events recorded on the launching stream,
+ * cols, axes, K of the rank-k product), each MXFP4 GEMM kernel (kind 3;
+ * d = M, N, K, 0), the sketch of a refresh step, from the row sample to V
+ * (kind 4; d = rows, cols, k + s, l_k), and metis_decompose's projection
+ * and rediagonalisation (kind 5; d = rows, cols, k, 1 on a refresh step)
+ * is bracketed by events recorded on the launching stream,
  * until the capacity is used up.  metis_timing_read waits
  * for the recorded events, writes up to max_records durations (ms) and
  * 5-tuples (kind, d0, d1, d2, d3), resets the record list and returns the

@@ -65,8 +65,10 @@ metis_status fail(metis_status st, const char* fmt, ...) {
 
 // When enabled, a pair of HIP events is recorded on the launching stream
 // around each main split-GEMM kernel (kind 0), each quantiser sweep (kind
-// 1: amax pass, kind 2: quantise pass) and each MXFP4 GEMM kernel (kind 3).  Events are created once, when timing
-// is enabled; recording them allocates nothing.
+// 1: amax pass, kind 2: quantise pass), each MXFP4 GEMM kernel (kind 3), the
+// sketch of a refresh step (kind 4) and metis_decompose's projection and
+// rediagonalisation (kind 5).  Events are created once, when timing is
+// enabled; recording them allocates nothing.
 struct TimingRec {
   hipEvent_t a, b;
   int64_t kind, d0, d1, d2, d3;
@@ -853,7 +855,7 @@ void launch_cholqr_pass(const double* g, int n, int64_t lr, int pass, double* ri
 
 // The sketch on refresh steps (V from the range of a row sample of M), then
 // the projection P = M V and its Gram matrix G = P^T P.
-metis_status decompose_project(DecompCall& c, hipStream_t st) {
+metis_status decompose_project(DecompCall& c, hipStream_t st, TimingRec** t_proj = nullptr) {
   metis_status s;
   const void* M = c.M;
   const int32_t dtype = c.dtype;
@@ -870,6 +872,7 @@ metis_status decompose_project(DecompCall& c, hipStream_t st) {
   const bool mfma_ok = dtype == METIS_BF16 && cols % 64 == 0 && ld % 8 == 0 && ((uintptr_t)M & 15) == 0;
 
   if (c.refresh) {
+    TimingRec* t_sk = timing_begin(st, 4, rows, cols, n, lr);
     const float scale = sample ? (float)sqrt((double)rows / (double)lr) : 1.0f;
     if (sample) {
       const uint32_t tag_s = tag_with_role(tag, kRoleSample);
@@ -928,9 +931,11 @@ metis_status decompose_project(DecompCall& c, hipStream_t st) {
     hipLaunchKernelGGL(sketch_v_kernel, dim3(grid1(cols * k, 256)), dim3(256), 0, st, w.b, cols, n, k,
                        w.z, w.theta, f->V);
     LAUNCH_CHECK();
+    timing_end(t_sk, st);
   }
 
   // projection and rediagonalisation (every step); V as three bf16 terms
+  if (t_proj) *t_proj = timing_begin(st, 5, rows, cols, k, c.refresh ? 1 : 0);
   if (mfma_ok) {
     // the split reduction into P happens inside the Gram kernel
     if ((s = mfma_product<3>((const uint16_t*)M, ld, rows, nullptr, f->V, cols, k, k, w.proj_nkb, w.proj_kbps,
@@ -1241,8 +1246,10 @@ metis_status metis_decompose(const void* M, int32_t dtype, int64_t rows, int64_t
     return fail(METIS_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, cv.used());
   if ((s = ensure_device_tables()) != METIS_OK) return s;
   hipStream_t st = (hipStream_t)stream;
-  if ((s = decompose_project(c, st)) != METIS_OK) return s;
+  TimingRec* t_proj = nullptr;
+  if ((s = decompose_project(c, st, &t_proj)) != METIS_OK) return s;
   if ((s = decompose_rediag(c, st)) != METIS_OK) return s;
+  timing_end(t_proj, st);
   if (c.refresh) f->refreshed_at = step;
   return METIS_OK;
 }
