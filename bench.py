@@ -713,6 +713,35 @@ def host_cpu_model():
     return None
 
 
+def oracle_c0_single_thread():
+    """The float64 oracle on the small single-layer workload (X 256 x 512, W
+    512 x 512 fp32, k = 8, s = 8, l_k = 64, RNE; decompose and quantise X and
+    W, forward GEMM) with its BLAS on one thread, in seconds (None if the
+    thread count cannot be limited)."""
+    import numpy as np
+    from oracle import philox, rsvd, split_gemm
+    from spectral_split_quantized_amd import synth
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        return None
+    X, W, _ = synth.layer_operands(0)
+    X = X.double().numpy()
+    W = W.double().numpy()
+    c = synth.CONFIGS[0]
+    cfg = rsvd.Config(k=c["k"], s=c["s"], l_k=c["l_k"], refresh=REFRESH, rounding="rne", seed=0)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        q = {}
+        for name, M, sample, oid in (("X", X, True, 2), ("W", W, False, 1)):
+            tag = philox.make_tag(0, oid, 0)
+            u, s, v, _ = rsvd.decompose(M, cfg, sample, tag, 0)
+            q[name] = split_gemm.quantize_operand(M, u.astype(np.float32), s.astype(np.float32),
+                                                  v.astype(np.float32), "rne", 0, tag, 0)
+        split_gemm.gemm_fwd(q["X"], q["W"])
+        return round(time.perf_counter() - t0, 3)
+
+
 def cpu_baseline(inputs_cpu, tokens, ncols):
     """Time the float64 oracle on a bounded sample of the gate projection:
     `tokens` rows of X and D and the first `ncols` output columns of W."""
@@ -722,15 +751,24 @@ def cpu_baseline(inputs_cpu, tokens, ncols):
     W = inputs_cpu["W"][:, :ncols].astype(np.float64)
     D = inputs_cpu["D"][:tokens, :ncols].astype(np.float64)
     cfg = rsvd.Config(k=K_RANK, s=OVERSAMPLE, l_k=L_K, refresh=REFRESH, rounding="sr", seed=0)
+    stages = {}
+
+    def timed(key, fn):
+        t = time.perf_counter()
+        out = fn()
+        stages[key] = round(time.perf_counter() - t, 3)
+        return out
+
     t0 = time.perf_counter()
     q = {}
     for name, M, sample, oid in (("X", X, True, 2), ("W", W, False, 1), ("D", D, True, 3)):
         tag = philox.make_tag(0, oid, 0)
-        u, s, v, _ = rsvd.decompose(M, cfg, sample, tag, 0)
-        q[name] = split_gemm.quantize_operand(M, u.astype(np.float32), s.astype(np.float32),
-                                              v.astype(np.float32), "sr", 0, tag, 0)
-    split_gemm.gemm_fwd(q["X"], q["W"])
-    split_gemm.gemm_bwd(q["D"], q["W"], q["X"])
+        u, s, v, _ = timed("decompose_" + name, lambda: rsvd.decompose(M, cfg, sample, tag, 0))
+        q[name] = timed("quantize_" + name,
+                        lambda: split_gemm.quantize_operand(M, u.astype(np.float32), s.astype(np.float32),
+                                                            v.astype(np.float32), "sr", 0, tag, 0))
+    timed("gemm_fwd", lambda: split_gemm.gemm_fwd(q["X"], q["W"]))
+    timed("gemm_bwd", lambda: split_gemm.gemm_bwd(q["D"], q["W"], q["X"]))
     dt = time.perf_counter() - t0
     l, h, n = tokens, X.shape[1], ncols
     flops = 0
@@ -751,8 +789,9 @@ def cpu_baseline(inputs_cpu, tokens, ncols):
     except Exception:  # pragma: no cover
         pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads or os.cpu_count(),
-            "kind": "oracle", "seconds": round(dt, 2), "cpu_model": host_cpu_model(),
+            "kind": "oracle", "seconds": round(dt, 2), "stage_seconds": stages, "cpu_model": host_cpu_model(),
             "host_logical_cpus": os.cpu_count(), "blas": blas,
+            "c0_single_thread_seconds": oracle_c0_single_thread(),
             "sample": "gate projection, first %d tokens x first %d output columns, refresh step "
                       "(decompose + quantise + fwd + bwd), float64 numpy oracle" % (tokens, ncols)}
 
@@ -1123,6 +1162,12 @@ def main():
                 "unit": "TFLOP/s", "frac": round(g_tflops / PEAK_F16_TFLOPS, 4), "traffic": traffic,
                 "kernel": "gemm_fp4_reg_kernel (main split GEMM)", "launches": len(g),
                 "avg_ms": round(g_ms / max(len(g), 1), 4)}
+    # per output shape: median, p10 and p90 of the launch times
+    by_shape = {}
+    for r in g:
+        by_shape.setdefault("%dx%dx%d" % (r[2], r[3], r[4]), []).append(r[1])
+    roofline["launch_ms_p10_p50_p90"] = {
+        k: [round(float(q), 4) for q in np.percentile(v, [10, 50, 90])] for k, v in sorted(by_shape.items())}
     # streaming: both quantiser sweeps (amax + quantise-on-store) of the
     # largest operand, X_down's residual in both orientations with SR, timed
     # alone after the timed steps (median of 5 calls)
