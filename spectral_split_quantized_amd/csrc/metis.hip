@@ -301,7 +301,7 @@ DecompWs carve_decompose(Carver& cv, int64_t rows, int64_t cols, int k, int n, i
   // takes enough slices of >= 16 rows for about 512 workgroups, since each
   // workgroup walks its rows one dependent batch of loads after another
   int64_t slices = lr >= 4096 ? 16 : (lr >= 512 ? 4 : 1);
-  const int64_t cblocks = (cols + 63) / 64, fill = (512 + cblocks - 1) / cblocks;
+  const int64_t cblocks = (cols + kSkbCols - 1) / kSkbCols, fill = (512 + cblocks - 1) / cblocks;
   const int64_t cap = lr / 16 > 1 ? lr / 16 : 1;
   if (slices < fill) slices = fill < cap ? fill : cap;
   if (slices < 1) slices = 1;
@@ -919,7 +919,7 @@ metis_status decompose_project(DecompCall& c, hipStream_t st, TimingRec** t_proj
       dst = t;
     }
     const float* Q = src;
-    hipLaunchKernelGGL(sketch_b_kernel, dim3(grid1(cols, 64), w.slices), dim3(256), 0, st, M, dtype, ld,
+    hipLaunchKernelGGL(sketch_b_kernel, dim3(grid1(cols, kSkbCols), w.slices), dim3(256), 0, st, M, dtype, ld,
                        w.idx, lr, cols, Q, n, w.rows_per_slice, w.bpart);
     LAUNCH_CHECK();
     hipLaunchKernelGGL(reduce_slices_kernel, dim3(grid1((int64_t)n * cols, 256)), dim3(256), 0, st,

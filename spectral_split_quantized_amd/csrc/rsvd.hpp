@@ -212,11 +212,37 @@ __global__ __launch_bounds__(256) void sketch_y_kernel(const void* __restrict__ 
 }
 
 // Partial B[j][c] over a slice of sample rows: part[slice][j][c] = the sum,
-// in sample-row order, of Q[s][j] M[idx[s]][c] (binary32 FMA).  64 columns
-// per block, one per lane.  Wave w owns the jw consecutive rows j of B from
-// w jw (jw: n / 4 rounded up to a multiple of 4), read from the Q tile in
-// LDS four at a time (all lanes read the same address), and the M values of
+// in sample-row order, of Q[s][j] M[idx[s]][c] (binary32 FMA).  kSkbCols
+// columns per block, four consecutive ones per lane, loaded as one 8-byte
+// (bf16) or 16-byte (fp32) vector when the rows allow it (vec), so each
+// lane keeps four times the bytes in flight and each Q value read from LDS
+// feeds four FMAs.  Wave w owns the jw consecutive rows j of B from w jw
+// (jw: n / 4 rounded up to a multiple of 4), read from the Q tile in LDS
+// four at a time (all lanes read the same address), and the M values of
 // eight sample rows are loaded before their FMAs.
+constexpr int kSkbCols = 256;
+__device__ __forceinline__ void skb_load4(const void* M, int dtype, int64_t base, int64_t c, int64_t cols, bool vec,
+                                          float (&v)[4]) {
+  if (vec) {
+    if (dtype == 0) {
+      const uint2 w = *(const uint2*)((const uint16_t*)M + base + c);
+      v[0] = __uint_as_float(w.x << 16);
+      v[1] = __uint_as_float(w.x & 0xFFFF0000u);
+      v[2] = __uint_as_float(w.y << 16);
+      v[3] = __uint_as_float(w.y & 0xFFFF0000u);
+    } else {
+      const float4 f = *(const float4*)((const float*)M + base + c);
+      v[0] = f.x;
+      v[1] = f.y;
+      v[2] = f.z;
+      v[3] = f.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = load_as_float(M, dtype, base + min(c + e, cols - 1));
+  }
+}
+
 __global__ __launch_bounds__(256) void sketch_b_kernel(const void* __restrict__ M, int dtype,
                                                        int64_t ld, const int32_t* __restrict__ idx,
                                                        int64_t ns, int64_t cols,
@@ -230,13 +256,17 @@ __global__ __launch_bounds__(256) void sketch_b_kernel(const void* __restrict__ 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int jw = ((n + 3) / 4 + 3) & ~3;
   const int j0 = wave * jw;
-  const int64_t c = (int64_t)blockIdx.x * 64 + lane;
-  const int64_t cl = c < cols ? c : cols - 1;  // a valid column for the loads
+  const int64_t c = (int64_t)blockIdx.x * kSkbCols + 4 * lane;  // first of this lane's four columns
+  // whole, aligned four-column vectors inside the row (dtype 0: bf16, 8 bytes)
+  const bool vec = (ld % 4 == 0) && (((uintptr_t)M & (dtype == 0 ? 7 : 15)) == 0) && c + 3 < cols;
+  const int64_t cl = c < cols ? c : cols - 1;
   const int64_t sb = (int64_t)blockIdx.y * rows_per_slice;
   const int64_t se = min(ns, sb + rows_per_slice);
-  float acc[kMaxN / 4];
+  float acc[4][kMaxN / 4];
 #pragma unroll
-  for (int t = 0; t < kMaxN / 4; ++t) acc[t] = 0.0f;
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int t = 0; t < kMaxN / 4; ++t) acc[e][t] = 0.0f;
   for (int64_t s0 = sb; s0 < se; s0 += 64) {
     __syncthreads();
     for (int e = tid; e < 64 * QP; e += 256) {
@@ -246,10 +276,16 @@ __global__ __launch_bounds__(256) void sketch_b_kernel(const void* __restrict__ 
     __syncthreads();
     const int lim = (int)min((int64_t)64, se - s0);
     for (int r0 = 0; r0 < lim; r0 += 8) {
-      float mv[8];
+      float mv[8][4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        mv[u] = (r0 + u < lim) ? load_as_float(M, dtype, (int64_t)idx[s0 + r0 + u] * ld + cl) : 0.0f;
+      for (int u = 0; u < 8; ++u) {
+        if (r0 + u < lim) {
+          skb_load4(M, dtype, (int64_t)idx[s0 + r0 + u] * ld, cl, cols, vec, mv[u]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mv[u][e] = 0.0f;
+        }
+      }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         if (r0 + u >= lim) break;
@@ -258,21 +294,28 @@ __global__ __launch_bounds__(256) void sketch_b_kernel(const void* __restrict__ 
         for (int t4 = 0; t4 < kMaxN / 16; ++t4) {
           if (4 * t4 < jw) {
             const float4 q = q4[t4];
-            acc[4 * t4 + 0] = fmaf(q.x, mv[u], acc[4 * t4 + 0]);
-            acc[4 * t4 + 1] = fmaf(q.y, mv[u], acc[4 * t4 + 1]);
-            acc[4 * t4 + 2] = fmaf(q.z, mv[u], acc[4 * t4 + 2]);
-            acc[4 * t4 + 3] = fmaf(q.w, mv[u], acc[4 * t4 + 3]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              acc[e][4 * t4 + 0] = fmaf(q.x, mv[u][e], acc[e][4 * t4 + 0]);
+              acc[e][4 * t4 + 1] = fmaf(q.y, mv[u][e], acc[e][4 * t4 + 1]);
+              acc[e][4 * t4 + 2] = fmaf(q.z, mv[u][e], acc[e][4 * t4 + 2]);
+              acc[e][4 * t4 + 3] = fmaf(q.w, mv[u][e], acc[e][4 * t4 + 3]);
+            }
           }
         }
       }
     }
   }
-  if (c < cols)
 #pragma unroll
-    for (int t = 0; t < kMaxN / 4; ++t) {
-      const int j = j0 + t;
-      if (t < jw && j < n) part[((int64_t)blockIdx.y * n + j) * cols + c] = acc[t];
+  for (int t = 0; t < kMaxN / 4; ++t) {
+    const int j = j0 + t;
+    if (t < jw && j < n) {
+      float* const prow = part + ((int64_t)blockIdx.y * n + j) * cols;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (c + e < cols) prow[c + e] = acc[e][t];
     }
+  }
 }
 
 // B[j][c] = scale * sum over slices (fixed order -> deterministic).
