@@ -1044,31 +1044,62 @@ __device__ __forceinline__ unsigned long long sign_key(float v, int64_t r) {
 
 // rs[p][j] = R[p][j] for j < k (D = I) or R[p][j] sign_j / sqrt(lambda_j)
 // (0 below the eigenvalue threshold), zero from k to the end of the last
-// 4-column group; ins[rl][p] = In[r0 + rl][p] (0 past row n).
+// 4-column group; ins[rl][p] = In[r0 + rl][p] (0 past row n).  Both tiles are
+// contiguous in memory (R is k x k, the 64 input rows are 64 k words); each
+// thread loads its share into registers before any LDS write, so a workgroup
+// pays one memory round trip per tile instead of one per element.
+// The workgroup is 256 threads.
 template <int NM, bool SCALE>
 __device__ __forceinline__ void rot_stage(double (*rs)[NM + 4], float (*ins)[NM + 1], const float* __restrict__ In,
                                           int64_t n, int64_t r0, int k, const double* __restrict__ R,
                                           const double* __restrict__ lam, const float* sg) {
+  constexpr int kRP = (NM * NM + 255) / 256;  // R entries per thread
+  constexpr int kIP = (64 * NM + 255) / 256;  // input entries per thread
   const int tid = threadIdx.x;
+  const int kk = k * k;
+  const int64_t avail = n - r0 < 64 ? n - r0 : 64;
+  const int ne = (int)avail * k;
+  const float* src = In + r0 * k;
+  double rv[kRP];
+  double lv[SCALE ? kRP : 1];
+  float iv[kIP];
+#pragma unroll
+  for (int i = 0; i < kRP; ++i) {
+    const int e = tid + 256 * i;
+    rv[i] = e < kk ? R[e] : 0.0;
+    if (SCALE) lv[i] = e < kk ? lam[e % k] : 0.0;
+  }
+#pragma unroll
+  for (int i = 0; i < kIP; ++i) {
+    const int e = tid + 256 * i;
+    iv[i] = e < ne ? src[e] : 0.0f;
+  }
   const double l0 = SCALE ? lam[0] : 0.0;
-  for (int e = tid; e < k * k; e += blockDim.x) {
-    const int p = e / k, j = e - p * k;
-    double v = R[e];
-    if (SCALE) {
-      const double lj = lam[j];
-      v = (l0 > 0.0 && lj > kEigZero * l0) ? v * (double)sg[j] / sqrt(lj) : 0.0;
+#pragma unroll
+  for (int i = 0; i < kRP; ++i) {
+    const int e = tid + 256 * i;
+    if (e < kk) {
+      const int p = e / k, j = e - p * k;
+      double v = rv[i];
+      if (SCALE) {
+        const double lj = lv[i];
+        v = (l0 > 0.0 && lj > kEigZero * l0) ? v * (double)sg[j] / sqrt(lj) : 0.0;
+      }
+      rs[p][j] = v;
     }
-    rs[p][j] = v;
   }
   const int kg = (k + 3) >> 2;
-  for (int e = tid; e < k * kg * 4; e += blockDim.x) {
+  for (int e = tid; e < k * kg * 4; e += 256) {
     const int p = e / (kg * 4), j = e - p * kg * 4;
     if (j >= k) rs[p][j] = 0.0;
   }
-  for (int e = tid; e < 64 * k; e += blockDim.x) {
-    const int rl = e / k, p = e - rl * k;
-    const int64_t r = r0 + rl;
-    ins[rl][p] = r < n ? In[r * k + p] : 0.0f;
+#pragma unroll
+  for (int i = 0; i < kIP; ++i) {
+    const int e = tid + 256 * i;
+    if (e < 64 * k) {
+      const int rl = e / k, p = e - rl * k;
+      ins[rl][p] = iv[i];
+    }
   }
 }
 
@@ -1179,7 +1210,18 @@ __global__ __launch_bounds__(256) void rot_u_kernel(const float* __restrict__ P,
     const int nloc = (int)(r1 - r0) * k;
     const float* src = Vn + r0 * k;
     float* dst = V + r0 * k;
-    for (int e = tid; e < nloc; e += 256) dst[e] = src[e] * sg[e % k];
+    constexpr int kIP = (64 * NM + 255) / 256;
+    float vv[kIP];
+#pragma unroll
+    for (int i = 0; i < kIP; ++i) {
+      const int e = tid + 256 * i;
+      vv[i] = e < nloc ? src[e] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < kIP; ++i) {
+      const int e = tid + 256 * i;
+      if (e < nloc) dst[e] = vv[i] * sg[e % k];
+    }
     return;
   }
   const int64_t r0 = (int64_t)blockIdx.x * 64;
