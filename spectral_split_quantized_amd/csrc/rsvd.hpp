@@ -475,15 +475,28 @@ __global__ __launch_bounds__(256) void gram_rows_kernel(const float* __restrict_
 
 // G[e] = sum of the blocks' partials, in a fixed order: 64 entries per
 // workgroup, wave q adds the partials b = q, q + 4, ... in order, then the
-// four sums are added pairwise.
+// four sums are added pairwise.  A lane fetches 32 of its partials before
+// adding them (the additions keep their order), so a wave pays one memory
+// round trip per 32 partials rather than one per partial.
 __global__ __launch_bounds__(256) void reduce_gram_kernel(const double* __restrict__ part, int blocks, int nn,
                                                           double* __restrict__ G) {
+  constexpr int kBatch = 32;
   __shared__ double red[4][64];
   const int el = threadIdx.x & 63, q = threadIdx.x >> 6;
   const int e = blockIdx.x * 64 + el;
   double s = 0.0;
   if (e < nn)
-    for (int b = q; b < blocks; b += 4) s += part[(int64_t)b * nn + e];
+    for (int b0 = q; b0 < blocks; b0 += 4 * kBatch) {
+      double v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int b = b0 + 4 * u;
+        v[u] = b < blocks ? part[(int64_t)b * nn + e] : 0.0;
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (b0 + 4 * u < blocks) s += v[u];
+    }
   red[q][el] = s;
   __syncthreads();
   if (q == 0 && e < nn) G[e] = (red[0][el] + red[1][el]) + (red[2][el] + red[3][el]);
