@@ -410,22 +410,39 @@ __global__ __launch_bounds__(256) void gram_rows_kernel(const float* __restrict_
 #pragma unroll
     for (int v = 0; v < T; ++v) acc[u][v] = 0.0;
   float val[PER];
+  // The split loop is outermost so that a thread's PER loads of one split
+  // (two splits per iteration) are in flight together; each element still
+  // adds its splits in order from zero.
   auto fetch = [&](int64_t r0) {
+    int64_t off[PER];
+    bool ok[PER];
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int e = tid + 256 * u;
-      float a = 0.0f;
-      if (e < 32 * n) {
+      const int r = e / n, j = e - r * n;
+      ok[u] = e < 32 * n && r0 + r < re;
+      off[u] = ok[u] ? (r0 + r) * pw + j : 0;
+      val[u] = 0.0f;
+    }
+    const int64_t sstride = nr * pw;
+#pragma unroll 2
+    for (int64_t sp = 0; sp < splits; ++sp) {
+      const float* src = part + sp * sstride;
+      float x[PER];
+#pragma unroll
+      for (int u = 0; u < PER; ++u) x[u] = src[off[u]];  // off = 0 (in bounds) where !ok
+#pragma unroll
+      for (int u = 0; u < PER; ++u)
+        if (ok[u]) val[u] += x[u];
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      if (ok[u]) {
+        const int e = tid + 256 * u;
         const int r = e / n, j = e - r * n;
-        if (r0 + r < re) {
-          const float* src = part + (r0 + r) * pw + j;
-#pragma unroll 4
-          for (int64_t sp = 0; sp < splits; ++sp) a += src[sp * nr * pw];
-          a = a * scale;
-          P[(r0 + r) * n + j] = a;
-        }
+        val[u] = val[u] * scale;
+        P[(r0 + r) * n + j] = val[u];
       }
-      val[u] = a;
     }
   };
   auto stash = [&](int b) {
