@@ -82,9 +82,37 @@ inline int64_t resid_prep_threads(int64_t rows, int64_t cols, int kp) {
   return (((rows + 31) & ~(int64_t)31) + ((cols + 63) & ~(int64_t)63)) * (kp / 8);
 }
 
+// A thread's eight factor entries (and the matching S entries) are loaded
+// before the scale is formed, from clamped in-bounds indices, so the loads
+// overlap each other and the Gram-diagonal read; entries outside the factor
+// are then set to zero.
 __global__ __launch_bounds__(256) void resid_prep_kernel(ResidPrep p) {
   __shared__ float pre_s;
   const int tid = threadIdx.x;
+  const int ng = p.kp >> 3, kc = 3 * p.kp;
+  const int64_t per_rb = 32 * (int64_t)ng;  // threads per 32 padded rows
+  const int64_t nu = ((p.rows + 31) >> 5) * per_rb;
+  const int64_t nv = ((p.cols + 63) >> 6) * 2 * per_rb;
+  const int64_t id = (int64_t)blockIdx.x * 256 + tid;
+  const bool live = id < nu + nv;
+  const bool is_u = id < nu;
+  const int64_t lid = is_u ? id : id - nu;
+  const int64_t rb = live ? lid / per_rb : 0;  // per_rb > 0 when any thread is live
+  const int rem = (int)(lid - rb * per_rb);
+  const int j0 = 8 * (rem >> 5);
+  const int64_t r = rb * 32 + (rem & 31);
+  const int64_t n = is_u ? p.rows : p.cols;
+  const float* F = is_u ? p.U : p.V;
+  float fv[8], sv[8];
+  if (live) {
+    const int64_t rc = r < n ? r : n - 1;  // n >= 1 for a live thread
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int jc = j0 + t < p.k ? j0 + t : p.k - 1;  // k >= 1 when kp > 0
+      fv[t] = F[rc * p.k + jc];
+      sv[t] = (is_u && p.S) ? p.S[jc] : 1.0f;
+    }
+  }
   if (tid < 64) {
     // max_j (float) sqrt(G_jj) = (float) sqrt(max_j G_jj): both are monotone
     float s0 = 0.0f;
@@ -104,26 +132,14 @@ __global__ __launch_bounds__(256) void resid_prep_kernel(ResidPrep p) {
   if (blockIdx.x == 0)
     for (int i = tid; i < p.nzero; i += 256) p.zero[i] = 0u;
   __syncthreads();
-  const int ng = p.kp >> 3, kc = 3 * p.kp;
-  const int64_t per_rb = 32 * (int64_t)ng;  // threads per 32 padded rows
-  const int64_t nu = ((p.rows + 31) >> 5) * per_rb;
-  const int64_t nv = ((p.cols + 63) >> 6) * 2 * per_rb;
-  const int64_t id = (int64_t)blockIdx.x * 256 + tid;
-  if (id >= nu + nv) return;
-  const bool is_u = id < nu;
-  const int64_t lid = is_u ? id : id - nu;
-  const int64_t rb = lid / per_rb;
-  const int rem = (int)(lid - rb * per_rb);
-  const int j0 = 8 * (rem >> 5);
-  const int64_t r = rb * 32 + (rem & 31);
+  if (!live) return;
   half8_t h, l;
   if (is_u) {
     const float pre = pre_s;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const int j = j0 + t;
       float x = 0.0f;
-      if (j < p.k && r < p.rows) x = __fmul_rn(__fmul_rn(p.U[r * p.k + j], p.S ? p.S[j] : 1.0f), pre);
+      if (j0 + t < p.k && r < p.rows) x = __fmul_rn(__fmul_rn(fv[t], sv[t]), pre);
       h[t] = (_Float16)x;
       l[t] = (_Float16)__fsub_rn(x, (float)h[t]);
     }
@@ -133,9 +149,8 @@ __global__ __launch_bounds__(256) void resid_prep_kernel(ResidPrep p) {
   } else {
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const int j = j0 + t;
       float v = 0.0f;
-      if (j < p.k && r < p.cols) v = __fmul_rn(p.V[r * p.k + j], kVPre);
+      if (j0 + t < p.k && r < p.cols) v = __fmul_rn(fv[t], kVPre);
       h[t] = (_Float16)v;
       l[t] = (_Float16)__fsub_rn(v, (float)h[t]);
     }
